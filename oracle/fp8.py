@@ -1,0 +1,78 @@
+"""Per-tensor e4m3 quantization and the ReLU^2 MLP with e4m3 forward GEMMs (oracle; test
+infrastructure only).
+
+Follows modded-nanogpt ``gpt.py``:
+
+* exact per-tensor scale (``_quantize_mlp_weights_and_scales``, exact-scale calls): the scale
+  is the tensor's absolute maximum, clamped below at 1e-12, divided by the e4m3 maximum 448.
+  The page forms it in the weights' bf16; here it is formed in float32 (the absolute maximum
+  of a bf16 tensor is exact in float32, so the scale is amax/448 rounded once). The quantized
+  value of v is e4m3(v / scale) with the division in float32;
+* delayed scale (``_refresh_delayed_scale``): a = nan_to_num(amax) clamped above at 1e12;
+  new = max(a * gain, floor); a slot whose a is 0 keeps its previous scale. For the ReLU^2
+  output the gain is FP8_POST_HEADROOM / 448 = 1.03/448 and the floor 1e-6. The page does this
+  in float32 tensors; so does this function;
+* the forward of ``ReLUSqrdMLP`` with fp8 arguments: both forward GEMMs take e4m3 operands with
+  per-tensor dequant scales, and relu(pre)^2 is quantized with the delayed post scale before the
+  down projection. The backward runs on the dequantized operands.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode
+from .mlp import relu_sq, relu_sq_backward
+
+_F32 = np.float32
+
+
+def per_tensor_scale(v) -> np.float32:
+    """max(amax(|v|), 1e-12) / 448 in float32."""
+    amax = _F32(np.max(np.abs(np.asarray(v, dtype=np.float32)))) if np.size(v) else _F32(0.0)
+    return _F32(max(amax, _F32(1e-12)) / _F32(E4M3_MAX))
+
+
+def quantize_per_tensor(v, scale=None):
+    """(codes, scale): codes = e4m3(fp32(v) / scale) with the scale of ``per_tensor_scale``
+    unless one is given."""
+    v32 = np.asarray(v, dtype=np.float32)
+    s = per_tensor_scale(v32) if scale is None else _F32(scale)
+    return e4m3_encode(v32 / s), s
+
+
+def dequantize(codes, scale) -> np.ndarray:
+    """scale * value(codes), in float64."""
+    return e4m3_decode(codes) * np.float64(scale)
+
+
+def next_delayed_scale(amax, prev_scale, gain, floor) -> np.float32:
+    """One slot of ``_refresh_delayed_scale``, in float32."""
+    a = _F32(np.nan_to_num(_F32(amax), nan=0.0, posinf=0.0, neginf=0.0))
+    a = min(a, _F32(1e12))
+    new = max(_F32(a * _F32(gain)), _F32(floor))
+    return _F32(new) if a > 0 else _F32(prev_scale)
+
+
+def relu_sq_fp8_forward(x_q, s_x, w1_q, s_w1, w2_q, s_w2, s_post=None, down_mult=1.0):
+    """ReLU^2 MLP forward on e4m3 operands: pre = (s_x x_q)(s_w1 W1_q)^T, post = relu(pre)^2,
+    out = down_mult * post_hat (s_w2 W2_q)^T, where post_hat = s_post * e4m3(fp32(post)/s_post)
+    when a post scale is given and post itself otherwise. Returns dict(pre, post, out,
+    post_amax)."""
+    xh = dequantize(x_q, s_x)
+    w1h = dequantize(w1_q, s_w1)
+    w2h = dequantize(w2_q, s_w2)
+    pre = xh @ w1h.T
+    post = relu_sq(pre)
+    if s_post is None:
+        post_used = post
+    else:
+        post_used = dequantize(e4m3_encode(post.astype(np.float32) / _F32(s_post)), s_post)
+    out = down_mult * (post_used @ w2h.T)
+    return {"pre": pre, "post": post, "out": out, "post_amax": float(np.max(post)) if post.size else 0.0}
+
+
+def relu_sq_fp8_backward(dout, x_q, s_x, w1_q, s_w1, w2_q, s_w2, down_mult=1.0):
+    """Backward of the fp8-forward ReLU^2 MLP: the plain backward applied to the dequantized
+    operands s_x x_q, s_w1 W1_q, s_w2 W2_q."""
+    return relu_sq_backward(dout, dequantize(x_q, s_x), dequantize(w1_q, s_w1),
+                            dequantize(w2_q, s_w2), down_mult)
