@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Throughput of one fused SwiGLU MLP training step (forward + backward) on one MI355X.
+
+A step is ``mlp_fwd`` (training: g|u saved) followed by ``mlp_bwd`` (dx, dW_gate, dW_up,
+dW_down) of the LLaMA-shaped MLP: x [2, 1024, 4096] (M = 2048 tokens), W_gate/W_up
+[11008, 4096], W_down [4096, 11008], bf16 storage, fp32 accumulation. Inputs are synthetic
+(``workloads.py``) and resident in HBM before timing starts.
+
+Prints one JSON line: TFLOP/s on the model FLOP count 18*M*d*H (2*M*N*K per GEMM), the
+fraction of the bf16 MFMA peak, the roofline of the slowest kernel stage (timed with HIP events
+on the library's stream inside the timed region), and the float64 oracle's throughput on a
+bounded sample on the host CPU.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+METRIC = "fused SwiGLU MLP fwd+bwd TFLOP/s and % bf16 MFMA peak, 4096×11008, 2048 tok"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (the library records them on its stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+def stage_flops(w) -> dict:
+    M, D, H, O = w.M, w.d_in, w.hidden, w.d_out
+    P = 2 * H if w.gated else H
+    return {
+        "up": 2.0 * M * D * P, "down": 2.0 * M * H * O, "dact": 2.0 * M * O * H,
+        "dw_down": 2.0 * O * H * M, "dx": 2.0 * M * P * D, "dw_up": 2.0 * P * D * M,
+        "recompute": 2.0 * M * D * P,
+    }
+
+
+def cpu_baseline(w, tensors, rows: int) -> dict:
+    """The float64 oracle (as it stands) on the first `rows` tokens of the workload, all of d
+    and H: forward + backward, timed on this host's cores."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    f64 = lambda t: t[:rows].to(torch.float64).numpy() if t.shape[0] == w.M else t.to(torch.float64).numpy()  # noqa: E731
+    a = {k: f64(v) for k, v in tensors.items()}
+    t0 = time.perf_counter()
+    if w.gated:
+        oracle.gated_forward(a["x"], a["w_gate"], a["w_up"], a["w_down"], w.gate_mult, w.down_mult)
+        oracle.gated_backward(a["dout"], a["x"], a["w_gate"], a["w_up"], a["w_down"], w.gate_mult, w.down_mult)
+    else:
+        oracle.relu_sq_forward(a["x"], a["w1"], a["w2"], w.down_mult)
+        oracle.relu_sq_backward(a["dout"], a["x"], a["w1"], a["w2"], w.down_mult)
+    secs = time.perf_counter() - t0
+    sample = w.replace(batch=(rows,))
+    threads = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
+    return {"value": round(sample.model_flops() / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(secs, 3),
+            "sample": f"first {rows} of {w.M} tokens, full d={w.d_in} H={w.hidden}: float64 numpy forward + "
+                      f"backward ({sample.model_flops() / 1e9:.1f} GFLOP on the model count)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="tokens in the oracle's CPU sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this engine is single-GPU "
+              "and has no multi-GPU path to time.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_mlp_gemms_amd as gm
+    from gated_mlp_gemms_amd.runner import runner_for
+    from workloads import HEADLINE, WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    log(f"[bench] workload {w.name}: building inputs")
+    tensors = make_inputs(w)
+    r = runner_for(w, tensors)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        if w.fp8_fwd:
+            r.quantize()
+            r.forward()
+            r.refresh_post_scale()
+            r.backward()
+        else:
+            r.step()
+        r.reset_grads()
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    stages = ["up", "down", "dact", "dw_down", "dx", "dw_up"] + (["recompute"] if w.recompute else [])
+    stage_id = {n: gm._lib.STAGES.index(n) for n in stages}
+    pairs = [[(ev.create(), ev.create()) for _ in stages] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        for n, (b, e) in zip(stages, pairs[i]):
+            gm._lib.check(gm.lib().mlp_time_stage_once(stage_id[n], b, e), "mlp_time_stage_once")
+        r.step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / args.steps
+    flops = w.model_flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    sf = stage_flops(w)
+    stage_us, stage_tf = {}, {}
+    for j, n in enumerate(stages):
+        us = 1e3 * sum(ev.elapsed_ms(*pairs[i][j]) for i in range(args.steps)) / args.steps
+        stage_us[n] = round(us, 2)
+        stage_tf[n] = round(sf[n] / (us * 1e-6) / 1e12, 1)
+    for row in pairs:
+        for b, e in row:
+            ev.destroy(b)
+            ev.destroy(e)
+    dom = max(stage_us, key=stage_us.get)
+    peak = PEAK_BF16_TFLOPS
+    roof = {"bound": "mfma", "achieved": stage_tf[dom], "peak": peak, "unit": "TFLOP/s",
+            "frac": round(stage_tf[dom] / peak, 4), "traffic": None, "kernel_stage": dom,
+            "flop_per_launch": sf[dom], "avg_launch_us": stage_us[dom]}
+    log(f"[bench] {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of bf16 peak); "
+        f"stages us {stage_us}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle on {args.cpu_rows} tokens")
+        cpu = cpu_baseline(w, tensors, args.cpu_rows)
+        log(f"[bench] oracle {cpu['seconds']} s, {cpu['value']} TFLOP/s on {cpu['cores']} threads")
+
+    dtype = "fp8-e4m3 fwd / bf16 bwd" if w.fp8_fwd else w.dtype
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "d_in": w.d_in, "hidden": w.hidden, "d_out": w.d_out,
+                   "act": w.act, "gate_mult": w.gate_mult, "down_mult": w.down_mult,
+                   "recompute": w.recompute, "grad_accum": w.grad_accum,
+                   "step": "mlp_fwd (training) + mlp_bwd (dx, all weight grads)",
+                   "model_flop_per_step": flops, "pct_of_bf16_peak": round(100 * tflops / peak, 2),
+                   "wall_s_timed": round(wall, 3)},
+        "stages_us": stage_us, "stages_tflops": stage_tf,
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,104 @@
+"""Fused transformer-MLP forward/backward for AMD MI355X (gfx950), behind the C ABI of
+``include/mlp.h``.
+
+The functions below carry the C entry points' names and only marshal arguments: torch tensors
+become device pointers, the current HIP stream is passed along, and a non-OK status raises
+``MlpError``. Every step of the MLP runs in the library's HIP kernels; there is no other path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from ._lib import (  # noqa: F401
+    LIB_PATH, MLP_ACT_RELU_SQ, MLP_ACT_SWIGLU, MLP_BF16, MLP_F32, MLP_GATE_INSIDE, MLP_GATE_OUTSIDE,
+    MLP_PHASE_BWD, MLP_PHASE_FWD, MLP_PHASE_FWD_INFER, MlpDesc, MlpError, MlpFp8, check, lib,
+)
+
+_ACTS = {"swiglu": MLP_ACT_SWIGLU, "relu_sq": MLP_ACT_RELU_SQ}
+_DTYPES = {torch.float32: MLP_F32, torch.bfloat16: MLP_BF16, "f32": MLP_F32, "bf16": MLP_BF16}
+_MODES = {"outside": MLP_GATE_OUTSIDE, "inside": MLP_GATE_INSIDE}
+_PHASES = {"fwd": MLP_PHASE_FWD, "fwd_infer": MLP_PHASE_FWD_INFER, "bwd": MLP_PHASE_BWD}
+
+
+def make_desc(M, d_in, hidden, d_out=None, act="swiglu", dtype=torch.bfloat16, gate_mult=1.0,
+              down_mult=1.0, gate_mode="outside", recompute=False, fp8_fwd=False) -> MlpDesc:
+    return MlpDesc(int(M), int(d_in), int(hidden), int(d_in if d_out is None else d_out), _ACTS[act],
+                   _DTYPES[dtype], float(gate_mult), float(down_mult), _MODES[gate_mode], int(bool(recompute)),
+                   int(bool(fp8_fwd)), 0)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_fp8(x_q, w1_q, w2_q, s_x, s_w1, s_w2, s_post=None, post_amax=None) -> MlpFp8:
+    return MlpFp8(*[_ptr(t) for t in (x_q, w1_q, w2_q, s_x, s_w1, s_w2, s_post, post_amax)])
+
+
+def workspace_bytes(desc: MlpDesc, phase: str) -> int:
+    n = lib().mlp_workspace_bytes(C.byref(desc), _PHASES[phase])
+    if n == 0:
+        raise MlpError(1, "mlp_workspace_bytes")
+    return int(n)
+
+
+def _workspace(desc, phase, workspace, device):
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    n = workspace_bytes(desc, phase)
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def mlp_fwd(desc, x, w_gate, w_up, w_down, out, saved_preact=None, fp8=None, workspace=None, stream=None):
+    ws, nws = _workspace(desc, "fwd", workspace, out.device)
+    st = lib().mlp_fwd(C.byref(desc), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out),
+                       _ptr(saved_preact), C.byref(fp8) if fp8 is not None else None, _ptr(ws), nws,
+                       _stream(stream))
+    check(st, "mlp_fwd")
+    return out
+
+
+def mlp_fwd_infer(desc, x, w_gate, w_up, w_down, out, fp8=None, workspace=None, stream=None):
+    ws, nws = _workspace(desc, "fwd_infer", workspace, out.device)
+    st = lib().mlp_fwd_infer(C.byref(desc), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out),
+                             C.byref(fp8) if fp8 is not None else None, _ptr(ws), nws, _stream(stream))
+    check(st, "mlp_fwd_infer")
+    return out
+
+
+def mlp_bwd(desc, dout, x, w_gate, w_up, w_down, saved_preact=None, dpreact=None, dx=None, dw_gate=None,
+            dw_up=None, dw_down=None, grad_accum=False, fp8=None, workspace=None, stream=None):
+    ws, nws = _workspace(desc, "bwd", workspace, dout.device)
+    st = lib().mlp_bwd(C.byref(desc), _ptr(dout), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                       _ptr(saved_preact), _ptr(dpreact), _ptr(dx), _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down),
+                       int(bool(grad_accum)), C.byref(fp8) if fp8 is not None else None, _ptr(ws), nws,
+                       _stream(stream))
+    check(st, "mlp_bwd")
+
+
+def mlp_quantize_e4m3(src, dst, scale, workspace=None, stream=None):
+    """Per-tensor e4m3 quantization of ``src`` (f32/bf16) into ``dst`` (uint8 or float8_e4m3fn)
+    and the fp32 device scalar ``scale``."""
+    if workspace is None:
+        workspace = torch.empty(int(lib().mlp_quantize_workspace_bytes()), dtype=torch.uint8, device=src.device)
+    st = lib().mlp_quantize_e4m3(_ptr(src), _DTYPES[src.dtype], src.numel(), _ptr(dst), _ptr(scale),
+                                 _ptr(workspace), workspace.numel(), _stream(stream))
+    check(st, "mlp_quantize_e4m3")
+
+
+def mlp_fp8_next_scale(amax: float, prev_scale: float, gain: float, floor: float) -> float:
+    return float(lib().mlp_fp8_next_scale(amax, prev_scale, gain, floor))

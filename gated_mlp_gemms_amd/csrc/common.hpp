@@ -1,0 +1,111 @@
+// Device-side helpers shared by every kernel of the MLP engine (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gmlp {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct e4m3 { uint8_t bits; };   // OCP FP8 E4M3 storage
+
+constexpr int kThreads = 256;    // 4 wave64 per workgroup
+constexpr int kWave = 64;
+
+template <typename T> struct ElemTraits;
+template <> struct ElemTraits<float> { static constexpr int bytes = 4; };
+template <> struct ElemTraits<bf16>  { static constexpr int bytes = 2; };
+template <> struct ElemTraits<e4m3>  { static constexpr int bytes = 1; };
+
+// ---- conversions -------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// fp32 -> OCP E4M3 code: nearest, ties to even mantissa, |v| >= 448 saturates to +-448,
+// NaN -> NaN code. Every step below is exact in fp32 except the final rint (the rounding).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __builtin_fabsf(v);
+  if (a != a) return sign | 0x7fu;
+  if (a >= 448.0f) return sign | 0x7eu;
+  if (a < 0.015625f) {                                  // below 2^-6: subnormal codes 0..8
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);  // a * 2^9 is exact
+  }
+  const int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;   // -6 .. 8
+  const float m = a * __uint_as_float((uint32_t)(127 - e) << 23);  // in [1, 2), exact
+  uint32_t mi = (uint32_t)__builtin_rintf((m - 1.0f) * 8.0f);      // 0..8
+  int ee = e + 7;
+  if (mi == 8u) { mi = 0u; ee += 1; }
+  return sign | ((uint32_t)ee << 3) | mi;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t s = c & 0x80u, e = (c >> 3) & 0xfu, m = c & 7u;
+  float mag;
+  if (e == 0) mag = (float)m * 0.001953125f;                        // m * 2^-9
+  else mag = __uint_as_float(((e + 120u) << 23) | (m << 20));       // 2^(e-7) * (1 + m/8)
+  if (e == 15u && m == 7u) mag = __builtin_nanf("");
+  return s ? -mag : mag;
+}
+
+// ---- activations (fp32) -------------------------------------------------------------------
+
+__device__ __forceinline__ float sigmoidf_(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+// ---- LDS tile geometry -------------------------------------------------------------------
+// Every operand tile in LDS is [rows][128 bytes]: the K extent of one pipeline stage is
+// 128 bytes of the element type (64 bf16, 32 fp32, 128 e4m3), split in 8 chunks of 16 bytes.
+// Chunk c of row r is stored at chunk slot c ^ swz(r); the XOR spreads the 16-byte reads of
+// 16 consecutive rows over distinct bank groups.
+__device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * 128 + ((chunk ^ lds_swz(row)) << 4);
+}
+
+// ---- tile scheduling ----------------------------------------------------------------------
+// Workgroups are handed to the 8 XCDs round robin (block b on XCD b % 8). Remap the launch
+// index so that each XCD works through one contiguous range of the logical tile order, which
+// keeps the tiles sharing operands in the same L2.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  constexpr int kXcd = 8;
+  const int q = total / kXcd, r = total % kXcd;
+  const int x = b % kXcd, i = b / kXcd;
+  return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// Grouped raster: tiles go column-major inside bands of `group_m` tile rows, so consecutive
+// tiles reuse the same B columns and a band of A rows.
+__device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n, int group_m,
+                                             int& tm, int& tn) {
+  const int per_group = group_m * tiles_n;
+  const int g = t / per_group;
+  const int first_m = g * group_m;
+  const int gsize = min(tiles_m - first_m, group_m);
+  const int in_g = t - g * per_group;
+  tm = first_m + in_g % gsize;
+  tn = in_g / gsize;
+}
+
+}  // namespace gmlp

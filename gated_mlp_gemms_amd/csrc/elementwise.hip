@@ -1,0 +1,219 @@
+// Memory-bound helper kernels of the MLP engine: the split-K reduction, the activation-only
+// pass of the "only dW_down" backward branch, and e4m3 quantize / widen.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gmlp {
+
+namespace {
+
+constexpr int kEwThreads = 256;
+
+inline int ew_grid(int64_t items) {
+  int64_t g = (items + kEwThreads - 1) / kEwThreads;
+  const int64_t cap = 256 * 64;   // 64 workgroups per CU is plenty for a streaming pass
+  if (g > cap) g = cap;
+  return (int)(g < 1 ? 1 : g);
+}
+
+template <typename T> __device__ __forceinline__ void load4(const void* p, float v[4]);
+template <> __device__ __forceinline__ void load4<float>(const void* p, float v[4]) {
+  f32x4 x = *reinterpret_cast<const f32x4*>(p);
+  v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+}
+template <> __device__ __forceinline__ void load4<bf16>(const void* p, float v[4]) {
+  u32x2 x = *reinterpret_cast<const u32x2*>(p);
+  v[0] = bf16_bits_to_f32(x[0] & 0xffffu); v[1] = bf16_bits_to_f32(x[0] >> 16);
+  v[2] = bf16_bits_to_f32(x[1] & 0xffffu); v[3] = bf16_bits_to_f32(x[1] >> 16);
+}
+template <typename T> __device__ __forceinline__ void store4(void* p, const float v[4]);
+template <> __device__ __forceinline__ void store4<float>(void* p, const float v[4]) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+}
+template <> __device__ __forceinline__ void store4<bf16>(void* p, const float v[4]) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+template <typename T> constexpr int esize() { return sizeof(T) == 4 ? 4 : 2; }
+
+// ---- split-K reduction: fixed summation order over the splits -----------------------------
+
+template <typename OutT>
+__global__ __launch_bounds__(kEwThreads) void splitk_reduce_kernel(
+    const float* __restrict__ partial, int splits, int M, int N, void* C0, void* C1, int64_t ldc,
+    int c_split, float alpha, const float* dev0, const float* dev1, int accumulate) {
+  float a = alpha;
+  if (dev0) a *= *dev0;
+  if (dev1) a *= *dev1;
+  const int n4 = N / 4;
+  const int64_t total = (int64_t)M * n4;
+  const int64_t plane = (int64_t)M * N;
+  for (int64_t i = blockIdx.x * (int64_t)kEwThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kEwThreads) {
+    const int m = (int)(i / n4), n = (int)(i % n4) * 4;
+    const float* src = partial + (int64_t)m * N + n;
+    f32x4 s = *reinterpret_cast<const f32x4*>(src);
+    for (int k = 1; k < splits; ++k) s += *reinterpret_cast<const f32x4*>(src + k * plane);
+    float v[4] = {a * s[0], a * s[1], a * s[2], a * s[3]};
+    const bool lo = m < c_split;
+    char* row = reinterpret_cast<char*>(lo ? C0 : C1) + (int64_t)(lo ? m : m - c_split) * ldc * esize<OutT>();
+    if (accumulate) {
+      float* q = reinterpret_cast<float*>(row) + n;
+      f32x4 o = *reinterpret_cast<f32x4*>(q);
+      o[0] += v[0]; o[1] += v[1]; o[2] += v[2]; o[3] += v[3];
+      *reinterpret_cast<f32x4*>(q) = o;
+    } else {
+      store4<OutT>(row + (int64_t)n * esize<OutT>(), v);
+    }
+  }
+}
+
+// ---- activation only -------------------------------------------------------------------------
+
+template <typename T>
+__global__ __launch_bounds__(kEwThreads) void gated_act_kernel(const void* preact, void* a_out, int M,
+                                                               int H, float gm, int inside) {
+  const int h4 = H / 4;
+  const int64_t total = (int64_t)M * h4;
+  for (int64_t i = blockIdx.x * (int64_t)kEwThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kEwThreads) {
+    const int m = (int)(i / h4), n = (int)(i % h4) * 4;
+    const char* row = reinterpret_cast<const char*>(preact) + (int64_t)m * 2 * H * esize<T>();
+    float g[4], u[4], a[4];
+    load4<T>(row + (int64_t)n * esize<T>(), g);
+    load4<T>(row + (int64_t)(H + n) * esize<T>(), u);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (inside) {
+        const float z = gm * g[r];
+        a[r] = z * sigmoidf_(z) * u[r];
+      } else {
+        a[r] = gm * (g[r] * sigmoidf_(g[r])) * u[r];
+      }
+    }
+    store4<T>(reinterpret_cast<char*>(a_out) + ((int64_t)m * H + n) * esize<T>(), a);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kEwThreads) void relu_sq_kernel(const void* pre, void* post, int64_t n,
+                                                             float alpha, const float* dev0,
+                                                             const float* dev1) {
+  float a = alpha;
+  if (dev0) a *= *dev0;
+  if (dev1) a *= *dev1;
+  const int64_t n4 = n / 4;
+  for (int64_t i = blockIdx.x * (int64_t)kEwThreads + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * kEwThreads) {
+    float v[4];
+    load4<T>(reinterpret_cast<const char*>(pre) + i * 4 * esize<T>(), v);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { const float t = fmaxf(a * v[r], 0.0f); v[r] = t * t; }
+    store4<T>(reinterpret_cast<char*>(post) + i * 4 * esize<T>(), v);
+  }
+}
+
+// ---- e4m3 quantize ---------------------------------------------------------------------------
+
+__global__ void zero_f32_kernel(float* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0.0f;
+}
+
+template <typename T> __device__ __forceinline__ float load1(const void* p, int64_t i);
+template <> __device__ __forceinline__ float load1<float>(const void* p, int64_t i) {
+  return reinterpret_cast<const float*>(p)[i];
+}
+template <> __device__ __forceinline__ float load1<bf16>(const void* p, int64_t i) {
+  return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kEwThreads) void absmax_kernel(const void* src, int64_t n, float* amax) {
+  float m = 0.0f;
+  for (int64_t i = blockIdx.x * (int64_t)kEwThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kEwThreads)
+    m = fmaxf(m, __builtin_fabsf(load1<T>(src, i)));
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float part[kEwThreads / 64];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kEwThreads / 64; ++w) m = fmaxf(m, part[w]);
+    if (m > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(m));
+  }
+}
+
+// scale = max(amax, 1e-12) / 448 (fp32, correctly rounded); q = e4m3(v / scale).
+template <typename T>
+__global__ __launch_bounds__(kEwThreads) void quantize_kernel(const void* src, int64_t n, uint8_t* dst,
+                                                              const float* amax, float* scale_out) {
+  const float s = __fdiv_rn(fmaxf(*amax, 1e-12f), 448.0f);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
+  for (int64_t i = blockIdx.x * (int64_t)kEwThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kEwThreads)
+    dst[i] = (uint8_t)f32_to_e4m3(__fdiv_rn(load1<T>(src, i), s));
+}
+
+__global__ __launch_bounds__(kEwThreads) void dequant_kernel(const uint8_t* src, uint16_t* dst, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)kEwThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kEwThreads)
+    dst[i] = (uint16_t)(__float_as_uint(e4m3_to_f32(src[i])) >> 16);   // exact: <= 4 significant bits
+}
+
+}  // namespace
+
+hipError_t run_splitk_reduce(DType io, const float* partial, int splits, int M, int N, void* C0,
+                             void* C1, int64_t ldc, int c_split, float alpha, const float* dev0,
+                             const float* dev1, int accumulate, hipStream_t s) {
+  const int grid = ew_grid((int64_t)M * (N / 4));
+  if (io == DT_BF16 && !accumulate)
+    hipLaunchKernelGGL(splitk_reduce_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, partial, splits, M,
+                       N, C0, C1, ldc, c_split, alpha, dev0, dev1, 0);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, partial, splits, M,
+                       N, C0, C1, ldc, c_split, alpha, dev0, dev1, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t run_gated_act(DType io, const void* preact, void* a, int M, int H, float gate_mult,
+                         int gate_inside, hipStream_t s) {
+  const int grid = ew_grid((int64_t)M * (H / 4));
+  if (io == DT_BF16)
+    hipLaunchKernelGGL(gated_act_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, preact, a, M, H, gate_mult, gate_inside);
+  else
+    hipLaunchKernelGGL(gated_act_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, preact, a, M, H, gate_mult, gate_inside);
+  return hipGetLastError();
+}
+
+hipError_t run_relu_sq_act(DType io, const void* pre, void* post, int64_t n, float alpha,
+                           const float* dev0, const float* dev1, hipStream_t s) {
+  const int grid = ew_grid(n / 4);
+  if (io == DT_BF16)
+    hipLaunchKernelGGL(relu_sq_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, pre, post, n, alpha, dev0, dev1);
+  else
+    hipLaunchKernelGGL(relu_sq_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, pre, post, n, alpha, dev0, dev1);
+  return hipGetLastError();
+}
+
+hipError_t run_quantize_e4m3(DType src_t, const void* src, int64_t n, void* dst, float* scale,
+                             float* ws, hipStream_t s) {
+  hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(64), 0, s, ws, 1);
+  const int grid = ew_grid(n);
+  if (src_t == DT_BF16) {
+    hipLaunchKernelGGL(absmax_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);
+    hipLaunchKernelGGL(quantize_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, src, n,
+                       reinterpret_cast<uint8_t*>(dst), ws, scale);
+  } else {
+    hipLaunchKernelGGL(absmax_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);
+    hipLaunchKernelGGL(quantize_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, src, n,
+                       reinterpret_cast<uint8_t*>(dst), ws, scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t run_dequant_e4m3_bf16(const void* src, void* dst, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(dequant_kernel, dim3(ew_grid(n)), dim3(kEwThreads), 0, s,
+                     reinterpret_cast<const uint8_t*>(src), reinterpret_cast<uint16_t*>(dst), n);
+  return hipGetLastError();
+}
+
+}  // namespace gmlp

@@ -1,0 +1,36 @@
+// Arguments of the MLP engine's GEMM kernel, shared by host dispatch and device code.
+#pragma once
+
+#include <stdint.h>
+
+namespace gmlp {
+
+enum Epi : int {
+  EPI_STORE = 0,    // C = alpha * acc (OutT); accumulate: C(f32) += alpha * acc; rows >= c_split go to C1
+  EPI_PARTIAL = 1,  // split-K: partial[split][m][n] = acc (fp32); a reduce kernel finishes
+  EPI_GATED = 2,    // g, u = alpha * acc pair; aux[m][n], aux[m][half+n] = g, u (flag 1);
+                    // C0[m][n] = a = act(g, u) (flag 2)
+  EPI_ACT = 3,      // pre = alpha * acc -> aux (flag 1); post = relu(pre)^2 -> C0 (flag 2)
+  EPI_DGATED = 4,   // da = alpha * acc; g, u <- aux; dg, du -> C0[m][n], C0[m][half+n];
+                    // a -> C1 (flag 2). C0 may equal aux.
+  EPI_DACT = 5,     // dpost = alpha * acc; pre <- aux; dpre -> C0; post -> C1 (flag 2)
+  EPI_F8ACT = 6,    // pre = alpha * acc -> aux (bf16, flag 1); post = relu(pre)^2;
+                    // C0 = e4m3(post / *s_post); *amax = max(*amax, max post)
+};
+
+struct GemmArgs {
+  int M, N, K;
+  const void* A; int64_t lda;
+  const void* B0; const void* B1; int64_t ldb; int b_split;
+  void* C0; int64_t ldc0; void* C1; int64_t ldc1; int c_split;
+  void* aux; int64_t ld_aux; int half;
+  float alpha; const float* alpha_dev0; const float* alpha_dev1;
+  float gate_mult; int gate_inside;
+  int accumulate;
+  int flags;
+  const float* s_post; float* amax;
+  int k_per_split; float* partial;
+  int tiles_m, tiles_n, group_m;
+};
+
+}  // namespace gmlp

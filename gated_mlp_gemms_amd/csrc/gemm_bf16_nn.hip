@@ -1,0 +1,30 @@
+// bf16 GEMMs with A K-major and B MN-major (dout W, dpreact W): the fused d-activation
+// backward kernels, dx and their split-K partial form.
+#include "gemm_kernel.hpp"
+#include "launch.hpp"
+
+namespace gmlp {
+
+template <int BM, int BN>
+static hipError_t dispatch(DType io, int epi, const GemmArgs& a, int grid, hipStream_t s) {
+  switch (epi) {
+    case EPI_DGATED: return launch_gemm<bf16, bf16, BM, BN, true, false, EPI_DGATED>(a, grid, s);
+    case EPI_DACT: return launch_gemm<bf16, bf16, BM, BN, true, false, EPI_DACT>(a, grid, s);
+    case EPI_STORE:
+      if (io == DT_BF16) return launch_gemm<bf16, bf16, BM, BN, true, false, EPI_STORE>(a, grid, s);
+      return hipErrorInvalidValue;
+    case EPI_PARTIAL: return launch_gemm<bf16, float, BM, BN, true, false, EPI_PARTIAL>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t run_gemm_bf16_nn(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s) {
+  switch (tile) {
+    case TILE_256x256: return dispatch<256, 256>(io, epi, a, grid, s);
+    case TILE_256x128: return dispatch<256, 128>(io, epi, a, grid, s);
+    case TILE_128x128: return dispatch<128, 128>(io, epi, a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gmlp

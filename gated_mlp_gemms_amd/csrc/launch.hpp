@@ -1,0 +1,49 @@
+// Host-side declarations of every kernel launch the C-ABI layer uses.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_args.hpp"
+
+namespace gmlp {
+
+enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
+enum Layout : int { NT = 0, NN = 1, TN = 2 };   // A K-major/B K-major, A K/B MN, A MN/B MN
+enum TileShape : int { TILE_256x256 = 0, TILE_256x128 = 1, TILE_128x128 = 2, TILE_COUNT = 3 };
+
+inline int tile_bm(int t) { return t == TILE_128x128 ? 128 : 256; }
+inline int tile_bn(int t) { return t == TILE_256x256 ? 256 : 128; }
+
+// One GEMM launch. `io` is the element type of the epilogue's stored/loaded tensors (for
+// EPI_STORE the output type; accumulate mode needs DT_F32). Returns hipErrorInvalidValue for a
+// combination that has no instantiation.
+hipError_t run_gemm(DType in, DType io, Layout layout, int epi, TileShape tile, const GemmArgs& a,
+                    int grid, hipStream_t stream);
+
+// Per-(input dtype, layout) launchers, one translation unit each.
+hipError_t run_gemm_bf16_nt(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
+hipError_t run_gemm_bf16_nn(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
+hipError_t run_gemm_bf16_tn(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
+hipError_t run_gemm_f32(Layout layout, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
+hipError_t run_gemm_e4m3_nt(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
+
+// out = alpha * sum_s partial[s] (fixed order), stored as `io` or added into fp32 (accumulate).
+// Rows >= c_split go to C1 (row - c_split).
+hipError_t run_splitk_reduce(DType io, const float* partial, int splits, int M, int N, void* C0,
+                             void* C1, int64_t ldc, int c_split, float alpha, const float* dev0,
+                             const float* dev1, int accumulate, hipStream_t s);
+
+// a[m][n] = act(g = pre[m][n], u = pre[m][H + n]) (gated) or relu(pre)^2.
+hipError_t run_gated_act(DType io, const void* preact, void* a, int M, int H, float gate_mult,
+                         int gate_inside, hipStream_t s);
+hipError_t run_relu_sq_act(DType io, const void* pre, void* post, int64_t n, float alpha,
+                           const float* dev0, const float* dev1, hipStream_t s);
+
+// Per-tensor e4m3 quantization: amax (into ws[0]), then scale and codes.
+hipError_t run_quantize_e4m3(DType src_t, const void* src, int64_t n, void* dst, float* scale,
+                             float* ws, hipStream_t s);
+// Exact e4m3 -> bf16 widening (every e4m3 value is a bf16 value).
+hipError_t run_dequant_e4m3_bf16(const void* src, void* dst, int64_t n, hipStream_t s);
+
+}  // namespace gmlp

@@ -1,0 +1,630 @@
+// C-ABI of the MLP engine: argument checks (all on the host, before any HIP call), workspace
+// layout, per-GEMM tile / split-K choice, and the launch sequence of the forward and backward.
+//
+// Forward (gated):  [gate/up GEMM + SwiGLU epilogue] -> a -> [down GEMM, x down_mult] -> out
+// Backward (gated): [recompute g,u]? -> [dout W_down GEMM + d(SwiGLU) epilogue: dg|du, a]
+//                   -> dW_down = dm dout^T a -> dx = [dg|du][W_gate; W_up] -> [dW_gate; dW_up]
+// (quack mlp.py MLPRecomputeFunc; flash-swiglu-mlp README "design points"). The ReLU^2 MLP
+// runs the same sequence with the relu^2 epilogues (modded-nanogpt gpt.py ReLUSqrdMLP).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "launch.hpp"
+#include "mlp.h"
+
+using namespace gmlp;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mlp_status fail(mlp_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+// ---- one-shot stage timing (mlp_time_stage_once) ----------------------------------------------
+
+struct StageHook { hipEvent_t begin = nullptr, end = nullptr; };
+thread_local StageHook g_hooks[MLP_STAGE_COUNT];
+
+// Records the armed begin event when constructed and the end event when destroyed, on `s`.
+struct StageScope {
+  StageHook* h = nullptr;
+  hipStream_t s;
+  StageScope(int stage, hipStream_t stream) : s(stream) {
+    if (g_hooks[stage].begin) {
+      h = &g_hooks[stage];
+      (void)hipEventRecord(h->begin, s);
+    }
+  }
+  ~StageScope() {
+    if (h) {
+      (void)hipEventRecord(h->end, s);
+      h->begin = h->end = nullptr;
+    }
+  }
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int esize(int dtype) { return dtype == MLP_BF16 ? 2 : 4; }
+DType io_of(const mlp_desc* d) { return d->dtype == MLP_BF16 ? DT_BF16 : DT_F32; }
+
+// ---- GEMM planning -------------------------------------------------------------------------
+
+struct Plan {
+  TileShape tile;
+  int splits, k_per_split, tiles_m, tiles_n, group_m, grid;
+};
+
+struct TileInfo { TileShape t; int bm, bn, slots; double eff; };
+// slots: workgroups per CU that fit (LDS: 128 KiB, 96 KiB, 64 KiB of 160 KiB); eff: assumed
+// fraction of the CU's MFMA rate a tile shape sustains (larger tiles re-read less).
+const TileInfo kTiles[] = {
+    {TILE_256x256, 256, 256, 1, 1.00},
+    {TILE_256x128, 256, 128, 1, 0.85},
+    {TILE_128x128, 128, 128, 2, 0.70},
+};
+
+int bk_of(DType in) { return in == DT_E4M3 ? 128 : (in == DT_BF16 ? 64 : 32); }
+
+// gated: N counts hidden units and a tile covers bn/2 of them (gate + up rows).
+Plan plan_gemm(DType in, int64_t M, int64_t N, int64_t K, bool allow_split, bool gated) {
+  const int bk = bk_of(in);
+  const double per_cu = (in == DT_E4M3 ? 2.0 : in == DT_BF16 ? 1.0 : 1.0 / 16.0) * 9.83e12;
+  Plan best{};
+  double best_t = 1e300;
+  for (const TileInfo& ti : kTiles) {
+    if (in == DT_F32 && ti.t != TILE_128x128) continue;
+    const int64_t bn_units = gated ? ti.bn / 2 : ti.bn;
+    const int64_t tm = (M + ti.bm - 1) / ti.bm, tn = (N + bn_units - 1) / bn_units;
+    const int max_split = allow_split ? 16 : 1;
+    for (int s = 1; s <= max_split; ++s) {
+      const int64_t kps = ((K + s - 1) / s + bk - 1) / bk * bk;
+      const int64_t s_eff = (K + kps - 1) / kps;
+      if (s_eff != s) continue;
+      const int64_t ntile = tm * tn * s;
+      const int64_t slots = 256LL * ti.slots;
+      const int64_t waves = (ntile + slots - 1) / slots;
+      double t = (double)waves * ti.slots * (2.0 * ti.bm * ti.bn * kps) / (ti.eff * per_cu);
+      if (s > 1) t += (2.0 * s * M * N * 4.0 + M * N * 4.0) / 6.0e12 + 4e-6;
+      if (t < best_t * 0.98) {
+        best_t = t;
+        best.tile = ti.t;
+        best.splits = s;
+        best.k_per_split = (int)kps;
+        best.tiles_m = (int)tm;
+        best.tiles_n = (int)tn;
+        best.group_m = (int)std::min<int64_t>(tm, 8);
+        best.grid = (int)ntile;
+      }
+    }
+  }
+  return best;
+}
+
+size_t partial_bytes(const Plan& p, int64_t M, int64_t N) {
+  return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+}
+
+// ---- workspace layout ----------------------------------------------------------------------
+
+struct WsLayout {
+  size_t act = 0, act_bytes = 0;        // a / post / post_q  [M, H]
+  size_t pre = 0, pre_bytes = 0;        // recomputed preact  [M, P]
+  size_t dpre = 0, dpre_bytes = 0;      // dpreact when the caller passes none
+  size_t xq = 0, xq_bytes = 0;          // widened e4m3 operands of the fp8 backward
+  size_t w1q = 0, w1q_bytes = 0;
+  size_t w2q = 0, w2q_bytes = 0;
+  size_t partial = 0, partial_bytes = 0;
+  size_t total = 0;
+};
+
+struct Gemms {   // the GEMMs a phase may run, in planning form
+  Plan down;          // forward down projection
+  Plan dw_down, dx, dw_up;
+};
+
+Gemms plan_all(const mlp_desc* d) {
+  const DType io = io_of(d);
+  const DType fin = d->fp8_fwd ? DT_E4M3 : io;
+  const bool gated = d->act == MLP_ACT_SWIGLU;
+  const int64_t M = d->M, D = d->d_in, H = d->hidden, O = d->d_out, P = gated ? 2 * H : H;
+  Gemms g;
+  g.down = plan_gemm(fin, M, O, H, true, false);
+  g.dw_down = plan_gemm(io, O, H, M, true, false);
+  g.dx = plan_gemm(io, M, D, P, true, false);
+  g.dw_up = plan_gemm(io, P, D, M, true, false);
+  return g;
+}
+
+WsLayout ws_layout(const mlp_desc* d, int phase) {
+  WsLayout L;
+  const bool gated = d->act == MLP_ACT_SWIGLU;
+  const int64_t M = d->M, D = d->d_in, H = d->hidden, O = d->d_out, P = gated ? 2 * H : H;
+  const size_t es = esize(d->dtype);
+  const Gemms g = plan_all(d);
+  size_t off = 0;
+  auto take = [&](size_t& at, size_t& sz, size_t bytes) { at = off; sz = bytes; off += round_up(bytes); };
+  if (phase == MLP_PHASE_FWD || phase == MLP_PHASE_FWD_INFER) {
+    take(L.act, L.act_bytes, (size_t)M * H * (d->fp8_fwd ? 1 : es));
+    take(L.partial, L.partial_bytes, partial_bytes(g.down, M, O));
+  } else {
+    take(L.act, L.act_bytes, (size_t)M * H * es);
+    if (d->recompute) take(L.pre, L.pre_bytes, (size_t)M * P * es);
+    else take(L.dpre, L.dpre_bytes, (size_t)M * P * es);
+    if (d->fp8_fwd) {
+      take(L.xq, L.xq_bytes, (size_t)M * D * 2);
+      take(L.w1q, L.w1q_bytes, (size_t)H * D * 2);
+      take(L.w2q, L.w2q_bytes, (size_t)O * H * 2);
+    }
+    const size_t pb = std::max({partial_bytes(g.dw_down, O, H), partial_bytes(g.dx, M, D),
+                                partial_bytes(g.dw_up, P, D)});
+    take(L.partial, L.partial_bytes, pb);
+  }
+  L.total = off;
+  return L;
+}
+
+// ---- argument checks -------------------------------------------------------------------------
+
+mlp_status check_desc(const mlp_desc* d) {
+  if (!d) return fail(MLP_ERR_INVALID_ARG, "desc is NULL");
+  if (d->M < 1 || d->d_in < 1 || d->hidden < 1 || d->d_out < 1)
+    return fail(MLP_ERR_INVALID_ARG, "sizes must be >= 1 (M=%lld d_in=%lld hidden=%lld d_out=%lld)",
+                (long long)d->M, (long long)d->d_in, (long long)d->hidden, (long long)d->d_out);
+  const int64_t lim = (int64_t)1 << 30;
+  if (d->M >= lim || d->d_in >= lim || d->hidden >= lim / 2 || d->d_out >= lim)
+    return fail(MLP_ERR_UNSUPPORTED, "a size is beyond 2^30 (2^29 for hidden)");
+  if (d->act != MLP_ACT_SWIGLU && d->act != MLP_ACT_RELU_SQ)
+    return fail(MLP_ERR_INVALID_ARG, "act %d is not an mlp_act", d->act);
+  if (d->dtype != MLP_F32 && d->dtype != MLP_BF16)
+    return fail(MLP_ERR_INVALID_ARG, "dtype %d is not an mlp_dtype", d->dtype);
+  if (d->gate_mode != MLP_GATE_OUTSIDE && d->gate_mode != MLP_GATE_INSIDE)
+    return fail(MLP_ERR_INVALID_ARG, "gate_mode %d is not an mlp_gate_mode", d->gate_mode);
+  if ((d->recompute != 0 && d->recompute != 1) || (d->fp8_fwd != 0 && d->fp8_fwd != 1))
+    return fail(MLP_ERR_INVALID_ARG, "recompute and fp8_fwd must be 0 or 1");
+  if (d->reserved != 0) return fail(MLP_ERR_INVALID_ARG, "reserved must be 0");
+  if (!isfinite(d->gate_mult) || !isfinite(d->down_mult))
+    return fail(MLP_ERR_INVALID_ARG, "gate_mult and down_mult must be finite");
+  if (d->fp8_fwd && (d->act != MLP_ACT_RELU_SQ || d->dtype != MLP_BF16))
+    return fail(MLP_ERR_UNSUPPORTED, "the e4m3 forward is implemented for ReLU^2 with bf16 I/O only");
+  const int q = d->fp8_fwd ? 16 : (d->dtype == MLP_BF16 ? 8 : 4);
+  if (d->d_in % q || d->hidden % q || d->d_out % q)
+    return fail(MLP_ERR_ALIGNMENT, "d_in, hidden and d_out must be multiples of %d (16-byte rows)", q);
+  return MLP_OK;
+}
+
+mlp_status need_ptr(const void* p, const char* name, bool align = true) {
+  if (!p) return fail(MLP_ERR_INVALID_ARG, "%s is NULL", name);
+  if (align && !aligned16(p)) return fail(MLP_ERR_ALIGNMENT, "%s is not 16-byte aligned", name);
+  if (!align && !aligned4(p)) return fail(MLP_ERR_ALIGNMENT, "%s is not 4-byte aligned", name);
+  return MLP_OK;
+}
+
+mlp_status need_null(const void* p, const char* name, const char* why) {
+  return p ? fail(MLP_ERR_INVALID_ARG, "%s must be NULL %s", name, why) : MLP_OK;
+}
+
+#define MLP_TRY(expr)                 \
+  do {                                \
+    const mlp_status st_ = (expr);    \
+    if (st_ != MLP_OK) return st_;    \
+  } while (0)
+
+mlp_status check_fp8(const mlp_desc* d, const mlp_fp8* f, bool fwd) {
+  if (!d->fp8_fwd) return need_null(f, "fp8", "unless desc->fp8_fwd");
+  if (!f) return fail(MLP_ERR_INVALID_ARG, "fp8 is NULL but desc->fp8_fwd is set");
+  MLP_TRY(need_ptr(f->x_q, "fp8->x_q"));
+  MLP_TRY(need_ptr(f->w1_q, "fp8->w1_q"));
+  MLP_TRY(need_ptr(f->w2_q, "fp8->w2_q"));
+  MLP_TRY(need_ptr(f->s_x, "fp8->s_x", false));
+  MLP_TRY(need_ptr(f->s_w1, "fp8->s_w1", false));
+  MLP_TRY(need_ptr(f->s_w2, "fp8->s_w2", false));
+  if (fwd) {
+    MLP_TRY(need_ptr(f->s_post, "fp8->s_post", false));
+    MLP_TRY(need_ptr(f->post_amax, "fp8->post_amax", false));
+  }
+  return MLP_OK;
+}
+
+mlp_status check_ws(const mlp_desc* d, int phase, const void* ws, size_t ws_bytes) {
+  const size_t need = ws_layout(d, phase).total;
+  if (ws_bytes < need)
+    return fail(MLP_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+  if (need && !ws) return fail(MLP_ERR_INVALID_ARG, "workspace is NULL");
+  if (ws && !aligned16(ws)) return fail(MLP_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+  return MLP_OK;
+}
+
+mlp_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MLP_OK;
+  return fail(MLP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// One GEMM, split along K when the plan says so (fp32 partials, then a fixed-order reduce
+// that applies the store epilogue).
+mlp_status gemm(DType in, DType io, Layout lay, int epi, const Plan& p, GemmArgs a, int64_t M,
+                int64_t N, int64_t K, void* partial, hipStream_t s, const char* what) {
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.tiles_m = p.tiles_m;
+  a.tiles_n = p.tiles_n;
+  a.group_m = p.group_m;
+  a.k_per_split = p.k_per_split;
+  if (p.splits > 1) {
+    GemmArgs b = a;
+    b.partial = reinterpret_cast<float*>(partial);
+    MLP_TRY(hip_status(run_gemm(in, DT_F32, lay, EPI_PARTIAL, p.tile, b, p.grid, s), what));
+    return hip_status(run_splitk_reduce(io, b.partial, p.splits, (int)M, (int)N, a.C0, a.C1, a.ldc0,
+                                        a.c_split, a.alpha, a.alpha_dev0, a.alpha_dev1, a.accumulate, s),
+                      what);
+  }
+  return hip_status(run_gemm(in, io, lay, epi, p.tile, a, p.grid, s), what);
+}
+
+GemmArgs base_args(const mlp_desc* d) {
+  GemmArgs a{};
+  a.alpha = 1.0f;
+  a.gate_mult = d->gate_mult;
+  a.gate_inside = d->gate_mode == MLP_GATE_INSIDE;
+  a.b_split = 1 << 30;
+  a.c_split = 1 << 30;
+  return a;
+}
+
+// Forward GEMM 1: the gated / ReLU^2 / e4m3 ReLU^2 up projection with its activation epilogue.
+// preact_out: where g|u or pre goes (NULL: not kept); act_out: where a / post / post_q goes.
+mlp_status up_projection(const mlp_desc* d, const void* x, const void* wg, const void* wu,
+                         const mlp_fp8* f, void* preact_out, void* act_out, hipStream_t s) {
+  const DType io = io_of(d);
+  const int64_t M = d->M, D = d->d_in, H = d->hidden;
+  GemmArgs a = base_args(d);
+  a.lda = D;
+  a.ldb = D;
+  a.C0 = act_out;
+  a.ldc0 = H;
+  a.aux = preact_out;
+  a.flags = (preact_out ? 1 : 0) | (act_out ? 2 : 0);
+  if (d->act == MLP_ACT_SWIGLU) {
+    a.A = x;
+    a.B0 = wg;
+    a.B1 = wu;
+    a.ld_aux = 2 * H;
+    a.half = (int)H;
+    const Plan p = plan_gemm(io, M, H, D, false, true);
+    return gemm(io, io, NT, EPI_GATED, p, a, M, H, D, nullptr, s, "gate/up projection");
+  }
+  a.ld_aux = H;
+  if (d->fp8_fwd) {
+    a.A = f->x_q;
+    a.B0 = f->w1_q;
+    a.alpha_dev0 = f->s_x;
+    a.alpha_dev1 = f->s_w1;
+    a.s_post = f->s_post;
+    a.amax = f->post_amax;
+    const Plan p = plan_gemm(DT_E4M3, M, H, D, false, false);
+    return gemm(DT_E4M3, DT_BF16, NT, EPI_F8ACT, p, a, M, H, D, nullptr, s, "e4m3 up projection");
+  }
+  a.A = x;
+  a.B0 = wg;
+  const Plan p = plan_gemm(io, M, H, D, false, false);
+  return gemm(io, io, NT, EPI_ACT, p, a, M, H, D, nullptr, s, "up projection");
+}
+
+mlp_status fwd_impl(const mlp_desc* d, const void* x, const void* wg, const void* wu, const void* wd,
+                    void* out, void* saved, const mlp_fp8* f, void* ws, size_t ws_bytes, void* stream,
+                    bool infer) {
+  MLP_TRY(check_desc(d));
+  const bool gated = d->act == MLP_ACT_SWIGLU;
+  if (!d->fp8_fwd) {
+    MLP_TRY(need_ptr(x, "x"));
+    MLP_TRY(need_ptr(wg, gated ? "w_gate" : "w_gate (W1)"));
+    MLP_TRY(need_ptr(wd, gated ? "w_down" : "w_down (W2)"));
+  }
+  if (gated) MLP_TRY(need_ptr(wu, "w_up"));
+  else MLP_TRY(need_null(wu, "w_up", "for ReLU^2"));
+  MLP_TRY(need_ptr(out, "out"));
+  if (!infer) {
+    if (d->recompute) MLP_TRY(need_null(saved, "saved_preact", "with recompute"));
+    else MLP_TRY(need_ptr(saved, "saved_preact"));
+  }
+  MLP_TRY(check_fp8(d, f, true));
+  const int phase = infer ? MLP_PHASE_FWD_INFER : MLP_PHASE_FWD;
+  MLP_TRY(check_ws(d, phase, ws, ws_bytes));
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const WsLayout L = ws_layout(d, phase);
+  char* w = reinterpret_cast<char*>(ws);
+  void* act = w + L.act;
+  const int64_t M = d->M, H = d->hidden, O = d->d_out;
+  {
+    StageScope st(MLP_STAGE_UP, s);
+    MLP_TRY(up_projection(d, x, wg, wu, f, infer ? nullptr : saved, act, s));
+  }
+
+  const DType io = io_of(d);
+  const DType fin = d->fp8_fwd ? DT_E4M3 : io;
+  GemmArgs b = base_args(d);
+  b.A = act;
+  b.lda = H;
+  b.B0 = d->fp8_fwd ? f->w2_q : wd;
+  b.ldb = H;
+  b.C0 = out;
+  b.ldc0 = O;
+  b.alpha = d->down_mult;
+  if (d->fp8_fwd) {
+    b.alpha_dev0 = f->s_post;
+    b.alpha_dev1 = f->s_w2;
+  }
+  const Plan p = plan_all(d).down;
+  StageScope st(MLP_STAGE_DOWN, s);
+  return gemm(fin, io, NT, EPI_STORE, p, b, M, O, H, w + L.partial, s, "down projection");
+}
+
+}  // namespace
+
+extern "C" {
+
+int mlp_abi_version(void) { return 1; }
+
+const char* mlp_status_string(int st) {
+  switch (st) {
+    case MLP_OK: return "MLP_OK";
+    case MLP_ERR_INVALID_ARG: return "MLP_ERR_INVALID_ARG";
+    case MLP_ERR_UNSUPPORTED: return "MLP_ERR_UNSUPPORTED";
+    case MLP_ERR_ALIGNMENT: return "MLP_ERR_ALIGNMENT";
+    case MLP_ERR_WORKSPACE: return "MLP_ERR_WORKSPACE";
+    case MLP_ERR_HIP: return "MLP_ERR_HIP";
+    default: return "unknown mlp_status";
+  }
+}
+
+const char* mlp_last_error(void) { return g_last_error.c_str(); }
+
+size_t mlp_workspace_bytes(const mlp_desc* d, int phase) {
+  if (check_desc(d) != MLP_OK) return 0;
+  if (phase < MLP_PHASE_FWD || phase > MLP_PHASE_BWD) {
+    fail(MLP_ERR_INVALID_ARG, "phase %d is not an mlp_phase", phase);
+    return 0;
+  }
+  return ws_layout(d, phase).total;
+}
+
+mlp_status mlp_fwd(const mlp_desc* d, const void* x, const void* wg, const void* wu, const void* wd,
+                   void* out, void* saved, const mlp_fp8* f, void* ws, size_t ws_bytes, void* stream) {
+  return fwd_impl(d, x, wg, wu, wd, out, saved, f, ws, ws_bytes, stream, false);
+}
+
+mlp_status mlp_fwd_infer(const mlp_desc* d, const void* x, const void* wg, const void* wu,
+                         const void* wd, void* out, const mlp_fp8* f, void* ws, size_t ws_bytes,
+                         void* stream) {
+  return fwd_impl(d, x, wg, wu, wd, out, nullptr, f, ws, ws_bytes, stream, true);
+}
+
+mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const void* wg, const void* wu,
+                   const void* wd, const void* saved, void* dpreact, void* dx, void* dwg, void* dwu,
+                   void* dwd, int grad_accum, const mlp_fp8* f, void* ws, size_t ws_bytes,
+                   void* stream) {
+  MLP_TRY(check_desc(d));
+  const bool gated = d->act == MLP_ACT_SWIGLU;
+  MLP_TRY(need_ptr(dout, "dout"));
+  if (!d->fp8_fwd) {
+    MLP_TRY(need_ptr(x, "x"));
+    MLP_TRY(need_ptr(wg, gated ? "w_gate" : "w_gate (W1)"));
+    MLP_TRY(need_ptr(wd, gated ? "w_down" : "w_down (W2)"));
+  }
+  if (gated) MLP_TRY(need_ptr(wu, "w_up"));
+  else MLP_TRY(need_null(wu, "w_up", "for ReLU^2"));
+  if (d->recompute) MLP_TRY(need_null(saved, "saved_preact", "with recompute"));
+  else MLP_TRY(need_ptr(saved, "saved_preact"));
+  if (dpreact) MLP_TRY(need_ptr(dpreact, "dpreact"));
+  if (dx) MLP_TRY(need_ptr(dx, "dx"));
+  if (dwd) MLP_TRY(need_ptr(dwd, "dw_down"));
+  if (gated) {
+    if ((dwg == nullptr) != (dwu == nullptr))
+      return fail(MLP_ERR_INVALID_ARG, "dw_gate and dw_up must both be given or both be NULL");
+    if (dwg) {
+      MLP_TRY(need_ptr(dwg, "dw_gate"));
+      MLP_TRY(need_ptr(dwu, "dw_up"));
+    }
+  } else {
+    MLP_TRY(need_null(dwu, "dw_up", "for ReLU^2"));
+    if (dwg) MLP_TRY(need_ptr(dwg, "dw_gate (dW1)"));
+  }
+  if (grad_accum != 0 && grad_accum != 1) return fail(MLP_ERR_INVALID_ARG, "grad_accum must be 0 or 1");
+  MLP_TRY(check_fp8(d, f, false));
+  MLP_TRY(check_ws(d, MLP_PHASE_BWD, ws, ws_bytes));
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const WsLayout L = ws_layout(d, MLP_PHASE_BWD);
+  const Gemms G = plan_all(d);
+  char* w = reinterpret_cast<char*>(ws);
+  void* partial = w + L.partial;
+  const DType io = io_of(d);
+  const DType gio = grad_accum ? DT_F32 : io;
+  const int64_t M = d->M, D = d->d_in, H = d->hidden, O = d->d_out, P = gated ? 2 * H : H;
+
+  // e4m3 path: the backward reads the exact bf16 widening of the forward's operands; their
+  // scales enter each GEMM's epilogue.
+  const float *sx = nullptr, *sw1 = nullptr, *sw2 = nullptr;
+  if (d->fp8_fwd) {
+    StageScope st(MLP_STAGE_WIDEN, s);
+    MLP_TRY(hip_status(run_dequant_e4m3_bf16(f->x_q, w + L.xq, M * D, s), "widen x_q"));
+    MLP_TRY(hip_status(run_dequant_e4m3_bf16(f->w1_q, w + L.w1q, H * D, s), "widen w1_q"));
+    MLP_TRY(hip_status(run_dequant_e4m3_bf16(f->w2_q, w + L.w2q, O * H, s), "widen w2_q"));
+    x = w + L.xq;
+    wg = w + L.w1q;
+    wd = w + L.w2q;
+    sx = f->s_x;
+    sw1 = f->s_w1;
+    sw2 = f->s_w2;
+  }
+
+  // pre-activation: saved by the forward, or recomputed from x (one extra GEMM)
+  const void* pre = saved;
+  if (d->recompute) {
+    GemmArgs a = base_args(d);
+    a.A = x;
+    a.lda = D;
+    a.B0 = wg;
+    a.B1 = wu;
+    a.ldb = D;
+    a.aux = w + L.pre;
+    a.ld_aux = P;
+    a.half = (int)H;
+    a.flags = 1;
+    a.alpha_dev0 = sx;
+    a.alpha_dev1 = sw1;
+    const int epi = gated ? EPI_GATED : EPI_ACT;
+    const Plan p = plan_gemm(io, M, H, D, false, gated);
+    StageScope st(MLP_STAGE_RECOMPUTE, s);
+    MLP_TRY(gemm(io, io, NT, epi, p, a, M, H, D, nullptr, s, "recompute pre-activation"));
+    pre = w + L.pre;
+  }
+
+  const bool need_dpre = dx != nullptr || dwg != nullptr;
+  void* dpre = dpreact ? dpreact : (d->recompute ? w + L.pre : w + L.dpre);
+  void* act = w + L.act;
+
+  if (need_dpre) {
+    // da = dm * dout W_down, fused with d(act) against the pre-activation; re-emits a / post
+    GemmArgs a = base_args(d);
+    a.A = dout;
+    a.lda = O;
+    a.B0 = wd;
+    a.ldb = H;
+    a.aux = const_cast<void*>(pre);
+    a.ld_aux = P;
+    a.half = (int)H;
+    a.C0 = dpre;
+    a.ldc0 = P;
+    a.C1 = act;
+    a.ldc1 = H;
+    a.flags = dwd ? 2 : 0;
+    a.alpha = d->down_mult;
+    a.alpha_dev0 = sw2;
+    const Plan p = plan_gemm(io, M, H, O, false, false);
+    StageScope st(MLP_STAGE_DACT, s);
+    MLP_TRY(gemm(io, io, NN, gated ? EPI_DGATED : EPI_DACT, p, a, M, H, O, nullptr, s,
+                 "d-activation GEMM"));
+  } else if (dwd) {
+    // only the down-projection gradient: the post-activation from the pre-activation alone
+    StageScope st(MLP_STAGE_ACT, s);
+    if (gated) MLP_TRY(hip_status(run_gated_act(io, pre, act, (int)M, (int)H, d->gate_mult,
+                                                d->gate_mode == MLP_GATE_INSIDE, s), "activation"));
+    else MLP_TRY(hip_status(run_relu_sq_act(io, pre, act, M * H, 1.0f, nullptr, nullptr, s), "activation"));
+  }
+
+  if (dwd) {   // dW_down (+)= dm * dout^T a
+    GemmArgs a = base_args(d);
+    a.A = dout;
+    a.lda = O;
+    a.B0 = act;
+    a.ldb = H;
+    a.C0 = dwd;
+    a.ldc0 = H;
+    a.alpha = d->down_mult;
+    a.accumulate = grad_accum;
+    StageScope st(MLP_STAGE_DW_DOWN, s);
+    MLP_TRY(gemm(io, gio, TN, EPI_STORE, G.dw_down, a, O, H, M, partial, s, "dW_down"));
+  }
+  if (dx) {    // dx = [dg | du] [W_gate; W_up]  (ReLU^2: dpre W1)
+    GemmArgs a = base_args(d);
+    a.A = dpre;
+    a.lda = P;
+    a.B0 = wg;
+    a.B1 = gated ? wu : nullptr;
+    a.b_split = (int)H;
+    a.ldb = D;
+    a.C0 = dx;
+    a.ldc0 = D;
+    a.alpha_dev0 = sw1;
+    StageScope st(MLP_STAGE_DX, s);
+    MLP_TRY(gemm(io, io, NN, EPI_STORE, G.dx, a, M, D, P, partial, s, "dx"));
+  }
+  if (dwg) {   // [dW_gate; dW_up] (+)= [dg | du]^T x  (ReLU^2: dW1 = dpre^T x)
+    GemmArgs a = base_args(d);
+    a.A = dpre;
+    a.lda = P;
+    a.B0 = x;
+    a.ldb = D;
+    a.C0 = dwg;
+    a.C1 = gated ? dwu : nullptr;
+    a.c_split = gated ? (int)H : (int)P;
+    a.ldc0 = D;
+    a.accumulate = grad_accum;
+    a.alpha_dev0 = sx;
+    StageScope st(MLP_STAGE_DW_UP, s);
+    MLP_TRY(gemm(io, gio, TN, EPI_STORE, G.dw_up, a, P, D, M, partial, s, "dW_gate/dW_up"));
+  }
+  return MLP_OK;
+}
+
+size_t mlp_quantize_workspace_bytes(void) { return kAlign; }
+
+mlp_status mlp_time_stage_once(int stage, void* begin, void* end) {
+  if (stage < 0 || stage >= MLP_STAGE_COUNT) return fail(MLP_ERR_INVALID_ARG, "stage %d is not an mlp_stage", stage);
+  if ((begin == nullptr) != (end == nullptr)) return fail(MLP_ERR_INVALID_ARG, "begin and end must both be set or both be NULL");
+  g_hooks[stage].begin = reinterpret_cast<hipEvent_t>(begin);
+  g_hooks[stage].end = reinterpret_cast<hipEvent_t>(end);
+  return MLP_OK;
+}
+
+mlp_status mlp_quantize_e4m3(const void* src, int dtype, int64_t n, void* dst, float* scale, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (dtype != MLP_F32 && dtype != MLP_BF16) return fail(MLP_ERR_INVALID_ARG, "dtype %d is not an mlp_dtype", dtype);
+  if (n < 1) return fail(MLP_ERR_INVALID_ARG, "n must be >= 1");
+  if (!src || !dst || !scale || !ws) return fail(MLP_ERR_INVALID_ARG, "src, dst, scale and workspace are required");
+  if (!aligned4(src) || !aligned4(scale) || !aligned16(ws))
+    return fail(MLP_ERR_ALIGNMENT, "src and scale must be 4-byte aligned, workspace 16-byte aligned");
+  if (ws_bytes < kAlign) return fail(MLP_ERR_WORKSPACE, "workspace of %zu bytes is smaller than %zu", ws_bytes, kAlign);
+  return hip_status(run_quantize_e4m3(dtype == MLP_BF16 ? DT_BF16 : DT_F32, src, n, dst, scale,
+                                      reinterpret_cast<float*>(ws), reinterpret_cast<hipStream_t>(stream)),
+                    "quantize");
+}
+
+float mlp_fp8_next_scale(float amax, float prev_scale, float gain, float floor_) {
+  float a = (isnan(amax) || isinf(amax)) ? 0.0f : amax;
+  if (a > 1e12f) a = 1e12f;
+  float fresh = a * gain;
+  if (fresh < floor_) fresh = floor_;
+  return a > 0.0f ? fresh : prev_scale;
+}
+
+}  // extern "C"
+
+namespace gmlp {
+
+hipError_t run_gemm(DType in, DType io, Layout layout, int epi, TileShape tile, const GemmArgs& a,
+                    int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  switch (in) {
+    case DT_BF16:
+      if (layout == NT) return run_gemm_bf16_nt(io, epi, tile, a, grid, s);
+      if (layout == NN) return run_gemm_bf16_nn(io, epi, tile, a, grid, s);
+      return run_gemm_bf16_tn(io, epi, tile, a, grid, s);
+    case DT_F32: return run_gemm_f32(layout, epi, tile, a, grid, s);
+    case DT_E4M3:
+      if (layout == NT) return run_gemm_e4m3_nt(io, epi, tile, a, grid, s);
+      return hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gmlp

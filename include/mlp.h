@@ -1,0 +1,194 @@
+/*
+ * gated_mlp: fused transformer-MLP forward and backward on AMD Instinct MI355X (gfx950).
+ *
+ *   gated:    g = x W_gate^T, u = x W_up^T, a = act(g, u), out = down_mult * a W_down^T
+ *   ReLU^2:   pre = x W1^T, post = relu(pre)^2,          out = down_mult * post W2^T
+ *
+ * The gated activation is SwiGLU: a = gate_mult * silu(g) * u (flash-swiglu-mlp README,
+ * "Falcon H1 style models"), or a = silu(gate_mult * g) * u with MLP_GATE_INSIDE. The ReLU^2
+ * MLP is modded-nanogpt gpt.py's ReLUSqrdMLP (relu(x @ W1.T)^2 @ W2.T). The backward follows
+ * quack mlp.py's MLPRecomputeFunc.backward: d-activation applied to dout W2 against the
+ * pre-activation (saved, or recomputed from x), dW2 = dout^T postact, dx = dpreact W1,
+ * dW1 = dpreact^T x, optionally added into existing fp32 gradient buffers
+ * (_compute_weight_grad with fuse_grad_accum).
+ *
+ * Conventions for every entry point:
+ *  - All tensors are dense row-major device buffers. x [M, d_in]; W_gate, W_up, W1 [H, d_in];
+ *    W_down, W2 [d_out, H] (nn.Linear layout); out, dout [M, d_out]; dx [M, d_in].
+ *  - The caller owns every buffer, including the workspace. The library never allocates or
+ *    frees device memory and never synchronizes: work is enqueued on `stream` (a hipStream_t;
+ *    NULL is the null stream) and the call returns once it is enqueued.
+ *  - Every argument check runs on the host before any HIP call; a failed check enqueues nothing
+ *    and returns a status (never aborts). mlp_last_error() then describes it (thread-local).
+ *    MLP_ERR_HIP reports a failed launch; faults inside kernels surface at the caller's next
+ *    synchronization.
+ *  - Device pointers must be 16-byte aligned. d_in, hidden and d_out must be multiples of 8
+ *    (bf16) or 4 (f32): rows must be 16-byte aligned (flash-swiglu-mlp README, supported
+ *    configurations; quack mlp.py's MLP.forward fast-path conditions). The e4m3 path needs
+ *    multiples of 16. M >= 1 is arbitrary.
+ */
+#ifndef GATED_MLP_H
+#define GATED_MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mlp_status {
+  MLP_OK = 0,
+  MLP_ERR_INVALID_ARG = 1,   /* null/extra pointer, bad size, bad enum, inconsistent flags */
+  MLP_ERR_UNSUPPORTED = 2,   /* a valid combination this library does not implement */
+  MLP_ERR_ALIGNMENT = 3,     /* pointer not 16-byte aligned, or a dim not a multiple of 8/4/16 */
+  MLP_ERR_WORKSPACE = 4,     /* workspace smaller than mlp_workspace_bytes() */
+  MLP_ERR_HIP = 5            /* a HIP launch failed */
+} mlp_status;
+
+typedef enum mlp_act { MLP_ACT_SWIGLU = 0, MLP_ACT_RELU_SQ = 1 } mlp_act;
+typedef enum mlp_dtype { MLP_F32 = 0, MLP_BF16 = 1 } mlp_dtype;
+/* where gate_mult enters SwiGLU: outside = gate_mult * silu(g) * u (the README's formula),
+ * inside = silu(gate_mult * g) * u. Identical at gate_mult = 1. */
+typedef enum mlp_gate_mode { MLP_GATE_OUTSIDE = 0, MLP_GATE_INSIDE = 1 } mlp_gate_mode;
+typedef enum mlp_phase { MLP_PHASE_FWD = 0, MLP_PHASE_FWD_INFER = 1, MLP_PHASE_BWD = 2 } mlp_phase;
+
+typedef struct mlp_desc {
+  int64_t M;          /* tokens: rows of x (the flattened [B, S]) */
+  int64_t d_in;       /* width of x */
+  int64_t hidden;     /* intermediate size H */
+  int64_t d_out;      /* width of out */
+  int32_t act;        /* mlp_act */
+  int32_t dtype;      /* mlp_dtype of x, weights, out, dout, dx, saved/d preact, fresh grads */
+  float gate_mult;    /* SwiGLU gate multiplier (1.0 = plain SwiGLU); ignored for ReLU^2 */
+  float down_mult;    /* scalar on the down projection's output (1.0 = none) */
+  int32_t gate_mode;  /* mlp_gate_mode */
+  int32_t recompute;  /* 1: nothing is saved; mlp_bwd recomputes the pre-activation from x */
+  int32_t fp8_fwd;    /* 1: e4m3 forward GEMMs (ReLU^2, bf16 only); see mlp_fp8 */
+  int32_t reserved;   /* must be 0 */
+} mlp_desc;
+
+/*
+ * e4m3 operands of the ReLU^2 forward (modded-nanogpt gpt.py: FP8 MLP constants,
+ * _mlp_fp8_args, _refresh_delayed_scale). Each quantized tensor carries one fp32 scale, its
+ * dequantized value being scale * e4m3_value. relu(pre)^2 is quantized with the delayed scale
+ * *s_post before the down projection, and max|relu(pre)^2| of the call is max-reduced into
+ * *post_amax (so the host can form the next s_post with mlp_fp8_next_scale). All pointers are
+ * device pointers; the scales are single floats.
+ */
+typedef struct mlp_fp8 {
+  const void* x_q;      /* e4m3 [M, d_in] */
+  const void* w1_q;     /* e4m3 [H, d_in] */
+  const void* w2_q;     /* e4m3 [d_out, H] */
+  const float* s_x;     /* scale of x_q */
+  const float* s_w1;    /* scale of w1_q */
+  const float* s_w2;    /* scale of w2_q */
+  const float* s_post;  /* scale relu(pre)^2 is quantized with (forward only) */
+  float* post_amax;     /* in/out: max(*post_amax, max|relu(pre)^2|) (forward only) */
+} mlp_fp8;
+
+/* Bytes of workspace the given phase needs for `desc` (upper bound over every skip
+ * combination). 0 for an invalid descriptor (see mlp_last_error). Host only. */
+size_t mlp_workspace_bytes(const mlp_desc* desc, int phase);
+
+/*
+ * Training forward (quack mlp.py: mlp_func with grad enabled; flash-swiglu-mlp README,
+ * "design points": fused gate/up forward, then the down projection).
+ *   out          [M, d_out]                          written
+ *   saved_preact gated: [M, 2H], row = [g | u]; ReLU^2: [M, H] pre. Written. Must be NULL
+ *                iff desc->recompute (then nothing is kept for the backward: quack's
+ *                MLPRecomputeFunc saves only x and the weights).
+ *   w_up         NULL for ReLU^2 (w_gate then holds W1, w_down holds W2).
+ *   fp8          non-NULL iff desc->fp8_fwd; x / w_gate / w_down are then not read.
+ */
+mlp_status mlp_fwd(const mlp_desc* desc, const void* x, const void* w_gate, const void* w_up,
+                   const void* w_down, void* out, void* saved_preact, const mlp_fp8* fp8,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Inference forward: same out as mlp_fwd (bit for bit), keeping no pre-activation
+ * (flash-swiglu-mlp README: the inference path saves no G/U). desc->recompute is ignored.
+ */
+mlp_status mlp_fwd_infer(const mlp_desc* desc, const void* x, const void* w_gate,
+                         const void* w_up, const void* w_down, void* out, const mlp_fp8* fp8,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward (quack mlp.py: MLPRecomputeFunc.backward, _compute_weight_grad; flash-swiglu-mlp
+ * README, "design points": fused dA/dG/dU with dA never stored, dG/dU written over G/U,
+ * merged dW_g/dW_u GEMM, single-accumulator dI).
+ *   saved_preact  as written by mlp_fwd; NULL iff desc->recompute.
+ *   dpreact       gated [M, 2H] = [dg | du], ReLU^2 [M, H]; written. NULL: kept in the
+ *                 workspace. May equal saved_preact (overwritten in place; no other overlap).
+ *   dx            [M, d_in], NULL to skip.
+ *   dw_gate/dw_up [H, d_in] (ReLU^2: dw_gate = dW1, dw_up NULL); both or neither (gated).
+ *   dw_down       [d_out, H], NULL to skip.
+ *   grad_accum    0: weight grads are written in desc->dtype; 1: they are fp32 buffers and the
+ *                 new gradient is added in place (buf = fp32(buf + grad)).
+ *   fp8           non-NULL iff desc->fp8_fwd: the backward GEMMs then read the dequantized
+ *                 x, W1, W2 of the forward (x / w_gate / w_down are not read).
+ * Skips: with dx and dw_gate/dw_up all NULL only the down-projection gradient is formed
+ * (quack's "only dW2 needed" branch); with dw_down NULL it is not.
+ */
+mlp_status mlp_bwd(const mlp_desc* desc, const void* dout, const void* x, const void* w_gate,
+                   const void* w_up, const void* w_down, const void* saved_preact,
+                   void* dpreact, void* dx, void* dw_gate, void* dw_up, void* dw_down,
+                   int grad_accum, const mlp_fp8* fp8, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Bytes of workspace mlp_quantize_e4m3 needs (a few floats). Host only. */
+size_t mlp_quantize_workspace_bytes(void);
+
+/*
+ * Per-tensor e4m3 quantization with the exact scale (modded-nanogpt gpt.py,
+ * _quantize_mlp_weights_and_scales, exact-scale calls): *scale = max(amax|src|, 1e-12) / 448
+ * in fp32, dst[i] = e4m3(src[i] / *scale) with IEEE fp32 division, round to nearest even,
+ * saturating at +-448 (OCP E4M3). src is f32 or bf16 (`dtype`), n >= 1 elements; dst and
+ * scale are device buffers written here.
+ */
+mlp_status mlp_quantize_e4m3(const void* src, int dtype, int64_t n, void* dst, float* scale,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The delayed-scale rule of modded-nanogpt gpt.py's _refresh_delayed_scale, for one slot, in
+ * fp32: a = amax with NaN/inf mapped to 0, clamped above at 1e12; returns max(a * gain, floor)
+ * if a > 0, else prev_scale. For relu(pre)^2 the page uses gain = 1.03/448, floor = 1e-6.
+ * Host only.
+ */
+float mlp_fp8_next_scale(float amax, float prev_scale, float gain, float floor_);
+
+/*
+ * Stages of mlp_fwd / mlp_fwd_infer / mlp_bwd, for mlp_time_stage_once:
+ *   UP        x W1^T with the activation epilogue (gated: gate and up together)
+ *   DOWN      a W2^T (the down projection, split-K reduce included)
+ *   RECOMPUTE the backward's x W1^T when desc->recompute
+ *   DACT      dout W2 with the d-activation epilogue
+ *   DW_DOWN   dW2 = dout^T a;   DX  dx = dpreact W1;   DW_UP  dW1 = dpreact^T x
+ *   ACT       the activation-only pass of the "only dW2" branch
+ *   WIDEN     the e4m3 -> bf16 widening of the e4m3 backward
+ */
+typedef enum mlp_stage {
+  MLP_STAGE_UP = 0, MLP_STAGE_DOWN = 1, MLP_STAGE_RECOMPUTE = 2, MLP_STAGE_DACT = 3,
+  MLP_STAGE_DW_DOWN = 4, MLP_STAGE_DX = 5, MLP_STAGE_DW_UP = 6, MLP_STAGE_ACT = 7,
+  MLP_STAGE_WIDEN = 8, MLP_STAGE_COUNT = 9
+} mlp_stage;
+
+/*
+ * Timing hook (profiling only): the next time the calling thread's mlp_* call runs `stage`,
+ * the library records `begin` on that call's stream before the stage's first launch and `end`
+ * after its last one; then the hook is cleared. begin/end are hipEvent_t created by the caller
+ * (hipEventCreate). Passing NULL events disarms the stage. Host only; nothing is enqueued here.
+ */
+mlp_status mlp_time_stage_once(int stage, void* begin, void* end);
+
+/* Human-readable name of a status; text of the last failed check on this thread. */
+const char* mlp_status_string(int status);
+const char* mlp_last_error(void);
+
+/* Version of this library's ABI (bumped on any change of the declarations above). */
+int mlp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GATED_MLP_H */

@@ -1,0 +1,166 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol, rejects bad
+arguments on the host before any HIP call, sizes its workspace, and its host-side fp8 scale
+rule matches the oracle's. No test here launches a kernel: every call below fails validation
+(or is host-only), so nothing reaches the GPU."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gated_mlp_gemms_amd as gm
+import oracle
+from gated_mlp_gemms_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000      # 16-byte aligned, never dereferenced: each call fails validation first
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "mlp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mlp_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = gm.lib()
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib._SIGNATURES), "binding and header disagree"
+    assert L.mlp_abi_version() == 1
+
+
+def _desc(**kw):
+    base = dict(M=300, d_in=264, hidden=712, d_out=200, act="swiglu", dtype="bf16")
+    base.update(kw)
+    return gm.make_desc(**base)
+
+
+def _fwd(d, x=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, out=FAKE, saved=FAKE, fp8=None, ws=FAKE, nws=None):
+    if nws is None:
+        nws = gm.lib().mlp_workspace_bytes(C.byref(d), gm.MLP_PHASE_FWD) if d.M > 0 else 0
+    return gm.lib().mlp_fwd(C.byref(d), x, wg, wu, wd, out, saved, C.byref(fp8) if fp8 else None, ws, nws, None)
+
+
+def _err():
+    return gm.lib().mlp_last_error().decode()
+
+
+def test_descriptor_checks():
+    L = gm.lib()
+    assert _fwd(_desc(M=0), nws=0) == gm._lib.MLP_ERR_INVALID_ARG
+    assert _fwd(_desc(d_in=260)) == gm._lib.MLP_ERR_ALIGNMENT and "multiples of 8" in _err()
+    assert _fwd(_desc(hidden=4, dtype="f32", d_in=4, d_out=6)) == gm._lib.MLP_ERR_ALIGNMENT
+    d = _desc()
+    d.act = 7
+    assert _fwd(d) == gm._lib.MLP_ERR_INVALID_ARG
+    d = _desc()
+    d.reserved = 1
+    assert _fwd(d) == gm._lib.MLP_ERR_INVALID_ARG
+    d = _desc(gate_mult=float("nan"))
+    assert _fwd(d) == gm._lib.MLP_ERR_INVALID_ARG
+    d = _desc(fp8_fwd=True)            # fp8 forward is ReLU^2 only
+    assert _fwd(d) == gm._lib.MLP_ERR_UNSUPPORTED
+    d = _desc(act="relu_sq", fp8_fwd=True, d_in=264)
+    assert _fwd(d, wu=None) == gm._lib.MLP_ERR_ALIGNMENT   # e4m3 rows need multiples of 16
+    assert L.mlp_workspace_bytes(None, 0) == 0
+    assert L.mlp_workspace_bytes(C.byref(_desc()), 9) == 0
+
+
+def test_pointer_checks():
+    d = _desc()
+    assert _fwd(d, x=None) == gm._lib.MLP_ERR_INVALID_ARG and "x is NULL" in _err()
+    assert _fwd(d, wu=None) == gm._lib.MLP_ERR_INVALID_ARG
+    assert _fwd(d, x=FAKE + 8) == gm._lib.MLP_ERR_ALIGNMENT
+    assert _fwd(d, saved=None) == gm._lib.MLP_ERR_INVALID_ARG          # training needs saved_preact
+    dr = _desc(recompute=True)
+    assert _fwd(dr, saved=FAKE) == gm._lib.MLP_ERR_INVALID_ARG         # ...and recompute forbids it
+    dq = _desc(act="relu_sq")
+    assert _fwd(dq) == gm._lib.MLP_ERR_INVALID_ARG and "w_up" in _err()  # ReLU^2 takes no W_up
+    fp8 = gm.make_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert _fwd(d, fp8=fp8) == gm._lib.MLP_ERR_INVALID_ARG             # fp8 struct without fp8_fwd
+    df = _desc(act="relu_sq", fp8_fwd=True, d_in=256, hidden=704, d_out=208)
+    assert _fwd(df, wu=None) == gm._lib.MLP_ERR_INVALID_ARG            # fp8_fwd without the struct
+    fp8.s_post = None
+    assert _fwd(df, wu=None, fp8=fp8) == gm._lib.MLP_ERR_INVALID_ARG and "s_post" in _err()
+
+
+def test_workspace_checks():
+    d = _desc()
+    need = gm.lib().mlp_workspace_bytes(C.byref(d), gm.MLP_PHASE_FWD)
+    assert need >= 300 * 712 * 2
+    assert _fwd(d, nws=need - 1) == gm._lib.MLP_ERR_WORKSPACE
+    assert _fwd(d, ws=None) == gm._lib.MLP_ERR_INVALID_ARG
+    assert _fwd(d, ws=FAKE + 4) == gm._lib.MLP_ERR_ALIGNMENT
+
+
+def test_backward_checks():
+    L = gm.lib()
+    d = _desc()
+    nws = L.mlp_workspace_bytes(C.byref(d), gm.MLP_PHASE_BWD)
+
+    def bwd(dd=d, saved=FAKE, dpre=None, dx=FAKE, dwg=FAKE, dwu=FAKE, dwd=FAKE, acc=0, ws=nws):
+        return L.mlp_bwd(C.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, saved, dpre, dx, dwg, dwu, dwd, acc,
+                         None, FAKE, ws, None)
+
+    assert bwd(dwu=None) == gm._lib.MLP_ERR_INVALID_ARG and "both" in _err()
+    assert bwd(acc=2) == gm._lib.MLP_ERR_INVALID_ARG
+    assert bwd(saved=None) == gm._lib.MLP_ERR_INVALID_ARG
+    assert bwd(dpre=FAKE + 2) == gm._lib.MLP_ERR_ALIGNMENT
+    assert bwd(ws=nws - 256) == gm._lib.MLP_ERR_WORKSPACE
+    dr = _desc(recompute=True)
+    assert bwd(dd=dr, saved=FAKE, ws=L.mlp_workspace_bytes(C.byref(dr), gm.MLP_PHASE_BWD)) == gm._lib.MLP_ERR_INVALID_ARG
+
+
+def test_workspace_sizes():
+    """The forward keeps a [M, H] activation in the workspace; the recompute backward holds the
+    recomputed [M, 2H] pre-activation instead of a dpreact buffer, so the caller saves the
+    M * 2 * H * dtype_size bytes of saved_preact (quack mlp.py, MLPRecomputeFunc docstring)."""
+    L = gm.lib()
+    for dt, es in (("bf16", 2), ("f32", 4)):
+        d = _desc(dtype=dt, d_in=256, hidden=704, d_out=208)
+        fwd = L.mlp_workspace_bytes(C.byref(d), gm.MLP_PHASE_FWD)
+        assert fwd >= 300 * 704 * es
+        assert L.mlp_workspace_bytes(C.byref(d), gm.MLP_PHASE_FWD_INFER) == fwd
+        b0 = L.mlp_workspace_bytes(C.byref(d), gm.MLP_PHASE_BWD)
+        dr = _desc(dtype=dt, d_in=256, hidden=704, d_out=208, recompute=True)
+        b1 = L.mlp_workspace_bytes(C.byref(dr), gm.MLP_PHASE_BWD)
+        assert b1 == b0 >= 300 * 704 * es + 300 * 2 * 704 * es
+
+
+def test_quantize_checks():
+    L = gm.lib()
+    assert L.mlp_quantize_e4m3(FAKE, 1, 0, FAKE, FAKE, FAKE, 256, None) == gm._lib.MLP_ERR_INVALID_ARG
+    assert L.mlp_quantize_e4m3(FAKE, 5, 10, FAKE, FAKE, FAKE, 256, None) == gm._lib.MLP_ERR_INVALID_ARG
+    assert L.mlp_quantize_e4m3(FAKE, 1, 10, FAKE, FAKE, FAKE, 8, None) == gm._lib.MLP_ERR_WORKSPACE
+    assert L.mlp_quantize_e4m3(None, 1, 10, FAKE, FAKE, FAKE, 256, None) == gm._lib.MLP_ERR_INVALID_ARG
+
+
+def test_next_scale_matches_oracle():
+    rng = np.random.default_rng(0)
+    amaxes = list(np.abs(rng.standard_normal(200)).astype(np.float32) * 10.0 ** rng.integers(-8, 14, 200))
+    amaxes += [0.0, float("nan"), float("inf"), float("-inf"), 1e-30, 5e11, 2e12, 448.0]
+    for gain, floor in ((1.03 / 448.0, 1e-6), (1.25 / 57344.0, 1e-12)):
+        for a in amaxes:
+            ours = np.float32(gm.mlp_fp8_next_scale(float(a), 0.5, gain, floor))
+            ref = oracle.next_delayed_scale(a, 0.5, gain, floor)
+            assert ours == ref, (a, gain, ours, ref)
+
+
+def test_product_and_oracle_share_no_code():
+    """The HIP path never imports the oracle and the oracle never imports the HIP path."""
+    pat_oracle = re.compile(r"^\s*(from|import)\s+oracle\b", re.M)
+    pat_prod = re.compile(r"^\s*(from|import)\s+gated_mlp_gemms_amd\b", re.M)
+    pkg = os.path.join(ROOT, "gated_mlp_gemms_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not pat_oracle.search(text), f
+                assert "oracle" not in text or f.endswith(".py") and "oracle" not in text, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith(".py"):
+            assert not pat_prod.search(open(os.path.join(ROOT, "oracle", f)).read()), f

@@ -1,0 +1,126 @@
+"""GPU parity at the full workload sizes, in the launch configuration the bench times (the same
+entry points, flags and shapes), against the float64 oracle on sampled outputs.
+
+Sampled entries are computed one by one from their definitions (``oracle.gated_sampled`` /
+``relu_sq_sampled``): rows of out and dx, and hidden units of every weight gradient. The samples
+include the first and last rows/units and tile boundaries.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import TOL, announce, assert_close, f64, run
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(n, k=24, seed=0):
+    rng = np.random.default_rng(seed)
+    edges = [0, n - 1] + [b for b in (127, 128, 255, 256, 511, 512) if b < n]
+    rest = rng.choice(n, size=max(0, k - len(edges)), replace=False)
+    return np.unique(np.concatenate([edges, rest]).astype(np.int64))
+
+
+def _check_gated(w, t, r, mode):
+    a = {k: f64(v) for k, v in t.items()}
+    rows, units = _sample(w.M, seed=1), _sample(w.hidden, seed=2)
+    s = oracle.gated_sampled(a["dout"], a["x"], a["w_gate"], a["w_up"], a["w_down"], rows, units,
+                             w.gate_mult, w.down_mult, mode)
+    tol = TOL[w.dtype]
+    assert_close("out[rows]", f64(r.out[rows]), s["out_rows"], tol)
+    assert_close("dx[rows]", f64(r.dx[rows]), s["dx_rows"], tol)
+    grads = [("dw_down[:,u]", r.dw_down[:, units], s["dw_down_cols"], "dw_down", (slice(None), units)),
+             ("dw_gate[u]", r.dw_gate[units], s["dw_gate_rows"], "dw_gate", (units,)),
+             ("dw_up[u]", r.dw_up[units], s["dw_up_rows"], "dw_up", (units,))]
+    for name, g, ref, key, idx in grads:
+        if w.grad_accum:
+            before = a[key][idx]
+            assert_close(name + "+buf", f64(g), oracle.accumulate(before, ref), tol)
+            assert_close(name + " delta", f64(g) - before, ref, tol)
+        else:
+            assert_close(name, f64(g), ref, tol)
+
+
+def test_llama_swiglu_full_size():
+    w = WORKLOADS["llama_swiglu_bf16_m2048_d4096_h11008"]
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.forward_infer()
+    r.backward(dpreact=False)
+    torch.cuda.synchronize()
+    assert torch.equal(r.out, r.out_infer)
+    # the saved g|u of sampled rows
+    a = {k: f64(v) for k, v in t.items()}
+    rows = _sample(w.M, seed=3)
+    f = oracle.gated_forward(a["x"][rows], a["w_gate"], a["w_up"], a["w_down"])
+    assert_close("g[rows]", f64(r.saved[rows, : w.hidden]), f["g"], TOL["bf16"])
+    assert_close("u[rows]", f64(r.saved[rows, w.hidden:]), f["u"], TOL["bf16"])
+    _check_gated(w, t, r, "outside")
+
+
+@pytest.mark.parametrize("mode", ["outside", "inside"])
+def test_falcon_h1_recompute_accumulate_full_size(mode):
+    w = WORKLOADS["falcon_h1_swiglu_bf16_m8192_d2048_h4864"]
+    announce(f"{w.name} {mode}")
+    t = make_inputs(w)
+    r = run(w, t, gate_mode=mode)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    _check_gated(w, t, r, mode)
+
+
+def _check_relu(w, t, r, x64=None, w1=None, w2=None, tol=None):
+    a = {k: f64(v) for k, v in t.items()}
+    x64 = a["x"] if x64 is None else x64
+    w1 = a["w1"] if w1 is None else w1
+    w2 = a["w2"] if w2 is None else w2
+    rows, units = _sample(w.M, seed=4), _sample(w.hidden, seed=5)
+    s = oracle.relu_sq_sampled(a["dout"], x64, w1, w2, rows, units, w.down_mult)
+    tol = tol or TOL[w.dtype]
+    assert_close("dx[rows]", f64(r.dx[rows]), s["dx_rows"], tol)
+    assert_close("dw2[:,u]", f64(r.dw_down[:, units]), s["dw2_cols"], tol)
+    assert_close("dw1[u]", f64(r.dw_gate[units]), s["dw1_rows"], tol)
+    return rows, s
+
+
+def test_gpt_relu_sq_full_size():
+    w = WORKLOADS["gpt_relu2_bf16_m49152_d768_h3072"]
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    rows, s = _check_relu(w, t, r)
+    assert_close("out[rows]", f64(r.out[rows]), s["out_rows"], TOL["bf16"])
+
+
+def test_gpt_relu_sq_fp8_full_size():
+    w = WORKLOADS["gpt_relu2_fp8fwd_m49152_d768_h3072"]
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.quantize()
+    r.forward()
+    r.refresh_post_scale()
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    sc = r.scales.cpu().numpy()
+    xq, w1q, w2q = r.x_q.cpu().numpy(), r.w1_q.cpu().numpy(), r.w2_q.cpu().numpy()
+    # the quantizer is bit-exact with the oracle's
+    for name, q, src, s_gpu in (("x", xq, t["x"], sc[0]), ("w1", w1q, t["w1"], sc[1]), ("w2", w2q, t["w2"], sc[2])):
+        q_ref, s_ref = oracle.quantize_per_tensor(src.to(torch.float32).numpy())
+        assert s_gpu == s_ref, name
+        np.testing.assert_array_equal(q, q_ref, err_msg=name)
+    rows = _sample(w.M, seed=6)
+    f = oracle.relu_sq_fp8_forward(xq[rows], sc[0], w1q, sc[1], w2q, sc[2], s_post=sc[3], down_mult=w.down_mult)
+    assert_close("out[rows]", f64(r.out[rows]), f["out"], TOL["fp8"])
+    assert_close("pre[rows]", f64(r.saved[rows]), f["pre"], TOL["bf16"])
+    xh = oracle.dequantize(xq, sc[0])
+    _check_relu(w, t, r, xh, oracle.dequantize(w1q, sc[1]), oracle.dequantize(w2q, sc[2]), TOL["fp8"])

@@ -1,0 +1,256 @@
+"""GPU parity of the HIP path against the float64 oracle, through the C ABI.
+
+Small problems are compared in full; their sizes span several tiles and end in ragged tails
+(M, d_in, hidden, d_out not multiples of the 256/128 tiles). The invariants at the end hold
+bit for bit on the GPU: inference forward == training forward, recompute == saved
+pre-activation, in-place dpreact == separate buffer, run-to-run determinism, power-of-two
+down_mult scaling, and the "only dW_down" skip branch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import TOL, announce, assert_close, check_full, f64, run
+from workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(act, dtype, M, d, H, do, **kw):
+    name = f"{act}_{dtype}_m{M}_d{d}_h{H}_o{do}"
+    return Workload(name, act, dtype, (M,), d, H, do, **kw)
+
+
+SMALL_GATED = [
+    _w("swiglu", "bf16", 300, 264, 712, 200),
+    _w("swiglu", "bf16", 300, 264, 712, 200, gate_mult=1.125, down_mult=2.0),
+    _w("swiglu", "bf16", 517, 512, 1400, 520, gate_mult=0.75, down_mult=1.5, seed=3),
+    _w("swiglu", "f32", 77, 132, 200, 68, gate_mult=1.125, down_mult=2.0),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_GATED, ids=lambda w: w.name)
+@pytest.mark.parametrize("mode", ["outside", "inside"])
+def test_gated_small(w, mode):
+    announce(f"gated {w.name} {mode}")
+    t = make_inputs(w)
+    r = run(w, t, gate_mode=mode)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    check_full(w, t, r, mode)
+
+
+def test_swiglu_f32_reference_config():
+    w = WORKLOADS["swiglu_f32_m64_d128_h384"]
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.forward_infer()
+    r.backward()
+    torch.cuda.synchronize()
+    check_full(w, t, r)
+    assert torch.equal(r.out, r.out_infer)
+
+
+@pytest.mark.parametrize("mode", ["outside", "inside"])
+def test_gated_recompute_accumulate_small(mode):
+    w = _w("swiglu", "bf16", 390, 256, 704, 264, gate_mult=1.125, down_mult=2.0, recompute=True, grad_accum=True)
+    announce(f"{w.name} recompute+accum {mode}")
+    t = make_inputs(w)
+    r = run(w, t, gate_mode=mode)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    check_full(w, t, r, mode)
+
+
+@pytest.mark.parametrize("w", [
+    _w("relu_sq", "bf16", 333, 200, 520, 264),
+    _w("relu_sq", "bf16", 600, 768, 3072, 768, down_mult=2.0, seed=5),
+    _w("relu_sq", "f32", 70, 44, 96, 36),
+    _w("relu_sq", "bf16", 257, 136, 392, 128, recompute=True, grad_accum=True),
+], ids=lambda w: w.name)
+def test_relu_sq_small(w):
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    check_full(w, t, r)
+
+
+def test_m_equals_one():
+    w = _w("swiglu", "bf16", 1, 64, 128, 64)
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    check_full(w, t, r)
+
+
+# ---- e4m3 ---------------------------------------------------------------------------------
+
+def test_quantize_e4m3_bit_exact():
+    import gated_mlp_gemms_amd as gm
+    rng = np.random.default_rng(0)
+    for dt, n in ((torch.bfloat16, 4099), (torch.float32, 70001), (torch.bfloat16, 1)):
+        announce(f"quantize {dt} n={n}")
+        v = torch.from_numpy(rng.standard_normal(n).astype(np.float32) * 3.0).to(dt)
+        v[0] = -2.5   # a value with a distinct magnitude
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        scale = torch.empty(1, dtype=torch.float32, device="cuda")
+        gm.mlp_quantize_e4m3(v.cuda(), dst, scale)
+        torch.cuda.synchronize()
+        q_ref, s_ref = oracle.quantize_per_tensor(v.to(torch.float32).numpy())
+        assert np.float32(scale.item()) == s_ref
+        np.testing.assert_array_equal(dst.cpu().numpy(), q_ref)
+
+
+def _fp8_run(w, t, announce_name):
+    announce(announce_name)
+    r = run(w, t)
+    r.quantize()
+    r.forward()                   # bootstrap post scale 1.0: records amax
+    r.refresh_post_scale()
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    return r
+
+
+def _fp8_oracle_inputs(r):
+    s = r.scales.cpu().numpy()
+    return (r.x_q.cpu().numpy(), s[0], r.w1_q.cpu().numpy(), s[1], r.w2_q.cpu().numpy(), s[2], s[3])
+
+
+@pytest.mark.parametrize("M,d,H,do,dm", [(300, 256, 704, 208, 1.0), (129, 768, 3072, 768, 2.0)])
+def test_fp8_forward_small(M, d, H, do, dm):
+    w = _w("relu_sq", "bf16", M, d, H, do, down_mult=dm, fp8_fwd=True)
+    t = make_inputs(w)
+    r = _fp8_run(w, t, w.name)
+    xq, sx, w1q, s1, w2q, s2, sp = _fp8_oracle_inputs(r)
+    # the quantized operands are bit-exact with the oracle's quantizer
+    for name, q, src in (("x", xq, t["x"]), ("w1", w1q, t["w1"]), ("w2", w2q, t["w2"])):
+        q_ref, s_ref = oracle.quantize_per_tensor(src.to(torch.float32).numpy())
+        np.testing.assert_array_equal(q, q_ref, err_msg=name)
+    f = oracle.relu_sq_fp8_forward(xq, sx, w1q, s1, w2q, s2, s_post=sp, down_mult=dm)
+    f_noq = oracle.relu_sq_fp8_forward(xq, sx, w1q, s1, w2q, s2, s_post=None, down_mult=dm)
+    assert_close("out", f64(r.out), f["out"], TOL["fp8"])
+    assert_close("out vs no post-q", f64(r.out), f_noq["out"], TOL["fp8"])
+    assert_close("pre", f64(r.saved), f["pre"], TOL["bf16"])
+    # the delayed scale came from this run's amax
+    # the delayed post scale came from this problem's max relu(pre)^2 (headroom 1.03)
+    assert abs(sp / (f["post_amax"] * 1.03 / 448) - 1) < 1e-2
+    b = oracle.relu_sq_fp8_backward(f64(r.dout), xq, sx, w1q, s1, w2q, s2, down_mult=dm)
+    for name, g, ref in (("dx", r.dx, b["dx"]), ("dw1", r.dw_gate, b["dw1"]), ("dw2", r.dw_down, b["dw2"])):
+        assert_close(name, f64(g), ref, TOL["fp8"])
+
+
+def test_fp8_on_grid_equals_bf16_path():
+    """Inputs on the e4m3 grid with amax = 448 * 2^k quantize exactly, so the fp8 forward must
+    agree with the bf16 forward up to accumulation order (outputs are then bf16-rounded)."""
+    rng = np.random.default_rng(1)
+    grid = oracle.e4m3_grid()
+    M, d, H = 256, 256, 512
+
+    def on_grid(shape, k):
+        v = rng.choice(grid[:110], size=shape) * rng.choice([-1.0, 1.0], size=shape)
+        v.flat[0] = 448.0
+        return torch.from_numpy((v * 2.0 ** k).astype(np.float32)).to(torch.bfloat16)
+
+    t = {"x": on_grid((M, d), -8), "w1": on_grid((H, d), -12), "w2": on_grid((d, H), -12),
+         "dout": torch.randn(M, d, generator=torch.Generator().manual_seed(0)).to(torch.bfloat16)}
+    w8 = _w("relu_sq", "bf16", M, d, H, d, fp8_fwd=True)
+    wb = _w("relu_sq", "bf16", M, d, H, d)
+    announce("fp8 on-grid vs bf16")
+    r8 = run(w8, t)
+    r8.quantize()
+    r8.forward()
+    rb = run(wb, t)
+    rb.forward()
+    torch.cuda.synchronize()
+    s = r8.scales.cpu().numpy()
+    assert s[0] == 2.0 ** -8 and s[1] == 2.0 ** -12 and s[2] == 2.0 ** -12
+    # pre is computed in fp32 either way; both sides round it to bf16
+    assert_close("pre fp8 vs bf16", f64(r8.saved), f64(rb.saved), 1e-2)
+
+
+# ---- invariants -------------------------------------------------------------------------------
+
+def test_infer_equals_train_forward_and_determinism():
+    w = _w("swiglu", "bf16", 300, 264, 712, 200, gate_mult=1.125, down_mult=2.0)
+    announce("infer == train, determinism")
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.forward_infer()
+    r.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(r.out, r.out_infer)
+    first = {k: v.clone() for k, v in r.grads().items()}
+    out1 = r.out.clone()
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(out1, r.out)
+    for k, v in r.grads().items():
+        assert torch.equal(first[k], v), k
+
+
+@pytest.mark.parametrize("act", ["swiglu", "relu_sq"])
+def test_recompute_equals_saved_and_inplace(act):
+    kw = dict(gate_mult=1.125, down_mult=2.0) if act == "swiglu" else {}
+    base = _w(act, "bf16", 300, 264, 712, 200, **kw)
+    t = make_inputs(base)
+    announce(f"recompute/in-place invariants {act}")
+    r0 = run(base, t)
+    r0.forward()
+    r0.backward()
+    r1 = run(base.replace(recompute=True), t)
+    r1.forward()
+    r1.backward()
+    r2 = run(base, t, dpreact_in_place=True)
+    r2.forward()
+    r2.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(r0.out, r1.out) and torch.equal(r0.out, r2.out)
+    for k, v in r0.grads().items():
+        assert torch.equal(v, r1.grads()[k]), f"recompute {k}"
+        assert torch.equal(v, r2.grads()[k]), f"in-place {k}"
+
+
+def test_power_of_two_down_mult_is_exact():
+    w1 = _w("swiglu", "bf16", 300, 264, 712, 200, gate_mult=1.125)
+    w2 = w1.replace(down_mult=2.0)
+    t = make_inputs(w1)
+    announce("down_mult = 2 exact")
+    r1, r2 = run(w1, t), run(w2, t)
+    for r in (r1, r2):
+        r.forward()
+        r.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(r2.out.float(), 2 * r1.out.float())
+    for k, v in r1.grads().items():
+        assert torch.equal(r2.grads()[k].float(), 2 * v.float()), k
+
+
+@pytest.mark.parametrize("act", ["swiglu", "relu_sq"])
+def test_only_dw_down_branch(act):
+    w = _w(act, "bf16", 300, 264, 712, 200)
+    t = make_inputs(w)
+    announce(f"only-dW_down branch {act}")
+    r = run(w, t)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    full = r.dw_down.clone()
+    r.dw_down.zero_()
+    r.backward(dx=False, dw_gate=False)
+    torch.cuda.synchronize()
+    assert torch.equal(full, r.dw_down)
