@@ -1,6 +1,6 @@
 // bf16 GEMMs with A K-major and B MN-major (dout W, dpreact W): the fused d-activation
 // backward kernels, dx and their split-K partial form.
-#include "gemm_kernel.hpp"
+#include "gemm_dma.hpp"
 #include "launch.hpp"
 
 namespace gmlp {
@@ -8,12 +8,12 @@ namespace gmlp {
 template <int BM, int BN>
 static hipError_t dispatch(DType io, int epi, const GemmArgs& a, int grid, hipStream_t s) {
   switch (epi) {
-    case EPI_DGATED: return launch_gemm<bf16, bf16, BM, BN, true, false, EPI_DGATED>(a, grid, s);
-    case EPI_DACT: return launch_gemm<bf16, bf16, BM, BN, true, false, EPI_DACT>(a, grid, s);
+    case EPI_DGATED: return launch_gemm_dma<bf16, bf16, BM, BN, true, false, EPI_DGATED>(a, grid, s);
+    case EPI_DACT: return launch_gemm_dma<bf16, bf16, BM, BN, true, false, EPI_DACT>(a, grid, s);
     case EPI_STORE:
-      if (io == DT_BF16) return launch_gemm<bf16, bf16, BM, BN, true, false, EPI_STORE>(a, grid, s);
+      if (io == DT_BF16) return launch_gemm_dma<bf16, bf16, BM, BN, true, false, EPI_STORE>(a, grid, s);
       return hipErrorInvalidValue;
-    case EPI_PARTIAL: return launch_gemm<bf16, float, BM, BN, true, false, EPI_PARTIAL>(a, grid, s);
+    case EPI_PARTIAL: return launch_gemm_dma<bf16, float, BM, BN, true, false, EPI_PARTIAL>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,6 +1,6 @@
 // bf16 GEMMs with both operands K-major (x W^T): the fused gate/up forward, the ReLU^2
 // forward, the down projection and their split-K partial form.
-#include "gemm_kernel.hpp"
+#include "gemm_dma.hpp"
 #include "launch.hpp"
 
 namespace gmlp {
@@ -8,12 +8,12 @@ namespace gmlp {
 template <int BM, int BN>
 static hipError_t dispatch(DType io, int epi, const GemmArgs& a, int grid, hipStream_t s) {
   switch (epi) {
-    case EPI_GATED: return launch_gemm<bf16, bf16, BM, BN, true, true, EPI_GATED>(a, grid, s);
-    case EPI_ACT: return launch_gemm<bf16, bf16, BM, BN, true, true, EPI_ACT>(a, grid, s);
+    case EPI_GATED: return launch_gemm_dma<bf16, bf16, BM, BN, true, true, EPI_GATED>(a, grid, s);
+    case EPI_ACT: return launch_gemm_dma<bf16, bf16, BM, BN, true, true, EPI_ACT>(a, grid, s);
     case EPI_STORE:
-      if (io == DT_BF16) return launch_gemm<bf16, bf16, BM, BN, true, true, EPI_STORE>(a, grid, s);
+      if (io == DT_BF16) return launch_gemm_dma<bf16, bf16, BM, BN, true, true, EPI_STORE>(a, grid, s);
       return hipErrorInvalidValue;
-    case EPI_PARTIAL: return launch_gemm<bf16, float, BM, BN, true, true, EPI_PARTIAL>(a, grid, s);
+    case EPI_PARTIAL: return launch_gemm_dma<bf16, float, BM, BN, true, true, EPI_PARTIAL>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

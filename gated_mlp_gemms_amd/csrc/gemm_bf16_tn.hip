@@ -1,6 +1,6 @@
 // bf16 GEMMs with both operands MN-major (dout^T a, dpreact^T x): the weight gradients,
 // written in bf16 or added into fp32 buffers, and their split-K partial form.
-#include "gemm_kernel.hpp"
+#include "gemm_dma.hpp"
 #include "launch.hpp"
 
 namespace gmlp {
@@ -9,9 +9,9 @@ template <int BM, int BN>
 static hipError_t dispatch(DType io, int epi, const GemmArgs& a, int grid, hipStream_t s) {
   switch (epi) {
     case EPI_STORE:
-      if (io == DT_BF16) return launch_gemm<bf16, bf16, BM, BN, false, false, EPI_STORE>(a, grid, s);
-      return launch_gemm<bf16, float, BM, BN, false, false, EPI_STORE>(a, grid, s);
-    case EPI_PARTIAL: return launch_gemm<bf16, float, BM, BN, false, false, EPI_PARTIAL>(a, grid, s);
+      if (io == DT_BF16) return launch_gemm_dma<bf16, bf16, BM, BN, false, false, EPI_STORE>(a, grid, s);
+      return launch_gemm_dma<bf16, float, BM, BN, false, false, EPI_STORE>(a, grid, s);
+    case EPI_PARTIAL: return launch_gemm_dma<bf16, float, BM, BN, false, false, EPI_PARTIAL>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,6 +1,6 @@
 // e4m3 x e4m3 GEMMs (both operands K-major) of the ReLU^2 forward: x_q W1_q^T with the
 // quantizing ReLU^2 epilogue, and post_q W2_q^T with the scaled bf16 store.
-#include "gemm_kernel.hpp"
+#include "gemm_dma.hpp"
 #include "launch.hpp"
 
 namespace gmlp {
@@ -8,11 +8,11 @@ namespace gmlp {
 template <int BM, int BN>
 static hipError_t dispatch(DType io, int epi, const GemmArgs& a, int grid, hipStream_t s) {
   switch (epi) {
-    case EPI_F8ACT: return launch_gemm<e4m3, bf16, BM, BN, true, true, EPI_F8ACT>(a, grid, s);
+    case EPI_F8ACT: return launch_gemm_dma<e4m3, bf16, BM, BN, true, true, EPI_F8ACT>(a, grid, s);
     case EPI_STORE:
-      if (io == DT_BF16) return launch_gemm<e4m3, bf16, BM, BN, true, true, EPI_STORE>(a, grid, s);
+      if (io == DT_BF16) return launch_gemm_dma<e4m3, bf16, BM, BN, true, true, EPI_STORE>(a, grid, s);
       return hipErrorInvalidValue;
-    case EPI_PARTIAL: return launch_gemm<e4m3, float, BM, BN, true, true, EPI_PARTIAL>(a, grid, s);
+    case EPI_PARTIAL: return launch_gemm_dma<e4m3, float, BM, BN, true, true, EPI_PARTIAL>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -206,6 +206,145 @@ template <bool KMAJ, typename T, int ROWS> struct TileSel;
 template <typename T, int ROWS> struct TileSel<true, T, ROWS> { using type = KMajorTile<T, ROWS>; };
 template <typename T, int ROWS> struct TileSel<false, T, ROWS> { using type = MNMajorTile<T, ROWS>; };
 
+// ---- fused epilogue ---------------------------------------------------------------------------
+// acc[i][j] holds the 32x32 block (i, j) of the wave's WM x WN tile with the MFMA operands
+// swapped (B tile rows as the instruction's rows): lane l owns output row m = l % 32 of the
+// block and, in register 4g + r, column 8g + 4(l / 32) + r.
+template <int EPI, typename IoT, int BM, int BN, int MI, int NI>
+__device__ __forceinline__ void epilogue(const GemmArgs& p, f32x16 (&acc)[MI][NI], int m0, int n0,
+                                         int split, int wm, int wn, int lane) {
+  constexpr bool GATED = EPI == EPI_GATED;
+  constexpr int WM = BM / 2, WN = BN / 2;
+  const int frow = lane & 31, fhalf = lane >> 5;
+  float alpha = p.alpha;
+  if (p.alpha_dev0) alpha *= *p.alpha_dev0;
+  if (p.alpha_dev1) alpha *= *p.alpha_dev1;
+  float local_amax = 0.0f;
+  (void)local_amax;
+
+  constexpr int NJ = GATED ? NI / 2 : NI;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int m = m0 + wm * WM + i * 32 + frow;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int nb = GATED ? n0 + wn * (BN / 4) + j * 32 : n0 + wn * WN + j * 32;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = nb + 8 * g + 4 * fhalf;
+        if (n >= p.N) continue;
+        // split-K partials stay unscaled: the reduce kernel applies alpha once
+        const float scale = EPI == EPI_PARTIAL ? 1.0f : alpha;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = scale * acc[i][j][4 * g + r];
+
+        if constexpr (EPI == EPI_STORE) {
+          const bool lo = m < p.c_split;
+          void* base = lo ? p.C0 : p.C1;
+          const int row = lo ? m : m - p.c_split;
+          if (p.accumulate) {
+            float* q = reinterpret_cast<float*>(elem_ptr<float>(base, row, p.ldc0, n));
+            float o[4];
+            Vec4<float>::load(q, o);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] += v[r];
+            Vec4<float>::store(q, o);
+          } else {
+            Vec4<IoT>::store(elem_ptr<IoT>(base, row, p.ldc0, n), v);
+          }
+        } else if constexpr (EPI == EPI_PARTIAL) {
+          const int64_t prow = (int64_t)split * p.M + m;
+          Vec4<float>::store(elem_ptr<float>(p.partial, prow, p.N, n), v);
+        } else if constexpr (EPI == EPI_GATED) {
+          float u[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) u[r] = alpha * acc[i][j + NJ][4 * g + r];
+          if (p.flags & 1) {
+            Vec4<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), v);
+            Vec4<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, p.half + n), u);
+          }
+          if (p.flags & 2) {
+            float a[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (p.gate_inside) {
+                const float z = p.gate_mult * v[r];
+                a[r] = z * sigmoidf_(z) * u[r];
+              } else {
+                a[r] = p.gate_mult * (v[r] * sigmoidf_(v[r])) * u[r];
+              }
+            }
+            Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), a);
+          }
+        } else if constexpr (EPI == EPI_ACT) {
+          if (p.flags & 1) Vec4<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), v);
+          if (p.flags & 2) {
+            float q[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) { const float t = fmaxf(v[r], 0.0f); q[r] = t * t; }
+            Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), q);
+          }
+        } else if constexpr (EPI == EPI_DGATED) {
+          float gg[4], uu[4], dg[4], du[4], a[4];
+          Vec4<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), gg);
+          Vec4<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, p.half + n), uu);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gm = p.gate_mult;
+            const float z = p.gate_inside ? gm * gg[r] : gg[r];
+            const float sg = sigmoidf_(z);
+            const float silu = z * sg;
+            const float dsilu = sg * (1.0f + z * (1.0f - sg));
+            if (p.gate_inside) {
+              dg[r] = v[r] * uu[r] * gm * dsilu;
+              du[r] = v[r] * silu;
+              a[r] = silu * uu[r];
+            } else {
+              dg[r] = v[r] * gm * uu[r] * dsilu;
+              du[r] = v[r] * gm * silu;
+              a[r] = gm * silu * uu[r];
+            }
+          }
+          Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), dg);
+          Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, p.half + n), du);
+          if (p.flags & 2) Vec4<IoT>::store(elem_ptr<IoT>(p.C1, m, p.ldc1, n), a);
+        } else if constexpr (EPI == EPI_DACT) {
+          float pre[4], dpre[4], post[4];
+          Vec4<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), pre);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float t = fmaxf(pre[r], 0.0f);
+            dpre[r] = v[r] * 2.0f * t;
+            post[r] = t * t;
+          }
+          Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), dpre);
+          if (p.flags & 2) Vec4<IoT>::store(elem_ptr<IoT>(p.C1, m, p.ldc1, n), post);
+        } else if constexpr (EPI == EPI_F8ACT) {
+          if (p.flags & 1) Vec4<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), v);
+          const float sp = *p.s_post;
+          uint32_t packed = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float t = fmaxf(v[r], 0.0f);
+            const float post = t * t;
+            local_amax = fmaxf(local_amax, post);
+            packed |= f32_to_e4m3(__fdiv_rn(post, sp)) << (8 * r);
+          }
+          *reinterpret_cast<uint32_t*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) = packed;
+        }
+      }
+    }
+  }
+  if constexpr (EPI == EPI_F8ACT) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) local_amax = fmaxf(local_amax, __shfl_xor(local_amax, off));
+    if (lane == 0 && local_amax > 0.0f)
+      atomicMax(reinterpret_cast<unsigned int*>(p.amax), __float_as_uint(local_amax));
+  }
+}
+
 // ---- the kernel --------------------------------------------------------------------------------
 
 template <typename T, typename IoT, int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI>
@@ -343,134 +482,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs p) {
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds row m (one per 32-row block) and 4 groups of 4 columns
-  float alpha = p.alpha;
-  if (p.alpha_dev0) alpha *= *p.alpha_dev0;
-  if (p.alpha_dev1) alpha *= *p.alpha_dev1;
-  float local_amax = 0.0f;
-  (void)local_amax;
-
-  constexpr int NJ = GATED ? NI / 2 : NI;
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int m = m0 + wm * WM + i * 32 + frow;
-    if (m >= p.M) continue;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int nb = GATED ? n0 + wn * (BN / 4) + j * 32 : n0 + wn * WN + j * 32;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = nb + 8 * g + 4 * fhalf;
-        if (n >= p.N) continue;
-        // split-K partials stay unscaled: the reduce kernel applies alpha once
-        const float scale = EPI == EPI_PARTIAL ? 1.0f : alpha;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = scale * acc[i][j][4 * g + r];
-
-        if constexpr (EPI == EPI_STORE) {
-          const bool lo = m < p.c_split;
-          void* base = lo ? p.C0 : p.C1;
-          const int row = lo ? m : m - p.c_split;
-          if (p.accumulate) {
-            float* q = reinterpret_cast<float*>(elem_ptr<float>(base, row, p.ldc0, n));
-            float o[4];
-            Vec4<float>::load(q, o);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] += v[r];
-            Vec4<float>::store(q, o);
-          } else {
-            Vec4<IoT>::store(elem_ptr<IoT>(base, row, p.ldc0, n), v);
-          }
-        } else if constexpr (EPI == EPI_PARTIAL) {
-          const int64_t prow = (int64_t)split * p.M + m;
-          Vec4<float>::store(elem_ptr<float>(p.partial, prow, p.N, n), v);
-        } else if constexpr (EPI == EPI_GATED) {
-          float u[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) u[r] = alpha * acc[i][j + NJ][4 * g + r];
-          if (p.flags & 1) {
-            Vec4<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), v);
-            Vec4<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, p.half + n), u);
-          }
-          if (p.flags & 2) {
-            float a[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (p.gate_inside) {
-                const float z = p.gate_mult * v[r];
-                a[r] = z * sigmoidf_(z) * u[r];
-              } else {
-                a[r] = p.gate_mult * (v[r] * sigmoidf_(v[r])) * u[r];
-              }
-            }
-            Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), a);
-          }
-        } else if constexpr (EPI == EPI_ACT) {
-          if (p.flags & 1) Vec4<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), v);
-          if (p.flags & 2) {
-            float q[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) { const float t = fmaxf(v[r], 0.0f); q[r] = t * t; }
-            Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), q);
-          }
-        } else if constexpr (EPI == EPI_DGATED) {
-          float gg[4], uu[4], dg[4], du[4], a[4];
-          Vec4<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), gg);
-          Vec4<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, p.half + n), uu);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float gm = p.gate_mult;
-            const float z = p.gate_inside ? gm * gg[r] : gg[r];
-            const float sg = sigmoidf_(z);
-            const float silu = z * sg;
-            const float dsilu = sg * (1.0f + z * (1.0f - sg));
-            if (p.gate_inside) {
-              dg[r] = v[r] * uu[r] * gm * dsilu;
-              du[r] = v[r] * silu;
-              a[r] = silu * uu[r];
-            } else {
-              dg[r] = v[r] * gm * uu[r] * dsilu;
-              du[r] = v[r] * gm * silu;
-              a[r] = gm * silu * uu[r];
-            }
-          }
-          Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), dg);
-          Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, p.half + n), du);
-          if (p.flags & 2) Vec4<IoT>::store(elem_ptr<IoT>(p.C1, m, p.ldc1, n), a);
-        } else if constexpr (EPI == EPI_DACT) {
-          float pre[4], dpre[4], post[4];
-          Vec4<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), pre);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float t = fmaxf(pre[r], 0.0f);
-            dpre[r] = v[r] * 2.0f * t;
-            post[r] = t * t;
-          }
-          Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), dpre);
-          if (p.flags & 2) Vec4<IoT>::store(elem_ptr<IoT>(p.C1, m, p.ldc1, n), post);
-        } else if constexpr (EPI == EPI_F8ACT) {
-          if (p.flags & 1) Vec4<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), v);
-          const float sp = *p.s_post;
-          uint32_t packed = 0;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float t = fmaxf(v[r], 0.0f);
-            const float post = t * t;
-            local_amax = fmaxf(local_amax, post);
-            packed |= f32_to_e4m3(__fdiv_rn(post, sp)) << (8 * r);
-          }
-          *reinterpret_cast<uint32_t*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) = packed;
-        }
-      }
-    }
-  }
-  if constexpr (EPI == EPI_F8ACT) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) local_amax = fmaxf(local_amax, __shfl_xor(local_amax, off));
-    if (lane == 0 && local_amax > 0.0f)
-      atomicMax(reinterpret_cast<unsigned int*>(p.amax), __float_as_uint(local_amax));
-  }
+  epilogue<EPI, IoT, BM, BN, MI, NI>(p, acc, m0, n0, split, wm, wn, lane);
 }
 
 template <typename T, typename IoT, int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI>
