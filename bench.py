@@ -95,6 +95,9 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
     ap.add_argument("--cpu-rows", type=int, default=512, help="tokens in the oracle's CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before warmup (a known-size "
+                         "reference for profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this engine is single-GPU "
@@ -106,6 +109,15 @@ def main():
     import gated_mlp_gemms_amd as gm
     from gated_mlp_gemms_amd.runner import runner_for
     from workloads import HEADLINE, WORKLOADS, make_inputs
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     w = WORKLOADS[args.workload or HEADLINE]
     log(f"[bench] workload {w.name}: building inputs")

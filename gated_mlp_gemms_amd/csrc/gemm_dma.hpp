@@ -1,18 +1,23 @@
 // The bf16 / e4m3 GEMM kernel: the same contraction and fused epilogues as gemm_kernel.hpp,
 // with operands moved HBM -> LDS by the LDS-DMA form of the global load (no VGPR staging, no
-// LDS store instructions) and a software-pipelined MFMA loop.
+// LDS store instructions) through a ring of LDS stages, and a software-pipelined MFMA loop.
 //
-// Per workgroup (4 wave64, 2 x 2 waves of WM x WN): two LDS stages of BK = 128 bytes of K.
-//  * K-major operand tiles are [rows][128 B], 16-byte chunks XOR-swizzled by row (lds_off).
-//  * MN-major operand tiles are [64 k-rows][rows * 2 B] (bf16), 16-byte chunks XOR-swizzled
-//    by (k-row % 4); fragments come out of LDS through the transposing 64-bit read, which hands
-//    each lane four consecutive k of one column.
-//  * K-step kt+1 is in flight (DMA) while step kt is multiplied; inside a step the fragments of
-//    substep s+1 are read while the MFMAs of substep s run. One barrier per K-step, placed
-//    before the last substep's MFMAs.
+// Per workgroup (4 wave64, 2 x 2 waves of WM x WN):
+//  * one K-step is 128 bytes of K per operand row: 64 k for bf16 (four K=16 MFMA substeps),
+//    128 k for e4m3 (two K=64 substeps); full 128-byte row segments keep every DMA request a
+//    whole cache line;
+//  * K-major operand tiles are [rows][ROWB], 16-byte chunks XOR-swizzled by row;
+//  * MN-major operand tiles (bf16) are [64 k-rows][rows * 2 B], chunks XOR-swizzled by
+//    (k-row % 4); fragments come out through the transposing 64-bit LDS read, which hands each
+//    lane four consecutive k of one column;
+//  * the ring holds NS K-steps. The DMA of step kt+NS is issued right after the barrier that
+//    ends step kt's reads, into the stage step kt used, so NS-1 steps are in flight while one
+//    is multiplied: the load latency of the shared L2 / last-level cache is hidden by depth.
+//    Inside a step the fragments of substep s+1 are read while the MFMAs of substep s run.
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "gemm_kernel.hpp"
 
@@ -27,29 +32,74 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(src, GMLP_LDS(lds_wave_base), 16, 0, 0);
 }
 
-__device__ __forceinline__ void wait_dma() {
-  // vmcnt(0); expcnt and lgkmcnt left at their maxima (no wait on them)
-  __builtin_amdgcn_s_waitcnt(0x0f70);
+// vmcnt(N), N < 64 (gfx9 encoding: low 4 bits in [3:0], high 2 bits in [15:14]); expcnt and
+// lgkmcnt left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// Scheduling pattern for one substep region: each MFMA is followed by its share of the LDS
+// reads of the next substep (and of the DMAs of a later K-step), so memory instructions issue
+// between MFMAs instead of stalling the matrix pipe.
+template <int I, int NM, int ND, int NV>
+__device__ __forceinline__ void interleave_step() {
+  constexpr int RP = (ND + NM - 1) / NM, VP = (NV + NM - 1) / NM;   // per MFMA slot
+  constexpr int R = ND - I * RP < RP ? (ND - I * RP > 0 ? ND - I * RP : 0) : RP;
+  constexpr int V = NV - I * VP < VP ? (NV - I * VP > 0 ? NV - I * VP : 0) : VP;
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // MFMA
+  if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // LDS reads
+  if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x010, V, 0);  // VMEM (the DMAs)
+}
+template <int NM, int ND, int NV, int... I>
+__device__ __forceinline__ void interleave_seq(std::integer_sequence<int, I...>) {
+  (interleave_step<I, NM, ND, NV>(), ...);
+}
+template <int NM, int ND, int NV>
+__device__ __forceinline__ void interleave() {
+  interleave_seq<NM, ND, NV>(std::make_integer_sequence<int, NM>{});
 }
 
-// ---- K-major operand: ROWS rows x 128 B per stage ------------------------------------------
-// One DMA instruction fills 1 KB = 8 rows: lane l -> row 8j + l/8, slot l%8, which holds the
-// row's logical chunk (l%8) ^ swz(row).
+// Bytes of K per operand row in one K-step.
+template <typename T> struct StepGeo;
+template <> struct StepGeo<bf16> { static constexpr int ROWB = 128; };
+template <> struct StepGeo<e4m3> { static constexpr int ROWB = 128; };
+
+// ---- K-major operand: ROWS rows x ROWB bytes per stage -------------------------------------
+// One DMA instruction fills 1 KB = 1024/ROWB rows: lane l -> row (1024/ROWB) j + l / CPR,
+// slot l % CPR (CPR = ROWB/16 chunks per row), which holds the row's logical chunk
+// slot ^ swz(row).
 template <typename T, int ROWS>
 struct KTileDma {
   static constexpr int ES = ElemTraits<T>::bytes;
   static constexpr int E = 16 / ES;
-  static constexpr int kInst = ROWS / 32;   // per wave per stage
+  static constexpr int ROWB = StepGeo<T>::ROWB;
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int RPI = 1024 / ROWB;            // rows per DMA instruction
+  static constexpr int kInst = ROWS / RPI / 4;       // per wave per stage
+  static_assert(kInst >= 1 && ROWS % (RPI * 4) == 0, "tile rows must split over 4 waves");
   const char* ptr[kInst];
   int kc[kInst];
+
+  // chunk swizzle: 16 consecutive rows reading one logical chunk hit 16 distinct 16-byte bank
+  // groups of a 256-byte bank cycle
+  static __device__ __forceinline__ int swz(int row) {
+    if constexpr (ROWB == 128) return (row ^ (row >> 3)) & 7;
+    else return (row >> 2) & 3;
+  }
+  static __device__ __forceinline__ int off(int row, int chunk) {
+    return row * ROWB + ((chunk ^ swz(row)) << 4);
+  }
 
   template <typename RowPtr>
   __device__ __forceinline__ void init(int wave, int lane, int kbeg, RowPtr row_base) {
 #pragma unroll
     for (int i = 0; i < kInst; ++i) {
       const int j = wave * kInst + i;
-      const int row = 8 * j + (lane >> 3);
-      const int c = (lane & 7) ^ lds_swz(row);
+      const int row = RPI * j + lane / CPR;
+      const int c = (lane % CPR) ^ swz(row);
       const char* b = row_base(row);
       kc[i] = c * E;
       ptr[i] = b ? b + (int64_t)(kbeg + c * E) * ES : nullptr;
@@ -64,17 +114,18 @@ struct KTileDma {
       dma16(src, tile + j * 1024);
     }
   }
-  // 16-byte chunk `ch` of LDS row `row`
   static __device__ __forceinline__ u32x4 read(const char* tile, int row, int ch) {
-    return *reinterpret_cast<const u32x4*>(tile + lds_off(row, ch));
+    return *reinterpret_cast<const u32x4*>(tile + off(row, ch));
   }
 };
 
 // ---- MN-major bf16 operand: 64 k-rows x ROWS columns per stage --------------------------------
 template <int ROWS>
 struct MNTileDma {
+  static constexpr int KROWS = 64;
   static constexpr int ROWB = ROWS * 2;               // bytes per k-row
-  static constexpr int kInst = ROWS / 32;             // per wave per stage
+  static constexpr int kInst = KROWS * ROWB / 1024 / 4;   // per wave per stage
+  static_assert(kInst >= 1, "tile too narrow");
   int krow[kInst];
   int col[kInst];
 
@@ -91,8 +142,8 @@ struct MNTileDma {
       col[i] = phys_chunk(pc, kr) * 8;                  // the XOR is an involution
     }
   }
-  // src(k) -> pointer to element (k, tile column 0); ncols: columns of the matrix left from
-  // tile column 0.
+  // src(k) -> pointer to element (k, tile column 0); ncols: columns of the matrix from tile
+  // column 0 on.
   template <typename SrcRow>
   __device__ __forceinline__ void issue(char* tile, int wave, int k0, int kend, int ncols, SrcRow src) const {
 #pragma unroll
@@ -128,22 +179,36 @@ struct MNTileDma {
   }
 };
 
+// Stages in the ring: as many as fit the 160 KiB of LDS, at most 4; tiles of 128 x 128 and
+// below keep room for two workgroups per CU (a second workgroup hides latency better than a
+// deeper ring).
+constexpr int ring_stages(int stage_bytes, int tile_elems) {
+  const int lds = 160 * 1024;
+  int n = lds / stage_bytes;
+  if (tile_elems <= 128 * 128 && (lds / 2) / stage_bytes >= 2) n = (lds / 2) / stage_bytes;
+  return n > 4 ? 4 : n;
+}
+
 template <typename T, typename IoT, int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmArgs p) {
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must split into 2x2 waves of 32x32 blocks");
-  static_assert(A_KMAJ && B_KMAJ || std::is_same<T, bf16>::value, "MN-major operands are bf16 only");
+  static_assert((A_KMAJ && B_KMAJ) || std::is_same<T, bf16>::value, "MN-major operands are bf16 only");
   constexpr int ES = ElemTraits<T>::bytes;
-  constexpr int E = 16 / ES;
-  constexpr int BK = 8 * E;
+  constexpr int ROWB = StepGeo<T>::ROWB;
+  constexpr int BK = ROWB / ES;
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int MI = WM / 32, NI = WN / 32;
-  constexpr int A_BYTES = BM * 128, STAGE = (BM + BN) * 128;
+  constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
+  constexpr int NS = ring_stages(STAGE, BM * BN);
+  static_assert(NS >= 2, "the ring needs two stages");
   constexpr bool GATED = EPI == EPI_GATED;
-  constexpr int NSUB = Mma<T>::kSub;
+  constexpr int KMMA = std::is_same<T, e4m3>::value ? 64 : 16;
+  constexpr int NSUB = BK / KMMA;
   constexpr int KC = Mma<T>::kChunks;
   static_assert(NSUB % 2 == 0, "fragment double buffer alternates per substep");
+  static_assert(A_KMAJ || BK == MNTileDma<BM>::KROWS, "MN-major stage depth");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -188,7 +253,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmArgs p)
   } else {
     nb.init(wave, lane);
   }
+  constexpr int N_DMA = (A_KMAJ ? KTileDma<T, BM>::kInst : MNTileDma<BM>::kInst) +
+                        (B_KMAJ ? KTileDma<T, BN>::kInst : MNTileDma<BN>::kInst);
+  static_assert((NS - 1) * N_DMA < 64, "vmcnt range");
 
+  // K-step kt into ring stage `stage`; steps past the end load zeros.
   auto issue = [&](int kt, int stage) {
     char* sa = smem + stage * STAGE;
     char* sb = sa + A_BYTES;
@@ -252,31 +321,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmArgs p)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  constexpr int N_RD = (A_KMAJ ? MI * KC : 2 * MI) + (B_KMAJ ? NI * KC : 2 * NI);
+  constexpr int N_MMA = MI * NI;
+
+  auto mma_all = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) Mma<T>::mma(fb[slot][j], fa[slot][i], acc[i][j]);
+  };
+
   if (nk > 0) {
-    issue(0, 0);
-    wait_dma();
-    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) issue(s, s);
+    wait_vmcnt<(NS - 1) * N_DMA>();   // step 0 landed
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
     read_frags(0, 0, 0);
   }
+  int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) issue(kt + 1, cur ^ 1);
+    const int nxt = cur + 1 == NS ? 0 : cur + 1;
+    // substeps 0 .. NSUB-2: read substep s+1's fragments while multiplying substep s
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      if (s + 1 < NSUB) {
-        read_frags(cur, s + 1, (s + 1) & 1);
-      } else if (more) {
-        wait_dma();
-        __syncthreads();
-        read_frags(cur ^ 1, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j) Mma<T>::mma(fb[s & 1][j], fa[s & 1][i], acc[i][j]);
+    for (int s = 0; s + 1 < NSUB; ++s) {
+      read_frags(cur, s + 1, (s + 1) & 1);
+      mma_all(s & 1);
+      interleave<N_MMA, N_RD, 0>();
     }
+    // last substep: step kt+1 must have landed (NS-2 younger steps may be in flight); after
+    // the barrier every wave is done reading this stage, which takes step kt+NS
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<(NS - 2) * N_DMA>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + NS, cur);
+    read_frags(nxt, 0, 0);
+    mma_all((NSUB - 1) & 1);
+    interleave<N_MMA, N_RD, N_DMA>();
+    cur = nxt;
   }
+  wait_vmcnt<0>();   // the trailing zero-fill DMAs
 
   epilogue<EPI, IoT, BM, BN, MI, NI>(p, acc, m0, n0, split, wm, wn, lane);
 }

@@ -72,12 +72,15 @@ struct Plan {
 };
 
 struct TileInfo { TileShape t; int bm, bn, slots; double eff; };
-// slots: workgroups per CU that fit (LDS: 128 KiB, 96 KiB, 64 KiB of 160 KiB); eff: assumed
-// fraction of the CU's MFMA rate a tile shape sustains (larger tiles re-read less).
+// slots: workgroups per CU that fit in LDS (a 2-stage 256x256 ring takes 128 KiB, a 3-stage
+// 256x128 one 144 KiB, a 2-stage 128x128 one 64 KiB). eff: the CU's MFMA rate a tile shape
+// sustains relative to 256x256, measured on the LLaMA-shaped GEMMs (2048 tokens, 4096 x 11008):
+// two 128x128 workgroups per CU hide latency as well as one 256x256 one at twice the
+// operand traffic; 256x128 trails both.
 const TileInfo kTiles[] = {
     {TILE_256x256, 256, 256, 1, 1.00},
-    {TILE_256x128, 256, 128, 1, 0.85},
-    {TILE_128x128, 128, 128, 2, 0.70},
+    {TILE_256x128, 256, 128, 1, 0.75},
+    {TILE_128x128, 128, 128, 2, 0.95},
 };
 
 int bk_of(DType in) { return in == DT_E4M3 ? 128 : (in == DT_BF16 ? 64 : 32); }
