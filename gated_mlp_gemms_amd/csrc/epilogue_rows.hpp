@@ -1,0 +1,211 @@
+// Fused epilogues that write whole row segments: the accumulators of each 32-row block-row of
+// a wave are staged through LDS (free once the K loop is done) and read back so that every
+// lane owns 8 consecutive columns of one row. Every global load and store is then 16 bytes of
+// a contiguous 128-256 byte row segment, instead of 8 bytes scattered over 32 rows.
+#pragma once
+
+#include "gemm_kernel.hpp"
+
+namespace gmlp {
+
+// ---- 8-element row pieces ---------------------------------------------------------------------
+
+template <typename T> struct Vec8;
+template <> struct Vec8<float> {
+  static __device__ __forceinline__ void load(const void* p, float v[8]) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { v[r] = a[r]; v[4 + r] = b[r]; }
+  }
+  static __device__ __forceinline__ void store(void* p, const float v[8]) {
+    reinterpret_cast<f32x4*>(p)[0] = f32x4{v[0], v[1], v[2], v[3]};
+    reinterpret_cast<f32x4*>(p)[1] = f32x4{v[4], v[5], v[6], v[7]};
+  }
+};
+template <> struct Vec8<bf16> {
+  static __device__ __forceinline__ void load(const void* p, float v[8]) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[2 * r] = bf16_bits_to_f32(x[r] & 0xffffu);
+      v[2 * r + 1] = bf16_bits_to_f32(x[r] >> 16);
+    }
+  }
+  static __device__ __forceinline__ void store(void* p, const float v[8]) {
+    *reinterpret_cast<u32x4*>(p) = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                         pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  }
+};
+
+// The epilogue function on 8 consecutive columns n .. n+7 of row m. v = alpha * acc (or the
+// raw accumulator for split-K partials); u = the up-projection values for the gated epilogue.
+template <int EPI, typename IoT>
+__device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int split, const float v[8],
+                                         const float u[8], float& local_amax) {
+  if constexpr (EPI == EPI_STORE) {
+    const bool lo = m < p.c_split;
+    void* base = lo ? p.C0 : p.C1;
+    const int row = lo ? m : m - p.c_split;
+    if (p.accumulate) {
+      float* q = reinterpret_cast<float*>(elem_ptr<float>(base, row, p.ldc0, n));
+      float o[8];
+      Vec8<float>::load(q, o);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) o[r] += v[r];
+      Vec8<float>::store(q, o);
+    } else {
+      Vec8<IoT>::store(elem_ptr<IoT>(base, row, p.ldc0, n), v);
+    }
+  } else if constexpr (EPI == EPI_PARTIAL) {
+    const int64_t prow = (int64_t)split * p.M + m;
+    Vec8<float>::store(elem_ptr<float>(p.partial, prow, p.N, n), v);
+  } else if constexpr (EPI == EPI_GATED) {
+    if (p.flags & 1) {
+      Vec8<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), v);
+      Vec8<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, p.half + n), u);
+    }
+    if (p.flags & 2) {
+      float a[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        if (p.gate_inside) {
+          const float z = p.gate_mult * v[r];
+          a[r] = z * sigmoidf_(z) * u[r];
+        } else {
+          a[r] = p.gate_mult * (v[r] * sigmoidf_(v[r])) * u[r];
+        }
+      }
+      Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), a);
+    }
+  } else if constexpr (EPI == EPI_ACT) {
+    if (p.flags & 1) Vec8<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), v);
+    if (p.flags & 2) {
+      float q[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) { const float t = fmaxf(v[r], 0.0f); q[r] = t * t; }
+      Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), q);
+    }
+  } else if constexpr (EPI == EPI_DGATED) {
+    float gg[8], uu[8], dg[8], du[8], a[8];
+    Vec8<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), gg);
+    Vec8<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, p.half + n), uu);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float gm = p.gate_mult;
+      const float z = p.gate_inside ? gm * gg[r] : gg[r];
+      const float sg = sigmoidf_(z);
+      const float silu = z * sg;
+      const float dsilu = sg * (1.0f + z * (1.0f - sg));
+      if (p.gate_inside) {
+        dg[r] = v[r] * uu[r] * gm * dsilu;
+        du[r] = v[r] * silu;
+        a[r] = silu * uu[r];
+      } else {
+        dg[r] = v[r] * gm * uu[r] * dsilu;
+        du[r] = v[r] * gm * silu;
+        a[r] = gm * silu * uu[r];
+      }
+    }
+    Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), dg);
+    Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, p.half + n), du);
+    if (p.flags & 2) Vec8<IoT>::store(elem_ptr<IoT>(p.C1, m, p.ldc1, n), a);
+  } else if constexpr (EPI == EPI_DACT) {
+    float pre[8], dpre[8], post[8];
+    Vec8<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), pre);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float t = fmaxf(pre[r], 0.0f);
+      dpre[r] = v[r] * 2.0f * t;
+      post[r] = t * t;
+    }
+    Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), dpre);
+    if (p.flags & 2) Vec8<IoT>::store(elem_ptr<IoT>(p.C1, m, p.ldc1, n), post);
+  } else if constexpr (EPI == EPI_F8ACT) {
+    if (p.flags & 1) Vec8<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), v);
+    const float sp = *p.s_post;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float t = fmaxf(v[r], 0.0f);
+      const float post = t * t;
+      local_amax = fmaxf(local_amax, post);
+      const uint32_t q = f32_to_e4m3(__fdiv_rn(post, sp));
+      if (r < 4) lo |= q << (8 * r);
+      else hi |= q << (8 * (r - 4));
+    }
+    *reinterpret_cast<u32x2*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) = u32x2{lo, hi};
+  }
+}
+
+// Bytes of LDS the row-staged epilogue uses (4 waves x 32 rows x padded WN fp32 columns).
+template <int BN>
+constexpr int epilogue_lds_bytes() { return 4 * 32 * ((BN / 2) * 4 + 16); }
+
+// acc[i][j]: the MFMA layout of the wave's WM x WN tile (see epilogue()). lds: this
+// workgroup's LDS, at least epilogue_lds_bytes<BN>() bytes, not in use by any wave.
+template <int EPI, typename IoT, int BM, int BN, int MI, int NI>
+__device__ __forceinline__ void epilogue_rows(const GemmArgs& p, f32x16 (&acc)[MI][NI], int m0, int n0,
+                                              int split, int wm, int wn, int lane, int wave, char* lds) {
+  constexpr bool GATED = EPI == EPI_GATED;
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int STRIDE = WN * 4 + 16;                 // padded: rows 16 bytes apart in bank space
+  constexpr int UNITS = GATED ? WN / 2 : WN;          // output columns of the wave
+  constexpr int LPR = UNITS / 8;                      // lanes per row
+  constexpr int RPI = 64 / LPR;                       // rows per pass
+  static_assert(32 % RPI == 0, "passes must cover the 32-row block-row");
+  const int frow = lane & 31, fhalf = lane >> 5;
+  char* wbuf = lds + wave * 32 * STRIDE;
+
+  float alpha = p.alpha;
+  if (p.alpha_dev0) alpha *= *p.alpha_dev0;
+  if (p.alpha_dev1) alpha *= *p.alpha_dev1;
+  const float scale = EPI == EPI_PARTIAL ? 1.0f : alpha;   // partials stay unscaled
+  float local_amax = 0.0f;
+
+  const int nbase = GATED ? n0 + wn * (BN / 4) : n0 + wn * WN;
+  const int rl = lane / LPR, cl = (lane % LPR) * 8;       // this lane's row-in-pass / column
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    // MFMA layout -> LDS rows: lane (row frow) writes columns j*32 + 8g + 4*fhalf .. +3
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = {scale * acc[i][j][4 * g], scale * acc[i][j][4 * g + 1],
+                         scale * acc[i][j][4 * g + 2], scale * acc[i][j][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(wbuf + frow * STRIDE + (j * 32 + 8 * g + 4 * fhalf) * 4) = v;
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    const int mrow0 = m0 + wm * WM + i * 32;
+#pragma unroll
+    for (int pass = 0; pass < 32 / RPI; ++pass) {
+      const int r = pass * RPI + rl;
+      const int m = mrow0 + r;
+      const int n = nbase + cl;
+      float v[8], u[8];
+      const f32x4* src = reinterpret_cast<const f32x4*>(wbuf + r * STRIDE + cl * 4);
+      f32x4 a0 = src[0], a1 = src[1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { v[q] = a0[q]; v[4 + q] = a1[q]; }
+      if constexpr (GATED) {
+        const f32x4* su = reinterpret_cast<const f32x4*>(wbuf + r * STRIDE + (UNITS + cl) * 4);
+        a0 = su[0];
+        a1 = su[1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { u[q] = a0[q]; u[4 + q] = a1[q]; }
+      }
+      if (m < p.M && n < p.N) epi_row8<EPI, IoT>(p, m, n, split, v, u, local_amax);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);       // reads done before the next block-row's writes
+    __builtin_amdgcn_wave_barrier();
+  }
+  if constexpr (EPI == EPI_F8ACT) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) local_amax = fmaxf(local_amax, __shfl_xor(local_amax, off));
+    if (lane == 0 && local_amax > 0.0f)
+      atomicMax(reinterpret_cast<unsigned int*>(p.amax), __float_as_uint(local_amax));
+  }
+}
+
+}  // namespace gmlp

@@ -19,6 +19,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "epilogue_rows.hpp"
 #include "gemm_kernel.hpp"
 
 namespace gmlp {
@@ -361,9 +362,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmArgs p)
     interleave<N_MMA, N_RD, N_DMA>();
     cur = nxt;
   }
-  wait_vmcnt<0>();   // the trailing zero-fill DMAs
-
-  epilogue<EPI, IoT, BM, BN, MI, NI>(p, acc, m0, n0, split, wm, wn, lane);
+  // the trailing zero-fill DMAs have landed and no wave reads the ring any more: its LDS
+  // becomes the epilogue's staging area
+  static_assert(epilogue_lds_bytes<BN>() <= NS * STAGE, "epilogue staging must fit the ring");
+  wait_vmcnt<0>();
+  wait_lgkmcnt0();
+  __builtin_amdgcn_s_barrier();
+  epilogue_rows<EPI, IoT, BM, BN, MI, NI>(p, acc, m0, n0, split, wm, wn, lane, wave, smem);
 }
 
 template <typename T, typename IoT, int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI>
