@@ -60,6 +60,21 @@ def stage_flops(w) -> dict:
     }
 
 
+def measured_traffic(workload: str, stage: str):
+    """HBM bytes per launch of `stage` from the committed PMC summary of this workload, if the
+    kernel sources are the ones the counters were taken on (else None)."""
+    from gated_mlp_gemms_amd.profile_summary import kernel_sources_sha256
+
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None, None
+    rec = json.load(open(path))
+    if rec.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None, f"{os.path.basename(path)} (stale: kernels changed since)"
+    st = rec.get("stages", {}).get(stage)
+    return (st["traffic_bytes"] if st else None), os.path.basename(path)
+
+
 def cpu_baseline(w, tensors, rows: int) -> dict:
     """The float64 oracle (as it stands) on the first `rows` tokens of the workload, all of d
     and H: forward + backward, timed on this host's cores."""
@@ -93,7 +108,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
-    ap.add_argument("--cpu-rows", type=int, default=512, help="tokens in the oracle's CPU sample")
+X
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warmup (a known-size "
@@ -168,9 +183,10 @@ def main():
             ev.destroy(e)
     dom = max(stage_us, key=stage_us.get)
     peak = PEAK_BF16_TFLOPS
+    traffic, traffic_src = measured_traffic(w.name, dom)
     roof = {"bound": "mfma", "achieved": stage_tf[dom], "peak": peak, "unit": "TFLOP/s",
-            "frac": round(stage_tf[dom] / peak, 4), "traffic": None, "kernel_stage": dom,
-            "flop_per_launch": sf[dom], "avg_launch_us": stage_us[dom]}
+            "frac": round(stage_tf[dom] / peak, 4), "traffic": traffic, "kernel_stage": dom,
+            "flop_per_launch": sf[dom], "avg_launch_us": stage_us[dom], "traffic_source": traffic_src}
     log(f"[bench] {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of bf16 peak); "
         f"stages us {stage_us}")
 

@@ -1,0 +1,152 @@
+"""Summaries of rocprofv3 output for the bench step (kernel durations and HBM traffic per stage).
+
+    python -m gated_mlp_gemms_amd.profile_summary trace  <kernel-trace dir> <out.txt>  --command "..."
+    python -m gated_mlp_gemms_amd.profile_summary traffic <fetch dir> <write dir> <out.json> --command "..."
+
+The trace summary lists every kernel's dispatch count and average / total duration from the
+`*_kernel_stats.csv` rocprofv3 writes with `--kernel-trace --stats --output-format csv`.
+
+The traffic summary reads two `--pmc` passes over the same command (FETCH_SIZE, then
+WRITE_SIZE, both in KiB per dispatch) that also ran one plain device copy of known size
+(`bench.py --copy-probe-mib N`): the copy's counters give the factors that turn each counter into
+bytes. Each step's dispatches are assigned to the step's stages in launch order (a split-K reduce
+belongs to the GEMM before it), and the per-stage bytes are averaged over the profiled steps. The
+output records a SHA-256 of the kernel sources, so a reader can tell whether the kernels changed
+since the counters were taken.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+STAGE_ORDER_GATED = ["up", "down", "dact", "dw_down", "dx", "dw_up"]
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(_HERE, "csrc", "*"))):
+        if f.endswith((".hip", ".hpp")):
+            h.update(os.path.basename(f).encode())
+            h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise SystemExit(f"no file matches {pattern}")
+    return hits[0]
+
+
+def short_name(name: str) -> str:
+    """A readable name for the engine's kernels (template arguments spelled out)."""
+    m = re.search(r"gemm_(dma_)?kernelI(.+?)Li(\d+)ELi(\d+)ELb(\d)ELb(\d)ELi(\d)E", name)
+    if m:
+        dma, types, bm, bn, ak, bk, epi = m.groups()
+        lay = {("1", "1"): "NT", ("1", "0"): "NN", ("0", "0"): "TN"}.get((ak, bk), "??")
+        epin = ["STORE", "PARTIAL", "GATED", "ACT", "DGATED", "DACT", "F8ACT"][int(epi)]
+        t = "e4m3" if "e4m3" in types else ("f32" if types.startswith("ff") else "bf16")
+        out = "f32" if "DF16bf" in types or types.endswith("f") else ""
+        return f"gemm{'' if dma else '_regstaged'}<{t},{lay},{bm}x{bn},{epin}{',' + out + ' out' if out else ''}>"
+    for k in ("splitk_reduce", "gated_act", "relu_sq_kernel", "absmax", "quantize_kernel", "dequant", "zero_f32"):
+        if k in name:
+            return k
+    return name.split("(")[0][:60]
+
+
+def summarize_trace(trace_dir: str, out_txt: str, command: str) -> None:
+    stats = _one(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
+    rows = list(csv.DictReader(open(stats)))
+    lines = [f"# rocprofv3 kernel statistics", f"# command: {command}", f"# kernel sources sha256: {kernel_sources_sha256()}",
+             "", f"{'kernel':64s} {'calls':>6s} {'avg us':>10s} {'total ms':>10s} {'%':>6s}"]
+    for r in rows:
+        name = r.get("Name") or r.get("KernelName") or r.get("Kernel_Name")
+        calls = int(r["Calls"])
+        avg_ns = float(r["AverageNs"])
+        tot_ns = float(r["TotalDurationNs"])
+        pct = float(r.get("Percentage", 0.0))
+        lines.append(f"{short_name(name):64s} {calls:6d} {avg_ns / 1e3:10.1f} {tot_ns / 1e6:10.3f} {pct:6.2f}")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _dispatches(pmc_dir: str, counter: str) -> list[tuple[int, str, float]]:
+    path = _one(os.path.join(pmc_dir, "**", "*counter_collection.csv"))
+    out = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    out.sort()
+    return out
+
+
+def _stage_bytes(disp, factor, stages):
+    """Average bytes per stage over the profiled steps; a step starts at each up-projection."""
+    per_step, cur, idx = [], None, -1
+    for _, name, kib in disp:
+        is_gemm = "gemm_" in name
+        epi = re.search(r"ELi(\d)EEEvNS_8GemmArgsE", name)
+        is_up = is_gemm and epi is not None and epi.group(1) in ("2", "3", "6")
+        if is_up:
+            cur = {}
+            per_step.append(cur)
+            idx = 0
+        elif cur is None:
+            continue
+        elif is_gemm:
+            idx += 1
+        if cur is None or idx >= len(stages):
+            continue
+        cur[stages[idx]] = cur.get(stages[idx], 0.0) + kib * 1024.0 * factor
+    full = [s for s in per_step if len(s) == len(stages)]
+    return {st: sum(s[st] for s in full) / len(full) for st in stages} if full else {}
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, out_json: str, command: str, copy_mib: int) -> None:
+    fetch, write = _dispatches(fetch_dir, "FETCH_SIZE"), _dispatches(write_dir, "WRITE_SIZE")
+    copy_bytes = copy_mib * 1024 * 1024
+    fc = [v for _, n, v in fetch if "copyBuffer" in n]
+    wc = [v for _, n, v in write if "copyBuffer" in n]
+    if not fc or not wc:
+        raise SystemExit("the profiled command ran no device copy (use bench.py --copy-probe-mib)")
+    f_factor = copy_bytes / (fc[0] * 1024.0)
+    w_factor = copy_bytes / (wc[0] * 1024.0)
+    fb = _stage_bytes(fetch, f_factor, STAGE_ORDER_GATED)
+    wb = _stage_bytes(write, w_factor, STAGE_ORDER_GATED)
+    res = {"command": command, "kernel_sources_sha256": kernel_sources_sha256(),
+           "copy_probe_bytes": copy_bytes, "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+           "stages": {st: {"fetch_bytes": round(fb.get(st, 0.0)), "write_bytes": round(wb.get(st, 0.0)),
+                           "traffic_bytes": round(fb.get(st, 0.0) + wb.get(st, 0.0))} for st in STAGE_ORDER_GATED}}
+    json.dump(res, open(out_json, "w"), indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("trace_dir")
+    t.add_argument("out_txt")
+    t.add_argument("--command", required=True)
+    f = sub.add_parser("traffic")
+    f.add_argument("fetch_dir")
+    f.add_argument("write_dir")
+    f.add_argument("out_json")
+    f.add_argument("--command", required=True)
+    f.add_argument("--copy-mib", type=int, default=256)
+    a = ap.parse_args(argv)
+    if a.what == "trace":
+        summarize_trace(a.trace_dir, a.out_txt, a.command)
+    else:
+        summarize_traffic(a.fetch_dir, a.write_dir, a.out_json, a.command, a.copy_mib)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
