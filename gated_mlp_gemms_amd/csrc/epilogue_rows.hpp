@@ -4,6 +4,8 @@
 // a contiguous 128-256 byte row segment, instead of 8 bytes scattered over 32 rows.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_kernel.hpp"
 
 namespace gmlp {
@@ -37,11 +39,42 @@ template <> struct Vec8<bf16> {
   }
 };
 
+// Tensors an epilogue reads besides the accumulators (saved g, u or pre; the fp32 buffer of an
+// accumulating store), fetched for a whole round before the round's LDS staging so their
+// latency overlaps it. Raw 16-byte pieces: bf16 x 8 or fp32 x 4 (two pieces for fp32 x 8).
+struct AuxPiece { u32x4 a, b, c; };
+
+template <int EPI, typename IoT>
+__device__ __forceinline__ void epi_prefetch(const GemmArgs& p, int m, int n, AuxPiece& x) {
+  if constexpr (EPI == EPI_DGATED) {
+    x.a = *reinterpret_cast<const u32x4*>(elem_ptr<IoT>(p.aux, m, p.ld_aux, n));
+    x.b = *reinterpret_cast<const u32x4*>(elem_ptr<IoT>(p.aux, m, p.ld_aux, p.half + n));
+  } else if constexpr (EPI == EPI_DACT) {
+    x.a = *reinterpret_cast<const u32x4*>(elem_ptr<IoT>(p.aux, m, p.ld_aux, n));
+  } else if constexpr (EPI == EPI_STORE) {
+    if (p.accumulate) {
+      const bool lo = m < p.c_split;
+      const float* q = reinterpret_cast<const float*>(elem_ptr<float>(lo ? p.C0 : p.C1, lo ? m : m - p.c_split, p.ldc0, n));
+      x.a = reinterpret_cast<const u32x4*>(q)[0];
+      x.c = reinterpret_cast<const u32x4*>(q)[1];
+    }
+  }
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const u32x4 x, float v[8]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    v[2 * r] = bf16_bits_to_f32(x[r] & 0xffffu);
+    v[2 * r + 1] = bf16_bits_to_f32(x[r] >> 16);
+  }
+}
+
 // The epilogue function on 8 consecutive columns n .. n+7 of row m. v = alpha * acc (or the
-// raw accumulator for split-K partials); u = the up-projection values for the gated epilogue.
+// raw accumulator for split-K partials); u = the up-projection values for the gated epilogue;
+// x = what epi_prefetch fetched for this piece.
 template <int EPI, typename IoT>
 __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int split, const float v[8],
-                                         const float u[8], float& local_amax) {
+                                         const float u[8], const AuxPiece& x, float& local_amax) {
   if constexpr (EPI == EPI_STORE) {
     const bool lo = m < p.c_split;
     void* base = lo ? p.C0 : p.C1;
@@ -49,9 +82,11 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
     if (p.accumulate) {
       float* q = reinterpret_cast<float*>(elem_ptr<float>(base, row, p.ldc0, n));
       float o[8];
-      Vec8<float>::load(q, o);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) o[r] += v[r];
+      for (int r = 0; r < 4; ++r) {
+        o[r] = __uint_as_float(x.a[r]) + v[r];
+        o[4 + r] = __uint_as_float(x.c[r]) + v[4 + r];
+      }
       Vec8<float>::store(q, o);
     } else {
       Vec8<IoT>::store(elem_ptr<IoT>(base, row, p.ldc0, n), v);
@@ -86,9 +121,10 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
       Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), q);
     }
   } else if constexpr (EPI == EPI_DGATED) {
+    static_assert(std::is_same<IoT, bf16>::value, "row-staged d-activation epilogues read bf16");
     float gg[8], uu[8], dg[8], du[8], a[8];
-    Vec8<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), gg);
-    Vec8<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, p.half + n), uu);
+    unpack_bf16x8(x.a, gg);
+    unpack_bf16x8(x.b, uu);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const float gm = p.gate_mult;
@@ -110,8 +146,9 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
     Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, p.half + n), du);
     if (p.flags & 2) Vec8<IoT>::store(elem_ptr<IoT>(p.C1, m, p.ldc1, n), a);
   } else if constexpr (EPI == EPI_DACT) {
+    static_assert(std::is_same<IoT, bf16>::value, "row-staged d-activation epilogues read bf16");
     float pre[8], dpre[8], post[8];
-    Vec8<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), pre);
+    unpack_bf16x8(x.a, pre);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const float t = fmaxf(pre[r], 0.0f);
@@ -137,24 +174,29 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
   }
 }
 
-// Bytes of LDS the row-staged epilogue uses (4 waves x 32 rows x padded WN fp32 columns).
-template <int BN>
-constexpr int epilogue_lds_bytes() { return 4 * 32 * ((BN / 2) * 4 + 16); }
+// Rows of a block-row staged per round: 32 with 4 waves, 16 with 8 (the staging of all waves
+// must fit the ring's LDS).
+template <int WAVES> constexpr int epilogue_rows_per_round() { return WAVES == 8 ? 16 : 32; }
+
+// Bytes of LDS the row-staged epilogue uses (waves x rows per round x padded WN fp32 columns).
+template <int BN, int WAVES>
+constexpr int epilogue_lds_bytes() { return WAVES * epilogue_rows_per_round<WAVES>() * ((BN / 2) * 4 + 16); }
 
 // acc[i][j]: the MFMA layout of the wave's WM x WN tile (see epilogue()). lds: this
 // workgroup's LDS, at least epilogue_lds_bytes<BN>() bytes, not in use by any wave.
-template <int EPI, typename IoT, int BM, int BN, int MI, int NI>
+template <int EPI, typename IoT, int BM, int BN, int MI, int NI, int WAVES>
 __device__ __forceinline__ void epilogue_rows(const GemmArgs& p, f32x16 (&acc)[MI][NI], int m0, int n0,
                                               int split, int wm, int wn, int lane, int wave, char* lds) {
   constexpr bool GATED = EPI == EPI_GATED;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = BM / (WAVES / 2), WN = BN / 2;
+  constexpr int RR = epilogue_rows_per_round<WAVES>();   // rows staged per round
   constexpr int STRIDE = WN * 4 + 16;                 // padded: rows 16 bytes apart in bank space
   constexpr int UNITS = GATED ? WN / 2 : WN;          // output columns of the wave
   constexpr int LPR = UNITS / 8;                      // lanes per row
   constexpr int RPI = 64 / LPR;                       // rows per pass
-  static_assert(32 % RPI == 0, "passes must cover the 32-row block-row");
+  static_assert(RR % RPI == 0, "passes must cover a round's rows");
   const int frow = lane & 31, fhalf = lane >> 5;
-  char* wbuf = lds + wave * 32 * STRIDE;
+  char* wbuf = lds + wave * RR * STRIDE;
 
   float alpha = p.alpha;
   if (p.alpha_dev0) alpha *= *p.alpha_dev0;
@@ -162,43 +204,55 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& p, f32x16 (&acc)[M
   const float scale = EPI == EPI_PARTIAL ? 1.0f : alpha;   // partials stay unscaled
   float local_amax = 0.0f;
 
-  const int nbase = GATED ? n0 + wn * (BN / 4) : n0 + wn * WN;
+  const int nbase = GATED ? n0 + wn * (WN / 2) : n0 + wn * WN;
   const int rl = lane / LPR, cl = (lane % LPR) * 8;       // this lane's row-in-pass / column
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
-    // MFMA layout -> LDS rows: lane (row frow) writes columns j*32 + 8g + 4*fhalf .. +3
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
+    for (int h = 0; h < 32 / RR; ++h) {
+      const int mrow0 = m0 + wm * WM + i * 32 + h * RR;
+      AuxPiece x[RR / RPI];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 v = {scale * acc[i][j][4 * g], scale * acc[i][j][4 * g + 1],
-                         scale * acc[i][j][4 * g + 2], scale * acc[i][j][4 * g + 3]};
-        *reinterpret_cast<f32x4*>(wbuf + frow * STRIDE + (j * 32 + 8 * g + 4 * fhalf) * 4) = v;
+      for (int pass = 0; pass < RR / RPI; ++pass) {
+        const int m = mrow0 + pass * RPI + rl, n = nbase + cl;
+        if (m < p.M && n < p.N) epi_prefetch<EPI, IoT>(p, m, n, x[pass]);
       }
-    __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_wave_barrier();
-    const int mrow0 = m0 + wm * WM + i * 32;
+      // MFMA layout -> LDS rows: lanes whose row falls in this round write columns
+      // j*32 + 8g + 4*fhalf .. +3 of row (frow - h*RR)
+      if (frow / RR == h) {
 #pragma unroll
-    for (int pass = 0; pass < 32 / RPI; ++pass) {
-      const int r = pass * RPI + rl;
-      const int m = mrow0 + r;
-      const int n = nbase + cl;
-      float v[8], u[8];
-      const f32x4* src = reinterpret_cast<const f32x4*>(wbuf + r * STRIDE + cl * 4);
-      f32x4 a0 = src[0], a1 = src[1];
+        for (int j = 0; j < NI; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) { v[q] = a0[q]; v[4 + q] = a1[q]; }
-      if constexpr (GATED) {
-        const f32x4* su = reinterpret_cast<const f32x4*>(wbuf + r * STRIDE + (UNITS + cl) * 4);
-        a0 = su[0];
-        a1 = su[1];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) { u[q] = a0[q]; u[4 + q] = a1[q]; }
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = {scale * acc[i][j][4 * g], scale * acc[i][j][4 * g + 1],
+                             scale * acc[i][j][4 * g + 2], scale * acc[i][j][4 * g + 3]};
+            *reinterpret_cast<f32x4*>(wbuf + (frow - h * RR) * STRIDE + (j * 32 + 8 * g + 4 * fhalf) * 4) = v;
+          }
       }
-      if (m < p.M && n < p.N) epi_row8<EPI, IoT>(p, m, n, split, v, u, local_amax);
+      __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): this wave's LDS writes are done
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int pass = 0; pass < RR / RPI; ++pass) {
+        const int r = pass * RPI + rl;
+        const int m = mrow0 + r;
+        const int n = nbase + cl;
+        float v[8], u[8];
+        const f32x4* src = reinterpret_cast<const f32x4*>(wbuf + r * STRIDE + cl * 4);
+        f32x4 a0 = src[0], a1 = src[1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { v[q] = a0[q]; v[4 + q] = a1[q]; }
+        if constexpr (GATED) {
+          const f32x4* su = reinterpret_cast<const f32x4*>(wbuf + r * STRIDE + (UNITS + cl) * 4);
+          a0 = su[0];
+          a1 = su[1];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { u[q] = a0[q]; u[4 + q] = a1[q]; }
+        }
+        if (m < p.M && n < p.N) epi_row8<EPI, IoT>(p, m, n, split, v, u, x[pass], local_amax);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);       // reads done before the next round's writes
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);       // reads done before the next block-row's writes
-    __builtin_amdgcn_wave_barrier();
   }
   if constexpr (EPI == EPI_F8ACT) {
 #pragma unroll

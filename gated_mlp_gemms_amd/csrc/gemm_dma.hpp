@@ -72,15 +72,15 @@ template <> struct StepGeo<e4m3> { static constexpr int ROWB = 128; };
 // One DMA instruction fills 1 KB = 1024/ROWB rows: lane l -> row (1024/ROWB) j + l / CPR,
 // slot l % CPR (CPR = ROWB/16 chunks per row), which holds the row's logical chunk
 // slot ^ swz(row).
-template <typename T, int ROWS>
+template <typename T, int ROWS, int WAVES>
 struct KTileDma {
   static constexpr int ES = ElemTraits<T>::bytes;
   static constexpr int E = 16 / ES;
   static constexpr int ROWB = StepGeo<T>::ROWB;
   static constexpr int CPR = ROWB / 16;
   static constexpr int RPI = 1024 / ROWB;            // rows per DMA instruction
-  static constexpr int kInst = ROWS / RPI / 4;       // per wave per stage
-  static_assert(kInst >= 1 && ROWS % (RPI * 4) == 0, "tile rows must split over 4 waves");
+  static constexpr int kInst = ROWS / RPI / WAVES;   // per wave per stage
+  static_assert(kInst >= 1 && ROWS % (RPI * WAVES) == 0, "tile rows must split over the waves");
   const char* ptr[kInst];
   int kc[kInst];
 
@@ -121,11 +121,11 @@ struct KTileDma {
 };
 
 // ---- MN-major bf16 operand: 64 k-rows x ROWS columns per stage --------------------------------
-template <int ROWS>
+template <int ROWS, int WAVES>
 struct MNTileDma {
   static constexpr int KROWS = 64;
   static constexpr int ROWB = ROWS * 2;               // bytes per k-row
-  static constexpr int kInst = KROWS * ROWB / 1024 / 4;   // per wave per stage
+  static constexpr int kInst = KROWS * ROWB / 1024 / WAVES;   // per wave per stage
   static_assert(kInst >= 1, "tile too narrow");
   int krow[kInst];
   int col[kInst];
@@ -190,15 +190,21 @@ constexpr int ring_stages(int stage_bytes, int tile_elems) {
   return n > 4 ? 4 : n;
 }
 
-template <typename T, typename IoT, int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmArgs p) {
+// WAVES = 4: 2 x 2 waves, one per SIMD (wave tile up to 128 x 128, 256 accumulator registers).
+// WAVES = 8: 4 x 2 waves, two per SIMD, so one wave's MFMAs fill the other's stalls (wave tile
+// 64 x 128, 128 accumulator registers, half the register file each).
+template <typename T, typename IoT, int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs p) {
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must split into 2x2 waves of 32x32 blocks");
   static_assert((A_KMAJ && B_KMAJ) || std::is_same<T, bf16>::value, "MN-major operands are bf16 only");
   constexpr int ES = ElemTraits<T>::bytes;
   constexpr int ROWB = StepGeo<T>::ROWB;
   constexpr int BK = ROWB / ES;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
+  constexpr int WGM = WAVES / 2;                     // wave rows; two wave columns
+  constexpr int WM = BM / WGM, WN = BN / 2;
   constexpr int MI = WM / 32, NI = WN / 32;
+  static_assert(MI >= 1 && NI >= 1, "tile too small for the wave grid");
   constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
   constexpr int NS = ring_stages(STAGE, BM * BN);
   static_assert(NS >= 2, "the ring needs two stages");
@@ -207,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmArgs p)
   constexpr int NSUB = BK / KMMA;
   constexpr int KC = Mma<T>::kChunks;
   static_assert(NSUB % 2 == 0, "fragment double buffer alternates per substep");
-  static_assert(A_KMAJ || BK == MNTileDma<BM>::KROWS, "MN-major stage depth");
+  static_assert(A_KMAJ || BK == MNTileDma<BM, WAVES>::KROWS, "MN-major stage depth");
 
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
 
@@ -227,10 +233,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmArgs p)
   const int nk = (kend - kbeg + BK - 1) / BK;
 
   // ---- DMA loaders
-  KTileDma<T, BM> ka;
-  KTileDma<T, BN> kb;
-  MNTileDma<BM> na;
-  MNTileDma<BN> nb;
+  KTileDma<T, BM, WAVES> ka;
+  KTileDma<T, BN, WAVES> kb;
+  MNTileDma<BM, WAVES> na;
+  MNTileDma<BN, WAVES> nb;
   if constexpr (A_KMAJ) {
     ka.init(wave, lane, kbeg, [&](int r) -> const char* {
       const int m = m0 + r;
@@ -254,8 +260,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmArgs p)
   } else {
     nb.init(wave, lane);
   }
-  constexpr int N_DMA = (A_KMAJ ? KTileDma<T, BM>::kInst : MNTileDma<BM>::kInst) +
-                        (B_KMAJ ? KTileDma<T, BN>::kInst : MNTileDma<BN>::kInst);
+  constexpr int N_DMA = (A_KMAJ ? KTileDma<T, BM, WAVES>::kInst : MNTileDma<BM, WAVES>::kInst) +
+                        (B_KMAJ ? KTileDma<T, BN, WAVES>::kInst : MNTileDma<BN, WAVES>::kInst);
   static_assert((NS - 1) * N_DMA < 64, "vmcnt range");
 
   // K-step kt into ring stage `stage`; steps past the end load zeros.
@@ -286,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmArgs p)
   for (int j = 0; j < NI; ++j) {
     if constexpr (GATED) {
       constexpr int NH = NI / 2;
-      b_base[j] = j < NH ? wn * (BN / 4) + j * 32 : BN / 2 + wn * (BN / 4) + (j - NH) * 32;
+      b_base[j] = j < NH ? wn * (WN / 2) + j * 32 : BN / 2 + wn * (WN / 2) + (j - NH) * 32;
     } else {
       b_base[j] = wn * WN + j * 32;
     }
@@ -300,16 +306,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmArgs p)
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        if constexpr (A_KMAJ) fa[slot][i][c] = KTileDma<T, BM>::read(sa, a_base[i] + frow, Mma<T>::chunk(s, fhalf, c));
-        else fa[slot][i][c] = MNTileDma<BM>::read(sa, a_base[i], s, lane);
+        if constexpr (A_KMAJ) fa[slot][i][c] = KTileDma<T, BM, WAVES>::read(sa, a_base[i] + frow, Mma<T>::chunk(s, fhalf, c));
+        else fa[slot][i][c] = MNTileDma<BM, WAVES>::read(sa, a_base[i], s, lane);
       }
     }
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        if constexpr (B_KMAJ) fb[slot][j][c] = KTileDma<T, BN>::read(sb, b_base[j] + frow, Mma<T>::chunk(s, fhalf, c));
-        else fb[slot][j][c] = MNTileDma<BN>::read(sb, b_base[j], s, lane);
+        if constexpr (B_KMAJ) fb[slot][j][c] = KTileDma<T, BN, WAVES>::read(sb, b_base[j] + frow, Mma<T>::chunk(s, fhalf, c));
+        else fb[slot][j][c] = MNTileDma<BN, WAVES>::read(sb, b_base[j], s, lane);
       }
     }
   };
@@ -364,16 +370,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const GemmArgs p)
   }
   // the trailing zero-fill DMAs have landed and no wave reads the ring any more: its LDS
   // becomes the epilogue's staging area
-  static_assert(epilogue_lds_bytes<BN>() <= NS * STAGE, "epilogue staging must fit the ring");
+  static_assert(epilogue_lds_bytes<BN, WAVES>() <= NS * STAGE, "epilogue staging must fit the ring");
   wait_vmcnt<0>();
   wait_lgkmcnt0();
   __builtin_amdgcn_s_barrier();
-  epilogue_rows<EPI, IoT, BM, BN, MI, NI>(p, acc, m0, n0, split, wm, wn, lane, wave, smem);
+  epilogue_rows<EPI, IoT, BM, BN, MI, NI, WAVES>(p, acc, m0, n0, split, wm, wn, lane, wave, smem);
 }
 
-template <typename T, typename IoT, int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI>
+template <typename T, typename IoT, int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int WAVES = 4>
 hipError_t launch_gemm_dma(const GemmArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_dma_kernel<T, IoT, BM, BN, A_KMAJ, B_KMAJ, EPI>), dim3(grid), dim3(kThreads),
+  hipLaunchKernelGGL((gemm_dma_kernel<T, IoT, BM, BN, A_KMAJ, B_KMAJ, EPI, WAVES>), dim3(grid), dim3(64 * WAVES),
                      0, stream, a);
   return hipGetLastError();
 }

@@ -10,10 +10,8 @@ namespace gmlp {
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
 enum Layout : int { NT = 0, NN = 1, TN = 2 };   // A K-major/B K-major, A K/B MN, A MN/B MN
-enum TileShape : int { TILE_256x256 = 0, TILE_256x128 = 1, TILE_128x128 = 2, TILE_COUNT = 3 };
-
-inline int tile_bm(int t) { return t == TILE_128x128 ? 128 : 256; }
-inline int tile_bn(int t) { return t == TILE_256x256 ? 256 : 128; }
+// Tile shapes of the bf16 / e4m3 kernel; _W8 runs the tile with 8 waves (two per SIMD).
+enum TileShape : int { TILE_256x256 = 0, TILE_256x128 = 1, TILE_128x128 = 2, TILE_256x256_W8 = 3, TILE_COUNT = 4 };
 
 // One GEMM launch. `io` is the element type of the epilogue's stored/loaded tensors (for
 // EPI_STORE the output type; accumulate mode needs DT_F32). Returns hipErrorInvalidValue for a

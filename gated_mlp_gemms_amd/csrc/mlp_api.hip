@@ -74,13 +74,14 @@ struct Plan {
 struct TileInfo { TileShape t; int bm, bn, slots; double eff; };
 // slots: workgroups per CU that fit in LDS (a 2-stage 256x256 ring takes 128 KiB, a 3-stage
 // 256x128 one 144 KiB, a 2-stage 128x128 one 64 KiB). eff: the CU's MFMA rate a tile shape
-// sustains relative to 256x256, measured on the LLaMA-shaped GEMMs (2048 tokens, 4096 x 11008):
-// two 128x128 workgroups per CU hide latency as well as one 256x256 one at twice the
-// operand traffic; 256x128 trails both.
+// sustains relative to a 4-wave 256x256 one, measured on the LLaMA-shaped GEMMs (2048 tokens,
+// 4096 x 11008): two 128x128 workgroups per CU come close at twice the operand traffic, the
+// 8-wave 256x256 tile beats both, 256x128 trails.
 const TileInfo kTiles[] = {
+    {TILE_256x256_W8, 256, 256, 1, 1.15},   // 8 waves: two per SIMD hide each other's stalls
     {TILE_256x256, 256, 256, 1, 1.00},
     {TILE_256x128, 256, 128, 1, 0.75},
-    {TILE_128x128, 128, 128, 2, 0.95},
+    {TILE_128x128, 128, 128, 2, 0.85},
 };
 
 int bk_of(DType in) { return in == DT_E4M3 ? 128 : (in == DT_BF16 ? 64 : 32); }
@@ -93,6 +94,7 @@ Plan plan_gemm(DType in, int64_t M, int64_t N, int64_t K, bool allow_split, bool
   double best_t = 1e300;
   for (const TileInfo& ti : kTiles) {
     if (in == DT_F32 && ti.t != TILE_128x128) continue;
+    if (in == DT_E4M3 && ti.t == TILE_256x256_W8) continue;
     const int64_t bn_units = gated ? ti.bn / 2 : ti.bn;
     const int64_t tm = (M + ti.bm - 1) / ti.bm, tn = (N + bn_units - 1) / bn_units;
     const int max_split = allow_split ? 16 : 1;
