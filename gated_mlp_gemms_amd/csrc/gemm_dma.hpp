@@ -16,6 +16,7 @@
 //    Inside a step the fragments of substep s+1 are read while the MFMAs of substep s run.
 #pragma once
 
+#include <climits>
 #include <type_traits>
 #include <utility>
 
@@ -27,10 +28,17 @@ namespace gmlp {
 // The DMA source of every tile slot that lies outside a matrix: 16 zero bytes.
 static __device__ __attribute__((aligned(16))) uint32_t g_zero_chunk[4];
 
-#define GMLP_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define GMLP_LDS(p) ((__attribute__((address_space(3))) char*)(p))
 
+// One LDS-DMA instruction: lane l's 16 bytes at src land at lds_wave_base + 16 l (the base is
+// wave-uniform and goes in M0). Issued as inline assembly on purpose: for the compiler's own
+// LDS-DMA builtin, the waitcnt pass cannot tell the DMA's LDS destination apart from a later
+// transposing LDS read and waits for every DMA in flight before each such read, which would
+// serialise the ring. The kernel counts its DMAs itself (wait_vmcnt), and the memory clobber
+// keeps every LDS access in program order around the issue.
 __device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, GMLP_LDS(lds_wave_base), 16, 0, 0);
+  const uint32_t lds = (uint32_t)(uintptr_t)GMLP_LDS(lds_wave_base);
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
 }
 
 // vmcnt(N), N < 64 (gfx9 encoding: low 4 bits in [3:0], high 2 bits in [15:14]); expcnt and
@@ -121,39 +129,48 @@ struct KTileDma {
 };
 
 // ---- MN-major bf16 operand: 64 k-rows x ROWS columns per stage --------------------------------
+// The operand may be two matrices stacked along K (rows k < k_split from the first, the rest
+// from the second, both with the same leading dimension). Each lane keeps the address of its
+// chunk in the first matrix at the first K-step; a K-step adds a uniform offset, and a lane whose
+// k-row lies in the second matrix adds the uniform distance between the two, so the issue is a
+// few selects per DMA and no branch.
 template <int ROWS, int WAVES>
 struct MNTileDma {
   static constexpr int KROWS = 64;
   static constexpr int ROWB = ROWS * 2;               // bytes per k-row
   static constexpr int kInst = KROWS * ROWB / 1024 / WAVES;   // per wave per stage
   static_assert(kInst >= 1, "tile too narrow");
+  const char* ptr[kInst];   // chunk address at K-step 0, as if every k-row were in the first matrix
   int krow[kInst];
-  int col[kInst];
+  bool col_ok[kInst];
 
   static __device__ __forceinline__ int phys_chunk(int c, int kr) { return c ^ ((kr & 3) << 2); }
 
-  __device__ __forceinline__ void init(int wave, int lane) {
+  // base: element (0, tile column 0) of the first matrix; ld_bytes: its row pitch; ncols:
+  // columns of the matrix from tile column 0 on.
+  __device__ __forceinline__ void init(int wave, int lane, const char* base, int64_t ld_bytes, int kbeg,
+                                       int ncols) {
 #pragma unroll
     for (int i = 0; i < kInst; ++i) {
       const int j = wave * kInst + i;
       const int byte = j * 1024 + lane * 16;
       const int kr = byte / ROWB;
-      const int pc = (byte % ROWB) >> 4;
+      const int col = phys_chunk((byte % ROWB) >> 4, kr) * 8;   // the XOR is an involution
       krow[i] = kr;
-      col[i] = phys_chunk(pc, kr) * 8;                  // the XOR is an involution
+      col_ok[i] = col < ncols;
+      ptr[i] = base + (int64_t)(kbeg + kr) * ld_bytes + col * 2;
     }
   }
-  // src(k) -> pointer to element (k, tile column 0); ncols: columns of the matrix from tile
-  // column 0 on.
-  template <typename SrcRow>
-  __device__ __forceinline__ void issue(char* tile, int wave, int k0, int kend, int ncols, SrcRow src) const {
+  // K-step starting at k0 (absolute); step_off: byte offset of this K-step from the first;
+  // second: distance from a k-row's address in the first matrix to its address in the second.
+  __device__ __forceinline__ void issue(char* tile, int wave, int k0, int kend, int64_t step_off, int k_split,
+                                        int64_t second) const {
 #pragma unroll
     for (int i = 0; i < kInst; ++i) {
       const int j = wave * kInst + i;
       const int k = k0 + krow[i];
-      const void* s = (k < kend && col[i] < ncols) ? (const void*)(src(k) + (int64_t)col[i] * 2)
-                                                   : (const void*)g_zero_chunk;
-      dma16(s, tile + j * 1024);
+      const char* s = ptr[i] + step_off + (k >= k_split ? second : 0);
+      dma16((k < kend && col_ok[i]) ? (const void*)s : (const void*)g_zero_chunk, tile + j * 1024);
     }
   }
   // Fragment of the 32-column block starting at tile column cb, K substep s (16 k): lane l gets
@@ -167,16 +184,12 @@ struct MNTileDma {
     const int off0 = kr * ROWB + (phys_chunk(c >> 3, kr) << 4) + (c & 7) * 2;
     const int off1 = off0 + 4 * ROWB;                  // k-row + 4: same (k-row % 4)
     typedef short i16x4 __attribute__((ext_vector_type(4)));
-    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(tile + off0));
-    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(tile + off1));
-    u32x4 r;
-    r[0] = (uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
-    r[1] = (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
-    r[2] = (uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16);
-    r[3] = (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16);
-    return r;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(tile + off0)));
+    const u32x2 v1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(tile + off1)));
+    return __builtin_shufflevector(v0, v1, 0, 1, 2, 3);
   }
 };
 
@@ -243,7 +256,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
       return m < p.M ? elem_ptr<T>(p.A, m, p.lda, 0) : nullptr;
     });
   } else {
-    na.init(wave, lane);
+    na.init(wave, lane, reinterpret_cast<const char*>(elem_ptr<T>(p.A, 0, p.lda, m0)), (int64_t)p.lda * ES, kbeg,
+            p.M - m0);
   }
   if constexpr (B_KMAJ) {
     kb.init(wave, lane, kbeg, [&](int r) -> const char* {
@@ -258,8 +272,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
       }
     });
   } else {
-    nb.init(wave, lane);
+    nb.init(wave, lane, reinterpret_cast<const char*>(elem_ptr<T>(p.B0, 0, p.ldb, n0)), (int64_t)p.ldb * ES, kbeg,
+            p.N - n0);
   }
+  // B stacked from two matrices along K (MN-major only): distance from B0's row k to B1's row
+  // k - b_split
+  const int64_t b_second = (!B_KMAJ && p.B1 != nullptr)
+      ? (reinterpret_cast<const char*>(p.B1) - reinterpret_cast<const char*>(p.B0)) - (int64_t)p.b_split * p.ldb * ES
+      : 0;
+  const int b_split = (!B_KMAJ && p.B1 != nullptr) ? p.b_split : INT_MAX;
   constexpr int N_DMA = (A_KMAJ ? KTileDma<T, BM, WAVES>::kInst : MNTileDma<BM, WAVES>::kInst) +
                         (B_KMAJ ? KTileDma<T, BN, WAVES>::kInst : MNTileDma<BN, WAVES>::kInst);
   static_assert((NS - 1) * N_DMA < 64, "vmcnt range");
@@ -271,15 +292,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     if constexpr (A_KMAJ) {
       ka.issue(sa, wave, kt * BK, kend - kbeg);
     } else {
-      na.issue(sa, wave, kbeg + kt * BK, kend, p.M - m0,
-               [&](int k) -> const char* { return elem_ptr<T>(p.A, k, p.lda, m0); });
+      na.issue(sa, wave, kbeg + kt * BK, kend, (int64_t)kt * BK * p.lda * ES, INT_MAX, 0);
     }
     if constexpr (B_KMAJ) {
       kb.issue(sb, wave, kt * BK, kend - kbeg);
     } else {
-      nb.issue(sb, wave, kbeg + kt * BK, kend, p.N - n0, [&](int k) -> const char* {
-        return k < p.b_split ? elem_ptr<T>(p.B0, k, p.ldb, n0) : elem_ptr<T>(p.B1, k - p.b_split, p.ldb, n0);
-      });
+      nb.issue(sb, wave, kbeg + kt * BK, kend, (int64_t)kt * BK * p.ldb * ES, b_split, b_second);
     }
   };
 
