@@ -177,6 +177,13 @@ def main():
         us = 1e3 * sum(ev.elapsed_ms(*pairs[i][j]) for i in range(args.steps)) / args.steps
         stage_us[n] = round(us, 2)
         stage_tf[n] = round(sf[n] / (us * 1e-6) / 1e12, 1)
+    # per-step spread: from the up-projection's start to the last weight gradient's end
+    j_up, j_last = stages.index("up"), stages.index("dw_up")
+    per_step = sorted(ev.elapsed_ms(pairs[i][j_up][0], pairs[i][j_last][1]) for i in range(args.steps))
+    q = lambda f: per_step[min(len(per_step) - 1, int(round(f * (len(per_step) - 1))))]
+    spread = {"median": round(q(0.5), 4), "min": round(per_step[0], 4), "p90": round(q(0.9), 4)}
+    fwd_us = round(stage_us["up"] + stage_us["down"], 2)
+    bwd_us = round(sum(v for k, v in stage_us.items() if k not in ("up", "down")), 2)
     for row in pairs:
         for b, e in row:
             ev.destroy(b)
@@ -189,6 +196,30 @@ def main():
             "flop_per_launch": sf[dom], "avg_launch_us": stage_us[dom], "traffic_source": traffic_src}
     log(f"[bench] {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of bf16 peak); "
         f"stages us {stage_us}")
+
+    # inference forward (no saved pre-activation), and the training step with cold caches: a
+    # 512 MiB write between steps evicts the operands from L2 and the last-level cache
+    n_side = max(1, min(args.steps, 20))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n_side):
+        r.forward_infer()
+    b.record()
+    torch.cuda.synchronize()
+    infer_us = round(1e3 * a.elapsed_time(b) / n_side, 2)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(n_side):
+        flush.fill_(1)
+        a.record()
+        r.step()
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
+    cold_ms = round(sorted(cold)[len(cold) // 2], 4)
+    log(f"[bench] step median {spread['median']} ms (min {spread['min']}, p90 {spread['p90']}); fwd {fwd_us} us, "
+        f"bwd {bwd_us} us; inference fwd {infer_us} us; cold-cache step {cold_ms} ms")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -209,6 +240,9 @@ def main():
                    "model_flop_per_step": flops, "pct_of_bf16_peak": round(100 * tflops / peak, 2),
                    "wall_s_timed": round(wall, 3)},
         "stages_us": stage_us, "stages_tflops": stage_tf,
+        "step_ms": spread, "fwd_us": fwd_us, "bwd_us": bwd_us,
+        "infer_fwd_us": infer_us, "infer_fwd_tflops": round(w.model_flops() / 3 / (infer_us * 1e-6) / 1e12, 1),
+        "cold_cache_ms_per_step": cold_ms,
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -73,15 +73,16 @@ struct Plan {
 
 struct TileInfo { TileShape t; int bm, bn, slots; double eff; };
 // slots: workgroups per CU that fit in LDS (a 2-stage 256x256 ring takes 128 KiB, a 3-stage
-// 256x128 one 144 KiB, a 2-stage 128x128 one 64 KiB). eff: the CU's MFMA rate a tile shape
-// sustains relative to a 4-wave 256x256 one, measured on the LLaMA-shaped GEMMs (2048 tokens,
-// 4096 x 11008): two 128x128 workgroups per CU come close at twice the operand traffic, the
-// 8-wave 256x256 tile beats both, 256x128 trails.
+// 256x128 one 144 KiB, a 2-stage 128x128 one 64 KiB). eff: the fraction of a CU's peak MFMA rate
+// one K-step of the tile sustains with every CU busy, measured per K-step on the bf16 GEMMs of
+// the 2048-token 4096 x 11008 SwiGLU step (random data, all three layouts, fused epilogues):
+// the 8-wave 256x256 tile takes ~1.95 us per 64-deep K-step, the 4-wave one ~2.1 us, a pair of
+// 128x128 workgroups ~1.2 us, and the 256x128 tile ~1.3 us.
 const TileInfo kTiles[] = {
-    {TILE_256x256_W8, 256, 256, 1, 1.15},   // 8 waves: two per SIMD hide each other's stalls
-    {TILE_256x256, 256, 256, 1, 1.00},
-    {TILE_256x128, 256, 128, 1, 0.75},
-    {TILE_128x128, 128, 128, 2, 0.85},
+    {TILE_256x256_W8, 256, 256, 1, 0.44},   // 8 waves: two per SIMD hide each other's stalls
+    {TILE_256x256, 256, 256, 1, 0.40},
+    {TILE_256x128, 256, 128, 1, 0.33},
+    {TILE_128x128, 128, 128, 2, 0.36},
 };
 
 int bk_of(DType in) { return in == DT_E4M3 ? 128 : (in == DT_BF16 ? 64 : 32); }
