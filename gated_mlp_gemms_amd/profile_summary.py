@@ -4,7 +4,11 @@
     python -m gated_mlp_gemms_amd.profile_summary traffic <fetch dir> <write dir> <out.json> --command "..."
 
 The trace summary lists every kernel's dispatch count and average / total duration from the
-`*_kernel_stats.csv` rocprofv3 writes with `--kernel-trace --stats --output-format csv`.
+`*_kernel_stats.csv` rocprofv3 writes with `--kernel-trace --stats --output-format csv`, then the
+average duration of each step stage's kernels, from the per-dispatch `*_kernel_trace.csv`, over
+the timed steps only (`--first-step`, `--steps`: the bench's warmup and step counts). A kernel
+instantiation that serves two stages (the same GEMM shape class for dW_down and dW_gate/dW_up)
+thus gets one average per stage, the figure the bench's per-stage HIP events measure.
 
 The traffic summary reads two `--pmc` passes over the same command (FETCH_SIZE, then
 WRITE_SIZE, both in KiB per dispatch) that also ran one plain device copy of known size
@@ -45,23 +49,56 @@ def _one(pattern: str) -> str:
     return hits[0]
 
 
+_GEMM = re.compile(r"gemm_(dma_)?kernelI(.+?)Li(\d+)ELi(\d+)ELb(\d)ELb(\d)ELi(\d)E(?:Li(\d+)E)?")
+_EPI = ["STORE", "PARTIAL", "GATED", "ACT", "DGATED", "DACT", "F8ACT"]
+
+
+# rocprofv3 prints some instantiations demangled (and their element types garbled)
+_GEMM_DEMANGLED = re.compile(r"gmlp::gemm_(dma_)?kernel<(.*), (\d+), (\d+), (true|false), (true|false), (\d)(?:, (\d+))?>")
+
+
+def _gemm_fields(name: str):
+    m = _GEMM.search(name)
+    if m:
+        return m.groups()
+    m = _GEMM_DEMANGLED.search(name)
+    if m:
+        dma, types, bm, bn, ak, bk, epi, waves = m.groups()
+        b = {"true": "1", "false": "0"}
+        if int(epi) == 1:
+            types += "f"   # split-K partials are fp32
+        return dma, types, bm, bn, b[ak], b[bk], epi, waves
+    return None
+
+
+def is_library_kernel(name: str) -> bool:
+    return "4gmlp" in name or "gmlp::" in name
+
+
+def gemm_epilogue(name: str):
+    """The epilogue index of one of this library's GEMM kernels (None for other kernels)."""
+    f = _gemm_fields(name)
+    return int(f[6]) if f else None
+
+
 def short_name(name: str) -> str:
     """A readable name for the engine's kernels (template arguments spelled out)."""
-    m = re.search(r"gemm_(dma_)?kernelI(.+?)Li(\d+)ELi(\d+)ELb(\d)ELb(\d)ELi(\d)E", name)
-    if m:
-        dma, types, bm, bn, ak, bk, epi = m.groups()
+    f = _gemm_fields(name)
+    if f:
+        dma, types, bm, bn, ak, bk, epi, waves = f
         lay = {("1", "1"): "NT", ("1", "0"): "NN", ("0", "0"): "TN"}.get((ak, bk), "??")
-        epin = ["STORE", "PARTIAL", "GATED", "ACT", "DGATED", "DACT", "F8ACT"][int(epi)]
+        epin = _EPI[int(epi)]
         t = "e4m3" if "e4m3" in types else ("f32" if types.startswith("ff") else "bf16")
         out = "f32" if "DF16bf" in types or types.endswith("f") else ""
-        return f"gemm{'' if dma else '_regstaged'}<{t},{lay},{bm}x{bn},{epin}{',' + out + ' out' if out else ''}>"
+        w = f",{waves}w" if waves else ""
+        return f"gemm{'' if dma else '_regstaged'}<{t},{lay},{bm}x{bn}{w},{epin}{',' + out + ' out' if out else ''}>"
     for k in ("splitk_reduce", "gated_act", "relu_sq_kernel", "absmax", "quantize_kernel", "dequant", "zero_f32"):
         if k in name:
             return k
     return name.split("(")[0][:60]
 
 
-def summarize_trace(trace_dir: str, out_txt: str, command: str) -> None:
+def summarize_trace(trace_dir: str, out_txt: str, command: str, first_step: int = 0, steps: int = 0) -> None:
     stats = _one(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
     rows = list(csv.DictReader(open(stats)))
     lines = [f"# rocprofv3 kernel statistics", f"# command: {command}", f"# kernel sources sha256: {kernel_sources_sha256()}",
@@ -73,8 +110,46 @@ def summarize_trace(trace_dir: str, out_txt: str, command: str) -> None:
         tot_ns = float(r["TotalDurationNs"])
         pct = float(r.get("Percentage", 0.0))
         lines.append(f"{short_name(name):64s} {calls:6d} {avg_ns / 1e3:10.1f} {tot_ns / 1e6:10.3f} {pct:6.2f}")
+    trace = _one(os.path.join(trace_dir, "**", "*kernel_trace.csv"))
+    disp = sorted((int(r["Dispatch_Id"]), r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+                  for r in csv.DictReader(open(trace)))
+    per_step = _per_step(disp, STAGE_ORDER_GATED)
+    timed = per_step[first_step:first_step + steps] if steps else per_step[first_step:]
+    lines += ["", f"# per-stage kernel time, average over {len(timed)} timed steps (dispatch order; a split-K "
+                  f"reduce counts with its GEMM)", f"{'stage':10s} {'kernels':64s} {'avg us':>10s}"]
+    for st in STAGE_ORDER_GATED:
+        if not timed:
+            break
+        kern = " + ".join(dict.fromkeys(short_name(n) for n, _ in timed[0][st]))
+        avg = sum(sum(d for _, d in s[st]) for s in timed) / len(timed)
+        lines.append(f"{st:10s} {kern:64s} {avg:10.1f}")
     open(out_txt, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def _per_step(disp, stages):
+    """Split this library's dispatches into steps (a step starts at each up-projection) and each
+    step into stages (each GEMM opens the next stage; other kernels join the current one). Only
+    whole steps are returned; launches of other libraries (a fill, a copy) are skipped."""
+    steps, cur, idx = [], None, -1
+    for _, name, val in disp:
+        if not is_library_kernel(name):
+            continue
+        epi = gemm_epilogue(name)
+        is_gemm = epi is not None
+        if epi in (2, 3, 6):   # GATED, ACT, F8ACT: the up-projection
+            cur = {st: [] for st in stages}
+            steps.append(cur)
+            idx = 0
+        elif cur is None:
+            continue
+        elif is_gemm:
+            idx += 1
+        if idx < len(stages):
+            cur[stages[idx]].append((name, val))
+        else:
+            cur["_extra"] = True
+    return [s for s in steps if all(s[st] for st in stages) and "_extra" not in s]
 
 
 def _dispatches(pmc_dir: str, counter: str) -> list[tuple[int, str, float]]:
@@ -87,29 +162,17 @@ def _dispatches(pmc_dir: str, counter: str) -> list[tuple[int, str, float]]:
     return out
 
 
-def _stage_bytes(disp, factor, stages):
-    """Average bytes per stage over the profiled steps; a step starts at each up-projection."""
-    per_step, cur, idx = [], None, -1
-    for _, name, kib in disp:
-        is_gemm = "gemm_" in name
-        epi = re.search(r"ELi(\d)EEEvNS_8GemmArgsE", name)
-        is_up = is_gemm and epi is not None and epi.group(1) in ("2", "3", "6")
-        if is_up:
-            cur = {}
-            per_step.append(cur)
-            idx = 0
-        elif cur is None:
-            continue
-        elif is_gemm:
-            idx += 1
-        if cur is None or idx >= len(stages):
-            continue
-        cur[stages[idx]] = cur.get(stages[idx], 0.0) + kib * 1024.0 * factor
-    full = [s for s in per_step if len(s) == len(stages)]
-    return {st: sum(s[st] for s in full) / len(full) for st in stages} if full else {}
+def _stage_bytes(disp, factor, stages, first_step=0, steps=0):
+    """Average bytes per stage over the timed steps."""
+    per_step = _per_step(disp, stages)
+    full = per_step[first_step:first_step + steps] if steps else per_step[first_step:]
+    if not full:
+        return {}
+    return {st: sum(sum(kib for _, kib in s[st]) for s in full) * 1024.0 * factor / len(full) for st in stages}
 
 
-def summarize_traffic(fetch_dir: str, write_dir: str, out_json: str, command: str, copy_mib: int) -> None:
+def summarize_traffic(fetch_dir: str, write_dir: str, out_json: str, command: str, copy_mib: int,
+                      first_step: int = 0, steps: int = 0) -> None:
     fetch, write = _dispatches(fetch_dir, "FETCH_SIZE"), _dispatches(write_dir, "WRITE_SIZE")
     copy_bytes = copy_mib * 1024 * 1024
     fc = [v for _, n, v in fetch if "copyBuffer" in n]
@@ -118,8 +181,8 @@ def summarize_traffic(fetch_dir: str, write_dir: str, out_json: str, command: st
         raise SystemExit("the profiled command ran no device copy (use bench.py --copy-probe-mib)")
     f_factor = copy_bytes / (fc[0] * 1024.0)
     w_factor = copy_bytes / (wc[0] * 1024.0)
-    fb = _stage_bytes(fetch, f_factor, STAGE_ORDER_GATED)
-    wb = _stage_bytes(write, w_factor, STAGE_ORDER_GATED)
+    fb = _stage_bytes(fetch, f_factor, STAGE_ORDER_GATED, first_step, steps)
+    wb = _stage_bytes(write, w_factor, STAGE_ORDER_GATED, first_step, steps)
     res = {"command": command, "kernel_sources_sha256": kernel_sources_sha256(),
            "copy_probe_bytes": copy_bytes, "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
            "stages": {st: {"fetch_bytes": round(fb.get(st, 0.0)), "write_bytes": round(wb.get(st, 0.0)),
@@ -135,17 +198,21 @@ def main(argv=None):
     t.add_argument("trace_dir")
     t.add_argument("out_txt")
     t.add_argument("--command", required=True)
+    t.add_argument("--first-step", type=int, default=0, help="whole steps to skip (the bench's warmup)")
+    t.add_argument("--steps", type=int, default=0, help="whole steps to average (0: all)")
     f = sub.add_parser("traffic")
     f.add_argument("fetch_dir")
     f.add_argument("write_dir")
     f.add_argument("out_json")
     f.add_argument("--command", required=True)
     f.add_argument("--copy-mib", type=int, default=256)
+    f.add_argument("--first-step", type=int, default=0)
+    f.add_argument("--steps", type=int, default=0)
     a = ap.parse_args(argv)
     if a.what == "trace":
-        summarize_trace(a.trace_dir, a.out_txt, a.command)
+        summarize_trace(a.trace_dir, a.out_txt, a.command, a.first_step, a.steps)
     else:
-        summarize_traffic(a.fetch_dir, a.write_dir, a.out_json, a.command, a.copy_mib)
+        summarize_traffic(a.fetch_dir, a.write_dir, a.out_json, a.command, a.copy_mib, a.first_step, a.steps)
 
 
 if __name__ == "__main__":
