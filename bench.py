@@ -75,6 +75,41 @@ def measured_traffic(workload: str, stage: str):
     return (st["traffic_bytes"] if st else None), os.path.basename(path)
 
 
+def vendor_gemm_reference(w, tensors, reps: int = 20) -> dict:
+    """The same six matrix products timed through torch.matmul (hipBLASLt on ROCm): operands in
+    the layouts this engine reads, plain bf16 outputs, no activation, no epilogue and no
+    elementwise kernels. Context only: it times a different, unfused computation."""
+    import torch
+
+    dev = "cuda"
+    x = tensors["x"].to(dev)
+    dout = tensors["dout"].to(dev)
+    if w.gated:
+        w_in = torch.cat([tensors["w_gate"], tensors["w_up"]]).to(dev)    # [2H, d]
+        w_out = tensors["w_down"].to(dev)
+    else:
+        w_in, w_out = tensors["w1"].to(dev), tensors["w2"].to(dev)
+    P = w_in.shape[0]
+    act = torch.randn(w.M, w.hidden, device=dev, dtype=x.dtype)
+    dpre = torch.randn(w.M, P, device=dev, dtype=x.dtype)
+    cases = {"up": lambda: x @ w_in.t(), "down": lambda: act @ w_out.t(), "dact": lambda: dout @ w_out,
+             "dw_down": lambda: dout.t() @ act, "dx": lambda: dpre @ w_in, "dw_up": lambda: dpre.t() @ x}
+    res = {}
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for k, fn in cases.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[k] = round(1e3 * a.elapsed_time(b) / reps, 2)
+    res["sum"] = round(sum(res.values()), 2)
+    return res
+
+
 def cpu_baseline(w, tensors, rows: int) -> dict:
     """The float64 oracle (as it stands) on the first `rows` tokens of the workload, all of d
     and H: forward + backward, timed on this host's cores."""
@@ -110,6 +145,8 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="tokens in the oracle's CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--vendor-gemm-reference", action="store_true",
+                    help="also time the six plain GEMMs through torch.matmul (hipBLASLt), for context")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warmup (a known-size "
                          "reference for profiler byte counters)")
@@ -221,6 +258,11 @@ def main():
     log(f"[bench] step median {spread['median']} ms (min {spread['min']}, p90 {spread['p90']}); fwd {fwd_us} us, "
         f"bwd {bwd_us} us; inference fwd {infer_us} us; cold-cache step {cold_ms} ms")
 
+    vendor = None
+    if args.vendor_gemm_reference:
+        vendor = vendor_gemm_reference(w, tensors)
+        log(f"[bench] torch.matmul (hipBLASLt) on the six plain GEMMs: {vendor} us")
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle on {args.cpu_rows} tokens")
@@ -245,6 +287,8 @@ def main():
         "cold_cache_ms_per_step": cold_ms,
         "roofline": roof, "cpu_baseline": cpu,
     }
+    if vendor is not None:
+        line["vendor_gemms_us"] = vendor
     print(json.dumps(line), flush=True)
 
 
