@@ -20,8 +20,10 @@ Every function states the passage it follows. Matrix products use ``numpy.matmul
 a library primitive; nothing else is blocked, fused or reordered.
 """
 from .mlp import (  # noqa: F401
-    sigmoid, silu, dsilu, relu_sq, drelu_sq,
+    sigmoid, silu, dsilu, relu_sq, drelu_sq, relu, drelu, gelu_tanh, dgelu_tanh, dsigmoid,
+    GATED_FNS, PLAIN_FNS,
     gated_forward, gated_backward, gated_sampled,
+    act_forward, act_backward, act_sampled,
     relu_sq_forward, relu_sq_backward, relu_sq_sampled,
     accumulate,
 )

@@ -25,6 +25,18 @@ dx = dpreact W1, dW1 = dpreact^T x. For the gated case W1 = [W_gate; W_up] and
 dpreact = [dg, du], so dx = dg W_gate + du W_up and [dW_gate; dW_up] = [dg, du]^T x
 (flash-swiglu README, "design points": merged dW_g/dW_u GEMM, single-accumulator dI).
 The backward recomputes g, u (or pre) from x: it keeps no state from the forward.
+
+Other activations. quack ``mlp.py`` names the set its MLP accepts (``Activation``: gelu_tanh_approx,
+relu, relu_sq, swiglu, swiglu_oai, reglu, geglu, glu; the gated ones are those in its gate map)
+but prints no formula; the standard definitions are used, with the gate multiplier placed as for
+SwiGLU:
+    gelu_tanh(z) = z/2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3)))   (Hendrycks & Gimpel, 2016,
+                                                                       the tanh approximation)
+    relu(z) = max(z, 0)                       (derivative 1 for z > 0, else 0)
+    glu:   a = sigmoid(g) * u                 (Dauphin et al., 2017)
+    reglu: a = relu(g) * u,  geglu: a = gelu_tanh(g) * u,  swiglu: a = silu(g) * u
+                                              (Shazeer, 2020, "GLU Variants Improve Transformer")
+swiglu_oai has no definition on the pages and is not provided.
 """
 from __future__ import annotations
 
@@ -70,24 +82,74 @@ def drelu_sq(z):
     return 2.0 * np.maximum(_f64(z), 0.0)
 
 
-def _gate_act(g, u, gate_mult, gate_mode):
+def relu(z):
+    """max(z, 0)."""
+    return np.maximum(_f64(z), 0.0)
+
+
+def drelu(z):
+    """d relu / dz: 1 for z > 0, 0 for z <= 0 (the subgradient 0 at the kink, as relu^2' = 0 there)."""
+    return (_f64(z) > 0.0).astype(np.float64)
+
+
+_GELU_C = np.sqrt(2.0 / np.pi)
+_GELU_K = 0.044715
+
+
+def gelu_tanh(z):
+    """z/2 * (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))): the tanh approximation of GELU."""
+    z = _f64(z)
+    return 0.5 * z * (1.0 + np.tanh(_GELU_C * (z + _GELU_K * z ** 3)))
+
+
+def dgelu_tanh(z):
+    """d gelu_tanh / dz = (1 + t)/2 + z/2 (1 - t^2) sqrt(2/pi) (1 + 3 * 0.044715 z^2), with t the
+    tanh of the definition."""
+    z = _f64(z)
+    t = np.tanh(_GELU_C * (z + _GELU_K * z ** 3))
+    return 0.5 * (1.0 + t) + 0.5 * z * (1.0 - t * t) * _GELU_C * (1.0 + 3.0 * _GELU_K * z * z)
+
+
+def dsigmoid(z):
+    """d sigmoid / dz = sigmoid(z) (1 - sigmoid(z))."""
+    s = sigmoid(z)
+    return s * (1.0 - s)
+
+
+# gate function f and its derivative of each gated activation: a = f(g) * u
+GATED_FNS = {"swiglu": (silu, dsilu), "geglu": (gelu_tanh, dgelu_tanh), "reglu": (relu, drelu),
+             "glu": (sigmoid, dsigmoid)}
+# activation f and its derivative of each non-gated activation: post = f(pre)
+PLAIN_FNS = {"relu_sq": (relu_sq, drelu_sq), "relu": (relu, drelu), "gelu_tanh": (gelu_tanh, dgelu_tanh)}
+
+
+def _gated_fn(act):
+    if act not in GATED_FNS:
+        raise ValueError(f"gated activation must be one of {sorted(GATED_FNS)}, got {act!r}")
+    return GATED_FNS[act]
+
+
+def _gate_act(g, u, gate_mult, gate_mode, act="swiglu"):
+    f, _ = _gated_fn(act)
     if gate_mode == "outside":
-        return gate_mult * silu(g) * u
+        return gate_mult * f(g) * u
     if gate_mode == "inside":
-        return silu(gate_mult * g) * u
+        return f(gate_mult * g) * u
     raise ValueError(f"gate_mode must be 'outside' or 'inside', got {gate_mode!r}")
 
 
-def _gate_act_grad(da, g, u, gate_mult, gate_mode):
+def _gate_act_grad(da, g, u, gate_mult, gate_mode, act="swiglu"):
     """(dg, du) for a = act(g, u) given da = dL/da (chain rule on the two formulas above)."""
+    f, df = _gated_fn(act)
     if gate_mode == "outside":
-        return da * gate_mult * u * dsilu(g), da * gate_mult * silu(g)
+        return da * gate_mult * u * df(g), da * gate_mult * f(g)
     if gate_mode == "inside":
-        return da * u * gate_mult * dsilu(gate_mult * g), da * silu(gate_mult * g)
+        return da * u * gate_mult * df(gate_mult * g), da * f(gate_mult * g)
     raise ValueError(f"gate_mode must be 'outside' or 'inside', got {gate_mode!r}")
 
 
-def gated_forward(x, w_gate, w_up, w_down, gate_mult=1.0, down_mult=1.0, gate_mode="outside"):
+def gated_forward(x, w_gate, w_up, w_down, gate_mult=1.0, down_mult=1.0, gate_mode="outside",
+                  act="swiglu"):
     """SwiGLU MLP forward in float64. Returns dict(g, u, a, out).
 
     Follows the flash-swiglu README's formula down_multiplier * down_proj(gate_multiplier *
@@ -96,13 +158,13 @@ def gated_forward(x, w_gate, w_up, w_down, gate_mult=1.0, down_mult=1.0, gate_mo
     x, w_gate, w_up, w_down = map(_f64, (x, w_gate, w_up, w_down))
     g = x @ w_gate.T
     u = x @ w_up.T
-    a = _gate_act(g, u, gate_mult, gate_mode)
+    a = _gate_act(g, u, gate_mult, gate_mode, act)
     out = down_mult * (a @ w_down.T)
     return {"g": g, "u": u, "a": a, "out": out}
 
 
 def gated_backward(dout, x, w_gate, w_up, w_down, gate_mult=1.0, down_mult=1.0,
-                   gate_mode="outside"):
+                   gate_mode="outside", act="swiglu"):
     """SwiGLU MLP backward in float64, recomputing g, u from x.
 
     Steps as in quack ``MLPRecomputeFunc.backward``: recompute the pre-activation, apply the
@@ -112,9 +174,9 @@ def gated_backward(dout, x, w_gate, w_up, w_down, gate_mult=1.0, down_mult=1.0,
     dout, x, w_gate, w_up, w_down = map(_f64, (dout, x, w_gate, w_up, w_down))
     g = x @ w_gate.T
     u = x @ w_up.T
-    a = _gate_act(g, u, gate_mult, gate_mode)
+    a = _gate_act(g, u, gate_mult, gate_mode, act)
     da = down_mult * (dout @ w_down)
-    dg, du = _gate_act_grad(da, g, u, gate_mult, gate_mode)
+    dg, du = _gate_act_grad(da, g, u, gate_mult, gate_mode, act)
     return {
         "dw_down": down_mult * (dout.T @ a),
         "dx": dg @ w_gate + du @ w_up,
@@ -125,7 +187,7 @@ def gated_backward(dout, x, w_gate, w_up, w_down, gate_mult=1.0, down_mult=1.0,
 
 
 def gated_sampled(dout, x, w_gate, w_up, w_down, rows, units, gate_mult=1.0, down_mult=1.0,
-                  gate_mode="outside"):
+                  gate_mode="outside", act="swiglu"):
     """The same definitions as ``gated_forward``/``gated_backward``, evaluated only where
     needed for a sample of outputs: out[rows], dx[rows], and the hidden units ``units`` of the
     weight gradients (dw_down[:, units], dw_gate[units, :], dw_up[units, :]).
@@ -140,17 +202,17 @@ def gated_sampled(dout, x, w_gate, w_up, w_down, rows, units, gate_mult=1.0, dow
     xr = x[rows]
     g = xr @ w_gate.T
     u = xr @ w_up.T
-    a = _gate_act(g, u, gate_mult, gate_mode)
+    a = _gate_act(g, u, gate_mult, gate_mode, act)
     out_rows = down_mult * (a @ w_down.T)
     da = down_mult * (dout[rows] @ w_down)
-    dg, du = _gate_act_grad(da, g, u, gate_mult, gate_mode)
+    dg, du = _gate_act_grad(da, g, u, gate_mult, gate_mode, act)
     dx_rows = dg @ w_gate + du @ w_up
     # units: all tokens, selected hidden units
     gc = x @ w_gate[units].T
     uc = x @ w_up[units].T
-    ac = _gate_act(gc, uc, gate_mult, gate_mode)
+    ac = _gate_act(gc, uc, gate_mult, gate_mode, act)
     dac = down_mult * (dout @ w_down[:, units])
-    dgc, duc = _gate_act_grad(dac, gc, uc, gate_mult, gate_mode)
+    dgc, duc = _gate_act_grad(dac, gc, uc, gate_mult, gate_mode, act)
     return {
         "out_rows": out_rows, "dx_rows": dx_rows,
         "dw_down_cols": down_mult * (dout.T @ ac),
@@ -158,24 +220,32 @@ def gated_sampled(dout, x, w_gate, w_up, w_down, rows, units, gate_mult=1.0, dow
     }
 
 
-def relu_sq_forward(x, w1, w2, down_mult=1.0):
-    """ReLU^2 MLP forward: pre = x W1^T, post = relu(pre)^2, out = down_mult * post W2^T
-    (modded-nanogpt ``gpt.py``, ``ReLUSqrdMLP`` comment and ``GPT._mlp``)."""
+def _plain_fn(act):
+    if act not in PLAIN_FNS:
+        raise ValueError(f"non-gated activation must be one of {sorted(PLAIN_FNS)}, got {act!r}")
+    return PLAIN_FNS[act]
+
+
+def act_forward(x, w1, w2, down_mult=1.0, act="relu_sq"):
+    """Non-gated MLP forward: pre = x W1^T, post = f(pre), out = down_mult * post W2^T
+    (modded-nanogpt ``gpt.py`` for f = relu^2: ``ReLUSqrdMLP`` comment and ``GPT._mlp``)."""
     x, w1, w2 = map(_f64, (x, w1, w2))
+    f, _ = _plain_fn(act)
     pre = x @ w1.T
-    post = relu_sq(pre)
+    post = f(pre)
     return {"pre": pre, "post": post, "out": down_mult * (post @ w2.T)}
 
 
-def relu_sq_backward(dout, x, w1, w2, down_mult=1.0):
-    """ReLU^2 MLP backward (quack ``MLPRecomputeFunc.backward`` with the non-gated ops):
-    dpre = (down_mult * dout W2) * 2 relu(pre); dW2 = down_mult * dout^T post;
-    dx = dpre W1; dW1 = dpre^T x. Returns dict(dx, dw1, dw2, dpre, post)."""
+def act_backward(dout, x, w1, w2, down_mult=1.0, act="relu_sq"):
+    """Non-gated MLP backward (quack ``MLPRecomputeFunc.backward`` with the non-gated ops):
+    dpre = (down_mult * dout W2) * f'(pre); dW2 = down_mult * dout^T post; dx = dpre W1;
+    dW1 = dpre^T x. Returns dict(dx, dw1, dw2, dpre, post)."""
     dout, x, w1, w2 = map(_f64, (dout, x, w1, w2))
+    f, df = _plain_fn(act)
     pre = x @ w1.T
-    post = relu_sq(pre)
+    post = f(pre)
     dpost = down_mult * (dout @ w2)
-    dpre = dpost * drelu_sq(pre)
+    dpre = dpost * df(pre)
     return {
         "dw2": down_mult * (dout.T @ post),
         "dx": dpre @ w1,
@@ -184,23 +254,39 @@ def relu_sq_backward(dout, x, w1, w2, down_mult=1.0):
     }
 
 
-def relu_sq_sampled(dout, x, w1, w2, rows, units, down_mult=1.0):
-    """``relu_sq_forward``/``relu_sq_backward`` evaluated on a sample: out[rows], dx[rows],
+def act_sampled(dout, x, w1, w2, rows, units, down_mult=1.0, act="relu_sq"):
+    """``act_forward``/``act_backward`` evaluated on a sample: out[rows], dx[rows],
     dw2[:, units], dw1[units, :] (sums restricted to the entries each sampled output needs)."""
     dout, x, w1, w2 = map(_f64, (dout, x, w1, w2))
+    f, df = _plain_fn(act)
     rows = np.asarray(rows)
     units = np.asarray(units)
     pre = x[rows] @ w1.T
-    out_rows = down_mult * (relu_sq(pre) @ w2.T)
-    dpre = down_mult * (dout[rows] @ w2) * drelu_sq(pre)
+    out_rows = down_mult * (f(pre) @ w2.T)
+    dpre = down_mult * (dout[rows] @ w2) * df(pre)
     dx_rows = dpre @ w1
     prec = x @ w1[units].T
-    dprec = down_mult * (dout @ w2[:, units]) * drelu_sq(prec)
+    dprec = down_mult * (dout @ w2[:, units]) * df(prec)
     return {
         "out_rows": out_rows, "dx_rows": dx_rows,
-        "dw2_cols": down_mult * (dout.T @ relu_sq(prec)),
+        "dw2_cols": down_mult * (dout.T @ f(prec)),
         "dw1_rows": dprec.T @ x,
     }
+
+
+def relu_sq_forward(x, w1, w2, down_mult=1.0):
+    """``act_forward`` with f = relu^2."""
+    return act_forward(x, w1, w2, down_mult, "relu_sq")
+
+
+def relu_sq_backward(dout, x, w1, w2, down_mult=1.0):
+    """``act_backward`` with f = relu^2."""
+    return act_backward(dout, x, w1, w2, down_mult, "relu_sq")
+
+
+def relu_sq_sampled(dout, x, w1, w2, rows, units, down_mult=1.0):
+    """``act_sampled`` with f = relu^2."""
+    return act_sampled(dout, x, w1, w2, rows, units, down_mult, "relu_sq")
 
 
 def accumulate(buf_before, grad):

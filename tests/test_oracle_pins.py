@@ -243,3 +243,162 @@ def test_sampled_equals_full(mode):
 def test_accumulate():
     buf = np.array([1.0, -2.0], dtype=np.float32)
     np.testing.assert_array_equal(oracle.accumulate(buf, np.array([0.5, 0.25])), [1.5, -1.75])
+
+
+# ---- the other activations of quack's ``Activation`` set (standard definitions) -------------
+
+GATED_OTHER = ["geglu", "reglu", "glu"]
+PLAIN_OTHER = ["relu", "gelu_tanh"]
+
+
+def _torch_gate_fn(act):
+    return {"swiglu": F.silu, "geglu": lambda z: F.gelu(z, approximate="tanh"), "reglu": torch.relu,
+            "glu": torch.sigmoid}[act]
+
+
+def _torch_plain_fn(act):
+    return {"relu_sq": lambda z: torch.relu(z) ** 2, "relu": torch.relu,
+            "gelu_tanh": lambda z: F.gelu(z, approximate="tanh")}[act]
+
+
+def test_gelu_tanh_is_the_library_tanh_gelu_and_close_to_erf_gelu():
+    z = np.linspace(-8.0, 8.0, 4001)
+    ref = F.gelu(torch.tensor(z), approximate="tanh").numpy()
+    np.testing.assert_allclose(oracle.gelu_tanh(z), ref, rtol=1e-14, atol=1e-15)
+    exact = F.gelu(torch.tensor(z)).numpy()                       # z * Phi(z), erf form
+    dev = np.abs(oracle.gelu_tanh(z) - exact).max()
+    assert 1e-5 < dev < 1e-3                                      # an approximation, a close one
+    assert oracle.gelu_tanh(np.array([0.0]))[0] == 0.0
+    assert oracle.dgelu_tanh(np.array([0.0]))[0] == 0.5
+    # far tails: gelu(z) -> z for z >> 0, -> 0 for z << 0
+    assert abs(oracle.gelu_tanh(np.array([12.0]))[0] - 12.0) < 1e-12
+    assert abs(oracle.gelu_tanh(np.array([-12.0]))[0]) < 1e-12
+
+
+@pytest.mark.parametrize("name", ["gelu_tanh", "sigmoid", "relu"])
+def test_scalar_derivatives_match_finite_differences(name):
+    f, df = {"gelu_tanh": (oracle.gelu_tanh, oracle.dgelu_tanh), "sigmoid": (oracle.sigmoid, oracle.dsigmoid),
+             "relu": (oracle.relu, oracle.drelu)}[name]
+    z = np.concatenate([np.linspace(-6.0, -0.01, 300), np.linspace(0.01, 6.0, 300)])   # off relu's kink
+    h = 1e-6
+    fd = (f(z + h) - f(z - h)) / (2 * h)
+    np.testing.assert_allclose(df(z), fd, rtol=1e-7, atol=1e-8)
+
+
+def test_relu_family_closed_forms():
+    z = np.array([-2.0, -0.0, 0.0, 1e-300, 3.5])
+    np.testing.assert_array_equal(oracle.relu(z), [0.0, 0.0, 0.0, 1e-300, 3.5])
+    np.testing.assert_array_equal(oracle.drelu(z), [0.0, 0.0, 0.0, 1.0, 1.0])
+    assert oracle.dsigmoid(np.array([0.0]))[0] == 0.25
+
+
+@pytest.mark.parametrize("act", GATED_OTHER)
+@pytest.mark.parametrize("mode", ["outside", "inside"])
+@pytest.mark.parametrize("gm,dm", [(1.0, 1.0), (1.125, 2.0)])
+def test_other_gated_match_torch_float64_autograd(act, mode, gm, dm):
+    rng = np.random.default_rng(zlib.crc32(repr((act, mode, gm, dm)).encode()))
+    M, d, H, do = 11, 16, 24, 8
+    x, wg, wu, wd, dout = (_rand(M, d, rng=rng), _rand(H, d, scale=0.3, rng=rng), _rand(H, d, scale=0.3, rng=rng),
+                           _rand(do, H, scale=0.2, rng=rng), _rand(M, do, rng=rng))
+    t = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (x, wg, wu, wd)]
+    fn = _torch_gate_fn(act)
+    g, u = F.linear(t[0], t[1]), F.linear(t[0], t[2])
+    a = gm * fn(g) * u if mode == "outside" else fn(gm * g) * u
+    out = dm * F.linear(a, t[3])
+    out.backward(torch.tensor(dout))
+    f = oracle.gated_forward(x, wg, wu, wd, gm, dm, mode, act)
+    b = oracle.gated_backward(dout, x, wg, wu, wd, gm, dm, mode, act)
+    for ours, ref in [(f["out"], out.detach().numpy()), (b["dx"], t[0].grad.numpy()),
+                      (b["dw_gate"], t[1].grad.numpy()), (b["dw_up"], t[2].grad.numpy()),
+                      (b["dw_down"], t[3].grad.numpy())]:
+        np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("act", PLAIN_OTHER)
+@pytest.mark.parametrize("dm", [1.0, 2.0])
+def test_other_plain_match_torch_float64_autograd(act, dm):
+    rng = np.random.default_rng(zlib.crc32(repr((act, dm)).encode()))
+    M, d, H, do = 13, 16, 48, 24
+    x, w1, w2, dout = _rand(M, d, rng=rng), _rand(H, d, scale=0.3, rng=rng), _rand(do, H, scale=0.2, rng=rng), _rand(M, do, rng=rng)
+    t = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (x, w1, w2)]
+    out = dm * F.linear(_torch_plain_fn(act)(F.linear(t[0], t[1])), t[2])
+    out.backward(torch.tensor(dout))
+    f = oracle.act_forward(x, w1, w2, dm, act)
+    b = oracle.act_backward(dout, x, w1, w2, dm, act)
+    for ours, ref in [(f["out"], out.detach().numpy()), (b["dx"], t[0].grad.numpy()),
+                      (b["dw1"], t[1].grad.numpy()), (b["dw2"], t[2].grad.numpy())]:
+        np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("act", GATED_OTHER)
+@pytest.mark.parametrize("mode", ["outside", "inside"])
+def test_other_gated_backward_matches_finite_differences(act, mode):
+    M, d, H, do = 3, 4, 5, 4
+    rng = np.random.default_rng(zlib.crc32(repr(("fd", act, mode)).encode()))
+    x, wg, wu = _rand(M, d, rng=rng), _rand(H, d, rng=rng), _rand(H, d, rng=rng)
+    wd, dout = _rand(do, H, rng=rng), _rand(M, do, rng=rng)
+    gm, dm = 1.125, 2.0
+    if act == "reglu":
+        z = (x @ wg.T) * (gm if mode == "inside" else 1.0)
+        assert np.min(np.abs(z)) > 1e-3   # keep relu's kink out of the stencil
+    g = oracle.gated_backward(dout, x, wg, wu, wd, gm, dm, mode, act)
+    loss = lambda: float(np.sum(dout * oracle.gated_forward(x, wg, wu, wd, gm, dm, mode, act)["out"]))  # noqa: E731
+    for name, arr in [("dx", x), ("dw_gate", wg), ("dw_up", wu), ("dw_down", wd)]:
+        np.testing.assert_allclose(g[name], _fd_grad(loss, arr), rtol=1e-6, atol=1e-7, err_msg=name)
+
+
+@pytest.mark.parametrize("act", PLAIN_OTHER)
+def test_other_plain_backward_matches_finite_differences(act):
+    M, d, H, do = 3, 4, 6, 3
+    rng = np.random.default_rng(zlib.crc32(repr(("fd", act)).encode()))
+    x, w1, w2, dout = _rand(M, d, rng=rng), _rand(H, d, rng=rng), _rand(do, H, rng=rng), _rand(M, do, rng=rng)
+    assert np.min(np.abs(x @ w1.T)) > 1e-3
+    b = oracle.act_backward(dout, x, w1, w2, 2.0, act)
+    loss = lambda: float(np.sum(dout * oracle.act_forward(x, w1, w2, 2.0, act)["out"]))  # noqa: E731
+    for name, arr in [("dx", x), ("dw1", w1), ("dw2", w2)]:
+        np.testing.assert_allclose(b[name], _fd_grad(loss, arr), rtol=1e-6, atol=1e-7, err_msg=name)
+
+
+def test_glu_and_reglu_special_cases():
+    """glu with a zero gate halves the up projection; reglu with a negative gate gives zeros."""
+    rng = np.random.default_rng(3)
+    x, wu, wd = _rand(4, 6, rng=rng), _rand(5, 6, rng=rng), _rand(3, 5, rng=rng)
+    zero = np.zeros((5, 6))
+    f = oracle.gated_forward(x, zero, wu, wd, act="glu")
+    np.testing.assert_allclose(f["a"], 0.5 * (x @ wu.T), rtol=0, atol=0)
+    neg = -np.abs(_rand(5, 6, rng=rng))
+    xp = np.abs(x)
+    f = oracle.gated_forward(xp, neg, wu, wd, act="reglu")
+    assert np.all(f["a"] == 0.0) and np.all(f["out"] == 0.0)
+
+
+@pytest.mark.parametrize("act", GATED_OTHER)
+def test_other_gated_sampled_equals_full(act):
+    rng = np.random.default_rng(11)
+    M, d, H, do = 9, 8, 12, 6
+    x, wg, wu, wd, dout = (_rand(M, d, rng=rng), _rand(H, d, rng=rng), _rand(H, d, rng=rng), _rand(do, H, rng=rng),
+                           _rand(M, do, rng=rng))
+    rows, units = np.array([0, 4, 8]), np.array([1, 7, 11])
+    f = oracle.gated_forward(x, wg, wu, wd, 1.125, 2.0, "inside", act)
+    b = oracle.gated_backward(dout, x, wg, wu, wd, 1.125, 2.0, "inside", act)
+    s = oracle.gated_sampled(dout, x, wg, wu, wd, rows, units, 1.125, 2.0, "inside", act)
+    np.testing.assert_allclose(s["out_rows"], f["out"][rows], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(s["dx_rows"], b["dx"][rows], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(s["dw_down_cols"], b["dw_down"][:, units], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(s["dw_gate_rows"], b["dw_gate"][units], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(s["dw_up_rows"], b["dw_up"][units], rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("act", PLAIN_OTHER)
+def test_other_plain_sampled_equals_full(act):
+    rng = np.random.default_rng(12)
+    M, d, H, do = 9, 8, 12, 6
+    x, w1, w2, dout = _rand(M, d, rng=rng), _rand(H, d, rng=rng), _rand(do, H, rng=rng), _rand(M, do, rng=rng)
+    rows, units = np.array([1, 5]), np.array([0, 6, 11])
+    f = oracle.act_forward(x, w1, w2, 2.0, act)
+    b = oracle.act_backward(dout, x, w1, w2, 2.0, act)
+    s = oracle.act_sampled(dout, x, w1, w2, rows, units, 2.0, act)
+    np.testing.assert_allclose(s["out_rows"], f["out"][rows], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(s["dx_rows"], b["dx"][rows], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(s["dw2_cols"], b["dw2"][:, units], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(s["dw1_rows"], b["dw1"][units], rtol=1e-13, atol=1e-13)
