@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm_args.hpp"
+
 namespace gmlp {
 
 typedef __bf16 bf16;
@@ -72,6 +74,107 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
 
 __device__ __forceinline__ float sigmoidf_(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+// tanh(y) = 1 - 2 / (e^(2y) + 1); saturates to +-1 when e^(2y) over- or underflows
+__device__ __forceinline__ float tanhf_(float y) {
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __expf(2.0f * y));
+}
+
+// The activation functions of the fused epilogues: ActFn (gemm_args.hpp).
+constexpr float kGeluC = 0.7978845608028654f;   // sqrt(2 / pi)
+constexpr float kGeluK = 0.044715f;
+
+// f(z[r]) for N values; the switch on the (uniform) function sits outside the element loop.
+template <int N>
+__device__ __forceinline__ void act_fn(int fn, const float (&z)[N], float (&f)[N]) {
+  switch (fn) {
+    case FN_SILU:
+#pragma unroll
+      for (int r = 0; r < N; ++r) f[r] = z[r] * sigmoidf_(z[r]);
+      break;
+    case FN_GELU_TANH:   // the same expression as in act_fn_grad, so both give identical bits
+#pragma unroll
+      for (int r = 0; r < N; ++r) {
+        const float z2 = z[r] * z[r];
+        f[r] = 0.5f * z[r] * (1.0f + tanhf_(kGeluC * (z[r] + kGeluK * z2 * z[r])));
+      }
+      break;
+    case FN_RELU:
+#pragma unroll
+      for (int r = 0; r < N; ++r) f[r] = fmaxf(z[r], 0.0f);
+      break;
+    case FN_SIGMOID:
+#pragma unroll
+      for (int r = 0; r < N; ++r) f[r] = sigmoidf_(z[r]);
+      break;
+    default:   // FN_RELU_SQ
+#pragma unroll
+      for (int r = 0; r < N; ++r) { const float t = fmaxf(z[r], 0.0f); f[r] = t * t; }
+  }
+}
+
+// f(z[r]) and f'(z[r]).
+template <int N>
+__device__ __forceinline__ void act_fn_grad(int fn, const float (&z)[N], float (&f)[N], float (&df)[N]) {
+  switch (fn) {
+    case FN_SILU:
+#pragma unroll
+      for (int r = 0; r < N; ++r) {
+        const float s = sigmoidf_(z[r]);
+        f[r] = z[r] * s;
+        df[r] = s * (1.0f + z[r] * (1.0f - s));
+      }
+      break;
+    case FN_GELU_TANH:
+#pragma unroll
+      for (int r = 0; r < N; ++r) {
+        const float z2 = z[r] * z[r];
+        const float t = tanhf_(kGeluC * (z[r] + kGeluK * z2 * z[r]));
+        f[r] = 0.5f * z[r] * (1.0f + t);
+        df[r] = 0.5f * (1.0f + t) + 0.5f * z[r] * (1.0f - t * t) * kGeluC * (1.0f + 3.0f * kGeluK * z2);
+      }
+      break;
+    case FN_RELU:
+#pragma unroll
+      for (int r = 0; r < N; ++r) { f[r] = fmaxf(z[r], 0.0f); df[r] = z[r] > 0.0f ? 1.0f : 0.0f; }
+      break;
+    case FN_SIGMOID:
+#pragma unroll
+      for (int r = 0; r < N; ++r) { const float s = sigmoidf_(z[r]); f[r] = s; df[r] = s * (1.0f - s); }
+      break;
+    default:   // FN_RELU_SQ
+#pragma unroll
+      for (int r = 0; r < N; ++r) { const float t = fmaxf(z[r], 0.0f); f[r] = t * t; df[r] = 2.0f * t; }
+  }
+}
+
+// Gated activation of N values: a = gm * f(g) * u (gate multiplier outside) or f(gm * g) * u.
+template <int N>
+__device__ __forceinline__ void gated_act(int fn, float gm, int inside, const float (&g)[N], const float (&u)[N],
+                                          float (&a)[N]) {
+  float z[N], f[N];
+#pragma unroll
+  for (int r = 0; r < N; ++r) z[r] = inside ? gm * g[r] : g[r];
+  act_fn<N>(fn, z, f);
+#pragma unroll
+  for (int r = 0; r < N; ++r) a[r] = (inside ? f[r] : gm * f[r]) * u[r];
+}
+
+// Its backward against da: dg, du, and the post-activation a re-emitted.
+template <int N>
+__device__ __forceinline__ void gated_act_grad(int fn, float gm, int inside, const float (&da)[N], const float (&g)[N],
+                                               const float (&u)[N], float (&dg)[N], float (&du)[N], float (&a)[N]) {
+  float z[N], f[N], df[N];
+#pragma unroll
+  for (int r = 0; r < N; ++r) z[r] = inside ? gm * g[r] : g[r];
+  act_fn_grad<N>(fn, z, f, df);
+#pragma unroll
+  for (int r = 0; r < N; ++r) {
+    dg[r] = da[r] * gm * u[r] * df[r];
+    du[r] = inside ? da[r] * f[r] : da[r] * gm * f[r];
+    a[r] = (inside ? f[r] : gm * f[r]) * u[r];
+  }
 }
 
 // ---- LDS tile geometry -------------------------------------------------------------------

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kEwThreads) void splitk_reduce_kernel(
 
 template <typename T>
 __global__ __launch_bounds__(kEwThreads) void gated_act_kernel(const void* preact, void* a_out, int M,
-                                                               int H, float gm, int inside) {
+                                                               int H, float gm, int inside, int fn) {
   const int h4 = H / 4;
   const int64_t total = (int64_t)M * h4;
   for (int64_t i = blockIdx.x * (int64_t)kEwThreads + threadIdx.x; i < total;
@@ -81,23 +81,15 @@ __global__ __launch_bounds__(kEwThreads) void gated_act_kernel(const void* preac
     float g[4], u[4], a[4];
     load4<T>(row + (int64_t)n * esize<T>(), g);
     load4<T>(row + (int64_t)(H + n) * esize<T>(), u);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (inside) {
-        const float z = gm * g[r];
-        a[r] = z * sigmoidf_(z) * u[r];
-      } else {
-        a[r] = gm * (g[r] * sigmoidf_(g[r])) * u[r];
-      }
-    }
+    gated_act<4>(fn, gm, inside, g, u, a);
     store4<T>(reinterpret_cast<char*>(a_out) + ((int64_t)m * H + n) * esize<T>(), a);
   }
 }
 
 template <typename T>
-__global__ __launch_bounds__(kEwThreads) void relu_sq_kernel(const void* pre, void* post, int64_t n,
-                                                             float alpha, const float* dev0,
-                                                             const float* dev1) {
+__global__ __launch_bounds__(kEwThreads) void plain_act_kernel(const void* pre, void* post, int64_t n,
+                                                               float alpha, const float* dev0,
+                                                               const float* dev1, int fn) {
   float a = alpha;
   if (dev0) a *= *dev0;
   if (dev1) a *= *dev1;
@@ -106,9 +98,11 @@ __global__ __launch_bounds__(kEwThreads) void relu_sq_kernel(const void* pre, vo
        i += (int64_t)gridDim.x * kEwThreads) {
     float v[4];
     load4<T>(reinterpret_cast<const char*>(pre) + i * 4 * esize<T>(), v);
+    float z[4], f[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) { const float t = fmaxf(a * v[r], 0.0f); v[r] = t * t; }
-    store4<T>(reinterpret_cast<char*>(post) + i * 4 * esize<T>(), v);
+    for (int r = 0; r < 4; ++r) z[r] = a * v[r];
+    act_fn<4>(fn, z, f);
+    store4<T>(reinterpret_cast<char*>(post) + i * 4 * esize<T>(), f);
   }
 }
 
@@ -175,22 +169,24 @@ hipError_t run_splitk_reduce(DType io, const float* partial, int splits, int M, 
 }
 
 hipError_t run_gated_act(DType io, const void* preact, void* a, int M, int H, float gate_mult,
-                         int gate_inside, hipStream_t s) {
+                         int gate_inside, int fn, hipStream_t s) {
   const int grid = ew_grid((int64_t)M * (H / 4));
   if (io == DT_BF16)
-    hipLaunchKernelGGL(gated_act_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, preact, a, M, H, gate_mult, gate_inside);
+    hipLaunchKernelGGL(gated_act_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, preact, a, M, H, gate_mult,
+                       gate_inside, fn);
   else
-    hipLaunchKernelGGL(gated_act_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, preact, a, M, H, gate_mult, gate_inside);
+    hipLaunchKernelGGL(gated_act_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, preact, a, M, H, gate_mult,
+                       gate_inside, fn);
   return hipGetLastError();
 }
 
-hipError_t run_relu_sq_act(DType io, const void* pre, void* post, int64_t n, float alpha,
-                           const float* dev0, const float* dev1, hipStream_t s) {
+hipError_t run_plain_act(DType io, const void* pre, void* post, int64_t n, float alpha,
+                         const float* dev0, const float* dev1, int fn, hipStream_t s) {
   const int grid = ew_grid(n / 4);
   if (io == DT_BF16)
-    hipLaunchKernelGGL(relu_sq_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, pre, post, n, alpha, dev0, dev1);
+    hipLaunchKernelGGL(plain_act_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, pre, post, n, alpha, dev0, dev1, fn);
   else
-    hipLaunchKernelGGL(relu_sq_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, pre, post, n, alpha, dev0, dev1);
+    hipLaunchKernelGGL(plain_act_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, pre, post, n, alpha, dev0, dev1, fn);
   return hipGetLastError();
 }
 

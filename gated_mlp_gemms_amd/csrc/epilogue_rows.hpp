@@ -73,8 +73,8 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4 x, float v[8]) {
 // raw accumulator for split-K partials); u = the up-projection values for the gated epilogue;
 // x = what epi_prefetch fetched for this piece.
 template <int EPI, typename IoT>
-__device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int split, const float v[8],
-                                         const float u[8], const AuxPiece& x, float& local_amax) {
+__device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int split, const float (&v)[8],
+                                         const float (&u)[8], const AuxPiece& x, float& local_amax) {
   if constexpr (EPI == EPI_STORE) {
     const bool lo = m < p.c_split;
     void* base = lo ? p.C0 : p.C1;
@@ -101,23 +101,14 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
     }
     if (p.flags & 2) {
       float a[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        if (p.gate_inside) {
-          const float z = p.gate_mult * v[r];
-          a[r] = z * sigmoidf_(z) * u[r];
-        } else {
-          a[r] = p.gate_mult * (v[r] * sigmoidf_(v[r])) * u[r];
-        }
-      }
+      gated_act<8>(p.act, p.gate_mult, p.gate_inside, v, u, a);
       Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), a);
     }
   } else if constexpr (EPI == EPI_ACT) {
     if (p.flags & 1) Vec8<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), v);
     if (p.flags & 2) {
       float q[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) { const float t = fmaxf(v[r], 0.0f); q[r] = t * t; }
+      act_fn<8>(p.act, v, q);
       Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), q);
     }
   } else if constexpr (EPI == EPI_DGATED) {
@@ -125,23 +116,7 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
     float gg[8], uu[8], dg[8], du[8], a[8];
     unpack_bf16x8(x.a, gg);
     unpack_bf16x8(x.b, uu);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float gm = p.gate_mult;
-      const float z = p.gate_inside ? gm * gg[r] : gg[r];
-      const float sg = sigmoidf_(z);
-      const float silu = z * sg;
-      const float dsilu = sg * (1.0f + z * (1.0f - sg));
-      if (p.gate_inside) {
-        dg[r] = v[r] * uu[r] * gm * dsilu;
-        du[r] = v[r] * silu;
-        a[r] = silu * uu[r];
-      } else {
-        dg[r] = v[r] * gm * uu[r] * dsilu;
-        du[r] = v[r] * gm * silu;
-        a[r] = gm * silu * uu[r];
-      }
-    }
+    gated_act_grad<8>(p.act, p.gate_mult, p.gate_inside, v, gg, uu, dg, du, a);
     Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), dg);
     Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, p.half + n), du);
     if (p.flags & 2) Vec8<IoT>::store(elem_ptr<IoT>(p.C1, m, p.ldc1, n), a);
@@ -149,12 +124,9 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
     static_assert(std::is_same<IoT, bf16>::value, "row-staged d-activation epilogues read bf16");
     float pre[8], dpre[8], post[8];
     unpack_bf16x8(x.a, pre);
+    act_fn_grad<8>(p.act, pre, post, dpre);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float t = fmaxf(pre[r], 0.0f);
-      dpre[r] = v[r] * 2.0f * t;
-      post[r] = t * t;
-    }
+    for (int r = 0; r < 8; ++r) dpre[r] *= v[r];
     Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), dpre);
     if (p.flags & 2) Vec8<IoT>::store(elem_ptr<IoT>(p.C1, m, p.ldc1, n), post);
   } else if constexpr (EPI == EPI_F8ACT) {

@@ -5,15 +5,20 @@
 
 namespace gmlp {
 
+// The activation functions of the fused epilogues (GemmArgs::act): the gate function f of a
+// gated activation a = f(g) * u (SwiGLU: silu, GeGLU: gelu_tanh, ReGLU: relu, GLU: sigmoid), or
+// the f of a non-gated post = f(pre) (relu^2, relu, gelu_tanh).
+enum ActFn : int { FN_SILU = 0, FN_GELU_TANH = 1, FN_RELU = 2, FN_SIGMOID = 3, FN_RELU_SQ = 4 };
+
 enum Epi : int {
   EPI_STORE = 0,    // C = alpha * acc (OutT); accumulate: C(f32) += alpha * acc; rows >= c_split go to C1
   EPI_PARTIAL = 1,  // split-K: partial[split][m][n] = acc (fp32); a reduce kernel finishes
   EPI_GATED = 2,    // g, u = alpha * acc pair; aux[m][n], aux[m][half+n] = g, u (flag 1);
-                    // C0[m][n] = a = act(g, u) (flag 2)
-  EPI_ACT = 3,      // pre = alpha * acc -> aux (flag 1); post = relu(pre)^2 -> C0 (flag 2)
+                    // C0[m][n] = a = act(g, u) (flag 2), act per GemmArgs::act
+  EPI_ACT = 3,      // pre = alpha * acc -> aux (flag 1); post = f(pre) -> C0 (flag 2)
   EPI_DGATED = 4,   // da = alpha * acc; g, u <- aux; dg, du -> C0[m][n], C0[m][half+n];
                     // a -> C1 (flag 2). C0 may equal aux.
-  EPI_DACT = 5,     // dpost = alpha * acc; pre <- aux; dpre -> C0; post -> C1 (flag 2)
+  EPI_DACT = 5,     // dpost = alpha * acc; pre <- aux; dpre = dpost * f'(pre) -> C0; post -> C1 (flag 2)
   EPI_F8ACT = 6,    // pre = alpha * acc -> aux (bf16, flag 1); post = relu(pre)^2;
                     // C0 = e4m3(post / *s_post); *amax = max(*amax, max post)
 };
@@ -26,6 +31,7 @@ struct GemmArgs {
   void* aux; int64_t ld_aux; int half;
   float alpha; const float* alpha_dev0; const float* alpha_dev1;
   float gate_mult; int gate_inside;
+  int act;          // ActFn of the GATED / DGATED / ACT / DACT epilogues (F8ACT is relu^2)
   int accumulate;
   int flags;
   const float* s_post; float* amax;

@@ -267,58 +267,30 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, f32x16 (&acc)[MI][NI
           }
           if (p.flags & 2) {
             float a[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (p.gate_inside) {
-                const float z = p.gate_mult * v[r];
-                a[r] = z * sigmoidf_(z) * u[r];
-              } else {
-                a[r] = p.gate_mult * (v[r] * sigmoidf_(v[r])) * u[r];
-              }
-            }
+            gated_act<4>(p.act, p.gate_mult, p.gate_inside, v, u, a);
             Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), a);
           }
         } else if constexpr (EPI == EPI_ACT) {
           if (p.flags & 1) Vec4<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), v);
           if (p.flags & 2) {
             float q[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) { const float t = fmaxf(v[r], 0.0f); q[r] = t * t; }
+            act_fn<4>(p.act, v, q);
             Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), q);
           }
         } else if constexpr (EPI == EPI_DGATED) {
           float gg[4], uu[4], dg[4], du[4], a[4];
           Vec4<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), gg);
           Vec4<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, p.half + n), uu);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float gm = p.gate_mult;
-            const float z = p.gate_inside ? gm * gg[r] : gg[r];
-            const float sg = sigmoidf_(z);
-            const float silu = z * sg;
-            const float dsilu = sg * (1.0f + z * (1.0f - sg));
-            if (p.gate_inside) {
-              dg[r] = v[r] * uu[r] * gm * dsilu;
-              du[r] = v[r] * silu;
-              a[r] = silu * uu[r];
-            } else {
-              dg[r] = v[r] * gm * uu[r] * dsilu;
-              du[r] = v[r] * gm * silu;
-              a[r] = gm * silu * uu[r];
-            }
-          }
+          gated_act_grad<4>(p.act, p.gate_mult, p.gate_inside, v, gg, uu, dg, du, a);
           Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), dg);
           Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, p.half + n), du);
           if (p.flags & 2) Vec4<IoT>::store(elem_ptr<IoT>(p.C1, m, p.ldc1, n), a);
         } else if constexpr (EPI == EPI_DACT) {
           float pre[4], dpre[4], post[4];
           Vec4<IoT>::load(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), pre);
+          act_fn_grad<4>(p.act, pre, post, dpre);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float t = fmaxf(pre[r], 0.0f);
-            dpre[r] = v[r] * 2.0f * t;
-            post[r] = t * t;
-          }
+          for (int r = 0; r < 4; ++r) dpre[r] *= v[r];
           Vec4<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), dpre);
           if (p.flags & 2) Vec4<IoT>::store(elem_ptr<IoT>(p.C1, m, p.ldc1, n), post);
         } else if constexpr (EPI == EPI_F8ACT) {

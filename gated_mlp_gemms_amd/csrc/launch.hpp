@@ -32,11 +32,11 @@ hipError_t run_splitk_reduce(DType io, const float* partial, int splits, int M, 
                              void* C1, int64_t ldc, int c_split, float alpha, const float* dev0,
                              const float* dev1, int accumulate, hipStream_t s);
 
-// a[m][n] = act(g = pre[m][n], u = pre[m][H + n]) (gated) or relu(pre)^2.
+// a[m][n] = act(g = pre[m][n], u = pre[m][H + n]) (gated), or post = f(alpha * pre); fn: ActFn.
 hipError_t run_gated_act(DType io, const void* preact, void* a, int M, int H, float gate_mult,
-                         int gate_inside, hipStream_t s);
-hipError_t run_relu_sq_act(DType io, const void* pre, void* post, int64_t n, float alpha,
-                           const float* dev0, const float* dev1, hipStream_t s);
+                         int gate_inside, int fn, hipStream_t s);
+hipError_t run_plain_act(DType io, const void* pre, void* post, int64_t n, float alpha,
+                         const float* dev0, const float* dev1, int fn, hipStream_t s);
 
 // Per-tensor e4m3 quantization: amax (into ws[0]), then scale and codes.
 hipError_t run_quantize_e4m3(DType src_t, const void* src, int64_t n, void* dst, float* scale,

@@ -62,6 +62,21 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int esize(int dtype) { return dtype == MLP_BF16 ? 2 : 4; }
+
+bool is_gated(int act) {
+  return act == MLP_ACT_SWIGLU || act == MLP_ACT_GEGLU || act == MLP_ACT_REGLU || act == MLP_ACT_GLU;
+}
+
+// The epilogues' function of an mlp_act: the gate function of a gated one, else f itself.
+int act_fn_of(int act) {
+  switch (act) {
+    case MLP_ACT_SWIGLU: return FN_SILU;
+    case MLP_ACT_GEGLU: case MLP_ACT_GELU_TANH: return FN_GELU_TANH;
+    case MLP_ACT_REGLU: case MLP_ACT_RELU: return FN_RELU;
+    case MLP_ACT_GLU: return FN_SIGMOID;
+    default: return FN_RELU_SQ;
+  }
+}
 DType io_of(const mlp_desc* d) { return d->dtype == MLP_BF16 ? DT_BF16 : DT_F32; }
 
 // ---- GEMM planning -------------------------------------------------------------------------
@@ -148,7 +163,7 @@ struct Gemms {   // the GEMMs a phase may run, in planning form
 Gemms plan_all(const mlp_desc* d) {
   const DType io = io_of(d);
   const DType fin = d->fp8_fwd ? DT_E4M3 : io;
-  const bool gated = d->act == MLP_ACT_SWIGLU;
+  const bool gated = is_gated(d->act);
   const int64_t M = d->M, D = d->d_in, H = d->hidden, O = d->d_out, P = gated ? 2 * H : H;
   Gemms g;
   g.down = plan_gemm(fin, M, O, H, true, false);
@@ -160,7 +175,7 @@ Gemms plan_all(const mlp_desc* d) {
 
 WsLayout ws_layout(const mlp_desc* d, int phase) {
   WsLayout L;
-  const bool gated = d->act == MLP_ACT_SWIGLU;
+  const bool gated = is_gated(d->act);
   const int64_t M = d->M, D = d->d_in, H = d->hidden, O = d->d_out, P = gated ? 2 * H : H;
   const size_t es = esize(d->dtype);
   const Gemms g = plan_all(d);
@@ -196,7 +211,7 @@ mlp_status check_desc(const mlp_desc* d) {
   const int64_t lim = (int64_t)1 << 30;
   if (d->M >= lim || d->d_in >= lim || d->hidden >= lim / 2 || d->d_out >= lim)
     return fail(MLP_ERR_UNSUPPORTED, "a size is beyond 2^30 (2^29 for hidden)");
-  if (d->act != MLP_ACT_SWIGLU && d->act != MLP_ACT_RELU_SQ)
+  if (d->act < MLP_ACT_SWIGLU || d->act > MLP_ACT_RELU)
     return fail(MLP_ERR_INVALID_ARG, "act %d is not an mlp_act", d->act);
   if (d->dtype != MLP_F32 && d->dtype != MLP_BF16)
     return fail(MLP_ERR_INVALID_ARG, "dtype %d is not an mlp_dtype", d->dtype);
@@ -289,12 +304,13 @@ GemmArgs base_args(const mlp_desc* d) {
   a.alpha = 1.0f;
   a.gate_mult = d->gate_mult;
   a.gate_inside = d->gate_mode == MLP_GATE_INSIDE;
+  a.act = act_fn_of(d->act);
   a.b_split = 1 << 30;
   a.c_split = 1 << 30;
   return a;
 }
 
-// Forward GEMM 1: the gated / ReLU^2 / e4m3 ReLU^2 up projection with its activation epilogue.
+// Forward GEMM 1: the gated / non-gated / e4m3 ReLU^2 up projection with its activation epilogue.
 // preact_out: where g|u or pre goes (NULL: not kept); act_out: where a / post / post_q goes.
 mlp_status up_projection(const mlp_desc* d, const void* x, const void* wg, const void* wu,
                          const mlp_fp8* f, void* preact_out, void* act_out, hipStream_t s) {
@@ -307,7 +323,7 @@ mlp_status up_projection(const mlp_desc* d, const void* x, const void* wg, const
   a.ldc0 = H;
   a.aux = preact_out;
   a.flags = (preact_out ? 1 : 0) | (act_out ? 2 : 0);
-  if (d->act == MLP_ACT_SWIGLU) {
+  if (is_gated(d->act)) {
     a.A = x;
     a.B0 = wg;
     a.B1 = wu;
@@ -337,14 +353,14 @@ mlp_status fwd_impl(const mlp_desc* d, const void* x, const void* wg, const void
                     void* out, void* saved, const mlp_fp8* f, void* ws, size_t ws_bytes, void* stream,
                     bool infer) {
   MLP_TRY(check_desc(d));
-  const bool gated = d->act == MLP_ACT_SWIGLU;
+  const bool gated = is_gated(d->act);
   if (!d->fp8_fwd) {
     MLP_TRY(need_ptr(x, "x"));
     MLP_TRY(need_ptr(wg, gated ? "w_gate" : "w_gate (W1)"));
     MLP_TRY(need_ptr(wd, gated ? "w_down" : "w_down (W2)"));
   }
   if (gated) MLP_TRY(need_ptr(wu, "w_up"));
-  else MLP_TRY(need_null(wu, "w_up", "for ReLU^2"));
+  else MLP_TRY(need_null(wu, "w_up", "for a non-gated activation"));
   MLP_TRY(need_ptr(out, "out"));
   if (!infer) {
     if (d->recompute) MLP_TRY(need_null(saved, "saved_preact", "with recompute"));
@@ -428,7 +444,7 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
                    void* dwd, int grad_accum, const mlp_fp8* f, void* ws, size_t ws_bytes,
                    void* stream) {
   MLP_TRY(check_desc(d));
-  const bool gated = d->act == MLP_ACT_SWIGLU;
+  const bool gated = is_gated(d->act);
   MLP_TRY(need_ptr(dout, "dout"));
   if (!d->fp8_fwd) {
     MLP_TRY(need_ptr(x, "x"));
@@ -436,7 +452,7 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
     MLP_TRY(need_ptr(wd, gated ? "w_down" : "w_down (W2)"));
   }
   if (gated) MLP_TRY(need_ptr(wu, "w_up"));
-  else MLP_TRY(need_null(wu, "w_up", "for ReLU^2"));
+  else MLP_TRY(need_null(wu, "w_up", "for a non-gated activation"));
   if (d->recompute) MLP_TRY(need_null(saved, "saved_preact", "with recompute"));
   else MLP_TRY(need_ptr(saved, "saved_preact"));
   if (dpreact) MLP_TRY(need_ptr(dpreact, "dpreact"));
@@ -450,7 +466,7 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
       MLP_TRY(need_ptr(dwu, "dw_up"));
     }
   } else {
-    MLP_TRY(need_null(dwu, "dw_up", "for ReLU^2"));
+    MLP_TRY(need_null(dwu, "dw_up", "for a non-gated activation"));
     if (dwg) MLP_TRY(need_ptr(dwg, "dw_gate (dW1)"));
   }
   if (grad_accum != 0 && grad_accum != 1) return fail(MLP_ERR_INVALID_ARG, "grad_accum must be 0 or 1");
@@ -533,8 +549,10 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
     // only the down-projection gradient: the post-activation from the pre-activation alone
     StageScope st(MLP_STAGE_ACT, s);
     if (gated) MLP_TRY(hip_status(run_gated_act(io, pre, act, (int)M, (int)H, d->gate_mult,
-                                                d->gate_mode == MLP_GATE_INSIDE, s), "activation"));
-    else MLP_TRY(hip_status(run_relu_sq_act(io, pre, act, M * H, 1.0f, nullptr, nullptr, s), "activation"));
+                                                d->gate_mode == MLP_GATE_INSIDE, act_fn_of(d->act), s),
+                                  "activation"));
+    else MLP_TRY(hip_status(run_plain_act(io, pre, act, M * H, 1.0f, nullptr, nullptr, act_fn_of(d->act), s),
+                            "activation"));
   }
 
   if (dwd) {   // dW_down (+)= dm * dout^T a
@@ -550,7 +568,7 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
     StageScope st(MLP_STAGE_DW_DOWN, s);
     MLP_TRY(gemm(io, gio, TN, EPI_STORE, G.dw_down, a, O, H, M, partial, s, "dW_down"));
   }
-  if (dx) {    // dx = [dg | du] [W_gate; W_up]  (ReLU^2: dpre W1)
+  if (dx) {    // dx = [dg | du] [W_gate; W_up]  (non-gated: dpre W1)
     GemmArgs a = base_args(d);
     a.A = dpre;
     a.lda = P;
@@ -564,7 +582,7 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
     StageScope st(MLP_STAGE_DX, s);
     MLP_TRY(gemm(io, io, NN, EPI_STORE, G.dx, a, M, D, P, partial, s, "dx"));
   }
-  if (dwg) {   // [dW_gate; dW_up] (+)= [dg | du]^T x  (ReLU^2: dW1 = dpre^T x)
+  if (dwg) {   // [dW_gate; dW_up] (+)= [dg | du]^T x  (non-gated: dW1 = dpre^T x)
     GemmArgs a = base_args(d);
     a.A = dpre;
     a.lda = P;

@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (make_desc, make_fp8, mlp_bwd, mlp_fp8_next_scale, mlp_fwd, mlp_fwd_infer,
+from . import (GATED_ACTS, make_desc, make_fp8, mlp_bwd, mlp_fp8_next_scale, mlp_fwd, mlp_fwd_infer,
                mlp_quantize_e4m3, workspace_bytes)
 
 E4M3_MAX = 448.0
@@ -21,7 +21,7 @@ class MlpRunner:
     def __init__(self, *, act, dtype, M, d_in, hidden, d_out, gate_mult=1.0, down_mult=1.0,
                  gate_mode="outside", recompute=False, grad_accum=False, fp8_fwd=False,
                  tensors: dict, device="cuda", dpreact_in_place=False):
-        self.gated = act == "swiglu"
+        self.gated = act in GATED_ACTS
         self.grad_accum = grad_accum
         self.fp8 = fp8_fwd
         tdt = torch.bfloat16 if dtype in ("bf16", torch.bfloat16) else torch.float32

@@ -1,12 +1,14 @@
 /*
  * gated_mlp: fused transformer-MLP forward and backward on AMD Instinct MI355X (gfx950).
  *
- *   gated:    g = x W_gate^T, u = x W_up^T, a = act(g, u), out = down_mult * a W_down^T
- *   ReLU^2:   pre = x W1^T, post = relu(pre)^2,          out = down_mult * post W2^T
+ *   gated:     g = x W_gate^T, u = x W_up^T, a = act(g, u), out = down_mult * a W_down^T
+ *   non-gated: pre = x W1^T, post = f(pre),               out = down_mult * post W2^T
  *
- * The gated activation is SwiGLU: a = gate_mult * silu(g) * u (flash-swiglu-mlp README,
- * "Falcon H1 style models"), or a = silu(gate_mult * g) * u with MLP_GATE_INSIDE. The ReLU^2
- * MLP is modded-nanogpt gpt.py's ReLUSqrdMLP (relu(x @ W1.T)^2 @ W2.T). The backward follows
+ * The headline gated activation is SwiGLU: a = gate_mult * silu(g) * u (flash-swiglu-mlp
+ * README, "Falcon H1 style models"), or a = silu(gate_mult * g) * u with MLP_GATE_INSIDE; the
+ * headline non-gated one is modded-nanogpt gpt.py's ReLUSqrdMLP (relu(x @ W1.T)^2 @ W2.T). The
+ * other members of quack mlp.py's Activation set are provided with their standard definitions
+ * (see mlp_act). The backward follows
  * quack mlp.py's MLPRecomputeFunc.backward: d-activation applied to dout W2 against the
  * pre-activation (saved, or recomputed from x), dW2 = dout^T postact, dx = dpreact W1,
  * dW1 = dpreact^T x, optionally added into existing fp32 gradient buffers
@@ -46,10 +48,26 @@ typedef enum mlp_status {
   MLP_ERR_HIP = 5            /* a HIP launch failed */
 } mlp_status;
 
-typedef enum mlp_act { MLP_ACT_SWIGLU = 0, MLP_ACT_RELU_SQ = 1 } mlp_act;
+/* Activations (quack mlp.py's Activation set; it names them, the definitions are the standard
+ * ones). Gated (w_gate and w_up; a = f(g) * u with the gate multiplier per mlp_gate_mode):
+ *   MLP_ACT_SWIGLU  f = silu(z) = z sigmoid(z)     MLP_ACT_GEGLU  f = gelu_tanh
+ *   MLP_ACT_REGLU   f = relu                       MLP_ACT_GLU    f = sigmoid
+ * Non-gated (w_gate holds W1, w_up is NULL; post = f(pre); gate_mult and gate_mode ignored):
+ *   MLP_ACT_RELU_SQ f = relu(z)^2                  MLP_ACT_RELU   f = relu(z) = max(z, 0)
+ *   MLP_ACT_GELU_TANH f = z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))
+ * relu's derivative is taken as 0 at z = 0. */
+typedef enum mlp_act {
+  MLP_ACT_SWIGLU = 0,
+  MLP_ACT_RELU_SQ = 1,
+  MLP_ACT_GEGLU = 2,
+  MLP_ACT_REGLU = 3,
+  MLP_ACT_GLU = 4,
+  MLP_ACT_GELU_TANH = 5,
+  MLP_ACT_RELU = 6
+} mlp_act;
 typedef enum mlp_dtype { MLP_F32 = 0, MLP_BF16 = 1 } mlp_dtype;
-/* where gate_mult enters SwiGLU: outside = gate_mult * silu(g) * u (the README's formula),
- * inside = silu(gate_mult * g) * u. Identical at gate_mult = 1. */
+/* where gate_mult enters a gated activation: outside = gate_mult * f(g) * u (the README's formula
+ * for SwiGLU), inside = f(gate_mult * g) * u. Identical at gate_mult = 1. */
 typedef enum mlp_gate_mode { MLP_GATE_OUTSIDE = 0, MLP_GATE_INSIDE = 1 } mlp_gate_mode;
 typedef enum mlp_phase { MLP_PHASE_FWD = 0, MLP_PHASE_FWD_INFER = 1, MLP_PHASE_BWD = 2 } mlp_phase;
 
@@ -60,7 +78,7 @@ typedef struct mlp_desc {
   int64_t d_out;      /* width of out */
   int32_t act;        /* mlp_act */
   int32_t dtype;      /* mlp_dtype of x, weights, out, dout, dx, saved/d preact, fresh grads */
-  float gate_mult;    /* SwiGLU gate multiplier (1.0 = plain SwiGLU); ignored for ReLU^2 */
+  float gate_mult;    /* gate multiplier of a gated activation (1.0 = none); ignored otherwise */
   float down_mult;    /* scalar on the down projection's output (1.0 = none) */
   int32_t gate_mode;  /* mlp_gate_mode */
   int32_t recompute;  /* 1: nothing is saved; mlp_bwd recomputes the pre-activation from x */
@@ -95,10 +113,10 @@ size_t mlp_workspace_bytes(const mlp_desc* desc, int phase);
  * Training forward (quack mlp.py: mlp_func with grad enabled; flash-swiglu-mlp README,
  * "design points": fused gate/up forward, then the down projection).
  *   out          [M, d_out]                          written
- *   saved_preact gated: [M, 2H], row = [g | u]; ReLU^2: [M, H] pre. Written. Must be NULL
+ *   saved_preact gated: [M, 2H], row = [g | u]; non-gated: [M, H] pre. Written. Must be NULL
  *                iff desc->recompute (then nothing is kept for the backward: quack's
  *                MLPRecomputeFunc saves only x and the weights).
- *   w_up         NULL for ReLU^2 (w_gate then holds W1, w_down holds W2).
+ *   w_up         NULL for a non-gated activation (w_gate then holds W1, w_down holds W2).
  *   fp8          non-NULL iff desc->fp8_fwd; x / w_gate / w_down are then not read.
  */
 mlp_status mlp_fwd(const mlp_desc* desc, const void* x, const void* w_gate, const void* w_up,
@@ -118,10 +136,10 @@ mlp_status mlp_fwd_infer(const mlp_desc* desc, const void* x, const void* w_gate
  * README, "design points": fused dA/dG/dU with dA never stored, dG/dU written over G/U,
  * merged dW_g/dW_u GEMM, single-accumulator dI).
  *   saved_preact  as written by mlp_fwd; NULL iff desc->recompute.
- *   dpreact       gated [M, 2H] = [dg | du], ReLU^2 [M, H]; written. NULL: kept in the
+ *   dpreact       gated [M, 2H] = [dg | du], non-gated [M, H]; written. NULL: kept in the
  *                 workspace. May equal saved_preact (overwritten in place; no other overlap).
  *   dx            [M, d_in], NULL to skip.
- *   dw_gate/dw_up [H, d_in] (ReLU^2: dw_gate = dW1, dw_up NULL); both or neither (gated).
+ *   dw_gate/dw_up [H, d_in] (non-gated: dw_gate = dW1, dw_up NULL); both or neither (gated).
  *   dw_down       [d_out, H], NULL to skip.
  *   grad_accum    0: weight grads are written in desc->dtype; 1: they are fp32 buffers and the
  *                 new gradient is added in place (buf = fp32(buf + grad)).

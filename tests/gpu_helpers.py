@@ -57,9 +57,10 @@ def check_full(w, t, r, gate_mode="outside", tol=None):
     tol = tol or TOL[w.dtype]
     a = oracle_weights(w, t)
     if w.gated:
-        f = oracle.gated_forward(a["x"], a["w_gate"], a["w_up"], a["w_down"], w.gate_mult, w.down_mult, gate_mode)
+        f = oracle.gated_forward(a["x"], a["w_gate"], a["w_up"], a["w_down"], w.gate_mult, w.down_mult, gate_mode,
+                                 w.act)
         b = oracle.gated_backward(a["dout"], a["x"], a["w_gate"], a["w_up"], a["w_down"], w.gate_mult,
-                                  w.down_mult, gate_mode)
+                                  w.down_mult, gate_mode, w.act)
         pairs = [("out", r.out, f["out"]), ("dx", r.dx, b["dx"])]
         grads = [("dw_gate", r.dw_gate, b["dw_gate"]), ("dw_up", r.dw_up, b["dw_up"]),
                  ("dw_down", r.dw_down, b["dw_down"])]
@@ -67,8 +68,8 @@ def check_full(w, t, r, gate_mode="outside", tol=None):
             pairs.append(("g", r.saved[:, : w.hidden], f["g"]))
             pairs.append(("u", r.saved[:, w.hidden:], f["u"]))
     else:
-        f = oracle.relu_sq_forward(a["x"], a["w1"], a["w2"], w.down_mult)
-        b = oracle.relu_sq_backward(a["dout"], a["x"], a["w1"], a["w2"], w.down_mult)
+        f = oracle.act_forward(a["x"], a["w1"], a["w2"], w.down_mult, w.act)
+        b = oracle.act_backward(a["dout"], a["x"], a["w1"], a["w2"], w.down_mult, w.act)
         pairs = [("out", r.out, f["out"]), ("dx", r.dx, b["dx"])]
         grads = [("dw1", r.dw_gate, b["dw1"]), ("dw2", r.dw_down, b["dw2"])]
         if r.saved is not None:

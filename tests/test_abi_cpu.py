@@ -164,3 +164,24 @@ def test_product_and_oracle_share_no_code():
     for f in os.listdir(os.path.join(ROOT, "oracle")):
         if f.endswith(".py"):
             assert not pat_prod.search(open(os.path.join(ROOT, "oracle", f)).read()), f
+
+
+@pytest.mark.parametrize("act,gated", [("swiglu", True), ("geglu", True), ("reglu", True), ("glu", True),
+                                       ("relu_sq", False), ("relu", False), ("gelu_tanh", False)])
+def test_activation_family_checks(act, gated):
+    """Every mlp_act passes the descriptor check; a gated one needs w_up, a non-gated one refuses
+    it; the e4m3 forward is ReLU^2 only."""
+    d = _desc(act=act)
+    wu = FAKE if gated else None
+    assert _fwd(d, wu=wu, ws=None) == gm._lib.MLP_ERR_INVALID_ARG and "workspace" in _err()
+    assert _fwd(d, wu=None if gated else FAKE) == gm._lib.MLP_ERR_INVALID_ARG and "w_up" in _err()
+    if act != "relu_sq":
+        df = _desc(act=act, fp8_fwd=True, d_in=256, hidden=704, d_out=208)
+        assert _fwd(df, wu=wu) == gm._lib.MLP_ERR_UNSUPPORTED
+
+
+def test_activation_enum_bounds():
+    for bad in (-1, 7, 100):
+        d = _desc()
+        d.act = bad
+        assert _fwd(d) == gm._lib.MLP_ERR_INVALID_ARG and "mlp_act" in _err()

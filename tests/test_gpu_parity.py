@@ -83,6 +83,72 @@ def test_relu_sq_small(w):
     check_full(w, t, r)
 
 
+# the other activations of quack's Activation set, through the same kernels
+OTHER_GATED = [
+    _w("geglu", "bf16", 300, 264, 712, 200, gate_mult=1.125, down_mult=2.0),
+    _w("reglu", "bf16", 300, 264, 712, 200, gate_mult=1.125, down_mult=2.0, seed=1),
+    _w("glu", "bf16", 300, 264, 712, 200, gate_mult=1.125, down_mult=2.0, seed=2),
+    _w("geglu", "f32", 77, 132, 200, 68, gate_mult=0.75),
+    _w("glu", "bf16", 517, 512, 1400, 520, seed=4, recompute=True, grad_accum=True),
+]
+
+
+@pytest.mark.parametrize("w", OTHER_GATED, ids=lambda w: w.name)
+@pytest.mark.parametrize("mode", ["outside", "inside"])
+def test_other_gated_small(w, mode):
+    announce(f"gated {w.name} {mode}")
+    t = make_inputs(w)
+    r = run(w, t, gate_mode=mode)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    check_full(w, t, r, mode)
+
+
+@pytest.mark.parametrize("w", [
+    _w("relu", "bf16", 333, 200, 520, 264),
+    _w("gelu_tanh", "bf16", 333, 200, 520, 264, down_mult=2.0, seed=1),
+    _w("gelu_tanh", "f32", 70, 44, 96, 36),
+    _w("relu", "bf16", 257, 136, 392, 128, recompute=True, grad_accum=True, seed=2),
+    _w("gelu_tanh", "bf16", 600, 768, 3072, 768, seed=5),
+], ids=lambda w: w.name)
+def test_other_plain_small(w):
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    check_full(w, t, r)
+
+
+@pytest.mark.parametrize("act", ["geglu", "reglu", "glu", "gelu_tanh", "relu"])
+def test_other_acts_infer_recompute_and_dw_down_only(act):
+    """Per activation: inference == training forward, recompute == saved pre-activation, and the
+    "only dW_down" branch (act-only kernel) == the full backward's dW_down, bit for bit."""
+    w = _w(act, "bf16", 300, 264, 712, 200, gate_mult=1.125 if act in ("geglu", "reglu", "glu") else 1.0)
+    announce(f"{act}: infer / recompute / only-dW_down")
+    t = make_inputs(w)
+    r = run(w, t, gate_mode="inside")
+    r.forward()
+    r.forward_infer()
+    r.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(r.out, r.out_infer)
+    grads = {k: v.clone() for k, v in r.grads().items()}
+    full_dwd = r.dw_down.clone()
+    rr = run(w.replace(recompute=True), t, gate_mode="inside")
+    rr.forward()
+    rr.backward()
+    torch.cuda.synchronize()
+    for k, v in grads.items():
+        assert torch.equal(rr.grads()[k], v), k
+    r.dw_down.zero_()
+    r.backward(dx=False, dw_gate=False)
+    torch.cuda.synchronize()
+    assert torch.equal(full_dwd, r.dw_down)
+
+
 def test_m_equals_one():
     w = _w("swiglu", "bf16", 1, 64, 128, 64)
     announce(w.name)

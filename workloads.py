@@ -33,7 +33,7 @@ import torch
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    act: str            # "swiglu" | "relu_sq"
+    act: str            # gated: "swiglu" | "geglu" | "reglu" | "glu"; else "relu_sq" | "relu" | "gelu_tanh"
     dtype: str          # storage dtype of x / weights / outputs: "f32" | "bf16"
     batch: tuple        # leading dims of x; M is their product
     d_in: int
@@ -52,7 +52,7 @@ class Workload:
 
     @property
     def gated(self) -> bool:
-        return self.act == "swiglu"
+        return self.act in ("swiglu", "geglu", "reglu", "glu")
 
     def model_flops(self) -> float:
         """2*M*N*K summed over the GEMMs of one forward+backward (gated 18*M*d*H, ReLU^2 12*M*d*H,
