@@ -110,6 +110,52 @@ def vendor_gemm_reference(w, tensors, reps: int = 20) -> dict:
     return res
 
 
+def decode_latency(w, tensors, tokens: int, reps: int = 50) -> dict:
+    """Inference forward at decode size (`tokens` rows of x, the workload's weights): average time
+    per call launched eagerly from Python and replayed from a captured HIP graph, and the weight
+    bytes per call over the graph time (a decode step reads every weight once)."""
+    import torch
+    from gated_mlp_gemms_amd.runner import runner_for
+
+    wd = w.replace(batch=(tokens,), grad_accum=False)
+    td = {k: v for k, v in tensors.items() if not k.startswith("dw")}
+    td["x"] = tensors["x"][:tokens].clone()
+    td["dout"] = tensors["dout"][:tokens].clone()
+    r = runner_for(wd, td)
+    if w.fp8_fwd:
+        r.quantize()
+    for _ in range(3):
+        r.forward_infer()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        r.forward_infer()
+    b.record()
+    torch.cuda.synchronize()
+    eager_us = 1e3 * a.elapsed_time(b) / reps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        r.forward_infer()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        r.forward_infer()
+    g.replay()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    graph_us = 1e3 * a.elapsed_time(b) / reps
+    wbytes = (w.hidden * w.d_in * (2 if w.gated else 1) + w.d_out * w.hidden) * (1 if w.fp8_fwd else w.elem_bytes)
+    del g, r
+    return {"tokens": tokens, "eager_us": round(eager_us, 2), "graph_us": round(graph_us, 2),
+            "weight_bytes": wbytes, "weight_GBps": round(wbytes / (graph_us * 1e-6) / 1e9, 1)}
+
+
 def cpu_baseline(w, tensors, rows: int) -> dict:
     """The float64 oracle (as it stands) on the first `rows` tokens of the workload, all of d
     and H: forward + backward, timed on this host's cores."""
@@ -145,6 +191,8 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="tokens in the oracle's CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-tokens", type=int, default=16,
+                    help="also time the inference forward at this many tokens, eager and from a graph (0: skip)")
     ap.add_argument("--vendor-gemm-reference", action="store_true",
                     help="also time the six plain GEMMs through torch.matmul (hipBLASLt), for context")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -258,6 +306,11 @@ def main():
     log(f"[bench] step median {spread['median']} ms (min {spread['min']}, p90 {spread['p90']}); fwd {fwd_us} us, "
         f"bwd {bwd_us} us; inference fwd {infer_us} us; cold-cache step {cold_ms} ms")
 
+    decode = None
+    if args.decode_tokens > 0:
+        decode = decode_latency(w, tensors, args.decode_tokens)
+        log(f"[bench] decode {decode}")
+
     vendor = None
     if args.vendor_gemm_reference:
         vendor = vendor_gemm_reference(w, tensors)
@@ -284,7 +337,7 @@ def main():
         "stages_us": stage_us, "stages_tflops": stage_tf,
         "step_ms": spread, "fwd_us": fwd_us, "bwd_us": bwd_us,
         "infer_fwd_us": infer_us, "infer_fwd_tflops": round(w.model_flops() / 3 / (infer_us * 1e-6) / 1e12, 1),
-        "cold_cache_ms_per_step": cold_ms,
+        "cold_cache_ms_per_step": cold_ms, "decode": decode,
         "roofline": roof, "cpu_baseline": cpu,
     }
     if vendor is not None:

@@ -62,6 +62,19 @@ def test_llama_swiglu_full_size():
     _check_gated(w, t, r, "outside")
 
 
+@pytest.mark.parametrize("name", ["llama_swiglu_bf16_tp8_m2048_d4096_h1376", "llama_swiglu_bf16_dp8_m256_d4096_h11008"])
+def test_llama_shard_shapes(name):
+    """One GPU's share of the LLaMA step under 8-way tensor or data parallelism."""
+    w = WORKLOADS[name]
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    _check_gated(w, t, r, "outside")
+
+
 @pytest.mark.parametrize("mode", ["outside", "inside"])
 def test_falcon_h1_recompute_accumulate_full_size(mode):
     w = WORKLOADS["falcon_h1_swiglu_bf16_m8192_d2048_h4864"]

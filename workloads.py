@@ -51,6 +51,10 @@ class Workload:
         return int(np.prod(self.batch))
 
     @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
     def gated(self) -> bool:
         return self.act in ("swiglu", "geglu", "reglu", "glu")
 
@@ -80,6 +84,10 @@ WORKLOADS = {
         Workload("gpt_relu2_bf16_m49152_d768_h3072", "relu_sq", "bf16", (48, 1024), 768, 3072, 768),
         Workload("gpt_relu2_fp8fwd_m49152_d768_h3072", "relu_sq", "bf16", (48, 1024), 768, 3072, 768,
                  fp8_fwd=True),
+        # one GPU's share of the LLaMA step on 8 GPUs: tensor parallel (hidden units split 8 ways,
+        # a gate/up pair kept together) and data parallel (tokens split 8 ways)
+        Workload("llama_swiglu_bf16_tp8_m2048_d4096_h1376", "swiglu", "bf16", (2, 1024), 4096, 1376, 4096),
+        Workload("llama_swiglu_bf16_dp8_m256_d4096_h11008", "swiglu", "bf16", (1, 256), 4096, 11008, 4096),
     ]
 }
 
