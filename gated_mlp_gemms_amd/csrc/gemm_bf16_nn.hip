@@ -24,6 +24,7 @@ hipError_t run_gemm_bf16_nn(DType io, int epi, TileShape tile, const GemmArgs& a
     case TILE_256x128: return dispatch<256, 128, 4>(io, epi, a, grid, s);
     case TILE_128x128: return dispatch<128, 128, 4>(io, epi, a, grid, s);
     case TILE_256x256_W8: return dispatch<256, 256, 8>(io, epi, a, grid, s);
+    case TILE_256x128_W8: return dispatch<256, 128, 8>(io, epi, a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

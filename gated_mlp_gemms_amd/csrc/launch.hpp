@@ -11,7 +11,9 @@ namespace gmlp {
 enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
 enum Layout : int { NT = 0, NN = 1, TN = 2 };   // A K-major/B K-major, A K/B MN, A MN/B MN
 // Tile shapes of the bf16 / e4m3 kernel; _W8 runs the tile with 8 waves (two per SIMD).
-enum TileShape : int { TILE_256x256 = 0, TILE_256x128 = 1, TILE_128x128 = 2, TILE_256x256_W8 = 3, TILE_COUNT = 4 };
+enum TileShape : int {
+  TILE_256x256 = 0, TILE_256x128 = 1, TILE_128x128 = 2, TILE_256x256_W8 = 3, TILE_256x128_W8 = 4, TILE_COUNT = 5
+};
 
 // One GEMM launch. `io` is the element type of the epilogue's stored/loaded tensors (for
 // EPI_STORE the output type; accumulate mode needs DT_F32). Returns hipErrorInvalidValue for a

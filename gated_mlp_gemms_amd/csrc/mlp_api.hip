@@ -97,6 +97,7 @@ const TileInfo kTiles[] = {
     {TILE_256x256_W8, 256, 256, 1, 0.44},   // 8 waves: two per SIMD hide each other's stalls
     {TILE_256x256, 256, 256, 1, 0.40},
     {TILE_256x128, 256, 128, 1, 0.33},
+    {TILE_256x128_W8, 256, 128, 1, 0.36},
     {TILE_128x128, 128, 128, 2, 0.36},
 };
 
@@ -110,7 +111,7 @@ Plan plan_gemm(DType in, int64_t M, int64_t N, int64_t K, bool allow_split, bool
   double best_t = 1e300;
   for (const TileInfo& ti : kTiles) {
     if (in == DT_F32 && ti.t != TILE_128x128) continue;
-    if (in == DT_E4M3 && ti.t == TILE_256x256_W8) continue;
+    if (in == DT_E4M3 && (ti.t == TILE_256x256_W8 || ti.t == TILE_256x128_W8)) continue;
     const int64_t bn_units = gated ? ti.bn / 2 : ti.bn;
     const int64_t tm = (M + ti.bm - 1) / ti.bm, tn = (N + bn_units - 1) / bn_units;
     const int max_split = allow_split ? 16 : 1;
