@@ -13,14 +13,15 @@ import torch
 
 from ._lib import (  # noqa: F401
     LIB_PATH, MLP_ACT_GEGLU, MLP_ACT_GELU_TANH, MLP_ACT_GLU, MLP_ACT_REGLU, MLP_ACT_RELU, MLP_ACT_RELU_SQ,
-    MLP_ACT_SWIGLU, MLP_BF16, MLP_F32, MLP_GATE_INSIDE, MLP_GATE_OUTSIDE,
+    MLP_ACT_SWIGLU, MLP_BF16, MLP_F16, MLP_F32, MLP_GATE_INSIDE, MLP_GATE_OUTSIDE,
     MLP_PHASE_BWD, MLP_PHASE_FWD, MLP_PHASE_FWD_INFER, MlpDesc, MlpError, MlpFp8, check, lib,
 )
 
 _ACTS = {"swiglu": MLP_ACT_SWIGLU, "relu_sq": MLP_ACT_RELU_SQ, "geglu": MLP_ACT_GEGLU, "reglu": MLP_ACT_REGLU,
          "glu": MLP_ACT_GLU, "gelu_tanh": MLP_ACT_GELU_TANH, "relu": MLP_ACT_RELU}
 GATED_ACTS = frozenset({"swiglu", "geglu", "reglu", "glu"})   # a = f(g) * u, weights w_gate and w_up
-_DTYPES = {torch.float32: MLP_F32, torch.bfloat16: MLP_BF16, "f32": MLP_F32, "bf16": MLP_BF16}
+_DTYPES = {torch.float32: MLP_F32, torch.bfloat16: MLP_BF16, torch.float16: MLP_F16, "f32": MLP_F32,
+           "bf16": MLP_BF16, "f16": MLP_F16}
 _MODES = {"outside": MLP_GATE_OUTSIDE, "inside": MLP_GATE_INSIDE}
 _PHASES = {"fwd": MLP_PHASE_FWD, "fwd_infer": MLP_PHASE_FWD_INFER, "bwd": MLP_PHASE_BWD}
 
@@ -94,7 +95,7 @@ def mlp_bwd(desc, dout, x, w_gate, w_up, w_down, saved_preact=None, dpreact=None
 
 
 def mlp_quantize_e4m3(src, dst, scale, workspace=None, stream=None):
-    """Per-tensor e4m3 quantization of ``src`` (f32/bf16) into ``dst`` (uint8 or float8_e4m3fn)
+    """Per-tensor e4m3 quantization of ``src`` (f32/bf16/f16) into ``dst`` (uint8 or float8_e4m3fn)
     and the fp32 device scalar ``scale``."""
     if workspace is None:
         workspace = torch.empty(int(lib().mlp_quantize_workspace_bytes()), dtype=torch.uint8, device=src.device)

@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(_HERE, "libgated_mlp.so")
 # enums of mlp.h
 MLP_OK, MLP_ERR_INVALID_ARG, MLP_ERR_UNSUPPORTED, MLP_ERR_ALIGNMENT, MLP_ERR_WORKSPACE, MLP_ERR_HIP = range(6)
 MLP_ACT_SWIGLU, MLP_ACT_RELU_SQ, MLP_ACT_GEGLU, MLP_ACT_REGLU, MLP_ACT_GLU, MLP_ACT_GELU_TANH, MLP_ACT_RELU = range(7)
-MLP_F32, MLP_BF16 = 0, 1
+MLP_F32, MLP_BF16, MLP_F16 = 0, 1, 2
 MLP_GATE_OUTSIDE, MLP_GATE_INSIDE = 0, 1
 MLP_PHASE_FWD, MLP_PHASE_FWD_INFER, MLP_PHASE_BWD = 0, 1, 2
 STAGES = ("up", "down", "recompute", "dact", "dw_down", "dx", "dw_up", "act", "widen")

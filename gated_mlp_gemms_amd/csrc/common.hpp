@@ -10,6 +10,8 @@ namespace gmlp {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -24,6 +26,7 @@ constexpr int kWave = 64;
 template <typename T> struct ElemTraits;
 template <> struct ElemTraits<float> { static constexpr int bytes = 4; };
 template <> struct ElemTraits<bf16>  { static constexpr int bytes = 2; };
+template <> struct ElemTraits<f16>   { static constexpr int bytes = 2; };
 template <> struct ElemTraits<e4m3>  { static constexpr int bytes = 1; };
 
 // ---- conversions -------------------------------------------------------------------------
@@ -40,6 +43,26 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// The 16-bit storage types as bits: to fp32 exactly, from fp32 rounded to nearest even (fp16:
+// the hardware conversion in the default rounding mode; beyond +-65504 it gives +-inf).
+template <typename T> struct Bits16;
+template <> struct Bits16<bf16> {
+  static __device__ __forceinline__ float to_f32(uint32_t h) { return bf16_bits_to_f32(h); }
+  static __device__ __forceinline__ uint32_t from_f32(float f) { return f32_to_bf16_bits(f); }
+};
+template <> struct Bits16<f16> {
+  static __device__ __forceinline__ float to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(f16, (uint16_t)(h & 0xffffu));
+  }
+  static __device__ __forceinline__ uint32_t from_f32(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (f16)f);
+  }
+};
+template <typename T>
+__device__ __forceinline__ uint32_t pack16x2(float lo, float hi) {
+  return Bits16<T>::from_f32(lo) | (Bits16<T>::from_f32(hi) << 16);
 }
 
 // fp32 -> OCP E4M3 code: nearest, ties to even mantissa, |v| >= 448 saturates to +-448,

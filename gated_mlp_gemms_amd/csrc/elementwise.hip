@@ -21,18 +21,22 @@ template <> __device__ __forceinline__ void load4<float>(const void* p, float v[
   f32x4 x = *reinterpret_cast<const f32x4*>(p);
   v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
 }
-template <> __device__ __forceinline__ void load4<bf16>(const void* p, float v[4]) {
+template <typename T> __device__ __forceinline__ void load4_16(const void* p, float v[4]) {
   u32x2 x = *reinterpret_cast<const u32x2*>(p);
-  v[0] = bf16_bits_to_f32(x[0] & 0xffffu); v[1] = bf16_bits_to_f32(x[0] >> 16);
-  v[2] = bf16_bits_to_f32(x[1] & 0xffffu); v[3] = bf16_bits_to_f32(x[1] >> 16);
+  v[0] = Bits16<T>::to_f32(x[0] & 0xffffu); v[1] = Bits16<T>::to_f32(x[0] >> 16);
+  v[2] = Bits16<T>::to_f32(x[1] & 0xffffu); v[3] = Bits16<T>::to_f32(x[1] >> 16);
 }
+template <> __device__ __forceinline__ void load4<bf16>(const void* p, float v[4]) { load4_16<bf16>(p, v); }
+template <> __device__ __forceinline__ void load4<f16>(const void* p, float v[4]) { load4_16<f16>(p, v); }
 template <typename T> __device__ __forceinline__ void store4(void* p, const float v[4]);
 template <> __device__ __forceinline__ void store4<float>(void* p, const float v[4]) {
   *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
 }
-template <> __device__ __forceinline__ void store4<bf16>(void* p, const float v[4]) {
-  *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+template <typename T> __device__ __forceinline__ void store4_16(void* p, const float v[4]) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack16x2<T>(v[0], v[1]), pack16x2<T>(v[2], v[3])};
 }
+template <> __device__ __forceinline__ void store4<bf16>(void* p, const float v[4]) { store4_16<bf16>(p, v); }
+template <> __device__ __forceinline__ void store4<f16>(void* p, const float v[4]) { store4_16<f16>(p, v); }
 template <typename T> constexpr int esize() { return sizeof(T) == 4 ? 4 : 2; }
 
 // ---- split-K reduction: fixed summation order over the splits -----------------------------
@@ -119,6 +123,9 @@ template <> __device__ __forceinline__ float load1<float>(const void* p, int64_t
 template <> __device__ __forceinline__ float load1<bf16>(const void* p, int64_t i) {
   return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
 }
+template <> __device__ __forceinline__ float load1<f16>(const void* p, int64_t i) {
+  return Bits16<f16>::to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+}
 
 template <typename T>
 __global__ __launch_bounds__(kEwThreads) void absmax_kernel(const void* src, int64_t n, float* amax) {
@@ -162,6 +169,9 @@ hipError_t run_splitk_reduce(DType io, const float* partial, int splits, int M, 
   if (io == DT_BF16 && !accumulate)
     hipLaunchKernelGGL(splitk_reduce_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, partial, splits, M,
                        N, C0, C1, ldc, c_split, alpha, dev0, dev1, 0);
+  else if (io == DT_F16 && !accumulate)
+    hipLaunchKernelGGL(splitk_reduce_kernel<f16>, dim3(grid), dim3(kEwThreads), 0, s, partial, splits, M,
+                       N, C0, C1, ldc, c_split, alpha, dev0, dev1, 0);
   else
     hipLaunchKernelGGL(splitk_reduce_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, partial, splits, M,
                        N, C0, C1, ldc, c_split, alpha, dev0, dev1, accumulate);
@@ -174,6 +184,9 @@ hipError_t run_gated_act(DType io, const void* preact, void* a, int M, int H, fl
   if (io == DT_BF16)
     hipLaunchKernelGGL(gated_act_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, preact, a, M, H, gate_mult,
                        gate_inside, fn);
+  else if (io == DT_F16)
+    hipLaunchKernelGGL(gated_act_kernel<f16>, dim3(grid), dim3(kEwThreads), 0, s, preact, a, M, H, gate_mult,
+                       gate_inside, fn);
   else
     hipLaunchKernelGGL(gated_act_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, preact, a, M, H, gate_mult,
                        gate_inside, fn);
@@ -185,6 +198,8 @@ hipError_t run_plain_act(DType io, const void* pre, void* post, int64_t n, float
   const int grid = ew_grid(n / 4);
   if (io == DT_BF16)
     hipLaunchKernelGGL(plain_act_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, pre, post, n, alpha, dev0, dev1, fn);
+  else if (io == DT_F16)
+    hipLaunchKernelGGL(plain_act_kernel<f16>, dim3(grid), dim3(kEwThreads), 0, s, pre, post, n, alpha, dev0, dev1, fn);
   else
     hipLaunchKernelGGL(plain_act_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, pre, post, n, alpha, dev0, dev1, fn);
   return hipGetLastError();
@@ -197,6 +212,10 @@ hipError_t run_quantize_e4m3(DType src_t, const void* src, int64_t n, void* dst,
   if (src_t == DT_BF16) {
     hipLaunchKernelGGL(absmax_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);
     hipLaunchKernelGGL(quantize_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, src, n,
+                       reinterpret_cast<uint8_t*>(dst), ws, scale);
+  } else if (src_t == DT_F16) {
+    hipLaunchKernelGGL(absmax_kernel<f16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);
+    hipLaunchKernelGGL(quantize_kernel<f16>, dim3(grid), dim3(kEwThreads), 0, s, src, n,
                        reinterpret_cast<uint8_t*>(dst), ws, scale);
   } else {
     hipLaunchKernelGGL(absmax_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);

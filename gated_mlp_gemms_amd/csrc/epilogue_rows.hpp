@@ -24,20 +24,22 @@ template <> struct Vec8<float> {
     reinterpret_cast<f32x4*>(p)[1] = f32x4{v[4], v[5], v[6], v[7]};
   }
 };
-template <> struct Vec8<bf16> {
+template <typename T> struct Vec8Bits16 {
   static __device__ __forceinline__ void load(const void* p, float v[8]) {
     const u32x4 x = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      v[2 * r] = bf16_bits_to_f32(x[r] & 0xffffu);
-      v[2 * r + 1] = bf16_bits_to_f32(x[r] >> 16);
+      v[2 * r] = Bits16<T>::to_f32(x[r] & 0xffffu);
+      v[2 * r + 1] = Bits16<T>::to_f32(x[r] >> 16);
     }
   }
   static __device__ __forceinline__ void store(void* p, const float v[8]) {
-    *reinterpret_cast<u32x4*>(p) = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                         pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    *reinterpret_cast<u32x4*>(p) = u32x4{pack16x2<T>(v[0], v[1]), pack16x2<T>(v[2], v[3]),
+                                         pack16x2<T>(v[4], v[5]), pack16x2<T>(v[6], v[7])};
   }
 };
+template <> struct Vec8<bf16> : Vec8Bits16<bf16> {};
+template <> struct Vec8<f16> : Vec8Bits16<f16> {};
 
 // Tensors an epilogue reads besides the accumulators (saved g, u or pre; the fp32 buffer of an
 // accumulating store), fetched for a whole round before the round's LDS staging so their
@@ -61,11 +63,12 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& p, int m, int n, Au
   }
 }
 
-__device__ __forceinline__ void unpack_bf16x8(const u32x4 x, float v[8]) {
+template <typename T>
+__device__ __forceinline__ void unpack16x8(const u32x4 x, float (&v)[8]) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    v[2 * r] = bf16_bits_to_f32(x[r] & 0xffffu);
-    v[2 * r + 1] = bf16_bits_to_f32(x[r] >> 16);
+    v[2 * r] = Bits16<T>::to_f32(x[r] & 0xffffu);
+    v[2 * r + 1] = Bits16<T>::to_f32(x[r] >> 16);
   }
 }
 
@@ -112,18 +115,18 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
       Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), q);
     }
   } else if constexpr (EPI == EPI_DGATED) {
-    static_assert(std::is_same<IoT, bf16>::value, "row-staged d-activation epilogues read bf16");
+    static_assert(ElemTraits<IoT>::bytes == 2, "row-staged d-activation epilogues read 16-bit aux data");
     float gg[8], uu[8], dg[8], du[8], a[8];
-    unpack_bf16x8(x.a, gg);
-    unpack_bf16x8(x.b, uu);
+    unpack16x8<IoT>(x.a, gg);
+    unpack16x8<IoT>(x.b, uu);
     gated_act_grad<8>(p.act, p.gate_mult, p.gate_inside, v, gg, uu, dg, du, a);
     Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), dg);
     Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, p.half + n), du);
     if (p.flags & 2) Vec8<IoT>::store(elem_ptr<IoT>(p.C1, m, p.ldc1, n), a);
   } else if constexpr (EPI == EPI_DACT) {
-    static_assert(std::is_same<IoT, bf16>::value, "row-staged d-activation epilogues read bf16");
+    static_assert(ElemTraits<IoT>::bytes == 2, "row-staged d-activation epilogues read 16-bit aux data");
     float pre[8], dpre[8], post[8];
-    unpack_bf16x8(x.a, pre);
+    unpack16x8<IoT>(x.a, pre);
     act_fn_grad<8>(p.act, pre, post, dpre);
 #pragma unroll
     for (int r = 0; r < 8; ++r) dpre[r] *= v[r];

@@ -1,32 +1,10 @@
-// bf16 GEMMs with both operands K-major (x W^T): the fused gate/up forward, the ReLU^2
-// forward, the down projection and their split-K partial form.
-#include "gemm_dma.hpp"
-#include "launch.hpp"
+// bf16 GEMMs in the NT layout (launch table: gemm_dispatch16.hpp).
+#include "gemm_dispatch16.hpp"
 
 namespace gmlp {
 
-template <int BM, int BN, int W>
-static hipError_t dispatch(DType io, int epi, const GemmArgs& a, int grid, hipStream_t s) {
-  switch (epi) {
-    case EPI_GATED: return launch_gemm_dma<bf16, bf16, BM, BN, true, true, EPI_GATED, W>(a, grid, s);
-    case EPI_ACT: return launch_gemm_dma<bf16, bf16, BM, BN, true, true, EPI_ACT, W>(a, grid, s);
-    case EPI_STORE:
-      if (io == DT_BF16) return launch_gemm_dma<bf16, bf16, BM, BN, true, true, EPI_STORE, W>(a, grid, s);
-      return hipErrorInvalidValue;
-    case EPI_PARTIAL: return launch_gemm_dma<bf16, float, BM, BN, true, true, EPI_PARTIAL, W>(a, grid, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 hipError_t run_gemm_bf16_nt(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s) {
-  switch (tile) {
-    case TILE_256x256: return dispatch<256, 256, 4>(io, epi, a, grid, s);
-    case TILE_256x128: return dispatch<256, 128, 4>(io, epi, a, grid, s);
-    case TILE_128x128: return dispatch<128, 128, 4>(io, epi, a, grid, s);
-    case TILE_256x256_W8: return dispatch<256, 256, 8>(io, epi, a, grid, s);
-    case TILE_256x128_W8: return dispatch<256, 128, 8>(io, epi, a, grid, s);
-    default: return hipErrorInvalidValue;
-  }
+  return run_gemm16<bf16, NT>(io, epi, tile, a, grid, s);
 }
 
 }  // namespace gmlp

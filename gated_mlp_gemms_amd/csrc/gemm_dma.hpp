@@ -74,6 +74,7 @@ __device__ __forceinline__ void interleave() {
 // Bytes of K per operand row in one K-step.
 template <typename T> struct StepGeo;
 template <> struct StepGeo<bf16> { static constexpr int ROWB = 128; };
+template <> struct StepGeo<f16> { static constexpr int ROWB = 128; };
 template <> struct StepGeo<e4m3> { static constexpr int ROWB = 128; };
 
 // ---- K-major operand: ROWS rows x ROWB bytes per stage -------------------------------------
@@ -209,7 +210,7 @@ constexpr int ring_stages(int stage_bytes, int tile_elems) {
 template <typename T, typename IoT, int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs p) {
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must split into 2x2 waves of 32x32 blocks");
-  static_assert((A_KMAJ && B_KMAJ) || std::is_same<T, bf16>::value, "MN-major operands are bf16 only");
+  static_assert((A_KMAJ && B_KMAJ) || ElemTraits<T>::bytes == 2, "MN-major operands are 16-bit only");
   constexpr int ES = ElemTraits<T>::bytes;
   constexpr int ROWB = StepGeo<T>::ROWB;
   constexpr int BK = ROWB / ES;
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
   constexpr int NS = ring_stages(STAGE, BM * BN);
   static_assert(NS >= 2, "the ring needs two stages");
   constexpr bool GATED = EPI == EPI_GATED;
-  constexpr int KMMA = std::is_same<T, e4m3>::value ? 64 : 16;
+  constexpr int KMMA = std::is_same<T, e4m3>::value ? 64 : 16;   // bf16 / fp16: 32x32x16
   constexpr int NSUB = BK / KMMA;
   constexpr int KC = Mma<T>::kChunks;
   static_assert(NSUB % 2 == 0, "fragment double buffer alternates per substep");

@@ -1,0 +1,10 @@
+// f16 GEMMs in the TN layout (launch table: gemm_dispatch16.hpp).
+#include "gemm_dispatch16.hpp"
+
+namespace gmlp {
+
+hipError_t run_gemm_f16_tn(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s) {
+  return run_gemm16<f16, TN>(io, epi, tile, a, grid, s);
+}
+
+}  // namespace gmlp

@@ -36,17 +36,19 @@ template <> struct Vec4<float> {
     *reinterpret_cast<f32x4*>(p) = x;
   }
 };
-template <> struct Vec4<bf16> {
+template <typename T> struct Vec4Bits16 {
   static __device__ __forceinline__ void load(const void* p, float v[4]) {
     u32x2 x = *reinterpret_cast<const u32x2*>(p);
-    v[0] = bf16_bits_to_f32(x[0] & 0xffffu); v[1] = bf16_bits_to_f32(x[0] >> 16);
-    v[2] = bf16_bits_to_f32(x[1] & 0xffffu); v[3] = bf16_bits_to_f32(x[1] >> 16);
+    v[0] = Bits16<T>::to_f32(x[0] & 0xffffu); v[1] = Bits16<T>::to_f32(x[0] >> 16);
+    v[2] = Bits16<T>::to_f32(x[1] & 0xffffu); v[3] = Bits16<T>::to_f32(x[1] >> 16);
   }
   static __device__ __forceinline__ void store(void* p, const float v[4]) {
-    u32x2 x = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    u32x2 x = {pack16x2<T>(v[0], v[1]), pack16x2<T>(v[2], v[3])};
     *reinterpret_cast<u32x2*>(p) = x;
   }
 };
+template <> struct Vec4<bf16> : Vec4Bits16<bf16> {};
+template <> struct Vec4<f16> : Vec4Bits16<f16> {};
 
 template <typename T>
 __device__ __forceinline__ char* elem_ptr(void* base, int64_t row, int64_t ld, int64_t col) {
@@ -91,6 +93,15 @@ template <> struct Mma<bf16> {
   static __device__ __forceinline__ void mma(const u32x4* a, const u32x4* b, f32x16& acc) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
                                                    __builtin_bit_cast(bf16x8, b[0]), acc, 0, 0, 0);
+  }
+};
+template <> struct Mma<f16> {
+  static constexpr int kSub = 4;     // 4 x K=16 per 64-element stage
+  static constexpr int kChunks = 1;
+  static __device__ __forceinline__ int chunk(int s, int half, int c) { return 2 * s + half; }
+  static __device__ __forceinline__ void mma(const u32x4* a, const u32x4* b, f32x16& acc) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[0]),
+                                                  __builtin_bit_cast(f16x8, b[0]), acc, 0, 0, 0);
   }
 };
 template <> struct Mma<float> {

@@ -8,7 +8,7 @@
 
 namespace gmlp {
 
-enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
+enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2, DT_F16 = 3 };
 enum Layout : int { NT = 0, NN = 1, TN = 2 };   // A K-major/B K-major, A K/B MN, A MN/B MN
 // Tile shapes of the bf16 / e4m3 kernel; _W8 runs the tile with 8 waves (two per SIMD).
 enum TileShape : int {
@@ -25,6 +25,9 @@ hipError_t run_gemm(DType in, DType io, Layout layout, int epi, TileShape tile, 
 hipError_t run_gemm_bf16_nt(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
 hipError_t run_gemm_bf16_nn(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
 hipError_t run_gemm_bf16_tn(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
+hipError_t run_gemm_f16_nt(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
+hipError_t run_gemm_f16_nn(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
+hipError_t run_gemm_f16_tn(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
 hipError_t run_gemm_f32(Layout layout, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
 hipError_t run_gemm_e4m3_nt(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
 

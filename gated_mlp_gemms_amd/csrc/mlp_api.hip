@@ -61,7 +61,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-int esize(int dtype) { return dtype == MLP_BF16 ? 2 : 4; }
+int esize(int dtype) { return dtype == MLP_F32 ? 4 : 2; }
 
 bool is_gated(int act) {
   return act == MLP_ACT_SWIGLU || act == MLP_ACT_GEGLU || act == MLP_ACT_REGLU || act == MLP_ACT_GLU;
@@ -77,7 +77,8 @@ int act_fn_of(int act) {
     default: return FN_RELU_SQ;
   }
 }
-DType io_of(const mlp_desc* d) { return d->dtype == MLP_BF16 ? DT_BF16 : DT_F32; }
+DType dtype_of(int dtype) { return dtype == MLP_BF16 ? DT_BF16 : dtype == MLP_F16 ? DT_F16 : DT_F32; }
+DType io_of(const mlp_desc* d) { return dtype_of(d->dtype); }
 
 // ---- GEMM planning -------------------------------------------------------------------------
 
@@ -101,12 +102,12 @@ const TileInfo kTiles[] = {
     {TILE_128x128, 128, 128, 2, 0.36},
 };
 
-int bk_of(DType in) { return in == DT_E4M3 ? 128 : (in == DT_BF16 ? 64 : 32); }
+int bk_of(DType in) { return in == DT_E4M3 ? 128 : (in == DT_F32 ? 32 : 64); }
 
 // gated: N counts hidden units and a tile covers bn/2 of them (gate + up rows).
 Plan plan_gemm(DType in, int64_t M, int64_t N, int64_t K, bool allow_split, bool gated) {
   const int bk = bk_of(in);
-  const double per_cu = (in == DT_E4M3 ? 2.0 : in == DT_BF16 ? 1.0 : 1.0 / 16.0) * 9.83e12;
+  const double per_cu = (in == DT_E4M3 ? 2.0 : in == DT_F32 ? 1.0 / 16.0 : 1.0) * 9.83e12;
   Plan best{};
   double best_t = 1e300;
   for (const TileInfo& ti : kTiles) {
@@ -214,7 +215,7 @@ mlp_status check_desc(const mlp_desc* d) {
     return fail(MLP_ERR_UNSUPPORTED, "a size is beyond 2^30 (2^29 for hidden)");
   if (d->act < MLP_ACT_SWIGLU || d->act > MLP_ACT_RELU)
     return fail(MLP_ERR_INVALID_ARG, "act %d is not an mlp_act", d->act);
-  if (d->dtype != MLP_F32 && d->dtype != MLP_BF16)
+  if (d->dtype != MLP_F32 && d->dtype != MLP_BF16 && d->dtype != MLP_F16)
     return fail(MLP_ERR_INVALID_ARG, "dtype %d is not an mlp_dtype", d->dtype);
   if (d->gate_mode != MLP_GATE_OUTSIDE && d->gate_mode != MLP_GATE_INSIDE)
     return fail(MLP_ERR_INVALID_ARG, "gate_mode %d is not an mlp_gate_mode", d->gate_mode);
@@ -225,7 +226,7 @@ mlp_status check_desc(const mlp_desc* d) {
     return fail(MLP_ERR_INVALID_ARG, "gate_mult and down_mult must be finite");
   if (d->fp8_fwd && (d->act != MLP_ACT_RELU_SQ || d->dtype != MLP_BF16))
     return fail(MLP_ERR_UNSUPPORTED, "the e4m3 forward is implemented for ReLU^2 with bf16 I/O only");
-  const int q = d->fp8_fwd ? 16 : (d->dtype == MLP_BF16 ? 8 : 4);
+  const int q = d->fp8_fwd ? 16 : (d->dtype == MLP_F32 ? 4 : 8);
   if (d->d_in % q || d->hidden % q || d->d_out % q)
     return fail(MLP_ERR_ALIGNMENT, "d_in, hidden and d_out must be multiples of %d (16-byte rows)", q);
   return MLP_OK;
@@ -613,13 +614,14 @@ mlp_status mlp_time_stage_once(int stage, void* begin, void* end) {
 
 mlp_status mlp_quantize_e4m3(const void* src, int dtype, int64_t n, void* dst, float* scale, void* ws,
                              size_t ws_bytes, void* stream) {
-  if (dtype != MLP_F32 && dtype != MLP_BF16) return fail(MLP_ERR_INVALID_ARG, "dtype %d is not an mlp_dtype", dtype);
+  if (dtype != MLP_F32 && dtype != MLP_BF16 && dtype != MLP_F16)
+    return fail(MLP_ERR_INVALID_ARG, "dtype %d is not an mlp_dtype", dtype);
   if (n < 1) return fail(MLP_ERR_INVALID_ARG, "n must be >= 1");
   if (!src || !dst || !scale || !ws) return fail(MLP_ERR_INVALID_ARG, "src, dst, scale and workspace are required");
   if (!aligned4(src) || !aligned4(scale) || !aligned16(ws))
     return fail(MLP_ERR_ALIGNMENT, "src and scale must be 4-byte aligned, workspace 16-byte aligned");
   if (ws_bytes < kAlign) return fail(MLP_ERR_WORKSPACE, "workspace of %zu bytes is smaller than %zu", ws_bytes, kAlign);
-  return hip_status(run_quantize_e4m3(dtype == MLP_BF16 ? DT_BF16 : DT_F32, src, n, dst, scale,
+  return hip_status(run_quantize_e4m3(dtype_of(dtype), src, n, dst, scale,
                                       reinterpret_cast<float*>(ws), reinterpret_cast<hipStream_t>(stream)),
                     "quantize");
 }
@@ -644,6 +646,10 @@ hipError_t run_gemm(DType in, DType io, Layout layout, int epi, TileShape tile, 
       if (layout == NT) return run_gemm_bf16_nt(io, epi, tile, a, grid, s);
       if (layout == NN) return run_gemm_bf16_nn(io, epi, tile, a, grid, s);
       return run_gemm_bf16_tn(io, epi, tile, a, grid, s);
+    case DT_F16:
+      if (layout == NT) return run_gemm_f16_nt(io, epi, tile, a, grid, s);
+      if (layout == NN) return run_gemm_f16_nn(io, epi, tile, a, grid, s);
+      return run_gemm_f16_tn(io, epi, tile, a, grid, s);
     case DT_F32: return run_gemm_f32(layout, epi, tile, a, grid, s);
     case DT_E4M3:
       if (layout == NT) return run_gemm_e4m3_nt(io, epi, tile, a, grid, s);

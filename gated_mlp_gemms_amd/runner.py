@@ -24,7 +24,7 @@ class MlpRunner:
         self.gated = act in GATED_ACTS
         self.grad_accum = grad_accum
         self.fp8 = fp8_fwd
-        tdt = torch.bfloat16 if dtype in ("bf16", torch.bfloat16) else torch.float32
+        tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}.get(dtype, dtype)
         self.desc = make_desc(M, d_in, hidden, d_out, act, tdt, gate_mult, down_mult, gate_mode,
                               recompute, fp8_fwd)
         dev = torch.device(device)

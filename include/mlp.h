@@ -65,7 +65,9 @@ typedef enum mlp_act {
   MLP_ACT_GELU_TANH = 5,
   MLP_ACT_RELU = 6
 } mlp_act;
-typedef enum mlp_dtype { MLP_F32 = 0, MLP_BF16 = 1 } mlp_dtype;
+/* I/O type of x, the weights, out, dout, dx, the saved / d pre-activation and fresh gradients.
+ * Accumulation and epilogue math are fp32 for all three; bf16 and fp16 use the 16-bit MFMA. */
+typedef enum mlp_dtype { MLP_F32 = 0, MLP_BF16 = 1, MLP_F16 = 2 } mlp_dtype;
 /* where gate_mult enters a gated activation: outside = gate_mult * f(g) * u (the README's formula
  * for SwiGLU), inside = f(gate_mult * g) * u. Identical at gate_mult = 1. */
 typedef enum mlp_gate_mode { MLP_GATE_OUTSIDE = 0, MLP_GATE_INSIDE = 1 } mlp_gate_mode;
@@ -161,7 +163,7 @@ size_t mlp_quantize_workspace_bytes(void);
  * Per-tensor e4m3 quantization with the exact scale (modded-nanogpt gpt.py,
  * _quantize_mlp_weights_and_scales, exact-scale calls): *scale = max(amax|src|, 1e-12) / 448
  * in fp32, dst[i] = e4m3(src[i] / *scale) with IEEE fp32 division, round to nearest even,
- * saturating at +-448 (OCP E4M3). src is f32 or bf16 (`dtype`), n >= 1 elements; dst and
+ * saturating at +-448 (OCP E4M3). src is f32, bf16 or fp16 (`dtype`), n >= 1 elements; dst and
  * scale are device buffers written here.
  */
 mlp_status mlp_quantize_e4m3(const void* src, int dtype, int64_t n, void* dst, float* scale,

@@ -10,7 +10,10 @@ import torch
 import oracle
 from gated_mlp_gemms_amd.runner import runner_for
 
-TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 8e-2}
+# fp32 1e-5, bf16 2e-2, e4m3 forward 8e-2 as the hot path's specification states; fp16, which it
+# does not name: 5e-3, ten fp16 unit roundoffs (2^-11), the bf16 bound scaled by the two
+# formats' roundoff ratio (2^-8 / 2^-11 = 8) with headroom (g, u, a and dpre are stored in fp16)
+TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 5e-3, "fp8": 8e-2}
 
 
 def f64(t: torch.Tensor) -> np.ndarray:

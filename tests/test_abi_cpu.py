@@ -185,3 +185,20 @@ def test_activation_enum_bounds():
         d = _desc()
         d.act = bad
         assert _fwd(d) == gm._lib.MLP_ERR_INVALID_ARG and "mlp_act" in _err()
+
+
+def test_fp16_descriptor_checks():
+    """fp16 I/O passes the descriptor check with 8-element row alignment; the e4m3 forward stays
+    bf16-only."""
+    d = _desc(dtype="f16")
+    assert _fwd(d, ws=None) == gm._lib.MLP_ERR_INVALID_ARG and "workspace" in _err()
+    assert _fwd(_desc(dtype="f16", d_in=260)) == gm._lib.MLP_ERR_ALIGNMENT
+    assert _fwd(_desc(act="relu_sq", dtype="f16", fp8_fwd=True, d_in=256, hidden=704, d_out=208),
+                wu=None) == gm._lib.MLP_ERR_UNSUPPORTED
+    d = _desc()
+    d.dtype = 3
+    assert _fwd(d) == gm._lib.MLP_ERR_INVALID_ARG and "mlp_dtype" in _err()
+    # workspace sizes of fp16 equal bf16's (both 2-byte I/O)
+    for ph in (gm.MLP_PHASE_FWD, gm.MLP_PHASE_FWD_INFER, gm.MLP_PHASE_BWD):
+        assert gm.lib().mlp_workspace_bytes(C.byref(_desc(dtype="f16")), ph) == \
+            gm.lib().mlp_workspace_bytes(C.byref(_desc(dtype="bf16")), ph)

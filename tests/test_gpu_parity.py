@@ -322,6 +322,44 @@ def test_only_dw_down_branch(act):
     assert torch.equal(full, r.dw_down)
 
 
+# fp16 I/O (the flash-swiglu README's other supported dtype), same kernels with the fp16 MFMA
+@pytest.mark.parametrize("w", [
+    _w("swiglu", "f16", 300, 264, 712, 200, gate_mult=1.125, down_mult=2.0),
+    _w("swiglu", "f16", 517, 512, 1400, 520, seed=3, recompute=True, grad_accum=True),
+    _w("geglu", "f16", 300, 264, 712, 200, seed=1),
+    _w("relu_sq", "f16", 333, 200, 520, 264),
+    _w("gelu_tanh", "f16", 257, 136, 392, 128, recompute=True, grad_accum=True, seed=2),
+], ids=lambda w: w.name)
+@pytest.mark.parametrize("mode", ["outside", "inside"])
+def test_fp16_small(w, mode):
+    announce(f"fp16 {w.name} {mode}")
+    t = make_inputs(w)
+    r = run(w, t, gate_mode=mode)
+    r.forward()
+    r.forward_infer()
+    r.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(r.out, r.out_infer)
+    check_full(w, t, r, mode)
+
+
+def test_fp16_quantize_e4m3_matches_oracle():
+    """The per-tensor e4m3 quantizer reads fp16 sources too: codes and scale bit-exact."""
+    import gated_mlp_gemms_amd as gm
+    announce("fp16 quantize")
+    rng = np.random.default_rng(21)
+    src = torch.tensor(rng.standard_normal(70001) * 3.0, dtype=torch.float16)
+    ref_q, ref_s = oracle.quantize_per_tensor(src.double().numpy())
+    d = src.cuda()
+    q = torch.empty(d.numel(), dtype=torch.uint8, device="cuda")
+    sc = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    gm.mlp_quantize_e4m3(d, q, sc, ws)
+    torch.cuda.synchronize()
+    assert float(sc.item()) == np.float32(ref_s)
+    assert np.array_equal(q.cpu().numpy(), ref_q)
+
+
 def _capture(fn):
     """Capture fn() into a HIP graph after one warm-up call on a side stream (default priority)."""
     s = torch.cuda.Stream()

@@ -34,7 +34,7 @@ import torch
 class Workload:
     name: str
     act: str            # gated: "swiglu" | "geglu" | "reglu" | "glu"; else "relu_sq" | "relu" | "gelu_tanh"
-    dtype: str          # storage dtype of x / weights / outputs: "f32" | "bf16"
+    dtype: str          # storage dtype of x / weights / outputs: "f32" | "bf16" | "f16"
     batch: tuple        # leading dims of x; M is their product
     d_in: int
     hidden: int
@@ -94,7 +94,7 @@ WORKLOADS = {
 # The workload the headline throughput is quoted on.
 HEADLINE = "llama_swiglu_bf16_m2048_d4096_h11008"
 
-_TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+_TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def torch_dtype(name: str) -> torch.dtype:
