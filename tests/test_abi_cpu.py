@@ -202,3 +202,12 @@ def test_fp16_descriptor_checks():
     for ph in (gm.MLP_PHASE_FWD, gm.MLP_PHASE_FWD_INFER, gm.MLP_PHASE_BWD):
         assert gm.lib().mlp_workspace_bytes(C.byref(_desc(dtype="f16")), ph) == \
             gm.lib().mlp_workspace_bytes(C.byref(_desc(dtype="bf16")), ph)
+
+
+def test_size_limits():
+    """Sizes that would overflow the kernels' 32-bit tile indexing are refused before any HIP
+    call: M, d_in, d_out >= 2^30, hidden >= 2^29."""
+    for kw in (dict(M=1 << 30), dict(d_in=1 << 30), dict(d_out=1 << 30), dict(hidden=1 << 29)):
+        assert _fwd(_desc(**kw), nws=0) == gm._lib.MLP_ERR_UNSUPPORTED, kw
+        assert "2^30" in _err()
+    assert _fwd(_desc(hidden=(1 << 29) - 8), ws=None) == gm._lib.MLP_ERR_INVALID_ARG   # passes the size check

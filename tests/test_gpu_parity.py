@@ -160,6 +160,72 @@ def test_m_equals_one():
     check_full(w, t, r)
 
 
+@pytest.mark.parametrize("act,dtype", [("swiglu", "bf16"), ("relu_sq", "bf16"), ("geglu", "f32"), ("glu", "f16")])
+def test_smallest_problem(act, dtype):
+    """The smallest legal problem: one token, every width one 16-byte row (8 elements; 4 fp32)."""
+    n = 4 if dtype == "f32" else 8
+    w = _w(act, dtype, 1, n, n, n, gate_mult=1.125, down_mult=2.0)
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t, gate_mode="inside")
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    check_full(w, t, r, "inside")
+
+
+def test_tall_thin_problem():
+    """Many tokens through a hidden layer of one 8-wide row: 1 tile column, ragged rows."""
+    w = _w("swiglu", "bf16", 1999, 8, 8, 16)
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    check_full(w, t, r)
+
+
+def test_backward_with_nothing_requested_is_a_no_op():
+    """mlp_bwd with dpreact, dx and every weight gradient NULL computes and writes nothing."""
+    w = _w("swiglu", "bf16", 300, 264, 712, 200)
+    announce("backward with no outputs")
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    for v in r.grads().values():
+        v.fill_(7.0)
+    torch.cuda.synchronize()
+    r.backward(dx=False, dw_gate=False, dw_down=False, dpreact=False)
+    torch.cuda.synchronize()
+    for k, v in r.grads().items():
+        assert bool((v == 7.0).all()), k
+
+
+@pytest.mark.parametrize("act", ["swiglu", "relu_sq"])
+def test_zero_inputs_give_exact_zeros(act):
+    """x = 0 gives out = 0 and zero weight gradients of W_gate / W_up (W1) exactly; dout = 0
+    gives dx = 0 and all weight gradients 0 exactly (no rounding can make a nonzero)."""
+    w = _w(act, "bf16", 300, 264, 712, 200)
+    announce(f"zero inputs {act}")
+    t = make_inputs(w)
+    t["x"] = torch.zeros_like(t["x"])
+    r = run(w, t)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    assert not bool(r.out.any())
+    assert not bool(r.dw_gate.any())
+    t = make_inputs(w)
+    t["dout"] = torch.zeros_like(t["dout"])
+    r = run(w, t)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    for k, v in r.grads().items():
+        assert not bool(v.any()), k
+
+
 # ---- e4m3 ---------------------------------------------------------------------------------
 
 def test_quantize_e4m3_bit_exact():
