@@ -71,6 +71,42 @@ __global__ __launch_bounds__(kEwThreads) void splitk_reduce_kernel(
   }
 }
 
+// ---- split-K reduce of the gated up projection ------------------------------------------------
+// partial[s][m][0 .. 2H) holds unscaled sums over K-slice s of [g | u]; g, u = alpha * (sum over s
+// in order); [g | u] -> preact (when given), a = act(g, u) -> a_out.
+template <typename T>
+__global__ __launch_bounds__(kEwThreads) void gated_reduce_kernel(const float* partial, int splits, int M,
+                                                                  int H, float alpha, const float* dev0,
+                                                                  const float* dev1, void* preact, void* a_out,
+                                                                  float gm, int inside, int fn) {
+  float al = alpha;
+  if (dev0) al *= *dev0;
+  if (dev1) al *= *dev1;
+  const int h4 = H / 4;
+  const int64_t total = (int64_t)M * h4;
+  const int64_t slice = (int64_t)M * 2 * H;
+  for (int64_t i = blockIdx.x * (int64_t)kEwThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kEwThreads) {
+    const int m = (int)(i / h4), n = (int)(i % h4) * 4;
+    const float* row = partial + (int64_t)m * 2 * H;
+    f32x4 g = *reinterpret_cast<const f32x4*>(row + n), u = *reinterpret_cast<const f32x4*>(row + H + n);
+    for (int sp = 1; sp < splits; ++sp) {
+      g += *reinterpret_cast<const f32x4*>(row + sp * slice + n);
+      u += *reinterpret_cast<const f32x4*>(row + sp * slice + H + n);
+    }
+    float gv[4], uv[4], a[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { gv[r] = al * g[r]; uv[r] = al * u[r]; }
+    if (preact) {
+      char* prow = reinterpret_cast<char*>(preact) + (int64_t)m * 2 * H * esize<T>();
+      store4<T>(prow + (int64_t)n * esize<T>(), gv);
+      store4<T>(prow + (int64_t)(H + n) * esize<T>(), uv);
+    }
+    gated_act<4>(fn, gm, inside, gv, uv, a);
+    store4<T>(reinterpret_cast<char*>(a_out) + ((int64_t)m * H + n) * esize<T>(), a);
+  }
+}
+
 // ---- activation only -------------------------------------------------------------------------
 
 template <typename T>
@@ -175,6 +211,22 @@ hipError_t run_splitk_reduce(DType io, const float* partial, int splits, int M, 
   else
     hipLaunchKernelGGL(splitk_reduce_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, partial, splits, M,
                        N, C0, C1, ldc, c_split, alpha, dev0, dev1, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t run_gated_reduce(DType io, const float* partial, int splits, int M, int H, float alpha,
+                            const float* dev0, const float* dev1, void* preact, void* a, float gate_mult,
+                            int gate_inside, int fn, hipStream_t s) {
+  const int grid = ew_grid((int64_t)M * (H / 4));
+  if (io == DT_BF16)
+    hipLaunchKernelGGL(gated_reduce_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, partial, splits, M, H,
+                       alpha, dev0, dev1, preact, a, gate_mult, gate_inside, fn);
+  else if (io == DT_F16)
+    hipLaunchKernelGGL(gated_reduce_kernel<f16>, dim3(grid), dim3(kEwThreads), 0, s, partial, splits, M, H,
+                       alpha, dev0, dev1, preact, a, gate_mult, gate_inside, fn);
+  else
+    hipLaunchKernelGGL(gated_reduce_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, partial, splits, M, H,
+                       alpha, dev0, dev1, preact, a, gate_mult, gate_inside, fn);
   return hipGetLastError();
 }
 

@@ -26,6 +26,8 @@ enum Epi : int {
 struct GemmArgs {
   int M, N, K;
   const void* A; int64_t lda;
+  // B from two matrices when B1 is set: MN-major B stacked along K (rows k >= b_split from B1,
+  // the [W_gate; W_up] of dx); K-major non-gated B stacked along N (rows n >= b_split from B1)
   const void* B0; const void* B1; int64_t ldb; int b_split;
   void* C0; int64_t ldc0; void* C1; int64_t ldc1; int c_split;
   void* aux; int64_t ld_aux; int half;

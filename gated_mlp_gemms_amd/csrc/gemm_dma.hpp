@@ -267,9 +267,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
         const int n = n0 + (r < half ? r : r - half);
         if (n >= p.N) return nullptr;
         return elem_ptr<T>(r < half ? p.B0 : p.B1, n, p.ldb, 0);
-      } else {
+      } else {   // rows n >= b_split come from B1 when given (stacked [W_gate; W_up])
         const int n = n0 + r;
-        return n < p.N ? elem_ptr<T>(p.B0, n, p.ldb, 0) : nullptr;
+        if (n >= p.N) return nullptr;
+        return (p.B1 != nullptr && n >= p.b_split) ? elem_ptr<T>(p.B1, n - p.b_split, p.ldb, 0)
+                                                   : elem_ptr<T>(p.B0, n, p.ldb, 0);
       }
     });
   } else {

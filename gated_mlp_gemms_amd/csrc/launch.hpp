@@ -37,6 +37,12 @@ hipError_t run_splitk_reduce(DType io, const float* partial, int splits, int M, 
                              void* C1, int64_t ldc, int c_split, float alpha, const float* dev0,
                              const float* dev1, int accumulate, hipStream_t s);
 
+// Split-K finish of the gated up projection: g|u = alpha * sum of the fp32 partials [s][M][2H] in
+// order; g|u -> preact [M, 2H] when non-NULL; a = act(g, u) -> a [M, H].
+hipError_t run_gated_reduce(DType io, const float* partial, int splits, int M, int H, float alpha,
+                            const float* dev0, const float* dev1, void* preact, void* a, float gate_mult,
+                            int gate_inside, int fn, hipStream_t s);
+
 // a[m][n] = act(g = pre[m][n], u = pre[m][H + n]) (gated), or post = f(alpha * pre); fn: ActFn.
 hipError_t run_gated_act(DType io, const void* preact, void* a, int M, int H, float gate_mult,
                          int gate_inside, int fn, hipStream_t s);

@@ -157,7 +157,36 @@ struct WsLayout {
   size_t total = 0;
 };
 
+// Small-M (decode) gated up projection: when the fused gate/up GEMM has fewer tiles than the
+// CUs, run it split along K over the stacked [W_gate; W_up] (N = 2H, 128 x 128 tiles, enough
+// slices for two workgroups per CU) into fp32 partials, and apply the activation in the reduce.
+// Returns splits = 1 when the fused kernel is the better choice.
+Plan plan_gated_split(DType in, int64_t M, int64_t H, int64_t D) {
+  Plan none{};
+  none.splits = 1;
+  if (in != DT_BF16 && in != DT_F16) return none;
+  if (M > 128) return none;   // decode sizes: a single 128-row tile
+  const Plan fused = plan_gemm(in, M, H, D, false, true);
+  const int64_t tm = 1, tn = (2 * H + 127) / 128, tiles = tm * tn;
+  if (fused.grid >= 256 || tiles >= 512) return none;
+  const int64_t want = std::min<int64_t>(16, (512 + tiles - 1) / tiles);
+  const int bk = bk_of(in);
+  const int64_t kps = ((D + want - 1) / want + bk - 1) / bk * bk;
+  const int64_t s = (D + kps - 1) / kps;
+  if (s < 2) return none;
+  Plan p{};
+  p.tile = TILE_128x128;
+  p.splits = (int)s;
+  p.k_per_split = (int)kps;
+  p.tiles_m = (int)tm;
+  p.tiles_n = (int)tn;
+  p.group_m = (int)std::min<int64_t>(tm, 8);
+  p.grid = (int)(tiles * s);
+  return p;
+}
+
 struct Gemms {   // the GEMMs a phase may run, in planning form
+  Plan up_split;      // forward gated up projection split along K (splits = 1: fused instead)
   Plan down;          // forward down projection
   Plan dw_down, dx, dw_up;
 };
@@ -168,6 +197,7 @@ Gemms plan_all(const mlp_desc* d) {
   const bool gated = is_gated(d->act);
   const int64_t M = d->M, D = d->d_in, H = d->hidden, O = d->d_out, P = gated ? 2 * H : H;
   Gemms g;
+  g.up_split = (gated && !d->fp8_fwd) ? plan_gated_split(io, M, H, D) : Plan{TILE_128x128, 1, 0, 0, 0, 0, 0};
   g.down = plan_gemm(fin, M, O, H, true, false);
   g.dw_down = plan_gemm(io, O, H, M, true, false);
   g.dx = plan_gemm(io, M, D, P, true, false);
@@ -185,7 +215,7 @@ WsLayout ws_layout(const mlp_desc* d, int phase) {
   auto take = [&](size_t& at, size_t& sz, size_t bytes) { at = off; sz = bytes; off += round_up(bytes); };
   if (phase == MLP_PHASE_FWD || phase == MLP_PHASE_FWD_INFER) {
     take(L.act, L.act_bytes, (size_t)M * H * (d->fp8_fwd ? 1 : es));
-    take(L.partial, L.partial_bytes, partial_bytes(g.down, M, O));
+    take(L.partial, L.partial_bytes, std::max(partial_bytes(g.down, M, O), partial_bytes(g.up_split, M, 2 * H)));
   } else {
     take(L.act, L.act_bytes, (size_t)M * H * es);
     if (d->recompute) take(L.pre, L.pre_bytes, (size_t)M * P * es);
@@ -315,7 +345,7 @@ GemmArgs base_args(const mlp_desc* d) {
 // Forward GEMM 1: the gated / non-gated / e4m3 ReLU^2 up projection with its activation epilogue.
 // preact_out: where g|u or pre goes (NULL: not kept); act_out: where a / post / post_q goes.
 mlp_status up_projection(const mlp_desc* d, const void* x, const void* wg, const void* wu,
-                         const mlp_fp8* f, void* preact_out, void* act_out, hipStream_t s) {
+                         const mlp_fp8* f, void* preact_out, void* act_out, void* partial, hipStream_t s) {
   const DType io = io_of(d);
   const int64_t M = d->M, D = d->d_in, H = d->hidden;
   GemmArgs a = base_args(d);
@@ -331,6 +361,24 @@ mlp_status up_projection(const mlp_desc* d, const void* x, const void* wg, const
     a.B1 = wu;
     a.ld_aux = 2 * H;
     a.half = (int)H;
+    const Plan ps = plan_all(d).up_split;
+    if (ps.splits > 1) {   // decode-size: split-K partials of [g | u], activation in the reduce
+      GemmArgs b = a;
+      b.M = (int)M;
+      b.N = (int)(2 * H);
+      b.K = (int)D;
+      b.b_split = (int)H;
+      b.tiles_m = ps.tiles_m;
+      b.tiles_n = ps.tiles_n;
+      b.group_m = ps.group_m;
+      b.k_per_split = ps.k_per_split;
+      b.partial = reinterpret_cast<float*>(partial);
+      MLP_TRY(hip_status(run_gemm(io, DT_F32, NT, EPI_PARTIAL, ps.tile, b, ps.grid, s), "gate/up projection"));
+      return hip_status(run_gated_reduce(io, b.partial, ps.splits, (int)M, (int)H, a.alpha, a.alpha_dev0,
+                                         a.alpha_dev1, preact_out, act_out, d->gate_mult,
+                                         d->gate_mode == MLP_GATE_INSIDE, a.act, s),
+                        "gate/up projection reduce");
+    }
     const Plan p = plan_gemm(io, M, H, D, false, true);
     return gemm(io, io, NT, EPI_GATED, p, a, M, H, D, nullptr, s, "gate/up projection");
   }
@@ -379,7 +427,7 @@ mlp_status fwd_impl(const mlp_desc* d, const void* x, const void* wg, const void
   const int64_t M = d->M, H = d->hidden, O = d->d_out;
   {
     StageScope st(MLP_STAGE_UP, s);
-    MLP_TRY(up_projection(d, x, wg, wu, f, infer ? nullptr : saved, act, s));
+    MLP_TRY(up_projection(d, x, wg, wu, f, infer ? nullptr : saved, act, w + L.partial, s));
   }
 
   const DType io = io_of(d);

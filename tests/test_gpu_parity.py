@@ -174,6 +174,27 @@ def test_smallest_problem(act, dtype):
     check_full(w, t, r, "inside")
 
 
+@pytest.mark.parametrize("w", [
+    _w("swiglu", "bf16", 16, 512, 1400, 520, gate_mult=1.125, down_mult=2.0),
+    _w("geglu", "bf16", 100, 1024, 2048, 512, seed=6),
+    _w("swiglu", "f16", 37, 768, 1024, 264, seed=7),
+], ids=lambda w: w.name)
+@pytest.mark.parametrize("mode", ["outside", "inside"])
+def test_decode_size_split_up_projection(w, mode):
+    """At decode sizes (M <= 128, few hidden tiles) the gated up projection runs split along K over
+    the stacked [W_gate; W_up] with the activation applied in the reduce; the training forward
+    (saved g|u), the inference forward and the backward against the oracle."""
+    announce(f"decode split {w.name} {mode}")
+    t = make_inputs(w)
+    r = run(w, t, gate_mode=mode)
+    r.forward()
+    r.forward_infer()
+    r.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(r.out, r.out_infer)
+    check_full(w, t, r, mode)
+
+
 def test_tall_thin_problem():
     """Many tokens through a hidden layer of one 8-wide row: 1 tile column, ragged rows."""
     w = _w("swiglu", "bf16", 1999, 8, 8, 16)
