@@ -159,10 +159,14 @@ constexpr int epilogue_lds_bytes() { return WAVES * epilogue_rows_per_round<WAVE
 
 // acc[i][j]: the MFMA layout of the wave's WM x WN tile (see epilogue()). lds: this
 // workgroup's LDS, at least epilogue_lds_bytes<BN>() bytes, not in use by any wave.
-template <int EPI, typename IoT, int BM, int BN, int MI, int NI, int WAVES>
-__device__ __forceinline__ void epilogue_rows(const GemmArgs& p, f32x16 (&acc)[MI][NI], int m0, int n0,
+template <int EPI, typename IoT, int BM, int BN, int MI, int NI, int WAVES, typename AccV>
+__device__ __forceinline__ void epilogue_rows(const GemmArgs& p, AccV (&acc)[MI][NI], int m0, int n0,
                                               int split, int wm, int wn, int lane, int wave, char* lds) {
   constexpr bool GATED = EPI == EPI_GATED;
+  // 32x32 blocks (16 values per lane: rows l%32, columns 8g + 4(l/32) + r) or 16x16 blocks
+  // (4 values per lane: row l%16, columns 4(l/16) + r)
+  constexpr bool B16 = sizeof(AccV) == 4 * sizeof(float);
+  constexpr int BLK = B16 ? 16 : 32;
   constexpr int WM = BM / (WAVES / 2), WN = BN / 2;
   constexpr int RR = epilogue_rows_per_round<WAVES>();   // rows staged per round
   constexpr int STRIDE = WN * 4 + 16;                 // padded: rows 16 bytes apart in bank space
@@ -170,7 +174,8 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& p, f32x16 (&acc)[M
   constexpr int LPR = UNITS / 8;                      // lanes per row
   constexpr int RPI = 64 / LPR;                       // rows per pass
   static_assert(RR % RPI == 0, "passes must cover a round's rows");
-  const int frow = lane & 31, fhalf = lane >> 5;
+  static_assert(RR <= BLK, "a round stays within one block row");
+  const int frow = lane & (BLK - 1), fhalf = lane >> 5, fq = lane >> 4;
   char* wbuf = lds + wave * RR * STRIDE;
 
   float alpha = p.alpha;
@@ -184,8 +189,8 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& p, f32x16 (&acc)[M
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
-    for (int h = 0; h < 32 / RR; ++h) {
-      const int mrow0 = m0 + wm * WM + i * 32 + h * RR;
+    for (int h = 0; h < BLK / RR; ++h) {
+      const int mrow0 = m0 + wm * WM + i * BLK + h * RR;
       AuxPiece x[RR / RPI];
 #pragma unroll
       for (int pass = 0; pass < RR / RPI; ++pass) {
@@ -196,13 +201,19 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& p, f32x16 (&acc)[M
       // j*32 + 8g + 4*fhalf .. +3 of row (frow - h*RR)
       if (frow / RR == h) {
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
+        for (int j = 0; j < NI; ++j) {
+          if constexpr (B16) {
+            const f32x4 v = {scale * acc[i][j][0], scale * acc[i][j][1], scale * acc[i][j][2], scale * acc[i][j][3]};
+            *reinterpret_cast<f32x4*>(wbuf + (frow - h * RR) * STRIDE + (j * 16 + 4 * fq) * 4) = v;
+          } else {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 v = {scale * acc[i][j][4 * g], scale * acc[i][j][4 * g + 1],
-                             scale * acc[i][j][4 * g + 2], scale * acc[i][j][4 * g + 3]};
-            *reinterpret_cast<f32x4*>(wbuf + (frow - h * RR) * STRIDE + (j * 32 + 8 * g + 4 * fhalf) * 4) = v;
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 v = {scale * acc[i][j][4 * g], scale * acc[i][j][4 * g + 1],
+                               scale * acc[i][j][4 * g + 2], scale * acc[i][j][4 * g + 3]};
+              *reinterpret_cast<f32x4*>(wbuf + (frow - h * RR) * STRIDE + (j * 32 + 8 * g + 4 * fhalf) * 4) = v;
+            }
           }
+        }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): this wave's LDS writes are done
       __builtin_amdgcn_wave_barrier();

@@ -71,6 +71,23 @@ __device__ __forceinline__ void interleave() {
   interleave_seq<NM, ND, NV>(std::make_integer_sequence<int, NM>{});
 }
 
+// Scheduling pattern of a rolling substep: per column block j, its MI MFMAs, then the refill of
+// B fragment j (RB LDS reads) and one of the NRA reads of the next substep's A fragments.
+template <int J, int MI, int RB, int NRA>
+__device__ __forceinline__ void interleave_roll_step() {
+  __builtin_amdgcn_sched_group_barrier(0x008, MI, 0);                            // MFMA
+  __builtin_amdgcn_sched_group_barrier(0x100, RB + (J < NRA ? 1 : 0), 0);       // LDS reads
+}
+template <int MI, int RB, int NRA, int... J>
+__device__ __forceinline__ void interleave_roll_seq(std::integer_sequence<int, J...>) {
+  (interleave_roll_step<J, MI, RB, NRA>(), ...);
+}
+template <int MI, int NI, int RB, int NRA>
+__device__ __forceinline__ void interleave_roll() {
+  static_assert(NRA <= NI, "A reads spread one per column block");
+  interleave_roll_seq<MI, RB, NRA>(std::make_integer_sequence<int, NI>{});
+}
+
 // Bytes of K per operand row in one K-step.
 template <typename T> struct StepGeo;
 template <> struct StepGeo<bf16> { static constexpr int ROWB = 128; };
@@ -145,7 +162,9 @@ struct MNTileDma {
   int krow[kInst];
   bool col_ok[kInst];
 
-  static __device__ __forceinline__ int phys_chunk(int c, int kr) { return c ^ ((kr & 3) << 2); }
+  // k-rows kr .. kr+3 land in distinct 64-byte groups, and k-rows 8 apart (read in the same pass
+  // by the 16x16 fragments) in distinct 32-byte halves of them
+  static __device__ __forceinline__ int phys_chunk(int c, int kr) { return c ^ ((kr & 3) << 2) ^ (((kr >> 3) & 1) << 1); }
 
   // base: element (0, tile column 0) of the first matrix; ld_bytes: its row pitch; ncols:
   // columns of the matrix from tile column 0 on.
@@ -192,6 +211,23 @@ struct MNTileDma {
         (__attribute__((address_space(3))) i16x4*)(tile + off1)));
     return __builtin_shufflevector(v0, v1, 0, 1, 2, 3);
   }
+  // Fragment of the 16-column block at tile column cb for the 16x16x32 MFMA, substep s (32 k):
+  // lane l gets k 8*(l/16) .. +7 of column cb + l%16. Each 16-lane group covers its 8 k with two
+  // transposing reads of four k-rows.
+  static __device__ __forceinline__ u32x4 read16(const char* tile, int cb, int s, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int kr = 32 * s + 8 * g + (i >> 2);
+    const int c = cb + 4 * (i & 3);
+    const int off0 = kr * ROWB + (phys_chunk(c >> 3, kr) << 4) + (c & 7) * 2;
+    const int off1 = off0 + 4 * ROWB;                  // k-row + 4: same (k-row % 4) and (k-row / 8)
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(tile + off0)));
+    const u32x2 v1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(tile + off1)));
+    return __builtin_shufflevector(v0, v1, 0, 1, 2, 3);
+  }
 };
 
 // Stages in the ring: as many as fit the 160 KiB of LDS, at most 4; tiles of 128 x 128 and
@@ -217,13 +253,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
   static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
   constexpr int WGM = WAVES / 2;                     // wave rows; two wave columns
   constexpr int WM = BM / WGM, WN = BN / 2;
-  constexpr int MI = WM / 32, NI = WN / 32;
+  // two waves per SIMD (16-bit types): 16x16x32 MFMA blocks; otherwise 32x32 blocks
+  constexpr bool M16 = WAVES == 8 && ES == 2;
+  constexpr int BLK = M16 ? 16 : 32;
+  constexpr int MI = WM / BLK, NI = WN / BLK;
   static_assert(MI >= 1 && NI >= 1, "tile too small for the wave grid");
   constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
   constexpr int NS = ring_stages(STAGE, BM * BN);
   static_assert(NS >= 2, "the ring needs two stages");
   constexpr bool GATED = EPI == EPI_GATED;
-  constexpr int KMMA = std::is_same<T, e4m3>::value ? 64 : 16;   // bf16 / fp16: 32x32x16
+  constexpr int KMMA = M16 ? 32 : (std::is_same<T, e4m3>::value ? 64 : 16);
   constexpr int NSUB = BK / KMMA;
   constexpr int KC = Mma<T>::kChunks;
   static_assert(NSUB % 2 == 0, "fragment double buffer alternates per substep");
@@ -305,49 +344,62 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
   };
 
   // ---- fragment rows / columns of this lane
-  const int frow = lane & 31, fhalf = lane >> 5;
+  const int frow = lane & (BLK - 1), fhalf = lane >> 5, fq = lane >> 4;
   int a_base[MI], b_base[NI];   // first tile row (K-major) / column (MN-major) of each block
 #pragma unroll
-  for (int i = 0; i < MI; ++i) a_base[i] = wm * WM + i * 32;
+  for (int i = 0; i < MI; ++i) a_base[i] = wm * WM + i * BLK;
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     if constexpr (GATED) {
       constexpr int NH = NI / 2;
-      b_base[j] = j < NH ? wn * (WN / 2) + j * 32 : BN / 2 + wn * (WN / 2) + (j - NH) * 32;
+      b_base[j] = j < NH ? wn * (WN / 2) + j * BLK : BN / 2 + wn * (WN / 2) + (j - NH) * BLK;
     } else {
-      b_base[j] = wn * WN + j * 32;
+      b_base[j] = wn * WN + j * BLK;
     }
   }
 
-  u32x4 fa[2][MI][KC], fb[2][NI][KC];
-  auto read_frags = [&](int stage, int s, int slot) {
+  // B fragments single-buffered for the 256-column 16x16 tiles (register budget): B fragment j
+  // of the next substep is read right after the last MFMA that uses the current one.
+  constexpr bool ROLL = M16 && NI >= 8;
+  u32x4 fa[2][MI][KC], fb[ROLL ? 1 : 2][NI][KC];
+  auto read_a = [&](int stage, int s, int slot) {
     const char* sa = smem + stage * STAGE;
-    const char* sb = sa + A_BYTES;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        if constexpr (A_KMAJ) fa[slot][i][c] = KTileDma<T, BM, WAVES>::read(sa, a_base[i] + frow, Mma<T>::chunk(s, fhalf, c));
+        if constexpr (A_KMAJ && M16) fa[slot][i][c] = KTileDma<T, BM, WAVES>::read(sa, a_base[i] + frow, 4 * s + fq);
+        else if constexpr (A_KMAJ) fa[slot][i][c] = KTileDma<T, BM, WAVES>::read(sa, a_base[i] + frow, Mma<T>::chunk(s, fhalf, c));
+        else if constexpr (M16) fa[slot][i][c] = MNTileDma<BM, WAVES>::read16(sa, a_base[i], s, lane);
         else fa[slot][i][c] = MNTileDma<BM, WAVES>::read(sa, a_base[i], s, lane);
       }
     }
+  };
+  auto read_b = [&](int stage, int s, int slot, int j) {
+    const char* sb = smem + stage * STAGE + A_BYTES;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        if constexpr (B_KMAJ) fb[slot][j][c] = KTileDma<T, BN, WAVES>::read(sb, b_base[j] + frow, Mma<T>::chunk(s, fhalf, c));
-        else fb[slot][j][c] = MNTileDma<BN, WAVES>::read(sb, b_base[j], s, lane);
-      }
+    for (int c = 0; c < KC; ++c) {
+      if constexpr (B_KMAJ && M16) fb[slot][j][c] = KTileDma<T, BN, WAVES>::read(sb, b_base[j] + frow, 4 * s + fq);
+      else if constexpr (B_KMAJ) fb[slot][j][c] = KTileDma<T, BN, WAVES>::read(sb, b_base[j] + frow, Mma<T>::chunk(s, fhalf, c));
+      else if constexpr (M16) fb[slot][j][c] = MNTileDma<BN, WAVES>::read16(sb, b_base[j], s, lane);
+      else fb[slot][j][c] = MNTileDma<BN, WAVES>::read(sb, b_base[j], s, lane);
     }
   };
+  auto read_frags = [&](int stage, int s, int slot) {
+    read_a(stage, s, slot);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) read_b(stage, s, ROLL ? 0 : slot, j);
+  };
 
-  f32x16 acc[MI][NI];
+  using AccV = typename std::conditional<M16, f32x4, f32x16>::type;
+  constexpr int ACC_N = M16 ? 4 : 16;
+  AccV acc[MI][NI];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NI; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < ACC_N; ++r) acc[i][j][r] = 0.0f;
 
   constexpr int N_RD = (A_KMAJ ? MI * KC : 2 * MI) + (B_KMAJ ? NI * KC : 2 * NI);
   constexpr int N_MMA = MI * NI;
@@ -356,8 +408,25 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NI; ++j) Mma<T>::mma(fb[slot][j], fa[slot][i], acc[i][j]);
+      for (int j = 0; j < NI; ++j) {
+        if constexpr (M16) Mma16<T>::mma(fb[ROLL ? 0 : slot][j][0], fa[slot][i][0], acc[i][j]);
+        else Mma<T>::mma(fb[slot][j], fa[slot][i], acc[i][j]);
+      }
   };
+  // ROLL: multiply the substep held in fa[slot] / fb, column block by column block, refilling
+  // B fragment j with substep s of `stage` as soon as its last MFMA is issued
+  auto mma_roll = [&](int slot, int stage, int s) {
+    if constexpr (ROLL) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) Mma16<T>::mma(fb[0][j][0], fa[slot][i][0], acc[i][j]);
+        read_b(stage, s, 0, j);
+      }
+    }
+  };
+  constexpr int RB = B_KMAJ ? KC : 2;             // LDS reads per B fragment
+  constexpr int NRA = (A_KMAJ ? KC : 2) * MI;     // LDS reads of the A fragments of a substep
 
   if (nk > 0) {
 #pragma unroll
@@ -373,9 +442,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     // substeps 0 .. NSUB-2: read substep s+1's fragments while multiplying substep s
 #pragma unroll
     for (int s = 0; s + 1 < NSUB; ++s) {
-      read_frags(cur, s + 1, (s + 1) & 1);
-      mma_all(s & 1);
-      interleave<N_MMA, N_RD, 0>();
+      if constexpr (ROLL) {
+        read_a(cur, s + 1, (s + 1) & 1);
+        mma_roll(s & 1, cur, s + 1);
+        interleave_roll<MI, NI, RB, NRA>();
+      } else {
+        read_frags(cur, s + 1, (s + 1) & 1);
+        mma_all(s & 1);
+        interleave<N_MMA, N_RD, 0>();
+      }
     }
     // last substep: step kt+1 must have landed (NS-2 younger steps may be in flight); after
     // the barrier every wave is done reading this stage, which takes step kt+NS
@@ -384,9 +459,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
     issue(kt + NS, cur);
-    read_frags(nxt, 0, 0);
-    mma_all((NSUB - 1) & 1);
-    interleave<N_MMA, N_RD, N_DMA>();
+    if constexpr (ROLL) {
+      read_a(nxt, 0, 0);
+      mma_roll((NSUB - 1) & 1, nxt, 0);
+      interleave_roll<MI, NI, RB, NRA>();
+    } else {
+      read_frags(nxt, 0, 0);
+      mma_all((NSUB - 1) & 1);
+      interleave<N_MMA, N_RD, N_DMA>();
+    }
     cur = nxt;
   }
   // the trailing zero-fill DMAs have landed and no wave reads the ring any more: its LDS

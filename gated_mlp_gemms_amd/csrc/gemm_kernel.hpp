@@ -104,6 +104,22 @@ template <> struct Mma<f16> {
                                                   __builtin_bit_cast(f16x8, b[0]), acc, 0, 0, 0);
   }
 };
+// 16x16x32 MFMA of the two-wave-per-SIMD kernels (v_mfma_f32_16x16x32_bf16 / _f16): one 16 x 16
+// fp32 block, 4 values per lane; with two waves per SIMD it issues closer to its nominal rate
+// than the 32x32x16 form does.
+template <typename T> struct Mma16;
+template <> struct Mma16<bf16> {
+  static __device__ __forceinline__ void mma(const u32x4& a, const u32x4& b, f32x4& acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   acc, 0, 0, 0);
+  }
+};
+template <> struct Mma16<f16> {
+  static __device__ __forceinline__ void mma(const u32x4& a, const u32x4& b, f32x4& acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                  acc, 0, 0, 0);
+  }
+};
 template <> struct Mma<float> {
   static constexpr int kSub = 4;     // 4 x (4 x K=2) per 32-element stage
   static constexpr int kChunks = 1;
