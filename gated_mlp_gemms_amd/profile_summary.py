@@ -92,7 +92,7 @@ def short_name(name: str) -> str:
         out = "f32" if "DF16bf" in types or types.endswith("f") else ""
         w = f",{waves}w" if waves else ""
         return f"gemm{'' if dma else '_regstaged'}<{t},{lay},{bm}x{bn}{w},{epin}{',' + out + ' out' if out else ''}>"
-    for k in ("splitk_reduce", "gated_act", "relu_sq_kernel", "absmax", "quantize_kernel", "dequant", "zero_f32"):
+    for k in ("splitk_reduce", "gated_reduce", "gated_act", "plain_act", "absmax", "quantize_kernel", "dequant", "zero_f32"):
         if k in name:
             return k
     return name.split("(")[0][:60]
