@@ -120,6 +120,8 @@ struct KTileDma {
     return row * ROWB + ((chunk ^ swz(row)) << 4);
   }
 
+  // row_base(row): the row's address; tile rows past the matrix are given an existing row (their
+  // products only reach output rows that are never stored), so no row needs a zero fill.
   template <typename RowPtr>
   __device__ __forceinline__ void init(int wave, int lane, int kbeg, RowPtr row_base) {
 #pragma unroll
@@ -127,19 +129,31 @@ struct KTileDma {
       const int j = wave * kInst + i;
       const int row = RPI * j + lane / CPR;
       const int c = (lane % CPR) ^ swz(row);
-      const char* b = row_base(row);
       kc[i] = c * E;
-      ptr[i] = b ? b + (int64_t)(kbeg + c * E) * ES : nullptr;
+      ptr[i] = row_base(row) + (int64_t)(kbeg + c * E) * ES;
     }
   }
+  // K-step at k_rel (relative to the split's first k) of a K range k_left long. A step wholly
+  // inside the range (all but the last partial step and the trailing zero steps; a uniform test)
+  // costs one address add per DMA; otherwise chunks past the range read the zero chunk.
   __device__ __forceinline__ void issue(char* tile, int wave, int k_rel, int k_left) const {
+    if (k_rel + ROWB / ES <= k_left) {
 #pragma unroll
-    for (int i = 0; i < kInst; ++i) {
-      const int j = wave * kInst + i;
-      const void* src = (ptr[i] && k_rel + kc[i] < k_left) ? (const void*)(ptr[i] + (int64_t)k_rel * ES)
-                                                           : (const void*)g_zero_chunk;
-      dma16(src, tile + j * 1024);
+      for (int i = 0; i < kInst; ++i) dma16(ptr[i] + (int64_t)k_rel * ES, tile + (wave * kInst + i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kInst; ++i) {
+        const void* src = k_rel + kc[i] < k_left ? (const void*)(ptr[i] + (int64_t)k_rel * ES)
+                                                 : (const void*)g_zero_chunk;
+        dma16(src, tile + (wave * kInst + i) * 1024);
+      }
     }
+  }
+  // DMA i of issue() alone, with a per-lane range check (no branch): for issuing the DMAs one
+  // at a time between MFMAs.
+  __device__ __forceinline__ void issue_i(char* tile, int wave, int i, int k_rel, int k_left) const {
+    const void* src = k_rel + kc[i] < k_left ? (const void*)(ptr[i] + (int64_t)k_rel * ES) : (const void*)g_zero_chunk;
+    dma16(src, tile + (wave * kInst + i) * 1024);
   }
   static __device__ __forceinline__ u32x4 read(const char* tile, int row, int ch) {
     return *reinterpret_cast<const u32x4*>(tile + off(row, ch));
@@ -160,14 +174,15 @@ struct MNTileDma {
   static_assert(kInst >= 1, "tile too narrow");
   const char* ptr[kInst];   // chunk address at K-step 0, as if every k-row were in the first matrix
   int krow[kInst];
-  bool col_ok[kInst];
 
   // k-rows kr .. kr+3 land in distinct 64-byte groups, and k-rows 8 apart (read in the same pass
   // by the 16x16 fragments) in distinct 32-byte halves of them
   static __device__ __forceinline__ int phys_chunk(int c, int kr) { return c ^ ((kr & 3) << 2) ^ (((kr >> 3) & 1) << 1); }
 
   // base: element (0, tile column 0) of the first matrix; ld_bytes: its row pitch; ncols:
-  // columns of the matrix from tile column 0 on.
+  // columns of the matrix from tile column 0 on (a multiple of 8). Chunks of tile columns past
+  // the matrix read its last chunk instead: their products only reach output columns that are
+  // never stored.
   __device__ __forceinline__ void init(int wave, int lane, const char* base, int64_t ld_bytes, int kbeg,
                                        int ncols) {
 #pragma unroll
@@ -175,23 +190,36 @@ struct MNTileDma {
       const int j = wave * kInst + i;
       const int byte = j * 1024 + lane * 16;
       const int kr = byte / ROWB;
-      const int col = phys_chunk((byte % ROWB) >> 4, kr) * 8;   // the XOR is an involution
+      const int col = min(phys_chunk((byte % ROWB) >> 4, kr) * 8, ncols - 8);   // the XOR is an involution
       krow[i] = kr;
-      col_ok[i] = col < ncols;
       ptr[i] = base + (int64_t)(kbeg + kr) * ld_bytes + col * 2;
     }
   }
   // K-step starting at k0 (absolute); step_off: byte offset of this K-step from the first;
   // second: distance from a k-row's address in the first matrix to its address in the second.
+  // A step wholly inside [.., kend) and on one side of k_split (a uniform test) costs one
+  // address add per DMA; otherwise each k-row is placed and range-checked on its own.
   __device__ __forceinline__ void issue(char* tile, int wave, int k0, int kend, int64_t step_off, int k_split,
                                         int64_t second) const {
+    if (k0 + KROWS <= kend && (k0 + KROWS <= k_split || k0 >= k_split)) {
+      const int64_t off = step_off + (k0 >= k_split ? second : 0);
 #pragma unroll
-    for (int i = 0; i < kInst; ++i) {
-      const int j = wave * kInst + i;
-      const int k = k0 + krow[i];
-      const char* s = ptr[i] + step_off + (k >= k_split ? second : 0);
-      dma16((k < kend && col_ok[i]) ? (const void*)s : (const void*)g_zero_chunk, tile + j * 1024);
+      for (int i = 0; i < kInst; ++i) dma16(ptr[i] + off, tile + (wave * kInst + i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kInst; ++i) {
+        const int k = k0 + krow[i];
+        const char* s = ptr[i] + step_off + (k >= k_split ? second : 0);
+        dma16(k < kend ? (const void*)s : (const void*)g_zero_chunk, tile + (wave * kInst + i) * 1024);
+      }
     }
+  }
+  // DMA i of issue() alone, placed and range-checked per lane (no branch)
+  __device__ __forceinline__ void issue_i(char* tile, int wave, int i, int k0, int kend, int64_t step_off, int k_split,
+                                          int64_t second) const {
+    const int k = k0 + krow[i];
+    const char* s = ptr[i] + step_off + (k >= k_split ? second : 0);
+    dma16(k < kend ? (const void*)s : (const void*)g_zero_chunk, tile + (wave * kInst + i) * 1024);
   }
   // Fragment of the 32-column block starting at tile column cb, K substep s (16 k): lane l gets
   // the 8 consecutive k 8*(l/32) .. +7 of column cb + l%32, via two transposing reads of four
@@ -292,8 +320,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
   MNTileDma<BN, WAVES> nb;
   if constexpr (A_KMAJ) {
     ka.init(wave, lane, kbeg, [&](int r) -> const char* {
-      const int m = m0 + r;
-      return m < p.M ? elem_ptr<T>(p.A, m, p.lda, 0) : nullptr;
+      return reinterpret_cast<const char*>(elem_ptr<T>(p.A, min(m0 + r, p.M - 1), p.lda, 0));
     });
   } else {
     na.init(wave, lane, reinterpret_cast<const char*>(elem_ptr<T>(p.A, 0, p.lda, m0)), (int64_t)p.lda * ES, kbeg,
@@ -303,12 +330,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     kb.init(wave, lane, kbeg, [&](int r) -> const char* {
       if constexpr (GATED) {
         const int half = BN / 2;
-        const int n = n0 + (r < half ? r : r - half);
-        if (n >= p.N) return nullptr;
+        const int n = min(n0 + (r < half ? r : r - half), p.N - 1);
         return elem_ptr<T>(r < half ? p.B0 : p.B1, n, p.ldb, 0);
       } else {   // rows n >= b_split come from B1 when given (stacked [W_gate; W_up])
-        const int n = n0 + r;
-        if (n >= p.N) return nullptr;
+        const int n = min(n0 + r, p.N - 1);
         return (p.B1 != nullptr && n >= p.b_split) ? elem_ptr<T>(p.B1, n - p.b_split, p.ldb, 0)
                                                    : elem_ptr<T>(p.B0, n, p.ldb, 0);
       }
@@ -340,6 +365,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
       kb.issue(sb, wave, kt * BK, kend - kbeg);
     } else {
       nb.issue(sb, wave, kbeg + kt * BK, kend, (int64_t)kt * BK * p.ldb * ES, b_split, b_second);
+    }
+  };
+
+  // DMA d (0 .. N_DMA-1: A's, then B's) of issue(kt, stage) alone
+  constexpr int KIA = A_KMAJ ? KTileDma<T, BM, WAVES>::kInst : MNTileDma<BM, WAVES>::kInst;
+  auto issue_one = [&](int kt, int stage, int d) {
+    char* sa = smem + stage * STAGE;
+    char* sb = sa + A_BYTES;
+    if (d < KIA) {
+      if constexpr (A_KMAJ) ka.issue_i(sa, wave, d, kt * BK, kend - kbeg);
+      else na.issue_i(sa, wave, d, kbeg + kt * BK, kend, (int64_t)kt * BK * p.lda * ES, INT_MAX, 0);
+    } else {
+      if constexpr (B_KMAJ) kb.issue_i(sb, wave, d - KIA, kt * BK, kend - kbeg);
+      else nb.issue_i(sb, wave, d - KIA, kbeg + kt * BK, kend, (int64_t)kt * BK * p.ldb * ES, b_split, b_second);
     }
   };
 
@@ -413,15 +452,28 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
         else Mma<T>::mma(fb[slot][j], fa[slot][i], acc[i][j]);
       }
   };
+  // Where the DMAs of step kt+NS go in the substep after the barrier: with both operands
+  // MN-major, spread over the column blocks (every wave issuing its DMAs at once held up the
+  // MFMAs queued behind them: dW GEMMs 6-8 % faster spread); with a K-major A, as one burst
+  // before the substep's first reads (issuing later made these GEMMs 2-4 % slower).
+  constexpr int DMA_COLS = A_KMAJ ? 0 : NI;
   // ROLL: multiply the substep held in fa[slot] / fb, column block by column block, refilling
-  // B fragment j with substep s of `stage` as soon as its last MFMA is issued
-  auto mma_roll = [&](int slot, int stage, int s) {
+  // B fragment j with substep s of `stage` as soon as its last MFMA is issued. kt_dma >= 0 and
+  // DMA_COLS > 0: also issue the DMAs of K-step kt_dma into stage_dma, spread over the first
+  // DMA_COLS column blocks.
+  auto mma_roll = [&](int slot, int stage, int s, int kt_dma, int stage_dma) {
     if constexpr (ROLL) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) Mma16<T>::mma(fb[0][j][0], fa[slot][i][0], acc[i][j]);
         read_b(stage, s, 0, j);
+        if constexpr (DMA_COLS > 0) {
+          if (kt_dma >= 0 && j < DMA_COLS) {
+#pragma unroll
+            for (int d = j * N_DMA / DMA_COLS; d < (j + 1) * N_DMA / DMA_COLS; ++d) issue_one(kt_dma, stage_dma, d);
+          }
+        }
       }
     }
   };
@@ -444,7 +496,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     for (int s = 0; s + 1 < NSUB; ++s) {
       if constexpr (ROLL) {
         read_a(cur, s + 1, (s + 1) & 1);
-        mma_roll(s & 1, cur, s + 1);
+        mma_roll(s & 1, cur, s + 1, -1, 0);
         interleave_roll<MI, NI, RB, NRA>();
       } else {
         read_frags(cur, s + 1, (s + 1) & 1);
@@ -458,12 +510,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     wait_vmcnt<(NS - 2) * N_DMA>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
-    issue(kt + NS, cur);
     if constexpr (ROLL) {
+      if constexpr (DMA_COLS == 0) issue(kt + NS, cur);
       read_a(nxt, 0, 0);
-      mma_roll((NSUB - 1) & 1, nxt, 0);
+      mma_roll((NSUB - 1) & 1, nxt, 0, kt + NS, cur);
       interleave_roll<MI, NI, RB, NRA>();
     } else {
+      issue(kt + NS, cur);
       read_frags(nxt, 0, 0);
       mma_all((NSUB - 1) & 1);
       interleave<N_MMA, N_RD, N_DMA>();
