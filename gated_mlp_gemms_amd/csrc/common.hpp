@@ -51,6 +51,13 @@ template <typename T> struct Bits16;
 template <> struct Bits16<bf16> {
   static __device__ __forceinline__ float to_f32(uint32_t h) { return bf16_bits_to_f32(h); }
   static __device__ __forceinline__ uint32_t from_f32(float f) { return f32_to_bf16_bits(f); }
+  // two at once with gfx950's packed conversion (v_cvt_pk_bf16_f32: nearest even, the same
+  // bits as f32_to_bf16_bits for every non-NaN input; NaN stays NaN)
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+  }
 };
 template <> struct Bits16<f16> {
   static __device__ __forceinline__ float to_f32(uint32_t h) {
@@ -59,11 +66,10 @@ template <> struct Bits16<f16> {
   static __device__ __forceinline__ uint32_t from_f32(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (f16)f);
   }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return from_f32(lo) | (from_f32(hi) << 16); }
 };
 template <typename T>
-__device__ __forceinline__ uint32_t pack16x2(float lo, float hi) {
-  return Bits16<T>::from_f32(lo) | (Bits16<T>::from_f32(hi) << 16);
-}
+__device__ __forceinline__ uint32_t pack16x2(float lo, float hi) { return Bits16<T>::pack2(lo, hi); }
 
 // fp32 -> OCP E4M3 code: nearest, ties to even mantissa, |v| >= 448 saturates to +-448,
 // NaN -> NaN code. Every step below is exact in fp32 except the final rint (the rounding).
