@@ -14,14 +14,21 @@ Follows modded-nanogpt ``gpt.py``:
   in float32 tensors; so does this function;
 * the forward of ``ReLUSqrdMLP`` with fp8 arguments: both forward GEMMs take e4m3 operands with
   per-tensor dequant scales, and relu(pre)^2 is quantized with the delayed post scale before the
-  down projection. The backward runs on the dequantized operands.
+  down projection. The backward runs on the dequantized operands;
+* the backward with fp8 gradients (``relu_sq_fp8_backward_e5m2``): the incoming gradient is
+  quantized to e5m2 with the static scale (FP8_GRAD_SCALE), dpre to e5m2 with the delayed dpre
+  scale (FP8_DPRE_HEADROOM / 57344 times the previous call's max|dpre|), and every backward
+  product takes fp8 operands: the gradients in e5m2, the weights, x and relu(pre)^2 in e4m3
+  (``_mlp_fp8_args`` hands the backward the e4m3 weight caches, the transposed e4m3 x, the
+  gradient and dpre scales and the dpre amax).
 """
 from __future__ import annotations
 
 import numpy as np
 
 from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode
-from .mlp import relu_sq, relu_sq_backward
+from .e5m2 import e5m2_decode, e5m2_encode
+from .mlp import drelu_sq, relu_sq, relu_sq_backward
 
 _F32 = np.float32
 
@@ -76,3 +83,42 @@ def relu_sq_fp8_backward(dout, x_q, s_x, w1_q, s_w1, w2_q, s_w2, down_mult=1.0):
     operands s_x x_q, s_w1 W1_q, s_w2 W2_q."""
     return relu_sq_backward(dout, dequantize(x_q, s_x), dequantize(w1_q, s_w1),
                             dequantize(w2_q, s_w2), down_mult)
+
+
+def quantize_e5m2(v, scale) -> np.ndarray:
+    """e5m2(fp32(v) / fp32(scale)) with the division in float32 (as for e4m3)."""
+    return e5m2_encode(np.asarray(v, dtype=np.float32) / _F32(scale))
+
+
+def relu_sq_fp8_backward_e5m2(dout, x_q, s_x, w1_q, s_w1, w2_q, s_w2, s_post, s_grad, s_dpre,
+                              down_mult=1.0):
+    """Backward of the fp8 ReLU^2 MLP with fp8 gradients, in the order the method takes it:
+
+    1. pre = (s_x x_q)(s_w1 W1_q)^T (the forward's pre-activation, re-derived here);
+    2. dout_hat = s_grad * e5m2(dout / s_grad)                 (static gradient scale);
+    3. dpre = down_mult * (dout_hat (s_w2 W2_q)) * relu^2'(pre);
+    4. dpre_hat = s_dpre * e5m2(dpre / s_dpre)                 (delayed dpre scale);
+    5. post_hat = s_post * e4m3(relu(pre)^2 / s_post)          (the forward's post operand);
+    6. dx = dpre_hat (s_w1 W1_q);  dW1 = dpre_hat^T (s_x x_q);  dW2 = down_mult * dout_hat^T post_hat.
+
+    Returns dict(dx, dw1, dw2, dpre (step 3, before quantization), dpre_amax = max|dpre|,
+    dout_q, dpre_q (the e5m2 codes))."""
+    xh = dequantize(x_q, s_x)
+    w1h = dequantize(w1_q, s_w1)
+    w2h = dequantize(w2_q, s_w2)
+    pre = xh @ w1h.T
+    dout_q = quantize_e5m2(dout, s_grad)
+    gh = e5m2_decode(dout_q) * np.float64(_F32(s_grad))
+    dpre = (down_mult * (gh @ w2h)) * drelu_sq(pre)
+    dpre_q = quantize_e5m2(dpre, s_dpre)
+    ph = e5m2_decode(dpre_q) * np.float64(_F32(s_dpre))
+    post_hat = dequantize(e4m3_encode(relu_sq(pre).astype(np.float32) / _F32(s_post)), s_post)
+    return {
+        "dx": ph @ w1h,
+        "dw1": ph.T @ xh,
+        "dw2": down_mult * (gh.T @ post_hat),
+        "dpre": dpre,
+        "dpre_amax": float(np.max(np.abs(dpre))) if dpre.size else 0.0,
+        "dout_q": dout_q,
+        "dpre_q": dpre_q,
+    }
