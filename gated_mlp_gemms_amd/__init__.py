@@ -13,7 +13,7 @@ import torch
 
 from ._lib import (  # noqa: F401
     LIB_PATH, MLP_ACT_GEGLU, MLP_ACT_GELU_TANH, MLP_ACT_GLU, MLP_ACT_REGLU, MLP_ACT_RELU, MLP_ACT_RELU_SQ,
-    MLP_ACT_SWIGLU, MLP_BF16, MLP_F16, MLP_F32, MLP_GATE_INSIDE, MLP_GATE_OUTSIDE,
+    MLP_ACT_SWIGLU, MLP_BF16, MLP_F16, MLP_F32, MLP_FP8_E4M3, MLP_FP8_E5M2, MLP_GATE_INSIDE, MLP_GATE_OUTSIDE,
     MLP_PHASE_BWD, MLP_PHASE_FWD, MLP_PHASE_FWD_INFER, MlpDesc, MlpError, MlpFp8, check, lib,
 )
 
@@ -27,10 +27,10 @@ _PHASES = {"fwd": MLP_PHASE_FWD, "fwd_infer": MLP_PHASE_FWD_INFER, "bwd": MLP_PH
 
 
 def make_desc(M, d_in, hidden, d_out=None, act="swiglu", dtype=torch.bfloat16, gate_mult=1.0,
-              down_mult=1.0, gate_mode="outside", recompute=False, fp8_fwd=False) -> MlpDesc:
+              down_mult=1.0, gate_mode="outside", recompute=False, fp8_fwd=False, fp8_bwd=False) -> MlpDesc:
     return MlpDesc(int(M), int(d_in), int(hidden), int(d_in if d_out is None else d_out), _ACTS[act],
                    _DTYPES[dtype], float(gate_mult), float(down_mult), _MODES[gate_mode], int(bool(recompute)),
-                   int(bool(fp8_fwd)), 0)
+                   int(bool(fp8_fwd)), int(bool(fp8_bwd)))
 
 
 def _ptr(t):
@@ -49,8 +49,10 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def make_fp8(x_q, w1_q, w2_q, s_x, s_w1, s_w2, s_post=None, post_amax=None) -> MlpFp8:
-    return MlpFp8(*[_ptr(t) for t in (x_q, w1_q, w2_q, s_x, s_w1, s_w2, s_post, post_amax)])
+def make_fp8(x_q, w1_q, w2_q, s_x, s_w1, s_w2, s_post=None, post_amax=None, w1t_q=None, w2t_q=None,
+             s_grad=None, s_dpre=None, dpre_amax=None) -> MlpFp8:
+    return MlpFp8(*[_ptr(t) for t in (x_q, w1_q, w2_q, s_x, s_w1, s_w2, s_post, post_amax, w1t_q, w2t_q,
+                                      s_grad, s_dpre, dpre_amax)])
 
 
 def workspace_bytes(desc: MlpDesc, phase: str) -> int:
@@ -102,6 +104,20 @@ def mlp_quantize_e4m3(src, dst, scale, workspace=None, stream=None):
     st = lib().mlp_quantize_e4m3(_ptr(src), _DTYPES[src.dtype], src.numel(), _ptr(dst), _ptr(scale),
                                  _ptr(workspace), workspace.numel(), _stream(stream))
     check(st, "mlp_quantize_e4m3")
+
+
+def mlp_quantize_fp8(src, fmt, scale, dst=None, dst_t=None, ld_t=None, relu_sq=False, stream=None):
+    """fp8 codes of the bf16 matrix ``src`` [rows, cols] with the given scale (a device fp32
+    scalar): row-major into ``dst`` and / or transposed into ``dst_t`` [cols, ld_t] (ld_t >= rows,
+    a multiple of 16; default rows rounded up to 16; the padding columns are zero). fmt: "e4m3"
+    or "e5m2"."""
+    rows, cols = src.shape
+    if ld_t is None:
+        ld_t = (rows + 15) // 16 * 16
+    f = {"e4m3": MLP_FP8_E4M3, "e5m2": MLP_FP8_E5M2}[fmt]
+    st = lib().mlp_quantize_fp8(_ptr(src), _DTYPES[src.dtype], rows, cols, f, int(bool(relu_sq)), _ptr(scale),
+                                _ptr(dst), _ptr(dst_t), int(ld_t), _stream(stream))
+    check(st, "mlp_quantize_fp8")
 
 
 def mlp_fp8_next_scale(amax: float, prev_scale: float, gain: float, floor: float) -> float:

@@ -13,6 +13,7 @@ MLP_ACT_SWIGLU, MLP_ACT_RELU_SQ, MLP_ACT_GEGLU, MLP_ACT_REGLU, MLP_ACT_GLU, MLP_
 MLP_F32, MLP_BF16, MLP_F16 = 0, 1, 2
 MLP_GATE_OUTSIDE, MLP_GATE_INSIDE = 0, 1
 MLP_PHASE_FWD, MLP_PHASE_FWD_INFER, MLP_PHASE_BWD = 0, 1, 2
+MLP_FP8_E4M3, MLP_FP8_E5M2 = 0, 1
 STAGES = ("up", "down", "recompute", "dact", "dw_down", "dx", "dw_up", "act", "widen")
 
 
@@ -20,7 +21,7 @@ class MlpDesc(C.Structure):
     _fields_ = [
         ("M", C.c_int64), ("d_in", C.c_int64), ("hidden", C.c_int64), ("d_out", C.c_int64),
         ("act", C.c_int32), ("dtype", C.c_int32), ("gate_mult", C.c_float), ("down_mult", C.c_float),
-        ("gate_mode", C.c_int32), ("recompute", C.c_int32), ("fp8_fwd", C.c_int32), ("reserved", C.c_int32),
+        ("gate_mode", C.c_int32), ("recompute", C.c_int32), ("fp8_fwd", C.c_int32), ("fp8_bwd", C.c_int32),
     ]
 
 
@@ -29,6 +30,8 @@ class MlpFp8(C.Structure):
         ("x_q", C.c_void_p), ("w1_q", C.c_void_p), ("w2_q", C.c_void_p),
         ("s_x", C.c_void_p), ("s_w1", C.c_void_p), ("s_w2", C.c_void_p),
         ("s_post", C.c_void_p), ("post_amax", C.c_void_p),
+        ("w1t_q", C.c_void_p), ("w2t_q", C.c_void_p), ("s_grad", C.c_void_p), ("s_dpre", C.c_void_p),
+        ("dpre_amax", C.c_void_p),
     ]
 
 
@@ -41,6 +44,7 @@ _SIGNATURES = {
                           C.POINTER(MlpFp8), _P, C.c_size_t, _P]),
     "mlp_quantize_workspace_bytes": (C.c_size_t, []),
     "mlp_quantize_e4m3": (C.c_int, [_P, C.c_int, C.c_int64, _P, _P, _P, C.c_size_t, _P]),
+    "mlp_quantize_fp8": (C.c_int, [_P, C.c_int, C.c_int64, C.c_int64, C.c_int, C.c_int, _P, _P, _P, C.c_int64, _P]),
     "mlp_fp8_next_scale": (C.c_float, [C.c_float, C.c_float, C.c_float, C.c_float]),
     "mlp_status_string": (C.c_char_p, [C.c_int]),
     "mlp_last_error": (C.c_char_p, []),

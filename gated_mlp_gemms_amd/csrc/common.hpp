@@ -19,6 +19,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct e4m3 { uint8_t bits; };   // OCP FP8 E4M3 storage
+// Operand pair of the fp8-gradient GEMMs: A holds OCP E5M2 codes (a gradient), B E4M3 codes
+// (a weight or activation); both one byte per element.
+struct f8g { uint8_t bits; };
 
 constexpr int kThreads = 256;    // 4 wave64 per workgroup
 constexpr int kWave = 64;
@@ -28,6 +31,7 @@ template <> struct ElemTraits<float> { static constexpr int bytes = 4; };
 template <> struct ElemTraits<bf16>  { static constexpr int bytes = 2; };
 template <> struct ElemTraits<f16>   { static constexpr int bytes = 2; };
 template <> struct ElemTraits<e4m3>  { static constexpr int bytes = 1; };
+template <> struct ElemTraits<f8g>   { static constexpr int bytes = 1; };
 
 // ---- conversions -------------------------------------------------------------------------
 
@@ -88,6 +92,25 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   int ee = e + 7;
   if (mi == 8u) { mi = 0u; ee += 1; }
   return sign | ((uint32_t)ee << 3) | mi;
+}
+
+// fp32 -> OCP E5M2 code: nearest, ties to even mantissa, |v| >= 57344 saturates to +-57344,
+// NaN -> 0x7F. Exact in fp32 up to the final rint, as for e4m3.
+__device__ __forceinline__ uint32_t f32_to_e5m2(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __builtin_fabsf(v);
+  if (a != a) return sign | 0x7fu;
+  if (a >= 57344.0f) return sign | 0x7bu;
+  if (a < 6.103515625e-05f) {                            // below 2^-14: subnormal codes 0..4
+    return sign | (uint32_t)__builtin_rintf(a * 65536.0f);  // a * 2^16 is exact
+  }
+  const int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;   // -14 .. 15
+  const float m = a * __uint_as_float((uint32_t)(127 - e) << 23);  // in [1, 2), exact
+  uint32_t mi = (uint32_t)__builtin_rintf((m - 1.0f) * 4.0f);      // 0..4
+  int ee = e + 15;
+  if (mi == 4u) { mi = 0u; ee += 1; }
+  return sign | ((uint32_t)ee << 2) | mi;
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {

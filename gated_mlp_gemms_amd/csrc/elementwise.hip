@@ -3,6 +3,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <algorithm>
+
 namespace gmlp {
 
 namespace {
@@ -196,7 +198,86 @@ __global__ __launch_bounds__(kEwThreads) void dequant_kernel(const uint8_t* src,
     dst[i] = (uint16_t)(__float_as_uint(e4m3_to_f32(src[i])) >> 16);   // exact: <= 4 significant bits
 }
 
+// fp8 codes of a [rows, cols] matrix, row-major and / or transposed, one 64 x 64 tile at a time
+// through LDS. Loads and row-major stores are 8 elements per lane along a row; the transposed
+// stores are 16 codes (16 source rows) per lane. Source rows past `rows` (up to the transposed
+// leading dimension) quantize to code 0, which pads the transposed output.
+template <bool CODES>
+__global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t rows, int64_t cols, int64_t ld_src,
+                                                      int relu_sq, int e5m2, const float* scale, uint8_t* dst,
+                                                      uint8_t* dst_t, int64_t ld_t, int64_t n_ct, int64_t n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[64][64];
+  const int tid = threadIdx.x;
+  const float sc = CODES ? 1.0f : *scale;
+  for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const int64_t r0 = (t / n_ct) * 64, c0 = (t % n_ct) * 64;
+    const int lc = (tid & 7) * 8;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int lr = (tid >> 3) + 32 * pass;
+      const int64_t r = r0 + lr, c = c0 + lc;
+      uint32_t lo = 0, hi = 0;
+      const bool in = r < rows && c < cols;
+      if (in) {
+        if constexpr (CODES) {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(src) + r * ld_src + c);
+          lo = x[0];
+          hi = x[1];
+        } else {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(src) + r * ld_src + c);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            float v = bf16_bits_to_f32((k & 1) ? (x[k >> 1] >> 16) : (x[k >> 1] & 0xffffu));
+            if (relu_sq) {
+              const float m = fmaxf(v, 0.0f);
+              v = m * m;
+            }
+            const float y = __fdiv_rn(v, sc);
+            const uint32_t q = e5m2 ? f32_to_e5m2(y) : f32_to_e4m3(y);
+            if (k < 4) lo |= q << (8 * k);
+            else hi |= q << (8 * (k - 4));
+          }
+        }
+        if (dst) *reinterpret_cast<u32x2*>(dst + r * cols + c) = u32x2{lo, hi};
+      }
+      *reinterpret_cast<u32x2*>(&tile[lr][lc]) = u32x2{lo, hi};
+    }
+    __syncthreads();
+    if (dst_t) {
+      const int oc = tid >> 2, orow = (tid & 3) * 16;
+      const int64_t c = c0 + oc, r = r0 + orow;
+      if (c < cols && r < ld_t) {
+        u32x4 w = {0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < 16; ++k) w[k >> 2] |= (uint32_t)tile[orow + k][oc] << (8 * (k & 3));
+        *reinterpret_cast<u32x4*>(dst_t + c * ld_t + r) = w;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
+
+hipError_t run_quantize_fp8_2d(DType src_t, const void* src, int64_t rows, int64_t cols, int64_t ld_src,
+                               int relu_sq, int e5m2, const float* scale, void* dst, void* dst_t,
+                               int64_t ld_t, hipStream_t s) {
+  if (rows < 1 || cols < 16 || cols % 16 || (dst_t && (ld_t < rows || ld_t % 16))) return hipErrorInvalidValue;
+  const int64_t cover = dst_t ? ld_t : rows;
+  const int64_t n_ct = (cols + 63) / 64, n_rt = (cover + 63) / 64, n_tiles = n_ct * n_rt;
+  const int grid = (int)std::min<int64_t>(n_tiles, 8192);
+  uint8_t* d = reinterpret_cast<uint8_t*>(dst);
+  uint8_t* dt = reinterpret_cast<uint8_t*>(dst_t);
+  if (src_t == DT_E4M3)
+    hipLaunchKernelGGL(quant2d_kernel<true>, dim3(grid), dim3(256), 0, s, src, rows, cols, ld_src, 0, 0, scale,
+                       d, dt, ld_t, n_ct, n_tiles);
+  else if (src_t == DT_BF16)
+    hipLaunchKernelGGL(quant2d_kernel<false>, dim3(grid), dim3(256), 0, s, src, rows, cols, ld_src, relu_sq, e5m2,
+                       scale, d, dt, ld_t, n_ct, n_tiles);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t run_splitk_reduce(DType io, const float* partial, int splits, int M, int N, void* C0,
                              void* C1, int64_t ldc, int c_split, float alpha, const float* dev0,

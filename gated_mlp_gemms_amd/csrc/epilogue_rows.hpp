@@ -51,7 +51,7 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& p, int m, int n, Au
   if constexpr (EPI == EPI_DGATED) {
     x.a = *reinterpret_cast<const u32x4*>(elem_ptr<IoT>(p.aux, m, p.ld_aux, n));
     x.b = *reinterpret_cast<const u32x4*>(elem_ptr<IoT>(p.aux, m, p.ld_aux, p.half + n));
-  } else if constexpr (EPI == EPI_DACT) {
+  } else if constexpr (EPI == EPI_DACT || EPI == EPI_F8DACT) {
     x.a = *reinterpret_cast<const u32x4*>(elem_ptr<IoT>(p.aux, m, p.ld_aux, n));
   } else if constexpr (EPI == EPI_STORE) {
     if (p.accumulate) {
@@ -142,6 +142,21 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
       const float post = t * t;
       local_amax = fmaxf(local_amax, post);
       const uint32_t q = f32_to_e4m3(__fdiv_rn(post, sp));
+      if (r < 4) lo |= q << (8 * r);
+      else hi |= q << (8 * (r - 4));
+    }
+    *reinterpret_cast<u32x2*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) = u32x2{lo, hi};
+  } else if constexpr (EPI == EPI_F8DACT) {
+    static_assert(ElemTraits<IoT>::bytes == 2, "the pre-activation is read as 16-bit data");
+    float pre[8];
+    unpack16x8<IoT>(x.a, pre);
+    const float sd = *p.s_post;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float dpre = v[r] * (2.0f * fmaxf(pre[r], 0.0f));
+      local_amax = fmaxf(local_amax, __builtin_fabsf(dpre));
+      const uint32_t q = f32_to_e5m2(__fdiv_rn(dpre, sd));
       if (r < 4) lo |= q << (8 * r);
       else hi |= q << (8 * (r - 4));
     }
@@ -240,7 +255,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& p, AccV (&acc)[MI]
       __builtin_amdgcn_wave_barrier();
     }
   }
-  if constexpr (EPI == EPI_F8ACT) {
+  if constexpr (EPI == EPI_F8ACT || EPI == EPI_F8DACT) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) local_amax = fmaxf(local_amax, __shfl_xor(local_amax, off));
     if (lane == 0 && local_amax > 0.0f)

@@ -21,6 +21,9 @@ enum Epi : int {
   EPI_DACT = 5,     // dpost = alpha * acc; pre <- aux; dpre = dpost * f'(pre) -> C0; post -> C1 (flag 2)
   EPI_F8ACT = 6,    // pre = alpha * acc -> aux (bf16, flag 1); post = relu(pre)^2;
                     // C0 = e4m3(post / *s_post); *amax = max(*amax, max post)
+  EPI_F8DACT = 7,   // dpre = alpha * acc * 2 max(pre, 0), pre <- aux (bf16);
+                    // C0 = e5m2(dpre / *s_post) (s_post holds the dpre scale here);
+                    // *amax = max(*amax, max |dpre|)
 };
 
 struct GemmArgs {

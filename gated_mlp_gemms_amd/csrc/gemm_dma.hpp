@@ -93,6 +93,7 @@ template <typename T> struct StepGeo;
 template <> struct StepGeo<bf16> { static constexpr int ROWB = 128; };
 template <> struct StepGeo<f16> { static constexpr int ROWB = 128; };
 template <> struct StepGeo<e4m3> { static constexpr int ROWB = 128; };
+template <> struct StepGeo<f8g> { static constexpr int ROWB = 128; };
 
 // ---- K-major operand: ROWS rows x ROWB bytes per stage -------------------------------------
 // One DMA instruction fills 1 KB = 1024/ROWB rows: lane l -> row (1024/ROWB) j + l / CPR,
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
   constexpr int NS = ring_stages(STAGE, BM * BN);
   static_assert(NS >= 2, "the ring needs two stages");
   constexpr bool GATED = EPI == EPI_GATED;
-  constexpr int KMMA = M16 ? 32 : (std::is_same<T, e4m3>::value ? 64 : 16);
+  constexpr int KMMA = M16 ? 32 : (ES == 1 ? 64 : 16);
   constexpr int NSUB = BK / KMMA;
   constexpr int KC = Mma<T>::kChunks;
   static_assert(NSUB % 2 == 0, "fragment double buffer alternates per substep");

@@ -147,6 +147,24 @@ template <> struct Mma<e4m3> {
   }
 };
 
+// A in e5m2, B in e4m3. The kernel passes the B fragment as the instruction's first source and
+// the A fragment as its second, so the format codes are e4m3 (0) for the first and e5m2 (1) for
+// the second.
+template <> struct Mma<f8g> {
+  static constexpr int kSub = 2;
+  static constexpr int kChunks = 2;
+  static __device__ __forceinline__ int chunk(int s, int half, int c) { return 4 * s + 2 * half + c; }
+  static __device__ __forceinline__ void mma(const u32x4* a, const u32x4* b, f32x16& acc) {
+    i32x8 av, bv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      av[i] = (int)a[0][i]; av[4 + i] = (int)a[1][i];
+      bv[i] = (int)b[0][i]; bv[4 + i] = (int)b[1][i];
+    }
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 1, 0, 127, 0, 127);
+  }
+};
+
 // ---- operand tile loaders ---------------------------------------------------------------------
 
 // K-major operand: ROWS rows of 8 chunks; thread t loads chunk (t % 8) of rows t/8 + 32 i.

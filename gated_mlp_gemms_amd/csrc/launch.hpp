@@ -8,7 +8,8 @@
 
 namespace gmlp {
 
-enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2, DT_F16 = 3 };
+// DT_F8G: the fp8-gradient GEMM operand pair (A e5m2, B e4m3); an input type only.
+enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2, DT_F16 = 3, DT_F8G = 4 };
 enum Layout : int { NT = 0, NN = 1, TN = 2 };   // A K-major/B K-major, A K/B MN, A MN/B MN
 // Tile shapes of the bf16 / e4m3 kernel; _W8 runs the tile with 8 waves (two per SIMD).
 enum TileShape : int {
@@ -30,6 +31,7 @@ hipError_t run_gemm_f16_nn(DType io, int epi, TileShape tile, const GemmArgs& a,
 hipError_t run_gemm_f16_tn(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
 hipError_t run_gemm_f32(Layout layout, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
 hipError_t run_gemm_e4m3_nt(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
+hipError_t run_gemm_f8g_nt(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
 
 // out = alpha * sum_s partial[s] (fixed order), stored as `io` or added into fp32 (accumulate).
 // Rows >= c_split go to C1 (row - c_split).
@@ -54,5 +56,14 @@ hipError_t run_quantize_e4m3(DType src_t, const void* src, int64_t n, void* dst,
                              float* ws, hipStream_t s);
 // Exact e4m3 -> bf16 widening (every e4m3 value is a bf16 value).
 hipError_t run_dequant_e4m3_bf16(const void* src, void* dst, int64_t n, hipStream_t s);
+
+// fp8 codes of a [rows, cols] row-major matrix (leading dimension ld_src elements), in row-major
+// form (dst, leading dimension cols; may be NULL) and transposed (dst_t [cols, ld_t], ld_t >= rows
+// a multiple of 16, columns rows .. ld_t-1 zero; may be NULL). src_t: DT_BF16 (value v), or
+// DT_E4M3 for existing codes (copied, no scale). relu_sq: quantize max(v, 0)^2 instead of v.
+// e5m2: OCP E5M2 codes, else E4M3; code = fmt(v / *scale). cols must be a multiple of 16.
+hipError_t run_quantize_fp8_2d(DType src_t, const void* src, int64_t rows, int64_t cols, int64_t ld_src,
+                               int relu_sq, int e5m2, const float* scale, void* dst, void* dst_t,
+                               int64_t ld_t, hipStream_t s);
 
 }  // namespace gmlp

@@ -102,17 +102,18 @@ const TileInfo kTiles[] = {
     {TILE_128x128, 128, 128, 2, 0.36},
 };
 
-int bk_of(DType in) { return in == DT_E4M3 ? 128 : (in == DT_F32 ? 32 : 64); }
+bool is_fp8(DType in) { return in == DT_E4M3 || in == DT_F8G; }
+int bk_of(DType in) { return is_fp8(in) ? 128 : (in == DT_F32 ? 32 : 64); }
 
 // gated: N counts hidden units and a tile covers bn/2 of them (gate + up rows).
 Plan plan_gemm(DType in, int64_t M, int64_t N, int64_t K, bool allow_split, bool gated) {
   const int bk = bk_of(in);
-  const double per_cu = (in == DT_E4M3 ? 2.0 : in == DT_F32 ? 1.0 / 16.0 : 1.0) * 9.83e12;
+  const double per_cu = (is_fp8(in) ? 2.0 : in == DT_F32 ? 1.0 / 16.0 : 1.0) * 9.83e12;
   Plan best{};
   double best_t = 1e300;
   for (const TileInfo& ti : kTiles) {
     if (in == DT_F32 && ti.t != TILE_128x128) continue;
-    if (in == DT_E4M3 && (ti.t == TILE_256x256_W8 || ti.t == TILE_256x128_W8)) continue;
+    if (is_fp8(in) && (ti.t == TILE_256x256_W8 || ti.t == TILE_256x128_W8)) continue;
     const int64_t bn_units = gated ? ti.bn / 2 : ti.bn;
     const int64_t tm = (M + ti.bm - 1) / ti.bm, tn = (N + bn_units - 1) / bn_units;
     const int max_split = allow_split ? 16 : 1;
@@ -153,9 +154,15 @@ struct WsLayout {
   size_t xq = 0, xq_bytes = 0;          // widened e4m3 operands of the fp8 backward
   size_t w1q = 0, w1q_bytes = 0;
   size_t w2q = 0, w2q_bytes = 0;
+  // fp8-gradient backward: e5m2 dout (row-major, transposed), e5m2 dpre (row-major,
+  // transposed), e4m3 relu(pre)^2 and x transposed; transposes have M padded to Mp
+  size_t gq = 0, gq_bytes = 0, gt = 0, gt_bytes = 0, pq = 0, pq_bytes = 0, pt = 0, pt_bytes = 0;
+  size_t postt = 0, postt_bytes = 0, xt = 0, xt_bytes = 0;
   size_t partial = 0, partial_bytes = 0;
   size_t total = 0;
 };
+
+int64_t pad16(int64_t v) { return (v + 15) / 16 * 16; }
 
 // Small-M (decode) gated up projection: when the fused gate/up GEMM has fewer tiles than the
 // CUs, run it split along K over the stacked [W_gate; W_up] (N = 2H, 128 x 128 tiles, enough
@@ -199,6 +206,13 @@ Gemms plan_all(const mlp_desc* d) {
   Gemms g;
   g.up_split = (gated && !d->fp8_fwd) ? plan_gated_split(io, M, H, D) : Plan{TILE_128x128, 1, 0, 0, 0, 0, 0};
   g.down = plan_gemm(fin, M, O, H, true, false);
+  if (d->fp8_bwd) {   // every backward product on fp8 operands; the token dimension padded
+    const int64_t Mp = pad16(M);
+    g.dw_down = plan_gemm(DT_F8G, O, H, Mp, true, false);
+    g.dx = plan_gemm(DT_F8G, M, D, H, true, false);
+    g.dw_up = plan_gemm(DT_F8G, H, D, Mp, true, false);
+    return g;
+  }
   g.dw_down = plan_gemm(io, O, H, M, true, false);
   g.dx = plan_gemm(io, M, D, P, true, false);
   g.dw_up = plan_gemm(io, P, D, M, true, false);
@@ -216,6 +230,18 @@ WsLayout ws_layout(const mlp_desc* d, int phase) {
   if (phase == MLP_PHASE_FWD || phase == MLP_PHASE_FWD_INFER) {
     take(L.act, L.act_bytes, (size_t)M * H * (d->fp8_fwd ? 1 : es));
     take(L.partial, L.partial_bytes, std::max(partial_bytes(g.down, M, O), partial_bytes(g.up_split, M, 2 * H)));
+  } else if (d->fp8_bwd) {
+    const int64_t Mp = pad16(M);
+    if (d->recompute) take(L.pre, L.pre_bytes, (size_t)M * H * es);
+    take(L.gq, L.gq_bytes, (size_t)M * O);
+    take(L.gt, L.gt_bytes, (size_t)O * Mp);
+    take(L.pq, L.pq_bytes, (size_t)M * H);
+    take(L.pt, L.pt_bytes, (size_t)H * Mp);
+    take(L.postt, L.postt_bytes, (size_t)H * Mp);
+    take(L.xt, L.xt_bytes, (size_t)D * Mp);
+    const size_t pb = std::max({partial_bytes(g.dw_down, O, H), partial_bytes(g.dx, M, D),
+                                partial_bytes(g.dw_up, H, D)});
+    take(L.partial, L.partial_bytes, pb);
   } else {
     take(L.act, L.act_bytes, (size_t)M * H * es);
     if (d->recompute) take(L.pre, L.pre_bytes, (size_t)M * P * es);
@@ -249,9 +275,10 @@ mlp_status check_desc(const mlp_desc* d) {
     return fail(MLP_ERR_INVALID_ARG, "dtype %d is not an mlp_dtype", d->dtype);
   if (d->gate_mode != MLP_GATE_OUTSIDE && d->gate_mode != MLP_GATE_INSIDE)
     return fail(MLP_ERR_INVALID_ARG, "gate_mode %d is not an mlp_gate_mode", d->gate_mode);
-  if ((d->recompute != 0 && d->recompute != 1) || (d->fp8_fwd != 0 && d->fp8_fwd != 1))
-    return fail(MLP_ERR_INVALID_ARG, "recompute and fp8_fwd must be 0 or 1");
-  if (d->reserved != 0) return fail(MLP_ERR_INVALID_ARG, "reserved must be 0");
+  if ((d->recompute != 0 && d->recompute != 1) || (d->fp8_fwd != 0 && d->fp8_fwd != 1) ||
+      (d->fp8_bwd != 0 && d->fp8_bwd != 1))
+    return fail(MLP_ERR_INVALID_ARG, "recompute, fp8_fwd and fp8_bwd must be 0 or 1");
+  if (d->fp8_bwd && !d->fp8_fwd) return fail(MLP_ERR_INVALID_ARG, "fp8_bwd needs fp8_fwd");
   if (!isfinite(d->gate_mult) || !isfinite(d->down_mult))
     return fail(MLP_ERR_INVALID_ARG, "gate_mult and down_mult must be finite");
   if (d->fp8_fwd && (d->act != MLP_ACT_RELU_SQ || d->dtype != MLP_BF16))
@@ -291,6 +318,16 @@ mlp_status check_fp8(const mlp_desc* d, const mlp_fp8* f, bool fwd) {
   if (fwd) {
     MLP_TRY(need_ptr(f->s_post, "fp8->s_post", false));
     MLP_TRY(need_ptr(f->post_amax, "fp8->post_amax", false));
+  } else if (d->fp8_bwd) {
+    MLP_TRY(need_ptr(f->w1t_q, "fp8->w1t_q"));
+    MLP_TRY(need_ptr(f->w2t_q, "fp8->w2t_q"));
+    MLP_TRY(need_ptr(f->s_post, "fp8->s_post", false));
+    MLP_TRY(need_ptr(f->s_grad, "fp8->s_grad", false));
+    MLP_TRY(need_ptr(f->s_dpre, "fp8->s_dpre", false));
+    MLP_TRY(need_ptr(f->dpre_amax, "fp8->dpre_amax", false));
+  } else {
+    MLP_TRY(need_null(f->w1t_q, "fp8->w1t_q", "unless desc->fp8_bwd"));
+    MLP_TRY(need_null(f->w2t_q, "fp8->w2t_q", "unless desc->fp8_bwd"));
   }
   return MLP_OK;
 }
@@ -449,11 +486,119 @@ mlp_status fwd_impl(const mlp_desc* d, const void* x, const void* wg, const void
   return gemm(fin, io, NT, EPI_STORE, p, b, M, O, H, w + L.partial, s, "down projection");
 }
 
+// Backward with fp8 gradients (ReLU^2, see mlp_fp8): dout -> e5m2 (row-major for the d-act
+// product, transposed for dW2); dpre_q = e5m2(dm (dout_q W2) 2 relu(pre) / s_dpre) from the
+// e5m2 x e4m3 product against the transposed W2 cache; dx = dpre_q W1 against the transposed W1
+// cache; dW1 = dpre_q^T x_q and dW2 = dm dout_q^T post_q from transposed copies (token dimension
+// zero-padded to a multiple of 16), so every product reads both operands along K.
+mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void* dx, void* dw1, void* dw2,
+                   int grad_accum, const mlp_fp8* f, char* w, const WsLayout& L, const Gemms& G, hipStream_t s) {
+  const int64_t M = d->M, D = d->d_in, H = d->hidden, O = d->d_out, Mp = pad16(M);
+  const DType gio = grad_accum ? DT_F32 : DT_BF16;
+  const bool need_dpre = dx != nullptr || dw1 != nullptr;
+
+  // pre-activation: saved by the forward, or recomputed with the forward's own e4m3 product
+  // (same plan, same bits)
+  const void* pre = saved;
+  if (d->recompute) {
+    GemmArgs a = base_args(d);
+    a.A = f->x_q;
+    a.lda = D;
+    a.B0 = f->w1_q;
+    a.ldb = D;
+    a.C0 = w + L.pre;
+    a.ldc0 = H;
+    a.alpha_dev0 = f->s_x;
+    a.alpha_dev1 = f->s_w1;
+    const Plan p = plan_gemm(DT_E4M3, M, H, D, false, false);
+    StageScope st(MLP_STAGE_RECOMPUTE, s);
+    MLP_TRY(gemm(DT_E4M3, DT_BF16, NT, EPI_STORE, p, a, M, H, D, nullptr, s, "recompute pre-activation"));
+    pre = w + L.pre;
+  }
+  void* gq = w + L.gq;
+  void* gt = w + L.gt;
+  void* pq = w + L.pq;
+  if (need_dpre) {   // dpre_q = e5m2(dm (dout_q W2) 2 relu(pre) / s_dpre), max|dpre| -> dpre_amax
+    StageScope st(MLP_STAGE_DACT, s);
+    MLP_TRY(hip_status(run_quantize_fp8_2d(DT_BF16, dout, M, O, O, 0, 1, f->s_grad, gq, dw2 ? gt : nullptr, Mp, s),
+                       "quantize dout"));
+    GemmArgs a = base_args(d);
+    a.A = gq;
+    a.lda = O;
+    a.B0 = f->w2t_q;
+    a.ldb = O;
+    a.C0 = pq;
+    a.ldc0 = H;
+    a.aux = const_cast<void*>(pre);
+    a.ld_aux = H;
+    a.alpha = d->down_mult;
+    a.alpha_dev0 = f->s_grad;
+    a.alpha_dev1 = f->s_w2;
+    a.s_post = f->s_dpre;
+    a.amax = f->dpre_amax;
+    const Plan p = plan_gemm(DT_F8G, M, H, O, false, false);
+    MLP_TRY(gemm(DT_F8G, DT_BF16, NT, EPI_F8DACT, p, a, M, H, O, nullptr, s, "fp8 d-activation GEMM"));
+  } else if (dw2) {
+    StageScope st(MLP_STAGE_DW_DOWN, s);
+    MLP_TRY(hip_status(run_quantize_fp8_2d(DT_BF16, dout, M, O, O, 0, 1, f->s_grad, nullptr, gt, Mp, s),
+                       "quantize dout"));
+  }
+  if (dw2) {   // dW2 (+)= dm dout_q^T post_q, post_q = e4m3(relu(pre)^2 / s_post)
+    StageScope st(MLP_STAGE_DW_DOWN, s);
+    MLP_TRY(hip_status(run_quantize_fp8_2d(DT_BF16, pre, M, H, H, 1, 0, f->s_post, nullptr, w + L.postt, Mp, s),
+                       "quantize relu(pre)^2"));
+    GemmArgs a = base_args(d);
+    a.A = gt;
+    a.lda = Mp;
+    a.B0 = w + L.postt;
+    a.ldb = Mp;
+    a.C0 = dw2;
+    a.ldc0 = H;
+    a.alpha = d->down_mult;
+    a.alpha_dev0 = f->s_grad;
+    a.alpha_dev1 = f->s_post;
+    a.accumulate = grad_accum;
+    MLP_TRY(gemm(DT_F8G, gio, NT, EPI_STORE, G.dw_down, a, O, H, Mp, w + L.partial, s, "fp8 dW_down"));
+  }
+  if (dx) {   // dx = dpre_q W1
+    GemmArgs a = base_args(d);
+    a.A = pq;
+    a.lda = H;
+    a.B0 = f->w1t_q;
+    a.ldb = H;
+    a.C0 = dx;
+    a.ldc0 = D;
+    a.alpha_dev0 = f->s_dpre;
+    a.alpha_dev1 = f->s_w1;
+    StageScope st(MLP_STAGE_DX, s);
+    MLP_TRY(gemm(DT_F8G, DT_BF16, NT, EPI_STORE, G.dx, a, M, D, H, w + L.partial, s, "fp8 dx"));
+  }
+  if (dw1) {   // dW1 (+)= dpre_q^T x_q
+    StageScope st(MLP_STAGE_DW_UP, s);
+    MLP_TRY(hip_status(run_quantize_fp8_2d(DT_E4M3, pq, M, H, H, 0, 0, nullptr, nullptr, w + L.pt, Mp, s),
+                       "transpose dpre_q"));
+    MLP_TRY(hip_status(run_quantize_fp8_2d(DT_E4M3, f->x_q, M, D, D, 0, 0, nullptr, nullptr, w + L.xt, Mp, s),
+                       "transpose x_q"));
+    GemmArgs a = base_args(d);
+    a.A = w + L.pt;
+    a.lda = Mp;
+    a.B0 = w + L.xt;
+    a.ldb = Mp;
+    a.C0 = dw1;
+    a.ldc0 = D;
+    a.alpha_dev0 = f->s_dpre;
+    a.alpha_dev1 = f->s_x;
+    a.accumulate = grad_accum;
+    MLP_TRY(gemm(DT_F8G, gio, NT, EPI_STORE, G.dw_up, a, H, D, Mp, w + L.partial, s, "fp8 dW1"));
+  }
+  return MLP_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int mlp_abi_version(void) { return 1; }
+int mlp_abi_version(void) { return 2; }
 
 const char* mlp_status_string(int st) {
   switch (st) {
@@ -521,6 +666,7 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
   }
   if (grad_accum != 0 && grad_accum != 1) return fail(MLP_ERR_INVALID_ARG, "grad_accum must be 0 or 1");
   MLP_TRY(check_fp8(d, f, false));
+  if (d->fp8_bwd) MLP_TRY(need_null(dpreact, "dpreact", "with fp8_bwd (dpre stays e5m2 in the workspace)"));
   MLP_TRY(check_ws(d, MLP_PHASE_BWD, ws, ws_bytes));
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -531,6 +677,7 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
   const DType io = io_of(d);
   const DType gio = grad_accum ? DT_F32 : io;
   const int64_t M = d->M, D = d->d_in, H = d->hidden, O = d->d_out, P = gated ? 2 * H : H;
+  if (d->fp8_bwd) return bwd_fp8(d, dout, saved, dx, dwg, dwd, grad_accum, f, w, L, G, s);
 
   // e4m3 path: the backward reads the exact bf16 widening of the forward's operands; their
   // scales enter each GEMM's epilogue.
@@ -674,6 +821,26 @@ mlp_status mlp_quantize_e4m3(const void* src, int dtype, int64_t n, void* dst, f
                     "quantize");
 }
 
+mlp_status mlp_quantize_fp8(const void* src, int dtype, int64_t rows, int64_t cols, int fmt, int relu_sq,
+                            const float* scale, void* dst, void* dst_t, int64_t ld_t, void* stream) {
+  if (dtype != MLP_BF16) return fail(MLP_ERR_UNSUPPORTED, "mlp_quantize_fp8 reads bf16 sources only");
+  if (fmt != MLP_FP8_E4M3 && fmt != MLP_FP8_E5M2) return fail(MLP_ERR_INVALID_ARG, "fmt %d is not an mlp_fp8_format", fmt);
+  if (relu_sq != 0 && relu_sq != 1) return fail(MLP_ERR_INVALID_ARG, "relu_sq must be 0 or 1");
+  if (rows < 1 || cols < 1 || rows >= ((int64_t)1 << 31) || cols >= ((int64_t)1 << 31))
+    return fail(MLP_ERR_INVALID_ARG, "rows and cols must be in [1, 2^31)");
+  if (cols % 16) return fail(MLP_ERR_ALIGNMENT, "cols must be a multiple of 16");
+  if (!dst && !dst_t) return fail(MLP_ERR_INVALID_ARG, "dst and dst_t are both NULL");
+  if (dst_t && (ld_t < rows || ld_t % 16))
+    return fail(MLP_ERR_INVALID_ARG, "ld_t must be >= rows and a multiple of 16");
+  MLP_TRY(need_ptr(src, "src"));
+  MLP_TRY(need_ptr(scale, "scale", false));
+  if (dst) MLP_TRY(need_ptr(dst, "dst"));
+  if (dst_t) MLP_TRY(need_ptr(dst_t, "dst_t"));
+  return hip_status(run_quantize_fp8_2d(DT_BF16, src, rows, cols, cols, relu_sq, fmt == MLP_FP8_E5M2, scale, dst,
+                                        dst_t, dst_t ? ld_t : 0, reinterpret_cast<hipStream_t>(stream)),
+                    "quantize fp8");
+}
+
 float mlp_fp8_next_scale(float amax, float prev_scale, float gain, float floor_) {
   float a = (isnan(amax) || isinf(amax)) ? 0.0f : amax;
   if (a > 1e12f) a = 1e12f;
@@ -701,6 +868,9 @@ hipError_t run_gemm(DType in, DType io, Layout layout, int epi, TileShape tile, 
     case DT_F32: return run_gemm_f32(layout, epi, tile, a, grid, s);
     case DT_E4M3:
       if (layout == NT) return run_gemm_e4m3_nt(io, epi, tile, a, grid, s);
+      return hipErrorInvalidValue;
+    case DT_F8G:
+      if (layout == NT) return run_gemm_f8g_nt(io, epi, tile, a, grid, s);
       return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;

@@ -10,23 +10,28 @@ from __future__ import annotations
 import torch
 
 from . import (GATED_ACTS, make_desc, make_fp8, mlp_bwd, mlp_fp8_next_scale, mlp_fwd, mlp_fwd_infer,
-               mlp_quantize_e4m3, workspace_bytes)
+               mlp_quantize_e4m3, mlp_quantize_fp8, workspace_bytes)
 
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
 POST_HEADROOM = 1.03   # delayed post scale = amax * 1.03 / 448, floor 1e-6
 POST_FLOOR = 1e-6
+GRAD_SCALE = 2.0 ** -6  # static e5m2 scale of dout; also the bootstrap dpre scale
+DPRE_HEADROOM = 1.25    # delayed dpre scale = amax * 1.25 / 57344, floor 1e-12
+DPRE_FLOOR = 1e-12
 
 
 class MlpRunner:
     def __init__(self, *, act, dtype, M, d_in, hidden, d_out, gate_mult=1.0, down_mult=1.0,
-                 gate_mode="outside", recompute=False, grad_accum=False, fp8_fwd=False,
+                 gate_mode="outside", recompute=False, grad_accum=False, fp8_fwd=False, fp8_bwd=False,
                  tensors: dict, device="cuda", dpreact_in_place=False):
         self.gated = act in GATED_ACTS
         self.grad_accum = grad_accum
         self.fp8 = fp8_fwd
+        self.fp8_bwd = fp8_bwd
         tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}.get(dtype, dtype)
         self.desc = make_desc(M, d_in, hidden, d_out, act, tdt, gate_mult, down_mult, gate_mode,
-                              recompute, fp8_fwd)
+                              recompute, fp8_fwd, fp8_bwd)
         dev = torch.device(device)
         up = {k: v.to(dev) for k, v in tensors.items()}
         self.t = up
@@ -59,13 +64,20 @@ class MlpRunner:
             self.x_q = torch.empty(M, d_in, dtype=torch.uint8, device=dev)
             self.w1_q = torch.empty(hidden, d_in, dtype=torch.uint8, device=dev)
             self.w2_q = torch.empty(d_out, hidden, dtype=torch.uint8, device=dev)
-            # one fp32 slot each: s_x, s_w1, s_w2, s_post, post_amax
-            self.scales = torch.zeros(5, dtype=torch.float32, device=dev)
+            # one fp32 slot each: s_x, s_w1, s_w2, s_post, post_amax, s_grad, s_dpre, dpre_amax
+            self.scales = torch.zeros(8, dtype=torch.float32, device=dev)
             self.scales[3] = 1.0              # bootstrap post scale
+            self.scales[5] = GRAD_SCALE
+            self.scales[6] = GRAD_SCALE       # bootstrap dpre scale
             self.ws_q = torch.empty(256, dtype=torch.uint8, device=dev)
             s = self.scales
-            self.fp8_args = make_fp8(self.x_q, self.w1_q, self.w2_q, s[0:1].data_ptr(), s[1:2].data_ptr(),
-                                     s[2:3].data_ptr(), s[3:4].data_ptr(), s[4:5].data_ptr())
+            sp = [s[i:i + 1].data_ptr() for i in range(8)]
+            extra = {}
+            if fp8_bwd:   # transposed e4m3 weight caches (the page's column-major copies)
+                self.w1t_q = torch.empty(d_in, hidden, dtype=torch.uint8, device=dev)
+                self.w2t_q = torch.empty(hidden, d_out, dtype=torch.uint8, device=dev)
+                extra = dict(w1t_q=self.w1t_q, w2t_q=self.w2t_q, s_grad=sp[5], s_dpre=sp[6], dpre_amax=sp[7])
+            self.fp8_args = make_fp8(self.x_q, self.w1_q, self.w2_q, sp[0], sp[1], sp[2], sp[3], sp[4], **extra)
 
     # ---- steps
     def quantize(self):
@@ -74,6 +86,17 @@ class MlpRunner:
         mlp_quantize_e4m3(self.x, self.x_q, s[0:1], self.ws_q)
         mlp_quantize_e4m3(self.w_gate, self.w1_q, s[1:2], self.ws_q)
         mlp_quantize_e4m3(self.w_down, self.w2_q, s[2:3], self.ws_q)
+        if self.fp8_bwd:
+            mlp_quantize_fp8(self.w_gate, "e4m3", s[1:2], dst_t=self.w1t_q, ld_t=self.w_gate.shape[0])
+            mlp_quantize_fp8(self.w_down, "e4m3", s[2:3], dst_t=self.w2t_q, ld_t=self.w_down.shape[0])
+
+    def refresh_dpre_scale(self):
+        """Host side of the delayed dpre scale: next = max(amax * 1.25/57344, 1e-12), kept when
+        amax is 0; amax is cleared. Synchronizes (reads amax)."""
+        amax = float(self.scales[7].item())
+        prev = float(self.scales[6].item())
+        self.scales[6] = mlp_fp8_next_scale(amax, prev, DPRE_HEADROOM / E5M2_MAX, DPRE_FLOOR)
+        self.scales[7] = 0.0
 
     def refresh_post_scale(self):
         """Host side of the delayed post scale: next = max(amax * 1.03/448, 1e-6), kept when
@@ -93,7 +116,7 @@ class MlpRunner:
 
     def backward(self, dx=True, dw_gate=True, dw_down=True, dpreact=True):
         mlp_bwd(self.desc, self.dout, self.x, self.w_gate, self.w_up, self.w_down, self.saved,
-                self.dpreact if dpreact else None, self.dx if dx else None,
+                self.dpreact if (dpreact and not self.fp8_bwd) else None, self.dx if dx else None,
                 self.dw_gate if dw_gate else None, self.dw_up if dw_gate else None,
                 self.dw_down if dw_down else None, self.grad_accum, self.fp8_args, self.ws_bwd)
 
@@ -120,7 +143,8 @@ class MlpRunner:
 
 def runner_for(w, tensors, device="cuda", **kw) -> MlpRunner:
     """A runner for a workload description with fields act, dtype, M, d_in, hidden, d_out,
-    gate_mult, down_mult, recompute, grad_accum, fp8_fwd."""
+    gate_mult, down_mult, recompute, grad_accum, fp8_fwd (and optionally fp8_bwd)."""
     return MlpRunner(act=w.act, dtype=w.dtype, M=w.M, d_in=w.d_in, hidden=w.hidden, d_out=w.d_out,
                      gate_mult=w.gate_mult, down_mult=w.down_mult, recompute=w.recompute,
-                     grad_accum=w.grad_accum, fp8_fwd=w.fp8_fwd, tensors=tensors, device=device, **kw)
+                     grad_accum=w.grad_accum, fp8_fwd=w.fp8_fwd, fp8_bwd=getattr(w, "fp8_bwd", False),
+                     tensors=tensors, device=device, **kw)

@@ -85,7 +85,8 @@ typedef struct mlp_desc {
   int32_t gate_mode;  /* mlp_gate_mode */
   int32_t recompute;  /* 1: nothing is saved; mlp_bwd recomputes the pre-activation from x */
   int32_t fp8_fwd;    /* 1: e4m3 forward GEMMs (ReLU^2, bf16 only); see mlp_fp8 */
-  int32_t reserved;   /* must be 0 */
+  int32_t fp8_bwd;    /* 1: fp8 backward GEMMs with e5m2 gradients (needs fp8_fwd); see mlp_fp8.
+                       * The forward ignores it. */
 } mlp_desc;
 
 /*
@@ -96,16 +97,36 @@ typedef struct mlp_desc {
  * *post_amax (so the host can form the next s_post with mlp_fp8_next_scale). All pointers are
  * device pointers; the scales are single floats.
  */
+/*
+ * With desc->fp8_bwd the backward runs every product in fp8 too (modded-nanogpt gpt.py: FP8
+ * MLP constants FP8_GRAD_SCALE and FP8_DPRE_HEADROOM, init_mlp_fp8's weight caches and
+ * _mlp_fp8_args): dout is quantized to e5m2 with the static scale *s_grad; dpre = down_mult *
+ * (dout_q W2) * 2 relu(pre) is quantized to e5m2 with the delayed scale *s_dpre, and its
+ * max|dpre| is max-reduced into *dpre_amax (the host forms the next s_dpre with
+ * mlp_fp8_next_scale, gain 1.25/57344, floor 1e-12); dx = dpre_q W1, dW1 = dpre_q^T x_q and
+ * dW2 = down_mult * dout_q^T post_q with post_q = e4m3(relu(pre)^2 / *s_post). The products
+ * take the transposed weight caches w1t_q / w2t_q (the same codes as w1_q / w2_q, transposed:
+ * the page's column-major caches) so that every fp8 GEMM reads both operands along K.
+ */
 typedef struct mlp_fp8 {
   const void* x_q;      /* e4m3 [M, d_in] */
   const void* w1_q;     /* e4m3 [H, d_in] */
   const void* w2_q;     /* e4m3 [d_out, H] */
   const float* s_x;     /* scale of x_q */
-  const float* s_w1;    /* scale of w1_q */
-  const float* s_w2;    /* scale of w2_q */
-  const float* s_post;  /* scale relu(pre)^2 is quantized with (forward only) */
+  const float* s_w1;    /* scale of w1_q (and w1t_q) */
+  const float* s_w2;    /* scale of w2_q (and w2t_q) */
+  const float* s_post;  /* scale relu(pre)^2 is quantized with (forward; fp8_bwd backward) */
   float* post_amax;     /* in/out: max(*post_amax, max|relu(pre)^2|) (forward only) */
+  const void* w1t_q;    /* e4m3 [d_in, H] = W1^T codes (fp8_bwd only, else NULL) */
+  const void* w2t_q;    /* e4m3 [H, d_out] = W2^T codes (fp8_bwd only, else NULL) */
+  const float* s_grad;  /* static e5m2 scale of dout (fp8_bwd only) */
+  const float* s_dpre;  /* delayed e5m2 scale of dpre (fp8_bwd only) */
+  float* dpre_amax;     /* in/out: max(*dpre_amax, max|dpre|) (fp8_bwd only) */
 } mlp_fp8;
+
+/* fp8 storage formats (OCP 8-bit floating point): E4M3 (max 448, no infinity) and E5M2 (max
+ * 57344). Encoders round to nearest even and saturate at the maximum; NaN stays NaN. */
+typedef enum mlp_fp8_format { MLP_FP8_E4M3 = 0, MLP_FP8_E5M2 = 1 } mlp_fp8_format;
 
 /* Bytes of workspace the given phase needs for `desc` (upper bound over every skip
  * combination). 0 for an invalid descriptor (see mlp_last_error). Host only. */
@@ -146,7 +167,10 @@ mlp_status mlp_fwd_infer(const mlp_desc* desc, const void* x, const void* w_gate
  *   grad_accum    0: weight grads are written in desc->dtype; 1: they are fp32 buffers and the
  *                 new gradient is added in place (buf = fp32(buf + grad)).
  *   fp8           non-NULL iff desc->fp8_fwd: the backward GEMMs then read the dequantized
- *                 x, W1, W2 of the forward (x / w_gate / w_down are not read).
+ *                 x, W1, W2 of the forward (x / w_gate / w_down are not read). With
+ *                 desc->fp8_bwd they run in fp8 instead (see mlp_fp8); dpreact must then be
+ *                 NULL (dpre exists only as e5m2 codes in the workspace) and M may be any
+ *                 value >= 1 (the token dimension is zero-padded to a multiple of 16 inside).
  * Skips: with dx and dw_gate/dw_up all NULL only the down-projection gradient is formed
  * (quack's "only dW2 needed" branch); with dw_down NULL it is not.
  */
@@ -170,9 +194,21 @@ mlp_status mlp_quantize_e4m3(const void* src, int dtype, int64_t n, void* dst, f
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fp8 codes with a given scale (modded-nanogpt gpt.py: the dual-layout caches of init_mlp_fp8,
+ * row-major and column-major copies of the same codes): code = fmt(v / *scale) with IEEE fp32
+ * division, v = src (or max(src, 0)^2 when relu_sq), src a bf16 [rows, cols] row-major matrix.
+ * dst [rows, cols] receives the row-major codes and dst_t [cols, ld_t] the transposed ones
+ * (ld_t >= rows, a multiple of 16; columns rows .. ld_t-1 of dst_t are set to 0); either may be
+ * NULL, not both. cols must be a multiple of 16; buffers 16-byte aligned; scale a device float.
+ */
+mlp_status mlp_quantize_fp8(const void* src, int dtype, int64_t rows, int64_t cols, int fmt, int relu_sq,
+                            const float* scale, void* dst, void* dst_t, int64_t ld_t, void* stream);
+
+/*
  * The delayed-scale rule of modded-nanogpt gpt.py's _refresh_delayed_scale, for one slot, in
  * fp32: a = amax with NaN/inf mapped to 0, clamped above at 1e12; returns max(a * gain, floor)
- * if a > 0, else prev_scale. For relu(pre)^2 the page uses gain = 1.03/448, floor = 1e-6.
+ * if a > 0, else prev_scale. For relu(pre)^2 the page uses gain = 1.03/448, floor = 1e-6; for
+ * dpre (fp8_bwd) gain = 1.25/57344, floor = 1e-12.
  * Host only.
  */
 float mlp_fp8_next_scale(float amax, float prev_scale, float gain, float floor_);

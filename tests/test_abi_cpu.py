@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib._SIGNATURES), "binding and header disagree"
-    assert L.mlp_abi_version() == 1
+    assert L.mlp_abi_version() == 2
 
 
 def _desc(**kw):
@@ -58,8 +58,10 @@ def test_descriptor_checks():
     d.act = 7
     assert _fwd(d) == gm._lib.MLP_ERR_INVALID_ARG
     d = _desc()
-    d.reserved = 1
+    d.fp8_bwd = 2
     assert _fwd(d) == gm._lib.MLP_ERR_INVALID_ARG
+    d = _desc(act="relu_sq", fp8_bwd=True, d_in=256, hidden=704, d_out=208)   # fp8_bwd needs fp8_fwd
+    assert _fwd(d, wu=None) == gm._lib.MLP_ERR_INVALID_ARG and "fp8_fwd" in _err()
     d = _desc(gate_mult=float("nan"))
     assert _fwd(d) == gm._lib.MLP_ERR_INVALID_ARG
     d = _desc(fp8_fwd=True)            # fp8 forward is ReLU^2 only
@@ -211,3 +213,47 @@ def test_size_limits():
         assert _fwd(_desc(**kw), nws=0) == gm._lib.MLP_ERR_UNSUPPORTED, kw
         assert "2^30" in _err()
     assert _fwd(_desc(hidden=(1 << 29) - 8), ws=None) == gm._lib.MLP_ERR_INVALID_ARG   # passes the size check
+
+
+def test_fp8_backward_checks():
+    """The fp8-gradient backward needs the transposed weight caches and the gradient / dpre
+    scales, keeps dpre in the workspace (dpreact must be NULL), and the plain fp8 backward must
+    not be handed the transposed caches."""
+    L = gm.lib()
+    d = _desc(act="relu_sq", fp8_fwd=True, fp8_bwd=True, M=300, d_in=256, hidden=704, d_out=208)
+    nws = L.mlp_workspace_bytes(C.byref(d), gm.MLP_PHASE_BWD)
+    assert nws > 300 * 704 + 704 * 304       # dpre codes, row-major and transposed (M padded to 304)
+    full = dict(w1t_q=FAKE, w2t_q=FAKE, s_grad=FAKE, s_dpre=FAKE, dpre_amax=FAKE)
+
+    def bwd(dd=d, dpre=None, ws=nws, **over):
+        kw = dict(full)
+        kw.update(over)
+        f = gm.make_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, **kw)
+        return L.mlp_bwd(C.byref(dd), FAKE, None, None, None, None, FAKE, dpre, FAKE, FAKE, None, FAKE, 0,
+                         C.byref(f), FAKE, ws, None)
+
+    for name in full:
+        assert bwd(**{name: None}) == gm._lib.MLP_ERR_INVALID_ARG and name in _err()
+    assert bwd(dpre=FAKE) == gm._lib.MLP_ERR_INVALID_ARG and "dpreact" in _err()
+    assert bwd(ws=nws - 16) == gm._lib.MLP_ERR_WORKSPACE
+    d8 = _desc(act="relu_sq", fp8_fwd=True, M=300, d_in=256, hidden=704, d_out=208)
+    assert bwd(dd=d8, ws=L.mlp_workspace_bytes(C.byref(d8), gm.MLP_PHASE_BWD)) == gm._lib.MLP_ERR_INVALID_ARG
+    assert "w1t_q" in _err()
+
+
+def test_quantize_fp8_checks():
+    L = gm.lib()
+
+    def q(dtype=gm.MLP_BF16, rows=100, cols=64, fmt=gm.MLP_FP8_E5M2, relu=0, scale=FAKE, dst=FAKE, dst_t=FAKE, ld_t=112):
+        return L.mlp_quantize_fp8(FAKE, dtype, rows, cols, fmt, relu, scale, dst, dst_t, ld_t, None)
+
+    assert q(dtype=gm.MLP_F32) == gm._lib.MLP_ERR_UNSUPPORTED
+    assert q(fmt=2) == gm._lib.MLP_ERR_INVALID_ARG
+    assert q(relu=3) == gm._lib.MLP_ERR_INVALID_ARG
+    assert q(cols=40) == gm._lib.MLP_ERR_ALIGNMENT
+    assert q(rows=0) == gm._lib.MLP_ERR_INVALID_ARG
+    assert q(dst=None, dst_t=None) == gm._lib.MLP_ERR_INVALID_ARG
+    assert q(ld_t=96) == gm._lib.MLP_ERR_INVALID_ARG          # below rows
+    assert q(ld_t=104) == gm._lib.MLP_ERR_INVALID_ARG         # not a multiple of 16
+    assert q(scale=None) == gm._lib.MLP_ERR_INVALID_ARG
+    assert q(dst_t=FAKE + 8) == gm._lib.MLP_ERR_ALIGNMENT

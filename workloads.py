@@ -45,6 +45,7 @@ class Workload:
     grad_accum: bool = False
     fp8_fwd: bool = False
     seed: int = 0
+    fp8_bwd: bool = False   # backward products in fp8 too (e5m2 gradients); needs fp8_fwd
 
     @property
     def M(self) -> int:
