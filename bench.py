@@ -231,6 +231,8 @@ def main():
             r.forward()
             r.refresh_post_scale()
             r.backward()
+            if w.fp8_bwd:
+                r.refresh_dpre_scale()
         else:
             r.step()
         r.reset_grads()
@@ -322,7 +324,7 @@ def main():
         cpu = cpu_baseline(w, tensors, args.cpu_rows)
         log(f"[bench] oracle {cpu['seconds']} s, {cpu['value']} TFLOP/s on {cpu['cores']} threads")
 
-    dtype = "fp8-e4m3 fwd / bf16 bwd" if w.fp8_fwd else w.dtype
+    dtype = ("fp8-e4m3 fwd / e5m2 x e4m3 bwd" if w.fp8_bwd else "fp8-e4m3 fwd / bf16 bwd") if w.fp8_fwd else w.dtype
     line = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),

@@ -24,6 +24,10 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 VALU ops in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the fused epilogues index the accumulator array with their loop counters: a loop left
+    # rolled (the default size limit of unroll pragmas stops the quantizing and d-activation
+    # epilogues of the larger tiles) moves the whole accumulator array to scratch memory
+    "-mllvm", "-pragma-unroll-threshold=200000",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

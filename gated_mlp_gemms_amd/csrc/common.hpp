@@ -113,6 +113,31 @@ __device__ __forceinline__ uint32_t f32_to_e5m2(float v) {
   return sign | ((uint32_t)ee << 2) | mi;
 }
 
+// Four codes (byte k from v[k]) with gfx950's packed conversions (v_cvt_pk_fp8_f32 /
+// v_cvt_pk_bf8_f32: nearest even) after saturating at the format maximum. Bit-identical to
+// f32_to_e4m3 / f32_to_e5m2 on every non-NaN fp32 input (checked on the GPU over all of them);
+// the conversion itself maps NaN to an unsigned code, so lanes holding a NaN take the integer
+// encoder instead.
+template <bool E5M2>
+__device__ __forceinline__ uint32_t f32x4_to_fp8(float v0, float v1, float v2, float v3) {
+  constexpr float kMax = E5M2 ? 57344.0f : 448.0f;
+  const float c0 = __builtin_amdgcn_fmed3f(v0, -kMax, kMax), c1 = __builtin_amdgcn_fmed3f(v1, -kMax, kMax);
+  const float c2 = __builtin_amdgcn_fmed3f(v2, -kMax, kMax), c3 = __builtin_amdgcn_fmed3f(v3, -kMax, kMax);
+  int w;
+  if constexpr (E5M2) {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c0, c1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c2, c3, w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, w, true);
+  }
+  if ((v0 != v0) | (v1 != v1) | (v2 != v2) | (v3 != v3)) {
+    auto enc = [](float x) { return E5M2 ? f32_to_e5m2(x) : f32_to_e4m3(x); };
+    return enc(v0) | (enc(v1) << 8) | (enc(v2) << 16) | (enc(v3) << 24);
+  }
+  return (uint32_t)w;
+}
+
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   const uint32_t s = c & 0x80u, e = (c >> 3) & 0xfu, m = c & 7u;
   float mag;

@@ -225,6 +225,7 @@ __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t r
           hi = x[1];
         } else {
           const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(src) + r * ld_src + c);
+          float y[8];
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             float v = bf16_bits_to_f32((k & 1) ? (x[k >> 1] >> 16) : (x[k >> 1] & 0xffffu));
@@ -232,10 +233,14 @@ __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t r
               const float m = fmaxf(v, 0.0f);
               v = m * m;
             }
-            const float y = __fdiv_rn(v, sc);
-            const uint32_t q = e5m2 ? f32_to_e5m2(y) : f32_to_e4m3(y);
-            if (k < 4) lo |= q << (8 * k);
-            else hi |= q << (8 * (k - 4));
+            y[k] = __fdiv_rn(v, sc);
+          }
+          if (e5m2) {
+            lo = f32x4_to_fp8<true>(y[0], y[1], y[2], y[3]);
+            hi = f32x4_to_fp8<true>(y[4], y[5], y[6], y[7]);
+          } else {
+            lo = f32x4_to_fp8<false>(y[0], y[1], y[2], y[3]);
+            hi = f32x4_to_fp8<false>(y[4], y[5], y[6], y[7]);
           }
         }
         if (dst) *reinterpret_cast<u32x2*>(dst + r * cols + c) = u32x2{lo, hi};

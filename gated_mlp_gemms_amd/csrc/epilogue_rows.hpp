@@ -135,32 +135,30 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
   } else if constexpr (EPI == EPI_F8ACT) {
     if (p.flags & 1) Vec8<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), v);
     const float sp = *p.s_post;
-    uint32_t lo = 0, hi = 0;
+    float y[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const float t = fmaxf(v[r], 0.0f);
       const float post = t * t;
       local_amax = fmaxf(local_amax, post);
-      const uint32_t q = f32_to_e4m3(__fdiv_rn(post, sp));
-      if (r < 4) lo |= q << (8 * r);
-      else hi |= q << (8 * (r - 4));
+      y[r] = __fdiv_rn(post, sp);
     }
-    *reinterpret_cast<u32x2*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) = u32x2{lo, hi};
+    *reinterpret_cast<u32x2*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) =
+        u32x2{f32x4_to_fp8<false>(y[0], y[1], y[2], y[3]), f32x4_to_fp8<false>(y[4], y[5], y[6], y[7])};
   } else if constexpr (EPI == EPI_F8DACT) {
     static_assert(ElemTraits<IoT>::bytes == 2, "the pre-activation is read as 16-bit data");
     float pre[8];
     unpack16x8<IoT>(x.a, pre);
     const float sd = *p.s_post;
-    uint32_t lo = 0, hi = 0;
+    float y[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const float dpre = v[r] * (2.0f * fmaxf(pre[r], 0.0f));
       local_amax = fmaxf(local_amax, __builtin_fabsf(dpre));
-      const uint32_t q = f32_to_e5m2(__fdiv_rn(dpre, sd));
-      if (r < 4) lo |= q << (8 * r);
-      else hi |= q << (8 * (r - 4));
+      y[r] = __fdiv_rn(dpre, sd);
     }
-    *reinterpret_cast<u32x2*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) = u32x2{lo, hi};
+    *reinterpret_cast<u32x2*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) =
+        u32x2{f32x4_to_fp8<true>(y[0], y[1], y[2], y[3]), f32x4_to_fp8<true>(y[4], y[5], y[6], y[7])};
   }
 }
 

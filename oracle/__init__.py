@@ -36,4 +36,5 @@ from .e5m2 import (  # noqa: F401
 from .fp8 import (  # noqa: F401
     per_tensor_scale, quantize_per_tensor, dequantize, next_delayed_scale,
     relu_sq_fp8_forward, relu_sq_fp8_backward, quantize_e5m2, relu_sq_fp8_backward_e5m2,
+    relu_sq_fp8_backward_e5m2_sampled,
 )

@@ -133,3 +133,32 @@ def relu_sq_fp8_backward_e5m2(dout, x_q, s_x, w1_q, s_w1, w2_q, s_w2, s_post, s_
         "dout_q": dout_q,
         "dpre_q": dpre_q,
     }
+
+
+def relu_sq_fp8_backward_e5m2_sampled(dout, x_q, s_x, w1_q, s_w1, w2_q, s_w2, s_post, s_grad, s_dpre,
+                                      rows, units, down_mult=1.0):
+    """``relu_sq_fp8_backward_e5m2`` on a sample: dx[rows], dw1[units] and dw2[:, units], each
+    entry formed by the same steps restricted to the dpre / post entries it needs (dpre[rows, :]
+    for dx, dpre[:, units] and post[:, units] for the weight gradients)."""
+    xh = dequantize(x_q, s_x)
+    w1h = dequantize(w1_q, s_w1)
+    w2h = dequantize(w2_q, s_w2)
+    gh = e5m2_decode(quantize_e5m2(dout, s_grad)) * np.float64(_F32(s_grad))
+
+    def dpre_hat(r_idx, u_idx):
+        pre = _bf16(xh[r_idx] @ w1h[u_idx].T)
+        dpost32 = (down_mult * (gh[r_idx] @ w2h[:, u_idx])).astype(np.float32)
+        dpre = (dpost32 * drelu_sq(pre).astype(np.float32)).astype(np.float64)
+        return e5m2_decode(quantize_e5m2(dpre, s_dpre)) * np.float64(_F32(s_dpre)), pre
+
+    every_row = np.arange(xh.shape[0])
+    every_unit = np.arange(w1h.shape[0])
+    ph_rows, _ = dpre_hat(rows, every_unit)
+    ph_units, pre_units = dpre_hat(every_row, units)
+    r32 = np.maximum(pre_units, 0.0).astype(np.float32)
+    post_hat = dequantize(e4m3_encode((r32 * r32) / _F32(s_post)), s_post)
+    return {
+        "dx_rows": ph_rows @ w1h,
+        "dw1_rows": ph_units.T @ xh,
+        "dw2_cols": down_mult * (gh.T @ post_hat),
+    }

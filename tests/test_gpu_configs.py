@@ -137,3 +137,47 @@ def test_gpt_relu_sq_fp8_full_size():
     assert_close("pre[rows]", f64(r.saved[rows]), f["pre"], TOL["bf16"])
     xh = oracle.dequantize(xq, sc[0])
     _check_relu(w, t, r, xh, oracle.dequantize(w1q, sc[1]), oracle.dequantize(w2q, sc[2]), TOL["fp8"])
+
+
+def test_gpt_relu_sq_fp8_backward_full_size():
+    """The fp8-gradient backward at the GPT MLP's full size, on sampled outputs. The delayed post
+    and dpre scales are formed from the oracle's own maxima of relu(pre)^2 and |dpre|."""
+    w = WORKLOADS["gpt_relu2_fp8_m49152_d768_h3072"]
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.quantize()
+    torch.cuda.synchronize()
+    q = []
+    for name, src, code, slot in (("x", t["x"], r.x_q, 0), ("w1", t["w1"], r.w1_q, 1), ("w2", t["w2"], r.w2_q, 2)):
+        q_ref, s_ref = oracle.quantize_per_tensor(src.to(torch.float32).numpy())
+        assert np.float32(r.scales[slot].item()) == s_ref, name
+        np.testing.assert_array_equal(code.cpu().numpy(), q_ref, err_msg=name)
+        q.append((q_ref, s_ref))
+    (xq, sx), (w1q, s1), (w2q, s2) = q
+    np.testing.assert_array_equal(r.w1t_q.cpu().numpy(), w1q.T)
+    np.testing.assert_array_equal(r.w2t_q.cpu().numpy(), w2q.T)
+    # delayed scales from the oracle: max relu(pre)^2 of the forward, max |dpre| of the backward
+    xh, w1h, w2h = oracle.dequantize(xq, sx), oracle.dequantize(w1q, s1), oracle.dequantize(w2q, s2)
+    pre = xh @ w1h.T
+    post_amax = float(np.max(np.maximum(pre, 0.0))) ** 2
+    s_grad = np.float32(2.0 ** -6)
+    g = oracle.e5m2_decode(oracle.quantize_e5m2(f64(t["dout"]), s_grad)) * np.float64(s_grad)
+    dpre_amax = float(np.max(np.abs((w.down_mult * (g @ w2h)) * (2.0 * np.maximum(pre, 0.0)))))
+    del pre, g
+    s_post = oracle.next_delayed_scale(post_amax, 1.0, np.float32(1.03) / np.float32(448.0), 1e-6)
+    s_dpre = oracle.next_delayed_scale(dpre_amax, s_grad, np.float32(1.25) / np.float32(57344.0), 1e-12)
+    r.scales[3] = float(s_post)
+    r.scales[5] = float(s_grad)
+    r.scales[6] = float(s_dpre)
+    r.scales[7] = 0.0
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    assert abs(float(r.scales[7].item()) / dpre_amax - 1.0) < 2e-2
+    rows, units = _sample(w.M, seed=7), _sample(w.hidden, seed=8)
+    s = oracle.relu_sq_fp8_backward_e5m2_sampled(f64(t["dout"]), xq, sx, w1q, s1, w2q, s2, s_post, s_grad, s_dpre,
+                                                 rows, units, w.down_mult)
+    assert_close("dx[rows]", f64(r.dx[rows]), s["dx_rows"], TOL["fp8"])
+    assert_close("dw1[u]", f64(r.dw_gate[units]), s["dw1_rows"], TOL["fp8"])
+    assert_close("dw2[:,u]", f64(r.dw_down[:, units]), s["dw2_cols"], TOL["fp8"])

@@ -179,3 +179,21 @@ def test_dpre_scale_rule_from_page_constants():
     assert oracle.next_delayed_scale(57344.0, 1.0, gain, floor) == np.float32(np.float32(57344.0) * gain)
     assert oracle.next_delayed_scale(0.0, 0.25, gain, floor) == np.float32(0.25)
     assert c["fp8_grad_scale"]["value"] == 2.0 ** -6
+
+
+def test_sampled_backward_equals_full():
+    rng = np.random.default_rng(5)
+    M, D, H = 40, 32, 48
+    x = rng.standard_normal((M, D))
+    w1 = rng.uniform(-1, 1, (H, D)) / np.sqrt(D)
+    w2 = rng.uniform(-1, 1, (D, H)) / np.sqrt(H)
+    dout = rng.standard_normal((M, D))
+    q = [oracle.quantize_per_tensor(v) for v in (x, w1, w2)]
+    args = (dout, q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], np.float32(0.01), np.float32(2.0 ** -6),
+            np.float32(0.002))
+    full = oracle.relu_sq_fp8_backward_e5m2(*args, down_mult=2.0)
+    rows, units = np.array([0, 7, 39]), np.array([1, 20, 47])
+    smp = oracle.relu_sq_fp8_backward_e5m2_sampled(*args, rows, units, down_mult=2.0)
+    np.testing.assert_allclose(smp["dx_rows"], full["dx"][rows], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(smp["dw1_rows"], full["dw1"][units], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(smp["dw2_cols"], full["dw2"][:, units], rtol=1e-12, atol=1e-14)

@@ -85,6 +85,9 @@ WORKLOADS = {
         Workload("gpt_relu2_bf16_m49152_d768_h3072", "relu_sq", "bf16", (48, 1024), 768, 3072, 768),
         Workload("gpt_relu2_fp8fwd_m49152_d768_h3072", "relu_sq", "bf16", (48, 1024), 768, 3072, 768,
                  fp8_fwd=True),
+        # the same with the backward in fp8 too (e5m2 gradients)
+        Workload("gpt_relu2_fp8_m49152_d768_h3072", "relu_sq", "bf16", (48, 1024), 768, 3072, 768,
+                 fp8_fwd=True, fp8_bwd=True),
         # one GPU's share of the LLaMA step on 8 GPUs: tensor parallel (hidden units split 8 ways,
         # a gate/up pair kept together) and data parallel (tokens split 8 ways)
         Workload("llama_swiglu_bf16_tp8_m2048_d4096_h1376", "swiglu", "bf16", (2, 1024), 4096, 1376, 4096),
