@@ -147,6 +147,17 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   return s ? -mag : mag;
 }
 
+// *amax = max(*amax, v) for v >= 0 (the float bits of non-negative values order as unsigned
+// integers). Every wave of a quantizing epilogue reports its maximum to the same word, and
+// same-address atomics serialize in L2, so a wave first reads the word and skips the atomic when
+// it cannot raise it (the word only grows: a stale read can only cost an unneeded atomic).
+__device__ __forceinline__ void amax_update(float* amax, float v) {
+  if (!(v > 0.0f)) return;
+  const unsigned int cur = __hip_atomic_load(reinterpret_cast<unsigned int*>(amax), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+  if (__float_as_uint(v) > cur) atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(v));
+}
+
 // ---- activations (fp32) -------------------------------------------------------------------
 
 __device__ __forceinline__ float sigmoidf_(float z) {

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kEwThreads) void absmax_kernel(const void* src, int
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < kEwThreads / 64; ++w) m = fmaxf(m, part[w]);
-    if (m > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(m));
+    amax_update(amax, m);
   }
 }
 

@@ -256,8 +256,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& p, AccV (&acc)[MI]
   if constexpr (EPI == EPI_F8ACT || EPI == EPI_F8DACT) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) local_amax = fmaxf(local_amax, __shfl_xor(local_amax, off));
-    if (lane == 0 && local_amax > 0.0f)
-      atomicMax(reinterpret_cast<unsigned int*>(p.amax), __float_as_uint(local_amax));
+    if (lane == 0) amax_update(p.amax, local_amax);
   }
 }
 

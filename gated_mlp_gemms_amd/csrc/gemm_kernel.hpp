@@ -357,8 +357,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, f32x16 (&acc)[MI][NI
   if constexpr (EPI == EPI_F8ACT) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) local_amax = fmaxf(local_amax, __shfl_xor(local_amax, off));
-    if (lane == 0 && local_amax > 0.0f)
-      atomicMax(reinterpret_cast<unsigned int*>(p.amax), __float_as_uint(local_amax));
+    if (lane == 0) amax_update(p.amax, local_amax);
   }
 }
 
