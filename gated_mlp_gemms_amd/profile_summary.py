@@ -2,6 +2,7 @@
 
     python -m gated_mlp_gemms_amd.profile_summary trace  <kernel-trace dir> <out.txt>  --command "..."
     python -m gated_mlp_gemms_amd.profile_summary traffic <fetch dir> <write dir> <out.json> --command "..."
+    python -m gated_mlp_gemms_amd.profile_summary mfma <pmc dir> <out.json> --command "..."
 
 The trace summary lists every kernel's dispatch count and average / total duration from the
 `*_kernel_stats.csv` rocprofv3 writes with `--kernel-trace --stats --output-format csv`, then the
@@ -191,6 +192,47 @@ def summarize_traffic(fetch_dir: str, write_dir: str, out_json: str, command: st
     print(json.dumps(res, indent=1))
 
 
+def _gpu_agent(pmc_dir: str) -> dict:
+    path = _one(os.path.join(pmc_dir, "**", "*agent_info.csv"))
+    for r in csv.DictReader(open(path)):
+        if r.get("Agent_Type", "").upper().endswith("GPU") or r.get("Name", "").startswith("gfx"):
+            return r
+    raise SystemExit("no GPU agent in the agent info")
+
+
+def summarize_mfma(pmc_dir: str, out_json: str, command: str, first_step: int = 0, steps: int = 0) -> None:
+    """MFMA busy fraction and shader clock per stage from one `--pmc SQ_VALU_MFMA_BUSY_CYCLES
+    GRBM_GUI_ACTIVE` pass. SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of every SIMD and
+    GRBM_GUI_ACTIVE the active cycles of every XCD, so busy / (GUI / XCDs * SIMDs) is the
+    fraction of SIMD cycles the matrix units worked, and GUI / XCDs / duration the clock."""
+    agent = _gpu_agent(pmc_dir)
+    n_xcc, n_simd = int(agent["Num_Xcc"]), int(agent["Simd_Count"])
+    path = _one(os.path.join(pmc_dir, "**", "*counter_collection.csv"))
+    per = {}
+    for r in csv.DictReader(open(path)):
+        d = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                   "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    disp = sorted((i, d["name"], (d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), d.get("GRBM_GUI_ACTIVE", 0.0), d["ns"]))
+                  for i, d in per.items())
+    steps_all = _per_step(disp, STAGE_ORDER_GATED)
+    timed = steps_all[first_step:first_step + steps] if steps else steps_all[first_step:]
+    stages = {}
+    for st in STAGE_ORDER_GATED:
+        busy = sum(v[0] for s in timed for _, v in s[st])
+        gui = sum(v[1] for s in timed for _, v in s[st])
+        ns = sum(v[2] for s in timed for _, v in s[st])
+        if not timed or gui <= 0 or ns <= 0:
+            continue
+        cyc = gui / n_xcc
+        stages[st] = {"kernel_us": round(ns / len(timed) / 1e3, 1), "sclk_ghz": round(cyc / ns, 3),
+                      "mfma_busy": round(busy / (cyc * n_simd), 4)}
+    res = {"command": command, "kernel_sources_sha256": kernel_sources_sha256(), "steps": len(timed),
+           "xcc": n_xcc, "simds": n_simd, "stages": stages}
+    json.dump(res, open(out_json, "w"), indent=1)
+    print(json.dumps(res, indent=1))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -208,9 +250,17 @@ def main(argv=None):
     f.add_argument("--copy-mib", type=int, default=256)
     f.add_argument("--first-step", type=int, default=0)
     f.add_argument("--steps", type=int, default=0)
+    m = sub.add_parser("mfma")
+    m.add_argument("pmc_dir")
+    m.add_argument("out_json")
+    m.add_argument("--command", required=True)
+    m.add_argument("--first-step", type=int, default=0)
+    m.add_argument("--steps", type=int, default=0)
     a = ap.parse_args(argv)
     if a.what == "trace":
         summarize_trace(a.trace_dir, a.out_txt, a.command, a.first_step, a.steps)
+    elif a.what == "mfma":
+        summarize_mfma(a.pmc_dir, a.out_json, a.command, a.first_step, a.steps)
     else:
         summarize_traffic(a.fetch_dir, a.write_dir, a.out_json, a.command, a.copy_mib, a.first_step, a.steps)
 
