@@ -380,6 +380,34 @@ mlp_status gemm(DType in, DType io, Layout lay, int epi, const Plan& p, GemmArgs
   return hip_status(run_gemm(in, io, lay, epi, p.tile, a, p.grid, s), what);
 }
 
+// A non-split GEMM over output columns [0, N) as two launches when that fills the CUs better:
+// 8-wave 256 x 256 tiles for the columns that make whole rounds of 256 tiles, 8-wave 256 x 128
+// tiles for the rest (one launch's last round otherwise idles part of the chip: the
+// d-activation GEMM of the LLaMA step has 344 tiles of 256 x 256 = 1.34 rounds, or 688 tiles of
+// 256 x 128, whose K loop moves 1.5x the operand bytes per FLOP). Column offsets move B (MN-major:
+// by columns; K-major: by rows), C0, C1 and aux; es = bytes per element of the outputs / aux.
+// Falls back to `whole` when the split does not apply.
+mlp_status gemm_cols_split(DType in, DType io, Layout lay, int epi, const Plan& whole, GemmArgs a, int64_t M,
+                           int64_t N, int64_t K, int es, hipStream_t s, const char* what) {
+  const int64_t tm = (M + 255) / 256;
+  const int64_t n1_tiles = tm > 0 ? 256 / tm : 0;   // N-tiles of one full round
+  const int64_t n1 = n1_tiles * 256;
+  if (in != DT_BF16 && in != DT_F16) return gemm(in, io, lay, epi, whole, a, M, N, K, nullptr, s, what);
+  if (whole.splits != 1 || tm > 256 || n1_tiles < 1 || n1 >= N || (N - n1) % 128 ||
+      (N - n1) / 128 * tm > 256)
+    return gemm(in, io, lay, epi, whole, a, M, N, K, nullptr, s, what);
+  const Plan p1 = plan_gemm(in, M, n1, K, false, false, TILE_256x256_W8);
+  const Plan p2 = plan_gemm(in, M, N - n1, K, false, false, TILE_256x128_W8);
+  MLP_TRY(gemm(in, io, lay, epi, p1, a, M, n1, K, nullptr, s, what));
+  GemmArgs b = a;
+  const int ebi = in == DT_F32 ? 4 : 2;
+  b.B0 = lay == NT ? static_cast<const char*>(a.B0) + n1 * a.ldb * ebi : static_cast<const char*>(a.B0) + n1 * ebi;
+  if (a.C0) b.C0 = static_cast<char*>(a.C0) + n1 * es;
+  if (a.C1) b.C1 = static_cast<char*>(a.C1) + n1 * es;
+  if (a.aux) b.aux = static_cast<char*>(a.aux) + n1 * es;
+  return gemm(in, io, lay, epi, p2, b, M, N - n1, K, nullptr, s, what);
+}
+
 GemmArgs base_args(const mlp_desc* d) {
   GemmArgs a{};
   a.alpha = 1.0f;
@@ -752,8 +780,8 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
     a.alpha_dev0 = sw2;
     const Plan p = plan_gemm(io, M, H, O, false, false);
     StageScope st(MLP_STAGE_DACT, s);
-    MLP_TRY(gemm(io, io, NN, gated ? EPI_DGATED : EPI_DACT, p, a, M, H, O, nullptr, s,
-                 "d-activation GEMM"));
+    MLP_TRY(gemm_cols_split(io, io, NN, gated ? EPI_DGATED : EPI_DACT, p, a, M, H, O, esize(d->dtype), s,
+                            "d-activation GEMM"));
   } else if (dwd) {
     // only the down-projection gradient: the post-activation from the pre-activation alone
     StageScope st(MLP_STAGE_ACT, s);

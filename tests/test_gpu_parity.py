@@ -512,3 +512,16 @@ def test_graph_replay_of_training_step():
         assert torch.equal(r.out, ref["out"])
         for k, v in r.grads().items():
             assert torch.equal(v, ref[k]), k
+
+
+def test_dact_column_split_against_oracle():
+    """A shape whose d-activation GEMM runs as two launches over the hidden units (8-wave
+    256 x 256 tiles for whole rounds, 256 x 128 tiles for the rest), compared in full."""
+    w = _w("swiglu", "bf16", 1800, 256, 8448, 200, gate_mult=1.125, down_mult=2.0, seed=9)
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    check_full(w, t, r)
