@@ -51,7 +51,7 @@ def _one(pattern: str) -> str:
 
 
 _GEMM = re.compile(r"gemm_(dma_)?kernelI(.+?)Li(\d+)ELi(\d+)ELb(\d)ELb(\d)ELi(\d)E(?:Li(\d+)E)?")
-_EPI = ["STORE", "PARTIAL", "GATED", "ACT", "DGATED", "DACT", "F8ACT"]
+_EPI = ["STORE", "PARTIAL", "GATED", "ACT", "DGATED", "DACT", "F8ACT", "F8DACT"]
 
 
 # rocprofv3 prints some instantiations demangled (and their element types garbled)
@@ -130,9 +130,10 @@ def summarize_trace(trace_dir: str, out_txt: str, command: str, first_step: int 
 
 def _per_step(disp, stages):
     """Split this library's dispatches into steps (a step starts at each up-projection) and each
-    step into stages (each GEMM opens the next stage; other kernels join the current one). Only
-    whole steps are returned; launches of other libraries (a fill, a copy) are skipped."""
-    steps, cur, idx = [], None, -1
+    step into stages (each GEMM opens the next stage, except one with the same epilogue as the GEMM
+    before it: a stage run as two launches over its output columns; other kernels join the current
+    stage). Only whole steps are returned; launches of other libraries (a fill, a copy) are skipped."""
+    steps, cur, idx, last_epi = [], None, -1, None
     for _, name, val in disp:
         if not is_library_kernel(name):
             continue
@@ -144,8 +145,10 @@ def _per_step(disp, stages):
             idx = 0
         elif cur is None:
             continue
-        elif is_gemm:
+        elif is_gemm and epi != last_epi:
             idx += 1
+        if is_gemm:
+            last_epi = epi
         if idx < len(stages):
             cur[stages[idx]].append((name, val))
         else:
