@@ -198,6 +198,89 @@ __global__ __launch_bounds__(kEwThreads) void dequant_kernel(const uint8_t* src,
     dst[i] = (uint16_t)(__float_as_uint(e4m3_to_f32(src[i])) >> 16);   // exact: <= 4 significant bits
 }
 
+// The same three passes 8 elements per lane per step: a 16-byte load of the source (bf16 / f16:
+// one; fp32: two), an 8-byte store of the codes, a 16-byte store of the widened values. Each
+// element goes through the same arithmetic as above (the hardware e4m3 conversion after
+// saturation encodes exactly as f32_to_e4m3), so the results are bit-identical. The elements
+// after the last whole group of 8 are taken one by one by the first workgroup. The host picks
+// these kernels only when the pointers are aligned for the vector accesses.
+template <typename T> __device__ __forceinline__ void load8(const char* p, float v[8]) {
+  if constexpr (sizeof(T) == 4) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { v[r] = a[r]; v[4 + r] = b[r]; }
+  } else {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[2 * r] = Bits16<T>::to_f32(x[r] & 0xffffu);
+      v[2 * r + 1] = Bits16<T>::to_f32(x[r] >> 16);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kEwThreads) void absmax8_kernel(const void* src, int64_t n, float* amax) {
+  const char* base = reinterpret_cast<const char*>(src);
+  const int64_t n8 = n / 8;
+  float m = 0.0f;
+  for (int64_t j = blockIdx.x * (int64_t)kEwThreads + threadIdx.x; j < n8; j += (int64_t)gridDim.x * kEwThreads) {
+    float v[8];
+    load8<T>(base + j * 8 * esize<T>(), v);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) m = fmaxf(m, __builtin_fabsf(v[r]));
+  }
+  if (blockIdx.x == 0)
+    for (int64_t i = n8 * 8 + threadIdx.x; i < n; i += kEwThreads) m = fmaxf(m, __builtin_fabsf(load1<T>(src, i)));
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float part[kEwThreads / 64];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kEwThreads / 64; ++w) m = fmaxf(m, part[w]);
+    amax_update(amax, m);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kEwThreads) void quantize8_kernel(const void* src, int64_t n, uint8_t* dst,
+                                                               const float* amax, float* scale_out) {
+  const float s = __fdiv_rn(fmaxf(*amax, 1e-12f), 448.0f);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
+  const char* base = reinterpret_cast<const char*>(src);
+  const int64_t n8 = n / 8;
+  for (int64_t j = blockIdx.x * (int64_t)kEwThreads + threadIdx.x; j < n8; j += (int64_t)gridDim.x * kEwThreads) {
+    float v[8];
+    load8<T>(base + j * 8 * esize<T>(), v);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v[r] = __fdiv_rn(v[r], s);
+    *reinterpret_cast<u32x2*>(dst + j * 8) =
+        u32x2{f32x4_to_fp8<false>(v[0], v[1], v[2], v[3]), f32x4_to_fp8<false>(v[4], v[5], v[6], v[7])};
+  }
+  if (blockIdx.x == 0)
+    for (int64_t i = n8 * 8 + threadIdx.x; i < n; i += kEwThreads)
+      dst[i] = (uint8_t)f32_to_e4m3(__fdiv_rn(load1<T>(src, i), s));
+}
+
+__global__ __launch_bounds__(kEwThreads) void dequant8_kernel(const uint8_t* src, uint16_t* dst, int64_t n) {
+  const int64_t n8 = n / 8;
+  for (int64_t j = blockIdx.x * (int64_t)kEwThreads + threadIdx.x; j < n8; j += (int64_t)gridDim.x * kEwThreads) {
+    const u32x2 c = *reinterpret_cast<const u32x2*>(src + j * 8);
+    u32x4 o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t w = c[r >> 1] >> (16 * (r & 1));
+      o[r] = (__float_as_uint(e4m3_to_f32(w & 0xffu)) >> 16) | (__float_as_uint(e4m3_to_f32((w >> 8) & 0xffu)) & 0xffff0000u);
+    }
+    *reinterpret_cast<u32x4*>(dst + j * 8) = o;
+  }
+  if (blockIdx.x == 0)
+    for (int64_t i = n8 * 8 + threadIdx.x; i < n; i += kEwThreads)
+      dst[i] = (uint16_t)(__float_as_uint(e4m3_to_f32(src[i])) >> 16);
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
 // fp8 codes of a [rows, cols] matrix, row-major and / or transposed, one 64 x 64 tile at a time
 // through LDS. Loads and row-major stores are 8 elements per lane along a row; the transposed
 // stores are 16 codes (16 source rows) per lane. Source rows past `rows` (up to the transposed
@@ -346,26 +429,42 @@ hipError_t run_plain_act(DType io, const void* pre, void* post, int64_t n, float
 hipError_t run_quantize_e4m3(DType src_t, const void* src, int64_t n, void* dst, float* scale,
                              float* ws, hipStream_t s) {
   hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(64), 0, s, ws, 1);
+  uint8_t* q = reinterpret_cast<uint8_t*>(dst);
+  if (aligned(src, 16) && aligned(dst, 8)) {
+    const int grid = ew_grid(std::max<int64_t>(n / 8, 1));
+    if (src_t == DT_BF16) {
+      hipLaunchKernelGGL(absmax8_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);
+      hipLaunchKernelGGL(quantize8_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, q, ws, scale);
+    } else if (src_t == DT_F16) {
+      hipLaunchKernelGGL(absmax8_kernel<f16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);
+      hipLaunchKernelGGL(quantize8_kernel<f16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, q, ws, scale);
+    } else {
+      hipLaunchKernelGGL(absmax8_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);
+      hipLaunchKernelGGL(quantize8_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, src, n, q, ws, scale);
+    }
+    return hipGetLastError();
+  }
   const int grid = ew_grid(n);
   if (src_t == DT_BF16) {
     hipLaunchKernelGGL(absmax_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);
-    hipLaunchKernelGGL(quantize_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, src, n,
-                       reinterpret_cast<uint8_t*>(dst), ws, scale);
+    hipLaunchKernelGGL(quantize_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, q, ws, scale);
   } else if (src_t == DT_F16) {
     hipLaunchKernelGGL(absmax_kernel<f16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);
-    hipLaunchKernelGGL(quantize_kernel<f16>, dim3(grid), dim3(kEwThreads), 0, s, src, n,
-                       reinterpret_cast<uint8_t*>(dst), ws, scale);
+    hipLaunchKernelGGL(quantize_kernel<f16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, q, ws, scale);
   } else {
     hipLaunchKernelGGL(absmax_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);
-    hipLaunchKernelGGL(quantize_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, src, n,
-                       reinterpret_cast<uint8_t*>(dst), ws, scale);
+    hipLaunchKernelGGL(quantize_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, src, n, q, ws, scale);
   }
   return hipGetLastError();
 }
 
 hipError_t run_dequant_e4m3_bf16(const void* src, void* dst, int64_t n, hipStream_t s) {
-  hipLaunchKernelGGL(dequant_kernel, dim3(ew_grid(n)), dim3(kEwThreads), 0, s,
-                     reinterpret_cast<const uint8_t*>(src), reinterpret_cast<uint16_t*>(dst), n);
+  const uint8_t* c = reinterpret_cast<const uint8_t*>(src);
+  uint16_t* o = reinterpret_cast<uint16_t*>(dst);
+  if (aligned(src, 8) && aligned(dst, 16))
+    hipLaunchKernelGGL(dequant8_kernel, dim3(ew_grid(std::max<int64_t>(n / 8, 1))), dim3(kEwThreads), 0, s, c, o, n);
+  else
+    hipLaunchKernelGGL(dequant_kernel, dim3(ew_grid(n)), dim3(kEwThreads), 0, s, c, o, n);
   return hipGetLastError();
 }
 

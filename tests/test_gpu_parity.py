@@ -265,6 +265,33 @@ def test_quantize_e4m3_bit_exact():
         np.testing.assert_array_equal(dst.cpu().numpy(), q_ref)
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_quantize_e4m3_tail_and_unaligned(dt, offset):
+    """The largest magnitude in the elements after the last whole group of 8 (the vector pass
+    must not miss it), and source / destination views 4 bytes off their allocations' start
+    (allowed by the ABI, not aligned for the vector pass, so the per-element pass runs): codes
+    and scale bit-exact."""
+    import gated_mlp_gemms_amd as gm
+    n = 8 * 1000 + 7
+    announce(f"quantize tail {dt} offset={offset}")
+    rng = np.random.default_rng(5)
+    v = torch.from_numpy(rng.standard_normal(n).astype(np.float32)).to(dt)
+    v[-1] = -37.0
+    so = 4 * offset // v.element_size()   # elements in 4 bytes
+    src = torch.zeros(n + so, dtype=dt, device="cuda")
+    src[so:] = v.cuda()
+    dst = torch.full((n + 4 * offset,), 0x55, dtype=torch.uint8, device="cuda")
+    scale = torch.empty(1, dtype=torch.float32, device="cuda")
+    gm.mlp_quantize_e4m3(src[so:], dst[4 * offset:], scale)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_per_tensor(v.to(torch.float32).numpy())
+    assert np.float32(scale.item()) == s_ref == np.float32(37.0) / np.float32(448.0)
+    got = dst.cpu().numpy()
+    np.testing.assert_array_equal(got[4 * offset:], q_ref)
+    assert np.all(got[:4 * offset] == 0x55)
+
+
 def _fp8_run(w, t, announce_name):
     announce(announce_name)
     r = run(w, t)
