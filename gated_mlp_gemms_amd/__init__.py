@@ -96,11 +96,15 @@ def mlp_bwd(desc, dout, x, w_gate, w_up, w_down, saved_preact=None, dpreact=None
     check(st, "mlp_bwd")
 
 
+def mlp_quantize_workspace_bytes() -> int:
+    return int(lib().mlp_quantize_workspace_bytes())
+
+
 def mlp_quantize_e4m3(src, dst, scale, workspace=None, stream=None):
     """Per-tensor e4m3 quantization of ``src`` (f32/bf16/f16) into ``dst`` (uint8 or float8_e4m3fn)
     and the fp32 device scalar ``scale``."""
     if workspace is None:
-        workspace = torch.empty(int(lib().mlp_quantize_workspace_bytes()), dtype=torch.uint8, device=src.device)
+        workspace = torch.empty(mlp_quantize_workspace_bytes(), dtype=torch.uint8, device=src.device)
     st = lib().mlp_quantize_e4m3(_ptr(src), _DTYPES[src.dtype], src.numel(), _ptr(dst), _ptr(scale),
                                  _ptr(workspace), workspace.numel(), _stream(stream))
     check(st, "mlp_quantize_e4m3")

@@ -219,12 +219,36 @@ template <typename T> __device__ __forceinline__ void load8(const char* p, float
   }
 }
 
+// Maximum over a workgroup (the result in thread 0).
+__device__ __forceinline__ float block_max(float m) {
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float part[kEwThreads / 64];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int w = 1; w < kEwThreads / 64; ++w) m = fmaxf(m, part[w]);
+  return m;
+}
+
+// The absmax in two passes and no atomics: each workgroup writes the maximum of its grid-stride
+// share (four 16-byte loads in flight per lane) to part[workgroup]; one workgroup then reduces
+// the parts into *amax. (Many workgroups finishing together on one atomic word serialize there.)
 template <typename T>
-__global__ __launch_bounds__(kEwThreads) void absmax8_kernel(const void* src, int64_t n, float* amax) {
+__global__ __launch_bounds__(kEwThreads) void absmax8_part_kernel(const void* src, int64_t n, float* part) {
   const char* base = reinterpret_cast<const char*>(src);
-  const int64_t n8 = n / 8;
+  const int64_t n8 = n / 8, stride = (int64_t)gridDim.x * kEwThreads;
   float m = 0.0f;
-  for (int64_t j = blockIdx.x * (int64_t)kEwThreads + threadIdx.x; j < n8; j += (int64_t)gridDim.x * kEwThreads) {
+  int64_t j = blockIdx.x * (int64_t)kEwThreads + threadIdx.x;
+  for (; j + 3 * stride < n8; j += 4 * stride) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8<T>(base + (j + u * stride) * 8 * esize<T>(), v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) m = fmaxf(m, __builtin_fabsf(v[u][r]));
+  }
+  for (; j < n8; j += stride) {
     float v[8];
     load8<T>(base + j * 8 * esize<T>(), v);
 #pragma unroll
@@ -232,14 +256,15 @@ __global__ __launch_bounds__(kEwThreads) void absmax8_kernel(const void* src, in
   }
   if (blockIdx.x == 0)
     for (int64_t i = n8 * 8 + threadIdx.x; i < n; i += kEwThreads) m = fmaxf(m, __builtin_fabsf(load1<T>(src, i)));
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  __shared__ float part[kEwThreads / 64];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < kEwThreads / 64; ++w) m = fmaxf(m, part[w]);
-    amax_update(amax, m);
-  }
+  m = block_max(m);
+  if (threadIdx.x == 0) part[blockIdx.x] = m;
+}
+
+__global__ __launch_bounds__(kEwThreads) void max_parts_kernel(const float* part, int parts, float* amax) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < parts; i += kEwThreads) m = fmaxf(m, part[i]);
+  m = block_max(m);
+  if (threadIdx.x == 0) *amax = m;
 }
 
 template <typename T>
@@ -428,22 +453,22 @@ hipError_t run_plain_act(DType io, const void* pre, void* post, int64_t n, float
 
 hipError_t run_quantize_e4m3(DType src_t, const void* src, int64_t n, void* dst, float* scale,
                              float* ws, hipStream_t s) {
-  hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(64), 0, s, ws, 1);
   uint8_t* q = reinterpret_cast<uint8_t*>(dst);
   if (aligned(src, 16) && aligned(dst, 8)) {
-    const int grid = ew_grid(std::max<int64_t>(n / 8, 1));
-    if (src_t == DT_BF16) {
-      hipLaunchKernelGGL(absmax8_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);
-      hipLaunchKernelGGL(quantize8_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, q, ws, scale);
-    } else if (src_t == DT_F16) {
-      hipLaunchKernelGGL(absmax8_kernel<f16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);
-      hipLaunchKernelGGL(quantize8_kernel<f16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, q, ws, scale);
-    } else {
-      hipLaunchKernelGGL(absmax8_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);
-      hipLaunchKernelGGL(quantize8_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, src, n, q, ws, scale);
-    }
+    const int64_t n8 = n / 8;
+    const int parts = (int)std::min<int64_t>(kQuantizeParts, std::max<int64_t>((n8 + 4 * kEwThreads - 1) / (4 * kEwThreads), 1));
+    float* part = ws + 64;
+    const int grid = ew_grid(std::max<int64_t>(n8, 1));
+    if (src_t == DT_BF16) hipLaunchKernelGGL(absmax8_part_kernel<bf16>, dim3(parts), dim3(kEwThreads), 0, s, src, n, part);
+    else if (src_t == DT_F16) hipLaunchKernelGGL(absmax8_part_kernel<f16>, dim3(parts), dim3(kEwThreads), 0, s, src, n, part);
+    else hipLaunchKernelGGL(absmax8_part_kernel<float>, dim3(parts), dim3(kEwThreads), 0, s, src, n, part);
+    hipLaunchKernelGGL(max_parts_kernel, dim3(1), dim3(kEwThreads), 0, s, part, parts, ws);
+    if (src_t == DT_BF16) hipLaunchKernelGGL(quantize8_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, q, ws, scale);
+    else if (src_t == DT_F16) hipLaunchKernelGGL(quantize8_kernel<f16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, q, ws, scale);
+    else hipLaunchKernelGGL(quantize8_kernel<float>, dim3(grid), dim3(kEwThreads), 0, s, src, n, q, ws, scale);
     return hipGetLastError();
   }
+  hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(64), 0, s, ws, 1);
   const int grid = ew_grid(n);
   if (src_t == DT_BF16) {
     hipLaunchKernelGGL(absmax_kernel<bf16>, dim3(grid), dim3(kEwThreads), 0, s, src, n, ws);

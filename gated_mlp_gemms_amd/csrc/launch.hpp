@@ -51,7 +51,10 @@ hipError_t run_gated_act(DType io, const void* preact, void* a, int M, int H, fl
 hipError_t run_plain_act(DType io, const void* pre, void* post, int64_t n, float alpha,
                          const float* dev0, const float* dev1, int fn, hipStream_t s);
 
-// Per-tensor e4m3 quantization: amax (into ws[0]), then scale and codes.
+// Per-tensor e4m3 quantization: amax (into ws[0], from per-workgroup maxima in ws[64 ..
+// 64 + kQuantizeParts)), then scale and codes. The workspace holds kQuantizeWsBytes.
+constexpr int kQuantizeParts = 2048;
+constexpr size_t kQuantizeWsBytes = 256 + kQuantizeParts * sizeof(float);
 hipError_t run_quantize_e4m3(DType src_t, const void* src, int64_t n, void* dst, float* scale,
                              float* ws, hipStream_t s);
 // Exact e4m3 -> bf16 widening (every e4m3 value is a bf16 value).

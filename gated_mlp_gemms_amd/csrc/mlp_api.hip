@@ -837,7 +837,7 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
   return MLP_OK;
 }
 
-size_t mlp_quantize_workspace_bytes(void) { return kAlign; }
+size_t mlp_quantize_workspace_bytes(void) { return kQuantizeWsBytes; }
 
 mlp_status mlp_time_stage_once(int stage, void* begin, void* end) {
   if (stage < 0 || stage >= MLP_STAGE_COUNT) return fail(MLP_ERR_INVALID_ARG, "stage %d is not an mlp_stage", stage);
@@ -855,7 +855,8 @@ mlp_status mlp_quantize_e4m3(const void* src, int dtype, int64_t n, void* dst, f
   if (!src || !dst || !scale || !ws) return fail(MLP_ERR_INVALID_ARG, "src, dst, scale and workspace are required");
   if (!aligned4(src) || !aligned4(scale) || !aligned16(ws))
     return fail(MLP_ERR_ALIGNMENT, "src and scale must be 4-byte aligned, workspace 16-byte aligned");
-  if (ws_bytes < kAlign) return fail(MLP_ERR_WORKSPACE, "workspace of %zu bytes is smaller than %zu", ws_bytes, kAlign);
+  if (ws_bytes < kQuantizeWsBytes)
+    return fail(MLP_ERR_WORKSPACE, "workspace of %zu bytes is smaller than %zu", ws_bytes, kQuantizeWsBytes);
   return hip_status(run_quantize_e4m3(dtype_of(dtype), src, n, dst, scale,
                                       reinterpret_cast<float*>(ws), reinterpret_cast<hipStream_t>(stream)),
                     "quantize");

@@ -10,7 +10,7 @@ from __future__ import annotations
 import torch
 
 from . import (GATED_ACTS, make_desc, make_fp8, mlp_bwd, mlp_fp8_next_scale, mlp_fwd, mlp_fwd_infer,
-               mlp_quantize_e4m3, mlp_quantize_fp8, workspace_bytes)
+               mlp_quantize_e4m3, mlp_quantize_fp8, mlp_quantize_workspace_bytes, workspace_bytes)
 
 E4M3_MAX = 448.0
 E5M2_MAX = 57344.0
@@ -69,7 +69,7 @@ class MlpRunner:
             self.scales[3] = 1.0              # bootstrap post scale
             self.scales[5] = GRAD_SCALE
             self.scales[6] = GRAD_SCALE       # bootstrap dpre scale
-            self.ws_q = torch.empty(256, dtype=torch.uint8, device=dev)
+            self.ws_q = torch.empty(mlp_quantize_workspace_bytes(), dtype=torch.uint8, device=dev)
             s = self.scales
             sp = [s[i:i + 1].data_ptr() for i in range(8)]
             extra = {}

@@ -180,7 +180,8 @@ mlp_status mlp_bwd(const mlp_desc* desc, const void* dout, const void* x, const 
                    int grad_accum, const mlp_fp8* fp8, void* workspace, size_t workspace_bytes,
                    void* stream);
 
-/* Bytes of workspace mlp_quantize_e4m3 needs (a few floats). Host only. */
+/* Bytes of workspace mlp_quantize_e4m3 needs (8448: the amax and the per-workgroup maxima it
+ * reduces). Host only. */
 size_t mlp_quantize_workspace_bytes(void);
 
 /*

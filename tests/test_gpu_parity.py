@@ -467,7 +467,7 @@ def test_fp16_quantize_e4m3_matches_oracle():
     d = src.cuda()
     q = torch.empty(d.numel(), dtype=torch.uint8, device="cuda")
     sc = torch.empty(1, dtype=torch.float32, device="cuda")
-    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(int(gm.mlp_quantize_workspace_bytes()), dtype=torch.uint8, device="cuda")
     gm.mlp_quantize_e4m3(d, q, sc, ws)
     torch.cuda.synchronize()
     assert float(sc.item()) == np.float32(ref_s)
