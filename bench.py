@@ -8,8 +8,9 @@ dW_down) of the LLaMA-shaped MLP: x [2, 1024, 4096] (M = 2048 tokens), W_gate/W_
 
 Prints one JSON line: TFLOP/s on the model FLOP count 18*M*d*H (2*M*N*K per GEMM), the
 fraction of the bf16 MFMA peak, the roofline of the slowest kernel stage (timed with HIP events
-on the library's stream inside the timed region), and the float64 oracle's throughput on a
-bounded sample on the host CPU.
+on the library's stream inside the timed region; priced at the dense peak of that stage's operand
+type: bf16, fp32, or fp8 for the e4m3 / e5m2 products of the fp8 workloads), and the float64
+oracle's throughput on a bounded sample on the host CPU.
 """
 from __future__ import annotations
 
@@ -22,6 +23,7 @@ import time
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
 PEAK_FP8_TFLOPS = 5000.0
+PEAK_FP32_TFLOPS = 157.3       # MI355X dense fp32 (published)
 PEAK_HBM_GBS = 8000.0
 METRIC = "fused SwiGLU MLP fwd+bwd TFLOP/s and % bf16 MFMA peak, 4096×11008, 2048 tok"
 
@@ -278,8 +280,12 @@ def main():
     dom = max(stage_us, key=stage_us.get)
     peak = PEAK_BF16_TFLOPS
     traffic, traffic_src = measured_traffic(w.name, dom)
-    roof = {"bound": "mfma", "achieved": stage_tf[dom], "peak": peak, "unit": "TFLOP/s",
-            "frac": round(stage_tf[dom] / peak, 4), "traffic": traffic, "kernel_stage": dom,
+    # the dominant stage's product is priced at the peak of its own operand type
+    fp8_stages = ({"up", "down", "recompute"} if w.fp8_fwd else set()) | \
+        ({"dact", "dw_down", "dx", "dw_up"} if w.fp8_bwd else set())
+    stage_peak = PEAK_FP8_TFLOPS if dom in fp8_stages else (PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS)
+    roof = {"bound": "mfma", "achieved": stage_tf[dom], "peak": stage_peak, "unit": "TFLOP/s",
+            "frac": round(stage_tf[dom] / stage_peak, 4), "traffic": traffic, "kernel_stage": dom,
             "flop_per_launch": sf[dom], "avg_launch_us": stage_us[dom], "traffic_source": traffic_src}
     log(f"[bench] {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of bf16 peak); "
         f"stages us {stage_us}")
