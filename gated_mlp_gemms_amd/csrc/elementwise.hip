@@ -306,32 +306,46 @@ __global__ __launch_bounds__(kEwThreads) void dequant8_kernel(const uint8_t* src
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// fp8 codes of a [rows, cols] matrix, row-major and / or transposed, one 64 x 64 tile at a time
-// through LDS. Loads and row-major stores are 8 elements per lane along a row; the transposed
-// stores are 16 codes (16 source rows) per lane. Source rows past `rows` (up to the transposed
-// leading dimension) quantize to code 0, which pads the transposed output.
+// fp8 codes of a [rows, cols] matrix, row-major and / or transposed, one 128 x 128 tile of codes
+// at a time through LDS (as 32-bit words, rows padded by one word). Every global access of a wave
+// covers whole 128-byte lines: a bf16 source row of the tile is 16 lanes x 16 bytes, a code row
+// 8 lanes x 16 bytes, and each transposed output column's 128 rows are written by 8 lanes of one
+// wave. For the transposed stores a lane reads a 16-row x 4-column block of codes (16 words),
+// regroups its bytes into the 4 columns in registers, and writes 16 bytes to each column. Source
+// rows past `rows` (up to the transposed leading dimension) give code 0, which pads the
+// transposed output.
+__device__ __forceinline__ uint32_t byte_col(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3, int j) {
+  const int sh = 8 * j;
+  return ((r0 >> sh) & 0xffu) | (((r1 >> sh) & 0xffu) << 8) | (((r2 >> sh) & 0xffu) << 16) | (((r3 >> sh) & 0xffu) << 24);
+}
+
 template <bool CODES>
 __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t rows, int64_t cols, int64_t ld_src,
                                                       int relu_sq, int e5m2, const float* scale, uint8_t* dst,
                                                       uint8_t* dst_t, int64_t ld_t, int64_t n_ct, int64_t n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[64][64];
+  constexpr int TW = 33;   // words per LDS row: 128 codes + 1 word of padding
+  __shared__ uint32_t tile[128 * TW];
   const int tid = threadIdx.x;
   const float sc = CODES ? 1.0f : *scale;
   for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-    const int64_t r0 = (t / n_ct) * 64, c0 = (t % n_ct) * 64;
-    const int lc = (tid & 7) * 8;
+    const int64_t r0 = (t / n_ct) * 128, c0 = (t % n_ct) * 128;
+    if constexpr (CODES) {   // 8 lanes x 16 codes per row, 32 rows per pass
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int lr = (tid >> 3) + 32 * pass;
-      const int64_t r = r0 + lr, c = c0 + lc;
-      uint32_t lo = 0, hi = 0;
-      const bool in = r < rows && c < cols;
-      if (in) {
-        if constexpr (CODES) {
-          const u32x2 x = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(src) + r * ld_src + c);
-          lo = x[0];
-          hi = x[1];
-        } else {
+      for (int pass = 0; pass < 4; ++pass) {
+        const int lr = (tid >> 3) + 32 * pass, lc = (tid & 7) * 16;
+        const int64_t r = r0 + lr, c = c0 + lc;
+        u32x4 x = {0, 0, 0, 0};
+        if (r < rows && c < cols) x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(src) + r * ld_src + c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tile[lr * TW + lc / 4 + q] = x[q];
+      }
+    } else {                 // 16 lanes x 8 values per row, 16 rows per pass
+#pragma unroll
+      for (int pass = 0; pass < 8; ++pass) {
+        const int lr = (tid >> 4) + 16 * pass, lc = (tid & 15) * 8;
+        const int64_t r = r0 + lr, c = c0 + lc;
+        uint32_t lo = 0, hi = 0;
+        if (r < rows && c < cols) {
           const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(src) + r * ld_src + c);
           float y[8];
 #pragma unroll
@@ -350,20 +364,28 @@ __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t r
             lo = f32x4_to_fp8<false>(y[0], y[1], y[2], y[3]);
             hi = f32x4_to_fp8<false>(y[4], y[5], y[6], y[7]);
           }
+          if (dst) *reinterpret_cast<u32x2*>(dst + r * cols + c) = u32x2{lo, hi};
         }
-        if (dst) *reinterpret_cast<u32x2*>(dst + r * cols + c) = u32x2{lo, hi};
+        tile[lr * TW + lc / 4] = lo;
+        tile[lr * TW + lc / 4 + 1] = hi;
       }
-      *reinterpret_cast<u32x2*>(&tile[lr][lc]) = u32x2{lo, hi};
     }
     __syncthreads();
-    if (dst_t) {
-      const int oc = tid >> 2, orow = (tid & 3) * 16;
-      const int64_t c = c0 + oc, r = r0 + orow;
-      if (c < cols && r < ld_t) {
-        u32x4 w = {0, 0, 0, 0};
+    if (dst_t) {   // lane: rows 16 rb .. 16 rb + 15, columns 4 cw .. 4 cw + 3 of the tile
+      const int rb = tid & 7, cw = tid >> 3;
+      const int64_t r = r0 + 16 * rb;
+      uint32_t w[16];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) w[k >> 2] |= (uint32_t)tile[orow + k][oc] << (8 * (k & 3));
-        *reinterpret_cast<u32x4*>(dst_t + c * ld_t + r) = w;
+      for (int k = 0; k < 16; ++k) w[k] = tile[(16 * rb + k) * TW + cw];
+      if (r < ld_t) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t c = c0 + 4 * cw + j;
+          if (c < cols)
+            *reinterpret_cast<u32x4*>(dst_t + c * ld_t + r) =
+                u32x4{byte_col(w[0], w[1], w[2], w[3], j), byte_col(w[4], w[5], w[6], w[7], j),
+                      byte_col(w[8], w[9], w[10], w[11], j), byte_col(w[12], w[13], w[14], w[15], j)};
+        }
       }
     }
     __syncthreads();
@@ -375,9 +397,10 @@ __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t r
 hipError_t run_quantize_fp8_2d(DType src_t, const void* src, int64_t rows, int64_t cols, int64_t ld_src,
                                int relu_sq, int e5m2, const float* scale, void* dst, void* dst_t,
                                int64_t ld_t, hipStream_t s) {
-  if (rows < 1 || cols < 16 || cols % 16 || (dst_t && (ld_t < rows || ld_t % 16))) return hipErrorInvalidValue;
+  if (rows < 1 || cols < 16 || cols % 16 || ld_src < cols || ld_src % 16 || (dst_t && (ld_t < rows || ld_t % 16)))
+    return hipErrorInvalidValue;
   const int64_t cover = dst_t ? ld_t : rows;
-  const int64_t n_ct = (cols + 63) / 64, n_rt = (cover + 63) / 64, n_tiles = n_ct * n_rt;
+  const int64_t n_ct = (cols + 127) / 128, n_rt = (cover + 127) / 128, n_tiles = n_ct * n_rt;
   const int grid = (int)std::min<int64_t>(n_tiles, 8192);
   uint8_t* d = reinterpret_cast<uint8_t*>(dst);
   uint8_t* dt = reinterpret_cast<uint8_t*>(dst_t);
