@@ -138,6 +138,10 @@ def test_quantize_checks():
     assert L.mlp_quantize_e4m3(FAKE, 1, 0, FAKE, FAKE, FAKE, 256, None) == gm._lib.MLP_ERR_INVALID_ARG
     assert L.mlp_quantize_e4m3(FAKE, 5, 10, FAKE, FAKE, FAKE, 256, None) == gm._lib.MLP_ERR_INVALID_ARG
     assert L.mlp_quantize_e4m3(FAKE, 1, 10, FAKE, FAKE, FAKE, 8, None) == gm._lib.MLP_ERR_WORKSPACE
+    # the workspace holds the amax and the per-workgroup maxima (2048 floats after 256 bytes)
+    need = gm.mlp_quantize_workspace_bytes()
+    assert need == 256 + 2048 * 4
+    assert L.mlp_quantize_e4m3(FAKE, 1, 10, FAKE, FAKE, FAKE, need - 1, None) == gm._lib.MLP_ERR_WORKSPACE
     assert L.mlp_quantize_e4m3(None, 1, 10, FAKE, FAKE, FAKE, 256, None) == gm._lib.MLP_ERR_INVALID_ARG
 
 
