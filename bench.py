@@ -332,7 +332,8 @@ def main():
 
     dtype = ("fp8-e4m3 fwd / e5m2 x e4m3 bwd" if w.fp8_bwd else "fp8-e4m3 fwd / bf16 bwd") if w.fp8_fwd else w.dtype
     line = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC if w.name == HEADLINE else f"MLP fwd+bwd TFLOP/s (model FLOP count), {w.name}",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic",

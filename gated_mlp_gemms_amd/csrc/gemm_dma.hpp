@@ -488,6 +488,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
     read_frags(0, 0, 0);
+    // drained here so that the loop header's LDS waits are counted from the loop body alone:
+    // the prologue issues these reads in another order, and a wait merged over both paths
+    // would be lgkmcnt(0) before the first MFMA of every K-step (waiting for the last B
+    // fragment refill instead of the first)
+    wait_lgkmcnt0();
   }
   int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {

@@ -32,6 +32,8 @@ import sys
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 STAGE_ORDER_GATED = ["up", "down", "dact", "dw_down", "dx", "dw_up"]
+# the backward with activation recompute re-runs the up projection before the d-activation
+STAGE_ORDER_RECOMPUTE = ["up", "down", "recompute", "dact", "dw_down", "dx", "dw_up"]
 
 
 def kernel_sources_sha256() -> str:
@@ -89,17 +91,20 @@ def short_name(name: str) -> str:
         dma, types, bm, bn, ak, bk, epi, waves = f
         lay = {("1", "1"): "NT", ("1", "0"): "NN", ("0", "0"): "TN"}.get((ak, bk), "??")
         epin = _EPI[int(epi)]
-        t = "e4m3" if "e4m3" in types else ("f32" if types.startswith("ff") else "bf16")
+        t = ("e5m2xe4m3" if "f8g" in types else "e4m3" if "e4m3" in types
+             else "f16" if types.startswith("DF16_") else "f32" if types.startswith("ff") else "bf16")
         out = "f32" if "DF16bf" in types or types.endswith("f") else ""
         w = f",{waves}w" if waves else ""
         return f"gemm{'' if dma else '_regstaged'}<{t},{lay},{bm}x{bn}{w},{epin}{',' + out + ' out' if out else ''}>"
-    for k in ("splitk_reduce", "gated_reduce", "gated_act", "plain_act", "absmax", "quantize_kernel", "dequant", "zero_f32"):
+    for k in ("splitk_reduce", "gated_reduce", "gated_act", "plain_act", "absmax8_part", "absmax", "max_parts",
+              "quantize8", "quantize_kernel", "quant2d", "dequant8", "dequant", "zero_f32"):
         if k in name:
             return k
     return name.split("(")[0][:60]
 
 
-def summarize_trace(trace_dir: str, out_txt: str, command: str, first_step: int = 0, steps: int = 0) -> None:
+def summarize_trace(trace_dir: str, out_txt: str, command: str, first_step: int = 0, steps: int = 0,
+                    stages: list[str] = STAGE_ORDER_GATED) -> None:
     stats = _one(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
     rows = list(csv.DictReader(open(stats)))
     lines = [f"# rocprofv3 kernel statistics", f"# command: {command}", f"# kernel sources sha256: {kernel_sources_sha256()}",
@@ -114,11 +119,11 @@ def summarize_trace(trace_dir: str, out_txt: str, command: str, first_step: int 
     trace = _one(os.path.join(trace_dir, "**", "*kernel_trace.csv"))
     disp = sorted((int(r["Dispatch_Id"]), r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
                   for r in csv.DictReader(open(trace)))
-    per_step = _per_step(disp, STAGE_ORDER_GATED)
+    per_step = _per_step(disp, stages)
     timed = per_step[first_step:first_step + steps] if steps else per_step[first_step:]
     lines += ["", f"# per-stage kernel time, average over {len(timed)} timed steps (dispatch order; a split-K "
                   f"reduce counts with its GEMM)", f"{'stage':10s} {'kernels':64s} {'avg us':>10s}"]
-    for st in STAGE_ORDER_GATED:
+    for st in stages:
         if not timed:
             break
         kern = " + ".join(dict.fromkeys(short_name(n) for n, _ in timed[0][st]))
@@ -128,31 +133,45 @@ def summarize_trace(trace_dir: str, out_txt: str, command: str, first_step: int 
     print("\n".join(lines))
 
 
+def is_reduce(name: str) -> bool:
+    return "splitk_reduce" in name or "gated_reduce" in name
+
+
 def _per_step(disp, stages):
     """Split this library's dispatches into steps (a step starts at each up-projection) and each
-    step into stages (each GEMM opens the next stage, except one with the same epilogue as the GEMM
-    before it: a stage run as two launches over its output columns; other kernels join the current
-    stage). Only whole steps are returned; launches of other libraries (a fill, a copy) are skipped."""
-    steps, cur, idx, last_epi = [], None, -1, None
+    step into stages. Each GEMM opens the next stage, except one with the same epilogue as the GEMM
+    before it (a stage run as two launches over its output columns). A split-K reduce joins the
+    GEMM before it; other kernels of the library (quantize, transpose, widen) prepare an operand
+    and join the GEMM after them. With a "recompute" stage, an up-projection GEMM right after the
+    down projection is the backward's recompute, not a new step. Only whole steps are returned;
+    launches of other libraries (a fill, a copy) are skipped."""
+    steps, cur, idx, last_epi, pending = [], None, -1, None, []
+    rec = stages.index("recompute") if "recompute" in stages else -1
     for _, name, val in disp:
         if not is_library_kernel(name):
             continue
         epi = gemm_epilogue(name)
-        is_gemm = epi is not None
-        if epi in (2, 3, 6):   # GATED, ACT, F8ACT: the up-projection
+        if epi is None:
+            if is_reduce(name) and cur is not None and 0 <= idx < len(stages):
+                cur[stages[idx]].append((name, val))
+            elif not is_reduce(name):
+                pending.append((name, val))
+            continue
+        if epi in (2, 3, 6) and not (cur is not None and rec > 0 and idx == rec - 1):   # an up projection
             cur = {st: [] for st in stages}
             steps.append(cur)
             idx = 0
         elif cur is None:
+            pending = []
             continue
-        elif is_gemm and epi != last_epi:
+        elif epi != last_epi:
             idx += 1
-        if is_gemm:
-            last_epi = epi
+        last_epi = epi
         if idx < len(stages):
-            cur[stages[idx]].append((name, val))
+            cur[stages[idx]].extend(pending + [(name, val)])
         else:
             cur["_extra"] = True
+        pending = []
     return [s for s in steps if all(s[st] for st in stages) and "_extra" not in s]
 
 
@@ -245,6 +264,7 @@ def main(argv=None):
     t.add_argument("--command", required=True)
     t.add_argument("--first-step", type=int, default=0, help="whole steps to skip (the bench's warmup)")
     t.add_argument("--steps", type=int, default=0, help="whole steps to average (0: all)")
+    t.add_argument("--recompute", action="store_true", help="the step's backward recomputes the pre-activation")
     f = sub.add_parser("traffic")
     f.add_argument("fetch_dir")
     f.add_argument("write_dir")
@@ -261,7 +281,8 @@ def main(argv=None):
     m.add_argument("--steps", type=int, default=0)
     a = ap.parse_args(argv)
     if a.what == "trace":
-        summarize_trace(a.trace_dir, a.out_txt, a.command, a.first_step, a.steps)
+        summarize_trace(a.trace_dir, a.out_txt, a.command, a.first_step, a.steps,
+                        STAGE_ORDER_RECOMPUTE if a.recompute else STAGE_ORDER_GATED)
     elif a.what == "mfma":
         summarize_mfma(a.pmc_dir, a.out_json, a.command, a.first_step, a.steps)
     else:

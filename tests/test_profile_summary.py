@@ -32,3 +32,39 @@ def test_stages_with_and_without_the_column_split():
     assert ps.short_name(steps[0]["down"][1][0]) == "splitk_reduce"
     assert ps.short_name(DACT_B) == "gemm<bf16,NN,256x128,8w,DGATED>"
     assert ps.short_name(DW) == "gemm<bf16,TN,256x256,8w,STORE>"
+
+
+ACT = _g(128, 128, 1, 1, 6, 4).replace("DF16bDF16b", "N4gmlp4e4m3EDF16b")     # e4m3 up projection
+DOWN8 = _g(256, 256, 1, 1, 0, 4).replace("DF16bDF16b", "N4gmlp4e4m3EDF16b")
+QUANT = "_ZN4gmlp12_GLOBAL__N_116quantize8_kernelEPKvlPhPKfi"
+ABSMAX = "_ZN4gmlp12_GLOBAL__N_119absmax8_part_kernelEPKvlPf"
+DACT8 = _g(128, 128, 1, 1, 7, 4).replace("DF16bDF16b", "N4gmlp3f8gEDF16b")
+T2D = "_ZN4gmlp12_GLOBAL__N_114quant2d_kernelEPKvlllPhlPKfiiPhl"
+DW8 = _g(256, 256, 1, 1, 0, 4).replace("DF16bDF16b", "N4gmlp3f8gEDF16b")
+DX8 = _g(256, 256, 1, 1, 1, 4).replace("DF16bDF16b", "N4gmlp3f8gEf")
+
+
+def test_operand_preparation_joins_the_next_gemm():
+    # fp8 step: per-tensor quantize before the up projection, dout quantize before the
+    # d-activation, transposes before the weight-gradient products
+    step = [ABSMAX, QUANT, ACT, DOWN8, QUANT, DACT8, T2D, DW8, DX8, RED, T2D, T2D, DW8]
+    names = step + step + [ABSMAX]
+    steps = ps._per_step([(i, n, 1.0) for i, n in enumerate(names)], ps.STAGE_ORDER_GATED)
+    assert len(steps) == 2
+    for s in steps:
+        assert [len(s[st]) for st in ps.STAGE_ORDER_GATED] == [3, 1, 2, 2, 2, 3]
+        assert [ps.short_name(n) for n, _ in s["up"]] == ["absmax8_part", "quantize8", "gemm<e4m3,NT,128x128,4w,F8ACT>"]
+        assert ps.short_name(s["dx"][-1][0]) == "splitk_reduce"
+    assert ps.short_name(DACT8) == "gemm<e5m2xe4m3,NT,128x128,4w,F8DACT>"
+
+
+def test_recompute_gemm_is_a_stage_not_a_new_step():
+    step = [UP, DOWN, RED, UP, DACT_A, DW, DX, RED, DW]
+    names = step + step
+    disp = [(i, n, 1.0) for i, n in enumerate(names)]
+    steps = ps._per_step(disp, ps.STAGE_ORDER_RECOMPUTE)
+    assert len(steps) == 2
+    assert [len(steps[0][st]) for st in ps.STAGE_ORDER_RECOMPUTE] == [1, 2, 1, 1, 1, 2, 1]
+    # without the recompute stage the same launches read as one up projection per forward and
+    # per backward, and no step is whole
+    assert ps._per_step(disp, ps.STAGE_ORDER_GATED) == []
