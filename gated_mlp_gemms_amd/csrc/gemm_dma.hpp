@@ -41,6 +41,21 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
   asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
 }
 
+// The same DMA with the address split into a wave-uniform 64-bit base (SGPRs) and a per-lane
+// 32-bit byte offset (one VGPR instead of a 64-bit pointer per lane).
+__device__ __forceinline__ void dma16s(const char* base, uint32_t voff, char* lds_wave_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)GMLP_LDS(lds_wave_base);
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+
+// A uniform address the optimizer may not look through: the per-lane sum opaque(base + step) +
+// offset then stays inside the K loop instead of being re-associated into a loop-invariant
+// 64-bit base + offset per lane and hoisted (which would cost two VGPRs per DMA).
+__device__ __forceinline__ const char* opaque_sgpr(const char* p) {
+  asm("" : "+s"(p));
+  return p;
+}
+
 // vmcnt(N), N < 64 (gfx9 encoding: low 4 bits in [3:0], high 2 bits in [15:14]); expcnt and
 // lgkmcnt left at their maxima.
 template <int N>
@@ -96,9 +111,13 @@ template <> struct StepGeo<e4m3> { static constexpr int ROWB = 128; };
 template <> struct StepGeo<f8g> { static constexpr int ROWB = 128; };
 
 // ---- K-major operand: ROWS rows x ROWB bytes per stage -------------------------------------
-// One DMA instruction fills 1 KB = 1024/ROWB rows: lane l -> row (1024/ROWB) j + l / CPR,
-// slot l % CPR (CPR = ROWB/16 chunks per row), which holds the row's logical chunk
-// slot ^ swz(row).
+// One DMA instruction fills 1 KB = 8 rows of 128 bytes: lane l -> row 8 j + l / 8, slot l % 8,
+// which holds the row's logical chunk slot ^ swz(row). A tile row comes from one of two bases
+// (the gate / up halves of a gated tile, or two matrices stacked along the rows): rows below
+// split_row from base0, the rest from base1, each base shifted so tile row r sits r row pitches
+// past it. With every row of the tile inside its matrix (interior), the lane part of an address
+// depends on the instruction only through the parity of j (the swizzle's row bit 3), so a lane
+// keeps two 32-bit offsets and the rest of each address is wave-uniform scalar arithmetic.
 template <typename T, int ROWS, int WAVES>
 struct KTileDma {
   static constexpr int ES = ElemTraits<T>::bytes;
@@ -107,54 +126,69 @@ struct KTileDma {
   static constexpr int CPR = ROWB / 16;
   static constexpr int RPI = 1024 / ROWB;            // rows per DMA instruction
   static constexpr int kInst = ROWS / RPI / WAVES;   // per wave per stage
+  static_assert(ROWB == 128 && RPI == 8, "128-byte K-steps: 8 rows per DMA instruction");
   static_assert(kInst >= 1 && ROWS % (RPI * WAVES) == 0, "tile rows must split over the waves");
-  const char* ptr[kInst];
-  int kc[kInst];
+  uint32_t voff[2];           // per lane, interior tiles: offset within an even / odd instruction's rows
+  const char* base0;          // uniform: the two bases at the split's first k
+  const char* base1;
+  int64_t ld_bytes;           // uniform row pitch (shared by both bases)
+  int split_row;              // uniform: first tile row read from base1
+  bool interior;              // uniform: no tile row is clamped
 
-  // chunk swizzle: 16 consecutive rows reading one logical chunk hit 16 distinct 16-byte bank
-  // groups of a 256-byte bank cycle
-  static __device__ __forceinline__ int swz(int row) {
-    if constexpr (ROWB == 128) return (row ^ (row >> 3)) & 7;
-    else return (row >> 2) & 3;
-  }
+  // chunk swizzle: 16 consecutive rows from a multiple of 16 reading one logical chunk hit 16
+  // distinct 16-byte bank groups of a 256-byte bank cycle (rows r and r + 8 differ in the XOR)
+  static __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
   static __device__ __forceinline__ int off(int row, int chunk) {
     return row * ROWB + ((chunk ^ swz(row)) << 4);
   }
 
-  // row_base(row): the row's address; tile rows past the matrix are given an existing row (their
-  // products only reach output rows that are never stored), so no row needs a zero fill.
-  template <typename RowPtr>
-  __device__ __forceinline__ void init(int wave, int lane, int kbeg, RowPtr row_base) {
+  // b0, b1: the shifted bases at k = 0; split: first tile row from b1; locate(r) -> {which,
+  // rel}: tile row r is `rel` row pitches past base `which` (rel = r unless the row is past its
+  // matrix: such rows are given an existing row, as their products only reach output rows that
+  // are never stored, so no row needs a zero fill). interior: locate(r) == {r >= split, r} for
+  // every tile row. split must be a multiple of 8 (an instruction's rows share one base).
+  __device__ __forceinline__ void init(int lane, int kbeg, const char* b0, const char* b1, int64_t ld, int split,
+                                       bool inner) {
+    base0 = b0 + (int64_t)kbeg * ES;
+    base1 = b1 + (int64_t)kbeg * ES;
+    ld_bytes = ld;
+    split_row = split;
+    interior = inner;
 #pragma unroll
-    for (int i = 0; i < kInst; ++i) {
-      const int j = wave * kInst + i;
-      const int row = RPI * j + lane / CPR;
-      const int c = (lane % CPR) ^ swz(row);
-      kc[i] = c * E;
-      ptr[i] = row_base(row) + (int64_t)(kbeg + c * E) * ES;
-    }
+    for (int par = 0; par < 2; ++par)
+      voff[par] = (uint32_t)((lane / CPR) * ld) + (uint32_t)((((lane % CPR) ^ (lane / CPR) ^ par)) * 16);
   }
-  // K-step at k_rel (relative to the split's first k) of a K range k_left long. A step wholly
-  // inside the range (all but the last partial step and the trailing zero steps; a uniform test)
-  // costs one address add per DMA; otherwise chunks past the range read the zero chunk.
-  __device__ __forceinline__ void issue(char* tile, int wave, int k_rel, int k_left) const {
-    if (k_rel + ROWB / ES <= k_left) {
+  // scalar base of instruction i (rows 8 j ..) at K offset k_rel
+  __device__ __forceinline__ const char* sbase(int wave, int i, int k_rel) const {
+    const int r = RPI * (wave * kInst + i);
+    return (r >= split_row ? base1 : base0) + (int64_t)r * ld_bytes + (int64_t)k_rel * ES;
+  }
+  // K-step at k_rel (relative to the split's first k) of a K range k_left long. An interior tile's
+  // step wholly inside the range (all but the last partial step and the trailing zero steps; a
+  // uniform test) is one scalar add per DMA; otherwise each lane places its row and chunk and
+  // chunks past the range read the zero chunk.
+  template <typename Locate>
+  __device__ __forceinline__ void issue(char* tile, int wave, int lane, int k_rel, int k_left, Locate locate) const {
+    if (interior && k_rel + ROWB / ES <= k_left) {
 #pragma unroll
-      for (int i = 0; i < kInst; ++i) dma16(ptr[i] + (int64_t)k_rel * ES, tile + (wave * kInst + i) * 1024);
+      for (int i = 0; i < kInst; ++i)
+        dma16s(sbase(wave, i, k_rel), ((wave * kInst + i) & 1) ? voff[1] : voff[0], tile + (wave * kInst + i) * 1024);
     } else {
 #pragma unroll
-      for (int i = 0; i < kInst; ++i) {
-        const void* src = k_rel + kc[i] < k_left ? (const void*)(ptr[i] + (int64_t)k_rel * ES)
-                                                 : (const void*)g_zero_chunk;
-        dma16(src, tile + (wave * kInst + i) * 1024);
-      }
+      for (int i = 0; i < kInst; ++i) issue_i(tile, wave, lane, i, k_rel, k_left, locate);
     }
   }
-  // DMA i of issue() alone, with a per-lane range check (no branch): for issuing the DMAs one
-  // at a time between MFMAs.
-  __device__ __forceinline__ void issue_i(char* tile, int wave, int i, int k_rel, int k_left) const {
-    const void* src = k_rel + kc[i] < k_left ? (const void*)(ptr[i] + (int64_t)k_rel * ES) : (const void*)g_zero_chunk;
-    dma16(src, tile + (wave * kInst + i) * 1024);
+  // DMA i of issue(), placed and range-checked per lane (no branch)
+  template <typename Locate>
+  __device__ __forceinline__ void issue_i(char* tile, int wave, int lane, int i, int k_rel, int k_left,
+                                          Locate locate) const {
+    const int row = RPI * (wave * kInst + i) + lane / CPR;
+    const int c = (lane % CPR) ^ swz(row);
+    const int2 loc = locate(row);
+    const char* b0k = opaque_sgpr(base0 + (int64_t)k_rel * ES);
+    const char* b1k = opaque_sgpr(base1 + (int64_t)k_rel * ES);
+    const char* src = (loc.x ? b1k : b0k) + ((int64_t)loc.y * ld_bytes + c * 16);
+    dma16(k_rel + c * E < k_left ? (const void*)src : (const void*)g_zero_chunk, tile + (wave * kInst + i) * 1024);
   }
   static __device__ __forceinline__ u32x4 read(const char* tile, int row, int ch) {
     return *reinterpret_cast<const u32x4*>(tile + off(row, ch));
@@ -163,63 +197,61 @@ struct KTileDma {
 
 // ---- MN-major bf16 operand: 64 k-rows x ROWS columns per stage --------------------------------
 // The operand may be two matrices stacked along K (rows k < k_split from the first, the rest
-// from the second, both with the same leading dimension). Each lane keeps the address of its
-// chunk in the first matrix at the first K-step; a K-step adds a uniform offset, and a lane whose
-// k-row lies in the second matrix adds the uniform distance between the two, so the issue is a
-// few selects per DMA and no branch.
+// from the second, both with the same leading dimension). Each lane keeps the 32-bit byte offset
+// of its chunk from a wave-uniform base (the first matrix at the split's first k); a K-step adds
+// a uniform offset to the base, plus the uniform distance between the two matrices when the step
+// lies in the second, so the issue of an in-range step is scalar arithmetic and no branch.
 template <int ROWS, int WAVES>
 struct MNTileDma {
   static constexpr int KROWS = 64;
   static constexpr int ROWB = ROWS * 2;               // bytes per k-row
   static constexpr int kInst = KROWS * ROWB / 1024 / WAVES;   // per wave per stage
   static_assert(kInst >= 1, "tile too narrow");
-  const char* ptr[kInst];   // chunk address at K-step 0, as if every k-row were in the first matrix
-  int krow[kInst];
+  uint32_t voff[kInst];   // per lane: k-row * pitch + column bytes, from base
+  const char* base;       // uniform
 
   // k-rows kr .. kr+3 land in distinct 64-byte groups, and k-rows 8 apart (read in the same pass
   // by the 16x16 fragments) in distinct 32-byte halves of them
   static __device__ __forceinline__ int phys_chunk(int c, int kr) { return c ^ ((kr & 3) << 2) ^ (((kr >> 3) & 1) << 1); }
+  static __device__ __forceinline__ int krow_of(int wave, int lane, int i) {
+    return ((wave * kInst + i) * 1024 + lane * 16) / ROWB;
+  }
 
-  // base: element (0, tile column 0) of the first matrix; ld_bytes: its row pitch; ncols:
-  // columns of the matrix from tile column 0 on (a multiple of 8). Chunks of tile columns past
-  // the matrix read its last chunk instead: their products only reach output columns that are
-  // never stored.
-  __device__ __forceinline__ void init(int wave, int lane, const char* base, int64_t ld_bytes, int kbeg,
+  // b: element (0, tile column 0) of the first matrix; ld_bytes: its row pitch; ncols: columns of
+  // the matrix from tile column 0 on (a multiple of 8). Chunks of tile columns past the matrix
+  // read its last chunk instead: their products only reach output columns that are never stored.
+  __device__ __forceinline__ void init(int wave, int lane, const char* b, int64_t ld_bytes, int kbeg,
                                        int ncols) {
+    base = b + (int64_t)kbeg * ld_bytes;
 #pragma unroll
     for (int i = 0; i < kInst; ++i) {
       const int j = wave * kInst + i;
       const int byte = j * 1024 + lane * 16;
       const int kr = byte / ROWB;
       const int col = min(phys_chunk((byte % ROWB) >> 4, kr) * 8, ncols - 8);   // the XOR is an involution
-      krow[i] = kr;
-      ptr[i] = base + (int64_t)(kbeg + kr) * ld_bytes + col * 2;
+      voff[i] = (uint32_t)(kr * ld_bytes) + (uint32_t)(col * 2);
     }
   }
   // K-step starting at k0 (absolute); step_off: byte offset of this K-step from the first;
   // second: distance from a k-row's address in the first matrix to its address in the second.
-  // A step wholly inside [.., kend) and on one side of k_split (a uniform test) costs one
-  // address add per DMA; otherwise each k-row is placed and range-checked on its own.
-  __device__ __forceinline__ void issue(char* tile, int wave, int k0, int kend, int64_t step_off, int k_split,
+  // A step wholly inside [.., kend) and on one side of k_split (a uniform test) costs one scalar
+  // address add; otherwise each k-row is placed and range-checked on its own.
+  __device__ __forceinline__ void issue(char* tile, int wave, int lane, int k0, int kend, int64_t step_off, int k_split,
                                         int64_t second) const {
     if (k0 + KROWS <= kend && (k0 + KROWS <= k_split || k0 >= k_split)) {
-      const int64_t off = step_off + (k0 >= k_split ? second : 0);
+      const char* b = base + step_off + (k0 >= k_split ? second : 0);
 #pragma unroll
-      for (int i = 0; i < kInst; ++i) dma16(ptr[i] + off, tile + (wave * kInst + i) * 1024);
+      for (int i = 0; i < kInst; ++i) dma16s(b, voff[i], tile + (wave * kInst + i) * 1024);
     } else {
 #pragma unroll
-      for (int i = 0; i < kInst; ++i) {
-        const int k = k0 + krow[i];
-        const char* s = ptr[i] + step_off + (k >= k_split ? second : 0);
-        dma16(k < kend ? (const void*)s : (const void*)g_zero_chunk, tile + (wave * kInst + i) * 1024);
-      }
+      for (int i = 0; i < kInst; ++i) issue_i(tile, wave, lane, i, k0, kend, step_off, k_split, second);
     }
   }
   // DMA i of issue() alone, placed and range-checked per lane (no branch)
-  __device__ __forceinline__ void issue_i(char* tile, int wave, int i, int k0, int kend, int64_t step_off, int k_split,
-                                          int64_t second) const {
-    const int k = k0 + krow[i];
-    const char* s = ptr[i] + step_off + (k >= k_split ? second : 0);
+  __device__ __forceinline__ void issue_i(char* tile, int wave, int lane, int i, int k0, int kend, int64_t step_off,
+                                          int k_split, int64_t second) const {
+    const int k = k0 + krow_of(wave, lane, i);
+    const char* s = opaque_sgpr(base + step_off) + (k >= k_split ? second : 0) + voff[i];
     dma16(k < kend ? (const void*)s : (const void*)g_zero_chunk, tile + (wave * kInst + i) * 1024);
   }
   // Fragment of the 32-column block starting at tile column cb, K substep s (16 k): lane l gets
@@ -314,31 +346,48 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
   const int kend = min(p.K, kbeg + p.k_per_split);
   const int nk = (kend - kbeg + BK - 1) / BK;
 
-  // ---- DMA loaders
-  KTileDma<T, BM, WAVES> ka;
-  KTileDma<T, BN, WAVES> kb;
-  MNTileDma<BM, WAVES> na;
-  MNTileDma<BN, WAVES> nb;
+  // ---- DMA loaders. With a K-major A (the DMAs of a K-step go out as one burst after the
+  // barrier), an 8-wave tile has its first four waves (one per SIMD) issue every DMA, so the
+  // other wave on each SIMD keeps issuing MFMAs while its partner is held up by the burst.
+  constexpr int DW = (WAVES == 8 && A_KMAJ && (B_KMAJ || BN == 128)) ? 4 : WAVES;
+  const bool dma_wave = DW == WAVES || wave < DW;
+  KTileDma<T, BM, DW> ka;
+  KTileDma<T, BN, DW> kb;
+  MNTileDma<BM, DW> na;
+  MNTileDma<BN, DW> nb;
+  // K-major tile rows: locA / locB(r) -> {base, rows past it} (rows past the matrix clamped)
+  const int b_half = BN / 2;
+  const int64_t ldb_bytes = (int64_t)p.ldb * ES;
+  auto locA = [&](int r) { return make_int2(0, min(m0 + r, p.M - 1) - m0); };
+  auto locB = [&](int r) {
+    if constexpr (GATED) {   // rows [0, BN/2) from B0 (gate), the rest from B1 (up)
+      return r < b_half ? make_int2(0, min(n0 + r, p.N - 1) - n0)
+                        : make_int2(1, min(n0 + r - b_half, p.N - 1) - (n0 - b_half));
+    } else {                 // rows n >= b_split from B1 when given (stacked [W_gate; W_up])
+      const int n = min(n0 + r, p.N - 1);
+      return make_int2(p.B1 != nullptr && n >= p.b_split ? 1 : 0, n - n0);
+    }
+  };
   if constexpr (A_KMAJ) {
-    ka.init(wave, lane, kbeg, [&](int r) -> const char* {
-      return reinterpret_cast<const char*>(elem_ptr<T>(p.A, min(m0 + r, p.M - 1), p.lda, 0));
-    });
+    const char* a0 = reinterpret_cast<const char*>(elem_ptr<T>(p.A, m0, p.lda, 0));
+    ka.init(lane, kbeg, a0, a0, (int64_t)p.lda * ES, BM, m0 + BM <= p.M);
   } else {
     na.init(wave, lane, reinterpret_cast<const char*>(elem_ptr<T>(p.A, 0, p.lda, m0)), (int64_t)p.lda * ES, kbeg,
             p.M - m0);
   }
   if constexpr (B_KMAJ) {
-    kb.init(wave, lane, kbeg, [&](int r) -> const char* {
-      if constexpr (GATED) {
-        const int half = BN / 2;
-        const int n = min(n0 + (r < half ? r : r - half), p.N - 1);
-        return elem_ptr<T>(r < half ? p.B0 : p.B1, n, p.ldb, 0);
-      } else {   // rows n >= b_split come from B1 when given (stacked [W_gate; W_up])
-        const int n = min(n0 + r, p.N - 1);
-        return (p.B1 != nullptr && n >= p.b_split) ? elem_ptr<T>(p.B1, n - p.b_split, p.ldb, 0)
-                                                   : elem_ptr<T>(p.B0, n, p.ldb, 0);
-      }
-    });
+    const char* b0 = reinterpret_cast<const char*>(elem_ptr<T>(p.B0, n0, p.ldb, 0));
+    if constexpr (GATED) {
+      const char* b1 = reinterpret_cast<const char*>(
+          reinterpret_cast<uintptr_t>(p.B1) + (int64_t)(n0 - b_half) * ldb_bytes);
+      kb.init(lane, kbeg, b0, b1, ldb_bytes, b_half, n0 + b_half <= p.N);
+    } else if (p.B1 != nullptr) {
+      const char* b1 = reinterpret_cast<const char*>(
+          reinterpret_cast<uintptr_t>(p.B1) + (int64_t)(n0 - p.b_split) * ldb_bytes);
+      kb.init(lane, kbeg, b0, b1, ldb_bytes, p.b_split - n0, n0 + BN <= p.N);
+    } else {
+      kb.init(lane, kbeg, b0, b0, ldb_bytes, BN, n0 + BN <= p.N);
+    }
   } else {
     nb.init(wave, lane, reinterpret_cast<const char*>(elem_ptr<T>(p.B0, 0, p.ldb, n0)), (int64_t)p.ldb * ES, kbeg,
             p.N - n0);
@@ -349,37 +398,39 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
       ? (reinterpret_cast<const char*>(p.B1) - reinterpret_cast<const char*>(p.B0)) - (int64_t)p.b_split * p.ldb * ES
       : 0;
   const int b_split = (!B_KMAJ && p.B1 != nullptr) ? p.b_split : INT_MAX;
-  constexpr int N_DMA = (A_KMAJ ? KTileDma<T, BM, WAVES>::kInst : MNTileDma<BM, WAVES>::kInst) +
-                        (B_KMAJ ? KTileDma<T, BN, WAVES>::kInst : MNTileDma<BN, WAVES>::kInst);
+  constexpr int N_DMA = (A_KMAJ ? KTileDma<T, BM, DW>::kInst : MNTileDma<BM, DW>::kInst) +
+                        (B_KMAJ ? KTileDma<T, BN, DW>::kInst : MNTileDma<BN, DW>::kInst);
   static_assert((NS - 1) * N_DMA < 64, "vmcnt range");
 
   // K-step kt into ring stage `stage`; steps past the end load zeros.
   auto issue = [&](int kt, int stage) {
+    if (!dma_wave) return;
     char* sa = smem + stage * STAGE;
     char* sb = sa + A_BYTES;
     if constexpr (A_KMAJ) {
-      ka.issue(sa, wave, kt * BK, kend - kbeg);
+      ka.issue(sa, wave, lane, kt * BK, kend - kbeg, locA);
     } else {
-      na.issue(sa, wave, kbeg + kt * BK, kend, (int64_t)kt * BK * p.lda * ES, INT_MAX, 0);
+      na.issue(sa, wave, lane, kbeg + kt * BK, kend, (int64_t)kt * BK * p.lda * ES, INT_MAX, 0);
     }
     if constexpr (B_KMAJ) {
-      kb.issue(sb, wave, kt * BK, kend - kbeg);
+      kb.issue(sb, wave, lane, kt * BK, kend - kbeg, locB);
     } else {
-      nb.issue(sb, wave, kbeg + kt * BK, kend, (int64_t)kt * BK * p.ldb * ES, b_split, b_second);
+      nb.issue(sb, wave, lane, kbeg + kt * BK, kend, (int64_t)kt * BK * p.ldb * ES, b_split, b_second);
     }
   };
 
   // DMA d (0 .. N_DMA-1: A's, then B's) of issue(kt, stage) alone
-  constexpr int KIA = A_KMAJ ? KTileDma<T, BM, WAVES>::kInst : MNTileDma<BM, WAVES>::kInst;
+  constexpr int KIA = A_KMAJ ? KTileDma<T, BM, DW>::kInst : MNTileDma<BM, DW>::kInst;
   auto issue_one = [&](int kt, int stage, int d) {
+    if (!dma_wave) return;
     char* sa = smem + stage * STAGE;
     char* sb = sa + A_BYTES;
     if (d < KIA) {
-      if constexpr (A_KMAJ) ka.issue_i(sa, wave, d, kt * BK, kend - kbeg);
-      else na.issue_i(sa, wave, d, kbeg + kt * BK, kend, (int64_t)kt * BK * p.lda * ES, INT_MAX, 0);
+      if constexpr (A_KMAJ) ka.issue_i(sa, wave, lane, d, kt * BK, kend - kbeg, locA);
+      else na.issue_i(sa, wave, lane, d, kbeg + kt * BK, kend, (int64_t)kt * BK * p.lda * ES, INT_MAX, 0);
     } else {
-      if constexpr (B_KMAJ) kb.issue_i(sb, wave, d - KIA, kt * BK, kend - kbeg);
-      else nb.issue_i(sb, wave, d - KIA, kbeg + kt * BK, kend, (int64_t)kt * BK * p.ldb * ES, b_split, b_second);
+      if constexpr (B_KMAJ) kb.issue_i(sb, wave, lane, d - KIA, kt * BK, kend - kbeg, locB);
+      else nb.issue_i(sb, wave, lane, d - KIA, kbeg + kt * BK, kend, (int64_t)kt * BK * p.ldb * ES, b_split, b_second);
     }
   };
 
