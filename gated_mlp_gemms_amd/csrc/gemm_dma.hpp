@@ -197,51 +197,74 @@ struct KTileDma {
 
 // ---- MN-major bf16 operand: 64 k-rows x ROWS columns per stage --------------------------------
 // The operand may be two matrices stacked along K (rows k < k_split from the first, the rest
-// from the second, both with the same leading dimension). Each lane keeps the 32-bit byte offset
-// of its chunk from a wave-uniform base (the first matrix at the split's first k); a K-step adds
-// a uniform offset to the base, plus the uniform distance between the two matrices when the step
-// lies in the second, so the issue of an in-range step is scalar arithmetic and no branch.
-template <int ROWS, int WAVES>
+// from the second, both with the same leading dimension). DMA instruction j fills KPI k-rows
+// (lane l: k-row KPI j + q, q = 16 l / ROWB, 16-byte chunk slot c = (16 l % ROWB) / 16). The
+// chunk's column depends on the instruction only through k-row bits 0, 1 and 3 (the swizzle), so
+// a lane keeps one 32-bit offset per pattern of those bits (4 for 256-column tiles, 2 for 128) and
+// the k-row base KPI j * pitch, the K-step and the jump to the second matrix are wave-uniform
+// scalar arithmetic. With PAT false (DMAs issued one at a time between MFMAs, where each one's
+// VALU work lands in the MFMA stream) a lane keeps one offset per instruction instead.
+template <int ROWS, int WAVES, bool PAT = true>
 struct MNTileDma {
   static constexpr int KROWS = 64;
   static constexpr int ROWB = ROWS * 2;               // bytes per k-row
+  static constexpr int KPI = 1024 / ROWB;             // k-rows per DMA instruction
   static constexpr int kInst = KROWS * ROWB / 1024 / WAVES;   // per wave per stage
   static_assert(kInst >= 1, "tile too narrow");
-  uint32_t voff[kInst];   // per lane: k-row * pitch + column bytes, from base
-  const char* base;       // uniform
+  static_assert(KPI == 2 || KPI == 4 || KPI == 8, "64- to 256-column tiles");
+  // instruction j's swizzle-relevant k-row bits (KPI j) & 0b1011 -> pattern index
+  static constexpr int NPAT = KPI == 2 ? 4 : 2;
+  static __device__ __forceinline__ int pattern(int j) {
+    const int b = (KPI * j) & 0b1011;
+    return KPI == 2 ? ((b >> 1) & 1) | (((b >> 3) & 1) << 1) : (b >> 3) & 1;
+  }
+  static __device__ __forceinline__ int pattern_row(int pat) {   // k-row KPI j of a j with this pattern
+    return KPI == 2 ? 2 * (pat & 1) + 8 * (pat >> 1) : 8 * pat;
+  }
+  static constexpr int NOFF = PAT ? NPAT : kInst;
+  uint32_t voff[NOFF];    // per lane: q * pitch + column bytes per pattern, or the whole offset per instruction
+  const char* base;       // uniform: the first matrix at the split's first k, tile column 0
+  int64_t ld_bytes;       // uniform pitch
 
   // k-rows kr .. kr+3 land in distinct 64-byte groups, and k-rows 8 apart (read in the same pass
   // by the 16x16 fragments) in distinct 32-byte halves of them
   static __device__ __forceinline__ int phys_chunk(int c, int kr) { return c ^ ((kr & 3) << 2) ^ (((kr >> 3) & 1) << 1); }
-  static __device__ __forceinline__ int krow_of(int wave, int lane, int i) {
-    return ((wave * kInst + i) * 1024 + lane * 16) / ROWB;
-  }
 
-  // b: element (0, tile column 0) of the first matrix; ld_bytes: its row pitch; ncols: columns of
-  // the matrix from tile column 0 on (a multiple of 8). Chunks of tile columns past the matrix
+  // b: element (0, tile column 0) of the first matrix; ld: its row pitch in bytes; ncols: columns
+  // of the matrix from tile column 0 on (a multiple of 8). Chunks of tile columns past the matrix
   // read its last chunk instead: their products only reach output columns that are never stored.
-  __device__ __forceinline__ void init(int wave, int lane, const char* b, int64_t ld_bytes, int kbeg,
-                                       int ncols) {
-    base = b + (int64_t)kbeg * ld_bytes;
+  __device__ __forceinline__ void init(int wave, int lane, const char* b, int64_t ld, int kbeg, int ncols) {
+    base = b + (int64_t)kbeg * ld;
+    ld_bytes = ld;
+    const int q = lane * 16 / ROWB, c = (lane * 16 % ROWB) >> 4;
 #pragma unroll
-    for (int i = 0; i < kInst; ++i) {
-      const int j = wave * kInst + i;
-      const int byte = j * 1024 + lane * 16;
-      const int kr = byte / ROWB;
-      const int col = min(phys_chunk((byte % ROWB) >> 4, kr) * 8, ncols - 8);   // the XOR is an involution
-      voff[i] = (uint32_t)(kr * ld_bytes) + (uint32_t)(col * 2);
+    for (int o = 0; o < NOFF; ++o) {
+      const int kr = PAT ? pattern_row(o) + q : KPI * (wave * kInst + o) + q;
+      const int col = min(phys_chunk(c, kr) * 8, ncols - 8);   // the XOR is an involution
+      voff[o] = (uint32_t)((PAT ? q : kr) * ld) + (uint32_t)(col * 2);
     }
+  }
+  // offset of instruction i (j = wave kInst + i) from the K-step's base; kbase: the scalar part
+  __device__ __forceinline__ int64_t kbase(int j) const { return PAT ? (int64_t)(KPI * j) * ld_bytes : 0; }
+  __device__ __forceinline__ uint32_t voff_of(int i, int j) const {
+    if constexpr (!PAT) return voff[i];
+    const int pat = pattern(j);
+    if constexpr (NPAT == 4) return pat & 2 ? (pat & 1 ? voff[3] : voff[2]) : (pat & 1 ? voff[1] : voff[0]);
+    else return pat ? voff[1] : voff[0];
   }
   // K-step starting at k0 (absolute); step_off: byte offset of this K-step from the first;
   // second: distance from a k-row's address in the first matrix to its address in the second.
-  // A step wholly inside [.., kend) and on one side of k_split (a uniform test) costs one scalar
-  // address add; otherwise each k-row is placed and range-checked on its own.
+  // A step wholly inside [.., kend) and on one side of k_split (a uniform test) costs scalar
+  // address arithmetic only; otherwise each k-row is placed and range-checked on its own.
   __device__ __forceinline__ void issue(char* tile, int wave, int lane, int k0, int kend, int64_t step_off, int k_split,
                                         int64_t second) const {
     if (k0 + KROWS <= kend && (k0 + KROWS <= k_split || k0 >= k_split)) {
       const char* b = base + step_off + (k0 >= k_split ? second : 0);
 #pragma unroll
-      for (int i = 0; i < kInst; ++i) dma16s(b, voff[i], tile + (wave * kInst + i) * 1024);
+      for (int i = 0; i < kInst; ++i) {
+        const int j = wave * kInst + i;
+        dma16s(b + kbase(j), voff_of(i, j), tile + j * 1024);
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < kInst; ++i) issue_i(tile, wave, lane, i, k0, kend, step_off, k_split, second);
@@ -250,9 +273,10 @@ struct MNTileDma {
   // DMA i of issue() alone, placed and range-checked per lane (no branch)
   __device__ __forceinline__ void issue_i(char* tile, int wave, int lane, int i, int k0, int kend, int64_t step_off,
                                           int k_split, int64_t second) const {
-    const int k = k0 + krow_of(wave, lane, i);
-    const char* s = opaque_sgpr(base + step_off) + (k >= k_split ? second : 0) + voff[i];
-    dma16(k < kend ? (const void*)s : (const void*)g_zero_chunk, tile + (wave * kInst + i) * 1024);
+    const int j = wave * kInst + i;
+    const int k = k0 + KPI * j + lane * 16 / ROWB;
+    const char* s = opaque_sgpr(base + step_off + kbase(j)) + (k >= k_split ? second : 0) + voff_of(i, j);
+    dma16(k < kend ? (const void*)s : (const void*)g_zero_chunk, tile + j * 1024);
   }
   // Fragment of the 32-column block starting at tile column cb, K substep s (16 k): lane l gets
   // the 8 consecutive k 8*(l/32) .. +7 of column cb + l%32, via two transposing reads of four
@@ -349,12 +373,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
   // ---- DMA loaders. With a K-major A (the DMAs of a K-step go out as one burst after the
   // barrier), an 8-wave tile has its first four waves (one per SIMD) issue every DMA, so the
   // other wave on each SIMD keeps issuing MFMAs while its partner is held up by the burst.
-  constexpr int DW = (WAVES == 8 && A_KMAJ && (B_KMAJ || BN == 128)) ? 4 : WAVES;
+  constexpr int DW = (WAVES == 8 && A_KMAJ) ? 4 : WAVES;
   const bool dma_wave = DW == WAVES || wave < DW;
   KTileDma<T, BM, DW> ka;
   KTileDma<T, BN, DW> kb;
-  MNTileDma<BM, DW> na;
-  MNTileDma<BN, DW> nb;
+  MNTileDma<BM, DW, A_KMAJ> na;   // offsets per pattern with the burst issue, per instruction when spread
+  MNTileDma<BN, DW, A_KMAJ> nb;
   // K-major tile rows: locA / locB(r) -> {base, rows past it} (rows past the matrix clamped)
   const int b_half = BN / 2;
   const int64_t ldb_bytes = (int64_t)p.ldb * ES;
@@ -372,8 +396,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     const char* a0 = reinterpret_cast<const char*>(elem_ptr<T>(p.A, m0, p.lda, 0));
     ka.init(lane, kbeg, a0, a0, (int64_t)p.lda * ES, BM, m0 + BM <= p.M);
   } else {
-    na.init(wave, lane, reinterpret_cast<const char*>(elem_ptr<T>(p.A, 0, p.lda, m0)), (int64_t)p.lda * ES, kbeg,
-            p.M - m0);
+    na.init(wave, lane, reinterpret_cast<const char*>(elem_ptr<T>(p.A, 0, p.lda, m0)), (int64_t)p.lda * ES, kbeg, p.M - m0);
   }
   if constexpr (B_KMAJ) {
     const char* b0 = reinterpret_cast<const char*>(elem_ptr<T>(p.B0, n0, p.ldb, 0));
@@ -389,8 +412,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
       kb.init(lane, kbeg, b0, b0, ldb_bytes, BN, n0 + BN <= p.N);
     }
   } else {
-    nb.init(wave, lane, reinterpret_cast<const char*>(elem_ptr<T>(p.B0, 0, p.ldb, n0)), (int64_t)p.ldb * ES, kbeg,
-            p.N - n0);
+    nb.init(wave, lane, reinterpret_cast<const char*>(elem_ptr<T>(p.B0, 0, p.ldb, n0)), (int64_t)p.ldb * ES, kbeg, p.N - n0);
   }
   // B stacked from two matrices along K (MN-major only): distance from B0's row k to B1's row
   // k - b_split
