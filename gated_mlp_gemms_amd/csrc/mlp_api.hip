@@ -283,6 +283,14 @@ mlp_status check_desc(const mlp_desc* d) {
     return fail(MLP_ERR_UNSUPPORTED, "a size is beyond 2^30 (2^29 for hidden)");
   if (d->act < MLP_ACT_SWIGLU || d->act > MLP_ACT_RELU)
     return fail(MLP_ERR_INVALID_ARG, "act %d is not an mlp_act", d->act);
+  // the GEMMs' DMA addresses are a scalar base plus a 32-bit per-lane offset of up to 64 rows of
+  // the operand: every leading dimension (d_in, d_out, the gate/up width, and the padded token
+  // count of the fp8 backward's transposed copies) must keep 64 row pitches under 4 GiB
+  const int64_t ld_lim = (int64_t)1 << 25;
+  if (d->d_in >= ld_lim || d->d_out >= ld_lim || (is_gated(d->act) ? 2 : 1) * d->hidden >= ld_lim ||
+      (d->fp8_bwd && d->M >= ld_lim))
+    return fail(MLP_ERR_UNSUPPORTED, "a leading dimension is 2^25 elements or more (d_in, d_out, the gate/up "
+                "width, or M with fp8_bwd): the DMA offsets are 32-bit");
   if (d->dtype != MLP_F32 && d->dtype != MLP_BF16 && d->dtype != MLP_F16)
     return fail(MLP_ERR_INVALID_ARG, "dtype %d is not an mlp_dtype", d->dtype);
   if (d->gate_mode != MLP_GATE_OUTSIDE && d->gate_mode != MLP_GATE_INSIDE)

@@ -28,6 +28,10 @@
  *    (bf16) or 4 (f32): rows must be 16-byte aligned (flash-swiglu-mlp README, supported
  *    configurations; quack mlp.py's MLP.forward fast-path conditions). The e4m3 path needs
  *    multiples of 16. M >= 1 is arbitrary.
+ *  - Size limits (MLP_ERR_UNSUPPORTED, before any HIP call): M, d_in, d_out < 2^30 and
+ *    hidden < 2^29; every leading dimension below 2^25 elements (d_in, d_out, 2 * hidden for a
+ *    gated activation or hidden otherwise, and M with fp8_bwd), since a GEMM operand is addressed
+ *    as a base plus a 32-bit offset spanning up to 64 rows.
  */
 #ifndef GATED_MLP_H
 #define GATED_MLP_H

@@ -216,7 +216,23 @@ def test_size_limits():
     for kw in (dict(M=1 << 30), dict(d_in=1 << 30), dict(d_out=1 << 30), dict(hidden=1 << 29)):
         assert _fwd(_desc(**kw), nws=0) == gm._lib.MLP_ERR_UNSUPPORTED, kw
         assert "2^30" in _err()
-    assert _fwd(_desc(hidden=(1 << 29) - 8), ws=None) == gm._lib.MLP_ERR_INVALID_ARG   # passes the size check
+
+
+def test_leading_dimension_limits():
+    """The GEMMs address an operand as a scalar base plus a 32-bit per-lane offset of up to 64
+    row pitches, so every leading dimension stays under 2^25 elements: d_in, d_out, the stacked
+    gate/up width 2 * hidden (hidden for a non-gated activation), and M when the fp8 backward
+    keeps transposed [*, M] copies. Refused before any HIP call; one below each limit passes."""
+    big = 1 << 25
+    for kw in (dict(d_in=big), dict(d_out=big), dict(hidden=big // 2), dict(act="relu_sq", hidden=big)):
+        assert _fwd(_desc(**kw), nws=0) == gm._lib.MLP_ERR_UNSUPPORTED, kw
+        assert "2^25" in _err()
+    fp8 = dict(act="relu_sq", fp8_fwd=True, fp8_bwd=True, d_in=256, hidden=704, d_out=256)
+    assert _fwd(_desc(M=big, **fp8), nws=0) == gm._lib.MLP_ERR_UNSUPPORTED and "2^25" in _err()
+    # just below each limit the size checks pass and the next check (a NULL workspace) fails
+    for kw in (dict(d_in=big - 8), dict(d_out=big - 8), dict(hidden=big // 2 - 8), dict(act="relu_sq", hidden=big - 8),
+               dict(M=(1 << 30) - 1)):
+        assert _fwd(_desc(**kw), ws=None) == gm._lib.MLP_ERR_INVALID_ARG, kw
 
 
 def test_fp8_backward_checks():
