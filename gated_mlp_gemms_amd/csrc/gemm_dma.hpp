@@ -2,7 +2,7 @@
 // with operands moved HBM -> LDS by the LDS-DMA form of the global load (no VGPR staging, no
 // LDS store instructions) through a ring of LDS stages, and a software-pipelined MFMA loop.
 //
-// Per workgroup (4 wave64, 2 x 2 waves of WM x WN):
+// Per workgroup (4 wave64 in 2 x 2, or 8 in 4 x 2 with two per SIMD; waves of WM x WN):
 //  * one K-step is 128 bytes of K per operand row: 64 k for bf16 (four K=16 MFMA substeps),
 //    128 k for e4m3 (two K=64 substeps); full 128-byte row segments keep every DMA request a
 //    whole cache line;
@@ -13,7 +13,9 @@
 //  * the ring holds NS K-steps. The DMA of step kt+NS is issued right after the barrier that
 //    ends step kt's reads, into the stage step kt used, so NS-1 steps are in flight while one
 //    is multiplied: the load latency of the shared L2 / last-level cache is hidden by depth.
-//    Inside a step the fragments of substep s+1 are read while the MFMAs of substep s run.
+//    Inside a step the fragments of substep s+1 are read while the MFMAs of substep s run;
+//  * a DMA address is a wave-uniform base (SGPRs) plus a 32-bit per-lane offset; in the 8-wave
+//    tiles with a K-major A, one wave per SIMD issues all of a step's DMAs.
 #pragma once
 
 #include <climits>
@@ -439,6 +441,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     } else {
       nb.issue(sb, wave, lane, kbeg + kt * BK, kend, (int64_t)kt * BK * p.ldb * ES, b_split, b_second);
     }
+    // the issuing wave is now behind its partner on the SIMD: it wins issue ties until the barrier
+    if constexpr (DW < WAVES) __builtin_amdgcn_s_setprio(1);
   };
 
   // DMA d (0 .. N_DMA-1: A's, then B's) of issue(kt, stage) alone
@@ -586,6 +590,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     // last substep: step kt+1 must have landed (NS-2 younger steps may be in flight); after
     // the barrier every wave is done reading this stage, which takes step kt+NS
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DW < WAVES) __builtin_amdgcn_s_setprio(0);
     wait_vmcnt<(NS - 2) * N_DMA>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
