@@ -600,7 +600,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
       mma_roll((NSUB - 1) & 1, nxt, 0, kt + NS, cur);
       interleave_roll<MI, NI, RB, NRA>();
     } else {
-      issue(kt + NS, cur);
+      if constexpr (WAVES == 4) {
+        // one wave per SIMD: a burst would idle the matrix pipe, so the DMAs take the branch-free
+        // per-lane form and the interleave pattern places them between the MFMAs
+#pragma unroll
+        for (int d = 0; d < N_DMA; ++d) issue_one(kt + NS, cur, d);
+      } else {
+        issue(kt + NS, cur);
+      }
       read_frags(nxt, 0, 0);
       mma_all((NSUB - 1) & 1);
       interleave<N_MMA, N_RD, N_DMA>();
