@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from gpu_helpers import TOL, announce, assert_close, f64, run
-from workloads import WORKLOADS, make_inputs
+from workloads import WORKLOADS, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +57,28 @@ def test_llama_swiglu_full_size():
     a = {k: f64(v) for k, v in t.items()}
     rows = _sample(w.M, seed=3)
     f = oracle.gated_forward(a["x"][rows], a["w_gate"], a["w_up"], a["w_down"])
+    assert_close("g[rows]", f64(r.saved[rows, : w.hidden]), f["g"], TOL["bf16"])
+    assert_close("u[rows]", f64(r.saved[rows, w.hidden:]), f["u"], TOL["bf16"])
+    _check_gated(w, t, r, "outside")
+
+
+def test_llama_like_ragged_in_every_dimension():
+    """A LLaMA-sized problem with no dimension a multiple of the tile: the same 8-wave tiles as
+    the LLaMA step, but with partial row and column tiles (M = 2000, H = 11000, d = 4104) and a
+    partial last K-step in every product (K = 4104, 11000, 2000, and 22000 for dx, whose stacked
+    [W_gate; W_up] changes matrix inside a K-step). Sampled outputs include the last rows and
+    hidden units, which the edge tiles produce."""
+    w = Workload("llama_ragged_swiglu_bf16_m2000_d4104_h11000", "swiglu", "bf16", (2000,), 4104, 11000, 4104,
+                 gate_mult=1.125, down_mult=2.0, seed=11)
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.backward(dpreact=False)
+    torch.cuda.synchronize()
+    a = {k: f64(v) for k, v in t.items()}
+    rows = _sample(w.M, seed=5)
+    f = oracle.gated_forward(a["x"][rows], a["w_gate"], a["w_up"], a["w_down"], w.gate_mult, w.down_mult)
     assert_close("g[rows]", f64(r.saved[rows, : w.hidden]), f["g"], TOL["bf16"])
     assert_close("u[rows]", f64(r.saved[rows, w.hidden:]), f["u"], TOL["bf16"])
     _check_gated(w, t, r, "outside")
