@@ -243,27 +243,34 @@ def main():
     ev = HipEvents()
     stages = ["up", "down", "dact", "dw_down", "dx", "dw_up"] + (["recompute"] if w.recompute else [])
     stage_id = {n: gm._lib.STAGES.index(n) for n in stages}
-    pairs = [[(ev.create(), ev.create()) for _ in stages] for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        for n, (b, e) in zip(stages, pairs[i]):
-            gm._lib.check(gm.lib().mlp_time_stage_once(stage_id[n], b, e), "mlp_time_stage_once")
-        r.step()
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(stop) / args.steps
-    flops = w.model_flops()
-    tflops = flops / (ms * 1e-3) / 1e12
 
+    def run_steps(hooked):
+        """K steps with HIP event pairs around the `hooked` stages (recorded by the library on
+        its stream); returns the event pairs and the average ms per step from torch events."""
+        pairs = [[(ev.create(), ev.create()) for _ in hooked] for _ in range(args.steps)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(args.steps):
+            for n, (b, e) in zip(hooked, pairs[i]):
+                gm._lib.check(gm.lib().mlp_time_stage_once(stage_id[n], b, e), "mlp_time_stage_once")
+            r.step()
+        stop.record()
+        torch.cuda.synchronize()
+        return pairs, start.elapsed_time(stop) / args.steps, time.perf_counter() - t0
+
+    def avg_us(pairs, j):
+        return 1e3 * sum(ev.elapsed_ms(*pairs[i][j]) for i in range(args.steps)) / args.steps
+
+    # stage pass: every stage's events (each record adds a little queue work, so this pass is not
+    # the one the headline is timed on)
+    log(f"[bench] stage pass: {args.steps} steps with events around every stage")
+    pairs, _, _ = run_steps(stages)
     sf = stage_flops(w)
     stage_us, stage_tf = {}, {}
     for j, n in enumerate(stages):
-        us = 1e3 * sum(ev.elapsed_ms(*pairs[i][j]) for i in range(args.steps)) / args.steps
+        us = avg_us(pairs, j)
         stage_us[n] = round(us, 2)
         stage_tf[n] = round(sf[n] / (us * 1e-6) / 1e12, 1)
     # per-step spread: from the up-projection's start to the last weight gradient's end
@@ -278,15 +285,28 @@ def main():
             ev.destroy(b)
             ev.destroy(e)
     dom = max(stage_us, key=stage_us.get)
+
+    # timed pass (the headline): events only around the dominant stage, whose average launch
+    # duration in these steps gives the roofline's achieved rate
+    log(f"[bench] timing {args.steps} steps (events around the {dom} stage)")
+    pairs, ms, wall = run_steps([dom])
+    dom_us = avg_us(pairs, 0)
+    for row in pairs:
+        for b, e in row:
+            ev.destroy(b)
+            ev.destroy(e)
+    flops = w.model_flops()
+    tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS
     traffic, traffic_src = measured_traffic(w.name, dom)
     # the dominant stage's product is priced at the peak of its own operand type
     fp8_stages = ({"up", "down", "recompute"} if w.fp8_fwd else set()) | \
         ({"dact", "dw_down", "dx", "dw_up"} if w.fp8_bwd else set())
     stage_peak = PEAK_FP8_TFLOPS if dom in fp8_stages else (PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS)
-    roof = {"bound": "mfma", "achieved": stage_tf[dom], "peak": stage_peak, "unit": "TFLOP/s",
-            "frac": round(stage_tf[dom] / stage_peak, 4), "traffic": traffic, "kernel_stage": dom,
-            "flop_per_launch": sf[dom], "avg_launch_us": stage_us[dom], "traffic_source": traffic_src}
+    dom_tf = round(sf[dom] / (dom_us * 1e-6) / 1e12, 1)
+    roof = {"bound": "mfma", "achieved": dom_tf, "peak": stage_peak, "unit": "TFLOP/s",
+            "frac": round(dom_tf / stage_peak, 4), "traffic": traffic, "kernel_stage": dom,
+            "flop_per_launch": sf[dom], "avg_launch_us": round(dom_us, 2), "traffic_source": traffic_src}
     log(f"[bench] {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of bf16 peak); "
         f"stages us {stage_us}")
 
