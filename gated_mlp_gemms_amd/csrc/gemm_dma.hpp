@@ -617,6 +617,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
   // the trailing zero-fill DMAs have landed and no wave reads the ring any more: its LDS
   // becomes the epilogue's staging area
   static_assert(epilogue_lds_bytes<BN, WAVES>() <= NS * STAGE, "epilogue staging must fit the ring");
+  if constexpr (DW < WAVES) __builtin_amdgcn_s_setprio(0);   // the last issue raised it
   wait_vmcnt<0>();
   wait_lgkmcnt0();
   __builtin_amdgcn_s_barrier();
