@@ -93,7 +93,9 @@ struct TileInfo { TileShape t; int bm, bn, slots; double eff; };
 // one K-step of the tile sustains with every CU busy, measured per K-step on the bf16 GEMMs of
 // the 2048-token 4096 x 11008 SwiGLU step (random data, all three layouts, fused epilogues):
 // the 8-wave 256x256 tile takes ~1.95 us per 64-deep K-step, the 4-wave one ~2.1 us, a pair of
-// 128x128 workgroups ~1.2 us, and the 256x128 tile ~1.3 us.
+// 128x128 workgroups ~1.2 us, and the 256x128 tile ~1.3 us. These were fitted before the 8-wave
+// tiles with a K-major A moved their DMAs to one wave per SIMD, which made those K-steps ~3-8 %
+// faster; that only widens the 8-wave tiles' lead, which the planner already gives them.
 const TileInfo kTiles[] = {
     {TILE_256x256_W8, 256, 256, 1, 0.44},   // 8 waves: two per SIMD hide each other's stalls
     {TILE_256x256, 256, 256, 1, 0.40},
