@@ -180,6 +180,10 @@ struct KTileDma {
       for (int i = 0; i < kInst; ++i) issue_i(tile, wave, lane, i, k_rel, k_left, locate);
     }
   }
+  // DMA i of an interior tile's K-step wholly in range (no per-lane work)
+  __device__ __forceinline__ void issue_fast_i(char* tile, int wave, int i, int k_rel) const {
+    dma16s(sbase(wave, i, k_rel), ((wave * kInst + i) & 1) ? voff[1] : voff[0], tile + (wave * kInst + i) * 1024);
+  }
   // DMA i of issue(), placed and range-checked per lane (no branch)
   template <typename Locate>
   __device__ __forceinline__ void issue_i(char* tile, int wave, int lane, int i, int k_rel, int k_left,
@@ -271,6 +275,12 @@ struct MNTileDma {
 #pragma unroll
       for (int i = 0; i < kInst; ++i) issue_i(tile, wave, lane, i, k0, kend, step_off, k_split, second);
     }
+  }
+  // DMA i of a K-step wholly in range; b: the step's uniform base (base + step offset, plus the
+  // jump to the second matrix when the step lies there)
+  __device__ __forceinline__ void issue_fast_i(char* tile, int wave, int i, const char* b) const {
+    const int j = wave * kInst + i;
+    dma16s(b + kbase(j), voff_of(i, j), tile + j * 1024);
   }
   // DMA i of issue() alone, placed and range-checked per lane (no branch)
   __device__ __forceinline__ void issue_i(char* tile, int wave, int lane, int i, int k0, int kend, int64_t step_off,
@@ -447,10 +457,23 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
 
   // DMA d (0 .. N_DMA-1: A's, then B's) of issue(kt, stage) alone
   constexpr int KIA = A_KMAJ ? KTileDma<T, BM, DW>::kInst : MNTileDma<BM, DW>::kInst;
-  auto issue_one = [&](int kt, int stage, int d) {
+  // FAST: the K-step is wholly in range and on one side of b_split, and K-major tiles are
+  // interior (the main part of the K loop): scalar bases, no per-lane work
+  auto issue_one = [&](int kt, int stage, int d, auto fast) {
     if (!dma_wave) return;
     char* sa = smem + stage * STAGE;
     char* sb = sa + A_BYTES;
+    if constexpr (decltype(fast)::value) {
+      if (d < KIA) {
+        if constexpr (A_KMAJ) ka.issue_fast_i(sa, wave, d, kt * BK);
+        else na.issue_fast_i(sa, wave, d, na.base + (int64_t)kt * BK * p.lda * ES);
+      } else {
+        if constexpr (B_KMAJ) kb.issue_fast_i(sb, wave, d - KIA, kt * BK);
+        else nb.issue_fast_i(sb, wave, d - KIA,
+                             nb.base + (int64_t)kt * BK * p.ldb * ES + (kbeg + kt * BK >= b_split ? b_second : 0));
+      }
+      return;
+    }
     if (d < KIA) {
       if constexpr (A_KMAJ) ka.issue_i(sa, wave, lane, d, kt * BK, kend - kbeg, locA);
       else na.issue_i(sa, wave, lane, d, kbeg + kt * BK, kend, (int64_t)kt * BK * p.lda * ES, INT_MAX, 0);
@@ -539,7 +562,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
   // B fragment j with substep s of `stage` as soon as its last MFMA is issued. kt_dma >= 0 and
   // DMA_COLS > 0: also issue the DMAs of K-step kt_dma into stage_dma, spread over the first
   // DMA_COLS column blocks.
-  auto mma_roll = [&](int slot, int stage, int s, int kt_dma, int stage_dma) {
+  auto mma_roll = [&](int slot, int stage, int s, int kt_dma, int stage_dma, auto fast) {
     if constexpr (ROLL) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
@@ -549,7 +572,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
         if constexpr (DMA_COLS > 0) {
           if (kt_dma >= 0 && j < DMA_COLS) {
 #pragma unroll
-            for (int d = j * N_DMA / DMA_COLS; d < (j + 1) * N_DMA / DMA_COLS; ++d) issue_one(kt_dma, stage_dma, d);
+            for (int d = j * N_DMA / DMA_COLS; d < (j + 1) * N_DMA / DMA_COLS; ++d) issue_one(kt_dma, stage_dma, d, fast);
           }
         }
       }
@@ -571,15 +594,24 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     // fragment refill instead of the first)
     wait_lgkmcnt0();
   }
+  // The spread DMA issue (both operands MN-major, or one wave per SIMD) takes the per-lane form
+  // only where a step may be partial: the K loop runs as a main part whose DMAs (of step kt+NS)
+  // are wholly in range, then the tail.
+  using fast_t = std::true_type;
+  using slow_t = std::false_type;
+  const int nk_full = (kend - kbeg) / BK;
+  const bool fast_ok = (!A_KMAJ || ka.interior) && (!B_KMAJ || kb.interior) &&
+                       (b_split == INT_MAX || b_split <= kbeg || b_split >= kend || (b_split - kbeg) % BK == 0);
+  const int nk_main = fast_ok ? max(0, min(nk, nk_full - NS)) : 0;
   int cur = 0;
-  for (int kt = 0; kt < nk; ++kt) {
+  auto k_step = [&](int kt, auto fast) {
     const int nxt = cur + 1 == NS ? 0 : cur + 1;
     // substeps 0 .. NSUB-2: read substep s+1's fragments while multiplying substep s
 #pragma unroll
     for (int s = 0; s + 1 < NSUB; ++s) {
       if constexpr (ROLL) {
         read_a(cur, s + 1, (s + 1) & 1);
-        mma_roll(s & 1, cur, s + 1, -1, 0);
+        mma_roll(s & 1, cur, s + 1, -1, 0, fast);
         interleave_roll<MI, NI, RB, NRA>();
       } else {
         read_frags(cur, s + 1, (s + 1) & 1);
@@ -597,14 +629,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     if constexpr (ROLL) {
       if constexpr (DMA_COLS == 0) issue(kt + NS, cur);
       read_a(nxt, 0, 0);
-      mma_roll((NSUB - 1) & 1, nxt, 0, kt + NS, cur);
+      mma_roll((NSUB - 1) & 1, nxt, 0, kt + NS, cur, fast);
       interleave_roll<MI, NI, RB, NRA>();
     } else {
       if constexpr (WAVES == 4) {
-        // one wave per SIMD: a burst would idle the matrix pipe, so the DMAs take the branch-free
-        // per-lane form and the interleave pattern places them between the MFMAs
+        // one wave per SIMD: a burst would idle the matrix pipe, so the DMAs go one at a time
+        // and the interleave pattern places them between the MFMAs
 #pragma unroll
-        for (int d = 0; d < N_DMA; ++d) issue_one(kt + NS, cur, d);
+        for (int d = 0; d < N_DMA; ++d) issue_one(kt + NS, cur, d, fast);
       } else {
         issue(kt + NS, cur);
       }
@@ -613,7 +645,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
       interleave<N_MMA, N_RD, N_DMA>();
     }
     cur = nxt;
+  };
+  int kt = 0;
+  // (not for the 4-wave 256x256 tiles: a second copy of their loop costs them registers)
+  if constexpr ((DMA_COLS > 0 && WAVES == 8) || (WAVES == 4 && BM * BN <= 256 * 128)) {
+    for (; kt < nk_main; ++kt) k_step(kt, fast_t{});
   }
+  for (; kt < nk; ++kt) k_step(kt, slow_t{});
   // the trailing zero-fill DMAs have landed and no wave reads the ring any more: its LDS
   // becomes the epilogue's staging area
   static_assert(epilogue_lds_bytes<BN, WAVES>() <= NS * STAGE, "epilogue staging must fit the ring");
