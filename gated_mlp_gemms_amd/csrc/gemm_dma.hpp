@@ -199,6 +199,12 @@ struct KTileDma {
   static __device__ __forceinline__ u32x4 read(const char* tile, int row, int ch) {
     return *reinterpret_cast<const u32x4*>(tile + off(row, ch));
   }
+  // The same read for row = rowbase + r with rowbase a multiple of 16: the swizzle of such a row
+  // is that of r, so the address splits into a wave-uniform block base plus a lane offset that is
+  // the same for every block (the block's position folds into the instruction's offset).
+  static __device__ __forceinline__ u32x4 read_block(const char* tile, int rowbase, int r, int ch) {
+    return *reinterpret_cast<const u32x4*>(tile + rowbase * ROWB + off(r, ch));
+  }
 };
 
 // ---- MN-major bf16 operand: 64 k-rows x ROWS columns per stage --------------------------------
@@ -487,7 +493,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
   const int frow = lane & (BLK - 1), fhalf = lane >> 5, fq = lane >> 4;
   int a_base[MI], b_base[NI];   // first tile row (K-major) / column (MN-major) of each block
 #pragma unroll
-  for (int i = 0; i < MI; ++i) a_base[i] = wm * WM + i * BLK;
+  for (int i = 0; i < MI; ++i) a_base[i] = wm * WM + i * BLK;   // multiples of 16 (read_block)
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     if constexpr (GATED) {
@@ -508,8 +514,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        if constexpr (A_KMAJ && M16) fa[slot][i][c] = KTileDma<T, BM, WAVES>::read(sa, a_base[i] + frow, 4 * s + fq);
-        else if constexpr (A_KMAJ) fa[slot][i][c] = KTileDma<T, BM, WAVES>::read(sa, a_base[i] + frow, Mma<T>::chunk(s, fhalf, c));
+        if constexpr (A_KMAJ && M16) fa[slot][i][c] = KTileDma<T, BM, WAVES>::read_block(sa, a_base[i], frow, 4 * s + fq);
+        else if constexpr (A_KMAJ) fa[slot][i][c] = KTileDma<T, BM, WAVES>::read_block(sa, a_base[i], frow, Mma<T>::chunk(s, fhalf, c));
         else if constexpr (M16) fa[slot][i][c] = MNTileDma<BM, WAVES>::read16(sa, a_base[i], s, lane);
         else fa[slot][i][c] = MNTileDma<BM, WAVES>::read(sa, a_base[i], s, lane);
       }
@@ -519,8 +525,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     const char* sb = smem + stage * STAGE + A_BYTES;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      if constexpr (B_KMAJ && M16) fb[slot][j][c] = KTileDma<T, BN, WAVES>::read(sb, b_base[j] + frow, 4 * s + fq);
-      else if constexpr (B_KMAJ) fb[slot][j][c] = KTileDma<T, BN, WAVES>::read(sb, b_base[j] + frow, Mma<T>::chunk(s, fhalf, c));
+      if constexpr (B_KMAJ && M16) fb[slot][j][c] = KTileDma<T, BN, WAVES>::read_block(sb, b_base[j], frow, 4 * s + fq);
+      else if constexpr (B_KMAJ) fb[slot][j][c] = KTileDma<T, BN, WAVES>::read_block(sb, b_base[j], frow, Mma<T>::chunk(s, fhalf, c));
       else if constexpr (M16) fb[slot][j][c] = MNTileDma<BN, WAVES>::read16(sb, b_base[j], s, lane);
       else fb[slot][j][c] = MNTileDma<BN, WAVES>::read(sb, b_base[j], s, lane);
     }
