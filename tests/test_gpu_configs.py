@@ -84,6 +84,35 @@ def test_llama_like_ragged_in_every_dimension():
     _check_gated(w, t, r, "outside")
 
 
+def test_llama_like_ragged_fp16_inside():
+    """The ragged LLaMA-sized problem in fp16 I/O with the multiplier inside the SiLU: the fp16
+    instantiations of the same 8-wave kernels and their edge tiles, at the fp16 bound."""
+    w = Workload("llama_ragged_swiglu_f16_m2000_d4104_h11000", "swiglu", "f16", (2000,), 4104, 11000, 4104,
+                 gate_mult=1.125, down_mult=2.0, seed=12)
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t, gate_mode="inside")
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    _check_gated(w, t, r, "inside")
+
+
+def test_relu_sq_ragged_in_every_dimension():
+    """A GPT-like ReLU^2 problem with no dimension a multiple of the tile (M = 12000, d = 776,
+    H = 3080): the 8-wave ReLU^2 and d-ReLU^2 epilogue kernels with partial tiles and partial last
+    K-steps, sampled against the oracle."""
+    w = Workload("gpt_ragged_relu2_bf16_m12000_d776_h3080", "relu_sq", "bf16", (12000,), 776, 3080, 776, seed=13)
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    rows, s = _check_relu(w, t, r)
+    assert_close("out[rows]", f64(r.out[rows]), s["out_rows"], TOL["bf16"])
+
+
 @pytest.mark.parametrize("name", ["llama_swiglu_bf16_tp8_m2048_d4096_h1376", "llama_swiglu_bf16_dp8_m256_d4096_h11008"])
 def test_llama_shard_shapes(name):
     """One GPU's share of the LLaMA step under 8-way tensor or data parallelism."""
