@@ -138,6 +138,22 @@ def test_falcon_h1_recompute_accumulate_full_size(mode):
     _check_gated(w, t, r, mode)
 
 
+def test_recompute_accumulate_ragged_in_every_dimension():
+    """Falcon-H1-style recompute + fp32 accumulate-into-grad on a problem with no dimension a
+    multiple of the tile (M = 6000, d = 2056, H = 4872): the backward's recompute GEMM and the
+    accumulating weight-gradient epilogues with partial tiles and partial last K-steps; the
+    accumulated buffers and their deltas against the oracle on sampled outputs."""
+    w = Workload("falcon_ragged_swiglu_bf16_m6000_d2056_h4872", "swiglu", "bf16", (6000,), 2056, 4872, 2056,
+                 gate_mult=1.125, down_mult=2.0, recompute=True, grad_accum=True, seed=14)
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    _check_gated(w, t, r, "outside")
+
+
 def _check_relu(w, t, r, x64=None, w1=None, w2=None, tol=None):
     a = {k: f64(v) for k, v in t.items()}
     x64 = a["x"] if x64 is None else x64
