@@ -600,7 +600,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
     // fragment refill instead of the first)
     wait_lgkmcnt0();
   }
-  // The spread DMA issue (both operands MN-major, or one wave per SIMD) takes the per-lane form
+  // The spread DMA issue (both operands MN-major, or a 4-wave tile) takes the per-lane form
   // only where a step may be partial: the K loop runs as a main part whose DMAs (of step kt+NS)
   // are wholly in range, then the tail.
   using fast_t = std::true_type;
