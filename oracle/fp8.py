@@ -25,7 +25,6 @@ Follows modded-nanogpt ``gpt.py``:
 from __future__ import annotations
 
 import numpy as np
-import torch
 
 from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode
 from .e5m2 import e5m2_decode, e5m2_encode
@@ -91,39 +90,33 @@ def quantize_e5m2(v, scale) -> np.ndarray:
     return e5m2_encode(np.asarray(v, dtype=np.float32) / _F32(scale))
 
 
-def _bf16(v) -> np.ndarray:
-    """Round to bfloat16 (nearest even) and back, as the method stores its pre-activation."""
-    return torch.from_numpy(np.asarray(v, dtype=np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
-
-
 def relu_sq_fp8_backward_e5m2(dout, x_q, s_x, w1_q, s_w1, w2_q, s_w2, s_post, s_grad, s_dpre,
                               down_mult=1.0):
     """Backward of the fp8 ReLU^2 MLP with fp8 gradients, in the order the method takes it:
 
-    1. pre = (s_x x_q)(s_w1 W1_q)^T, kept as the forward saves it: rounded to bf16 (the
-       pre-activation is stored in the I/O dtype and the backward reads the stored values);
+    1. pre = (s_x x_q)(s_w1 W1_q)^T (the forward's pre-activation, re-derived here);
     2. dout_hat = s_grad * e5m2(dout / s_grad)                 (static gradient scale);
-    3. dpre = down_mult * (dout_hat (s_w2 W2_q)) * relu^2'(pre), formed in fp32 (the product
-       rounded to fp32, then the fp32 multiply by 2 max(pre, 0)): the quantizer's decision in
-       step 4 is taken in the precision the kernel forms dpre in;
+    3. dpre = down_mult * (dout_hat (s_w2 W2_q)) * relu^2'(pre);
     4. dpre_hat = s_dpre * e5m2(dpre / s_dpre)                 (delayed dpre scale);
-    5. post_hat = s_post * e4m3(relu(pre)^2 / s_post)          (relu(pre)^2 in fp32);
+    5. post_hat = s_post * e4m3(relu(pre)^2 / s_post)          (the forward's post operand);
     6. dx = dpre_hat (s_w1 W1_q);  dW1 = dpre_hat^T (s_x x_q);  dW2 = down_mult * dout_hat^T post_hat.
+
+    Steps 1, 3 and 5 are float64: no page states an intermediate precision for them, so none is
+    imposed. Each quantizer takes its input as float32 and divides by its scale in float32 (the
+    codec's own definition, as for the e4m3 operands).
 
     Returns dict(dx, dw1, dw2, dpre (step 3, before quantization), dpre_amax = max|dpre|,
     dout_q, dpre_q (the e5m2 codes))."""
     xh = dequantize(x_q, s_x)
     w1h = dequantize(w1_q, s_w1)
     w2h = dequantize(w2_q, s_w2)
-    pre = _bf16(xh @ w1h.T)
+    pre = xh @ w1h.T
     dout_q = quantize_e5m2(dout, s_grad)
     gh = e5m2_decode(dout_q) * np.float64(_F32(s_grad))
-    dpost32 = (down_mult * (gh @ w2h)).astype(np.float32)
-    dpre = (dpost32 * drelu_sq(pre).astype(np.float32)).astype(np.float64)
+    dpre = (down_mult * (gh @ w2h)) * drelu_sq(pre)
     dpre_q = quantize_e5m2(dpre, s_dpre)
     ph = e5m2_decode(dpre_q) * np.float64(_F32(s_dpre))
-    r32 = np.maximum(pre, 0.0).astype(np.float32)
-    post_hat = dequantize(e4m3_encode((r32 * r32) / _F32(s_post)), s_post)
+    post_hat = dequantize(e4m3_encode(relu_sq(pre).astype(np.float32) / _F32(s_post)), s_post)
     return {
         "dx": ph @ w1h,
         "dw1": ph.T @ xh,
@@ -146,17 +139,15 @@ def relu_sq_fp8_backward_e5m2_sampled(dout, x_q, s_x, w1_q, s_w1, w2_q, s_w2, s_
     gh = e5m2_decode(quantize_e5m2(dout, s_grad)) * np.float64(_F32(s_grad))
 
     def dpre_hat(r_idx, u_idx):
-        pre = _bf16(xh[r_idx] @ w1h[u_idx].T)
-        dpost32 = (down_mult * (gh[r_idx] @ w2h[:, u_idx])).astype(np.float32)
-        dpre = (dpost32 * drelu_sq(pre).astype(np.float32)).astype(np.float64)
+        pre = xh[r_idx] @ w1h[u_idx].T
+        dpre = (down_mult * (gh[r_idx] @ w2h[:, u_idx])) * drelu_sq(pre)
         return e5m2_decode(quantize_e5m2(dpre, s_dpre)) * np.float64(_F32(s_dpre)), pre
 
     every_row = np.arange(xh.shape[0])
     every_unit = np.arange(w1h.shape[0])
     ph_rows, _ = dpre_hat(rows, every_unit)
     ph_units, pre_units = dpre_hat(every_row, units)
-    r32 = np.maximum(pre_units, 0.0).astype(np.float32)
-    post_hat = dequantize(e4m3_encode((r32 * r32) / _F32(s_post)), s_post)
+    post_hat = dequantize(e4m3_encode(relu_sq(pre_units).astype(np.float32) / _F32(s_post)), s_post)
     return {
         "dx_rows": ph_rows @ w1h,
         "dw1_rows": ph_units.T @ xh,

@@ -327,9 +327,10 @@ def test_fp8_forward_small(M, d, H, do, dm):
     # the delayed scale came from this run's amax
     # the delayed post scale came from this problem's max relu(pre)^2 (headroom 1.03)
     assert abs(sp / (f["post_amax"] * 1.03 / 448) - 1) < 1e-2
+    # the backward is bf16 GEMMs on the exact widening of the e4m3 operands: the bf16 bound
     b = oracle.relu_sq_fp8_backward(f64(r.dout), xq, sx, w1q, s1, w2q, s2, down_mult=dm)
     for name, g, ref in (("dx", r.dx, b["dx"]), ("dw1", r.dw_gate, b["dw1"]), ("dw2", r.dw_down, b["dw2"])):
-        assert_close(name, f64(g), ref, TOL["fp8"])
+        assert_close(name, f64(g), ref, TOL["bf16"])
 
 
 def test_fp8_on_grid_equals_bf16_path():
