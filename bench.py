@@ -52,6 +52,52 @@ class HipEvents:
         self.hip.hipEventDestroy(ev)
 
 
+def host_info() -> dict:
+    """This host's CPU: logical CPUs, the ones this process may run on, and the model name."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+def device_info() -> dict:
+    """The GPU the step ran on: name, architecture and compute-unit count (torch), the maximum
+    shader clock and CU count rocminfo reports for the gfx agent, and the ROCm / HIP versions."""
+    import subprocess
+
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
+            "hip": torch.version.hip, "rocm": None, "max_sclk_mhz": None}
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            info["rocm"] = fh.read().strip()
+    except OSError:
+        pass
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+        for agent in out.split("Agent ")[1:]:
+            if "gfx9" not in agent:
+                continue
+            for line in agent.splitlines():
+                line = line.strip()
+                if line.startswith("Max Clock Freq. (MHz):"):
+                    info["max_sclk_mhz"] = int(line.split(":")[1].split()[0])
+                elif line.startswith("Compute Unit:"):
+                    info["rocminfo_cus"] = int(line.split(":")[1].split()[0])
+            break
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
+    return info
+
+
 def stage_flops(w) -> dict:
     M, D, H, O = w.M, w.d_in, w.hidden, w.d_out
     P = 2 * H if w.gated else H
@@ -179,8 +225,10 @@ def cpu_baseline(w, tensors, rows: int) -> dict:
     secs = time.perf_counter() - t0
     sample = w.replace(batch=(rows,))
     threads = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
+    host = host_info()
     return {"value": round(sample.model_flops() / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(secs, 3),
+            "kind": "oracle", "seconds": round(secs, 3), "cores_meaning": "BLAS threads the oracle's matmuls ran on",
+            "host_nproc": host["nproc"], "host_usable_cpus": host["usable_cpus"], "cpu_model": host["cpu_model"],
             "sample": f"first {rows} of {w.M} tokens, full d={w.d_in} H={w.hidden}: float64 numpy forward + "
                       f"backward ({sample.model_flops() / 1e9:.1f} GFLOP on the model count)"}
 
@@ -246,19 +294,28 @@ def main():
 
     def run_steps(hooked):
         """K steps with HIP event pairs around the `hooked` stages (recorded by the library on
-        its stream); returns the event pairs and the average ms per step from torch events."""
+        its stream) and one torch event at every step boundary (the same stream); returns the
+        event pairs, the average ms per step, the K per-step times and the wall time."""
         pairs = [[(ev.create(), ev.create()) for _ in hooked] for _ in range(args.steps)]
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        start.record()
+        marks[0].record()
         for i in range(args.steps):
             for n, (b, e) in zip(hooked, pairs[i]):
                 gm._lib.check(gm.lib().mlp_time_stage_once(stage_id[n], b, e), "mlp_time_stage_once")
             r.step()
-        stop.record()
+            marks[i + 1].record()
         torch.cuda.synchronize()
-        return pairs, start.elapsed_time(stop) / args.steps, time.perf_counter() - t0
+        wall = time.perf_counter() - t0
+        per = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+        return pairs, marks[0].elapsed_time(marks[-1]) / args.steps, per, wall
+
+    def spread_of(per_step):
+        v = sorted(per_step)
+        q = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))]  # noqa: E731
+        return {"median": round(q(0.5), 4), "min": round(v[0], 4), "p90": round(q(0.9), 4),
+                "mean": round(sum(v) / len(v), 4)}
 
     def avg_us(pairs, j):
         return 1e3 * sum(ev.elapsed_ms(*pairs[i][j]) for i in range(args.steps)) / args.steps
@@ -266,18 +323,13 @@ def main():
     # stage pass: every stage's events (each record adds a little queue work, so this pass is not
     # the one the headline is timed on)
     log(f"[bench] stage pass: {args.steps} steps with events around every stage")
-    pairs, _, _ = run_steps(stages)
+    pairs, _, _, _ = run_steps(stages)
     sf = stage_flops(w)
     stage_us, stage_tf = {}, {}
     for j, n in enumerate(stages):
         us = avg_us(pairs, j)
         stage_us[n] = round(us, 2)
         stage_tf[n] = round(sf[n] / (us * 1e-6) / 1e12, 1)
-    # per-step spread: from the up-projection's start to the last weight gradient's end
-    j_up, j_last = stages.index("up"), stages.index("dw_up")
-    per_step = sorted(ev.elapsed_ms(pairs[i][j_up][0], pairs[i][j_last][1]) for i in range(args.steps))
-    q = lambda f: per_step[min(len(per_step) - 1, int(round(f * (len(per_step) - 1))))]
-    spread = {"median": round(q(0.5), 4), "min": round(per_step[0], 4), "p90": round(q(0.9), 4)}
     fwd_us = round(stage_us["up"] + stage_us["down"], 2)
     bwd_us = round(sum(v for k, v in stage_us.items() if k not in ("up", "down")), 2)
     for row in pairs:
@@ -289,7 +341,8 @@ def main():
     # timed pass (the headline): events only around the dominant stage, whose average launch
     # duration in these steps gives the roofline's achieved rate
     log(f"[bench] timing {args.steps} steps (events around the {dom} stage)")
-    pairs, ms, wall = run_steps([dom])
+    pairs, ms, per_step, wall = run_steps([dom])
+    spread = spread_of(per_step)
     dom_us = avg_us(pairs, 0)
     for row in pairs:
         for b, e in row:
@@ -331,7 +384,7 @@ def main():
         cold.append(a.elapsed_time(b))
     del flush
     cold_ms = round(sorted(cold)[len(cold) // 2], 4)
-    log(f"[bench] step median {spread['median']} ms (min {spread['min']}, p90 {spread['p90']}); fwd {fwd_us} us, "
+    log(f"[bench] timed steps: median {spread['median']} ms (min {spread['min']}, p90 {spread['p90']}); fwd {fwd_us} us, "
         f"bwd {bwd_us} us; inference fwd {infer_us} us; cold-cache step {cold_ms} ms")
 
     decode = None
@@ -350,6 +403,11 @@ def main():
         cpu = cpu_baseline(w, tensors, args.cpu_rows)
         log(f"[bench] oracle {cpu['seconds']} s, {cpu['value']} TFLOP/s on {cpu['cores']} threads")
 
+    dev = device_info()
+    log(f"[bench] device {dev}")
+    from workloads import digest
+
+    inputs_sha = {k: digest(v) for k, v in tensors.items()}
     dtype = ("fp8-e4m3 fwd / e5m2 x e4m3 bwd" if w.fp8_bwd else "fp8-e4m3 fwd / bf16 bwd") if w.fp8_fwd else w.dtype
     line = {
         "metric": METRIC if w.name == HEADLINE else f"MLP fwd+bwd TFLOP/s (model FLOP count), {w.name}",
@@ -364,10 +422,11 @@ def main():
                    "model_flop_per_step": flops, "pct_of_bf16_peak": round(100 * tflops / peak, 2),
                    "wall_s_timed": round(wall, 3)},
         "stages_us": stage_us, "stages_tflops": stage_tf,
-        "step_ms": spread, "fwd_us": fwd_us, "bwd_us": bwd_us,
+        "step_ms": spread, "median_step_tflops": round(flops / (spread["median"] * 1e-3) / 1e12, 2), "fwd_us": fwd_us, "bwd_us": bwd_us,
         "infer_fwd_us": infer_us, "infer_fwd_tflops": round(w.model_flops() / 3 / (infer_us * 1e-6) / 1e12, 1),
         "cold_cache_ms_per_step": cold_ms, "decode": decode,
         "roofline": roof, "cpu_baseline": cpu,
+        "device": dev, "host": host_info(), "inputs_sha256": inputs_sha,
     }
     if vendor is not None:
         line["vendor_gemms_us"] = vendor

@@ -139,4 +139,4 @@ def make_inputs(w: Workload) -> dict:
 
 def digest(t: torch.Tensor) -> str:
     """SHA-256 of a tensor's bytes (logged next to results so runs can be matched)."""
-    return hashlib.sha256(t.contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()[:16]
+    return hashlib.sha256(t.contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()
