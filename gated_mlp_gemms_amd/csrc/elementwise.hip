@@ -319,13 +319,15 @@ __device__ __forceinline__ uint32_t byte_col(uint32_t r0, uint32_t r1, uint32_t 
   return ((r0 >> sh) & 0xffu) | (((r1 >> sh) & 0xffu) << 8) | (((r2 >> sh) & 0xffu) << 16) | (((r3 >> sh) & 0xffu) << 24);
 }
 
-template <bool CODES>
+// SRC: 0 existing codes (copied), 1 bf16 values, 2 fp32 values.
+template <int SRC>
 __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t rows, int64_t cols, int64_t ld_src,
                                                       int relu_sq, int e5m2, const float* scale, uint8_t* dst,
                                                       uint8_t* dst_t, int64_t ld_t, int64_t n_ct, int64_t n_tiles) {
   constexpr int TW = 33;   // words per LDS row: 128 codes + 1 word of padding
   __shared__ uint32_t tile[128 * TW];
   const int tid = threadIdx.x;
+  constexpr bool CODES = SRC == 0;
   const float sc = CODES ? 1.0f : *scale;
   for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
     const int64_t r0 = (t / n_ct) * 128, c0 = (t % n_ct) * 128;
@@ -346,11 +348,21 @@ __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t r
         const int64_t r = r0 + lr, c = c0 + lc;
         uint32_t lo = 0, hi = 0;
         if (r < rows && c < cols) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(src) + r * ld_src + c);
+          float in[8];
+          if constexpr (SRC == 2) {
+            const u32x4* q = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(src) + r * ld_src + c);
+            const u32x4 x0 = q[0], x1 = q[1];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { in[k] = __uint_as_float(x0[k]); in[4 + k] = __uint_as_float(x1[k]); }
+          } else {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(src) + r * ld_src + c);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) in[k] = bf16_bits_to_f32((k & 1) ? (x[k >> 1] >> 16) : (x[k >> 1] & 0xffffu));
+          }
           float y[8];
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            float v = bf16_bits_to_f32((k & 1) ? (x[k >> 1] >> 16) : (x[k >> 1] & 0xffffu));
+            float v = in[k];
             if (relu_sq) {
               const float m = fmaxf(v, 0.0f);
               v = m * m;
@@ -405,10 +417,13 @@ hipError_t run_quantize_fp8_2d(DType src_t, const void* src, int64_t rows, int64
   uint8_t* d = reinterpret_cast<uint8_t*>(dst);
   uint8_t* dt = reinterpret_cast<uint8_t*>(dst_t);
   if (src_t == DT_E4M3)
-    hipLaunchKernelGGL(quant2d_kernel<true>, dim3(grid), dim3(256), 0, s, src, rows, cols, ld_src, 0, 0, scale,
+    hipLaunchKernelGGL(quant2d_kernel<0>, dim3(grid), dim3(256), 0, s, src, rows, cols, ld_src, 0, 0, scale,
                        d, dt, ld_t, n_ct, n_tiles);
   else if (src_t == DT_BF16)
-    hipLaunchKernelGGL(quant2d_kernel<false>, dim3(grid), dim3(256), 0, s, src, rows, cols, ld_src, relu_sq, e5m2,
+    hipLaunchKernelGGL(quant2d_kernel<1>, dim3(grid), dim3(256), 0, s, src, rows, cols, ld_src, relu_sq, e5m2,
+                       scale, d, dt, ld_t, n_ct, n_tiles);
+  else if (src_t == DT_F32)
+    hipLaunchKernelGGL(quant2d_kernel<2>, dim3(grid), dim3(256), 0, s, src, rows, cols, ld_src, relu_sq, e5m2,
                        scale, d, dt, ld_t, n_ct, n_tiles);
   else
     return hipErrorInvalidValue;

@@ -53,6 +53,8 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& p, int m, int n, Au
     x.b = *reinterpret_cast<const u32x4*>(elem_ptr<IoT>(p.aux, m, p.ld_aux, p.half + n));
   } else if constexpr (EPI == EPI_DACT || EPI == EPI_F8DACT) {
     x.a = *reinterpret_cast<const u32x4*>(elem_ptr<IoT>(p.aux, m, p.ld_aux, n));
+    if constexpr (ElemTraits<IoT>::bytes == 4)   // fp32 pre-activation: 8 values in two pieces
+      x.c = *reinterpret_cast<const u32x4*>(elem_ptr<IoT>(p.aux, m, p.ld_aux, n + 4));
   } else if constexpr (EPI == EPI_STORE) {
     if (p.accumulate) {
       const bool lo = m < p.c_split;
@@ -146,9 +148,13 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
     *reinterpret_cast<u32x2*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) =
         u32x2{f32x4_to_fp8<false>(y[0], y[1], y[2], y[3]), f32x4_to_fp8<false>(y[4], y[5], y[6], y[7])};
   } else if constexpr (EPI == EPI_F8DACT) {
-    static_assert(ElemTraits<IoT>::bytes == 2, "the pre-activation is read as 16-bit data");
     float pre[8];
-    unpack16x8<IoT>(x.a, pre);
+    if constexpr (ElemTraits<IoT>::bytes == 4) {   // fp32 pre-activation (the fp8-gradient backward)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) { pre[r] = __uint_as_float(x.a[r]); pre[4 + r] = __uint_as_float(x.c[r]); }
+    } else {
+      unpack16x8<IoT>(x.a, pre);
+    }
     const float sd = *p.s_post;
     float y[8];
 #pragma unroll

@@ -19,9 +19,9 @@ enum Epi : int {
   EPI_DGATED = 4,   // da = alpha * acc; g, u <- aux; dg, du -> C0[m][n], C0[m][half+n];
                     // a -> C1 (flag 2). C0 may equal aux.
   EPI_DACT = 5,     // dpost = alpha * acc; pre <- aux; dpre = dpost * f'(pre) -> C0; post -> C1 (flag 2)
-  EPI_F8ACT = 6,    // pre = alpha * acc -> aux (bf16, flag 1); post = relu(pre)^2;
+  EPI_F8ACT = 6,    // pre = alpha * acc -> aux (bf16 or fp32, flag 1); post = relu(pre)^2;
                     // C0 = e4m3(post / *s_post); *amax = max(*amax, max post)
-  EPI_F8DACT = 7,   // dpre = alpha * acc * 2 max(pre, 0), pre <- aux (bf16);
+  EPI_F8DACT = 7,   // dpre = alpha * acc * 2 max(pre, 0), pre <- aux (bf16 or fp32);
                     // C0 = e5m2(dpre / *s_post) (s_post holds the dpre scale here);
                     // *amax = max(*amax, max |dpre|)
 };

@@ -9,7 +9,10 @@ namespace gmlp {
 template <int BM, int BN, int W>
 static hipError_t dispatch(DType io, int epi, const GemmArgs& a, int grid, hipStream_t s) {
   switch (epi) {
-    case EPI_F8DACT: return launch_gemm_dma<f8g, bf16, BM, BN, true, true, EPI_F8DACT, W>(a, grid, s);
+    case EPI_F8DACT:   // io: the type of the pre-activation it reads
+      if (io == DT_BF16) return launch_gemm_dma<f8g, bf16, BM, BN, true, true, EPI_F8DACT, W>(a, grid, s);
+      if (io == DT_F32) return launch_gemm_dma<f8g, float, BM, BN, true, true, EPI_F8DACT, W>(a, grid, s);
+      return hipErrorInvalidValue;
     case EPI_STORE:
       if (io == DT_BF16) return launch_gemm_dma<f8g, bf16, BM, BN, true, true, EPI_STORE, W>(a, grid, s);
       if (io == DT_F32) return launch_gemm_dma<f8g, float, BM, BN, true, true, EPI_STORE, W>(a, grid, s);

@@ -246,7 +246,7 @@ WsLayout ws_layout(const mlp_desc* d, int phase) {
     take(L.partial, L.partial_bytes, std::max(partial_bytes(g.down, M, O), partial_bytes(g.up_split, M, 2 * H)));
   } else if (d->fp8_bwd) {
     const int64_t Mp = pad16(M);
-    if (d->recompute) take(L.pre, L.pre_bytes, (size_t)M * H * es);
+    if (d->recompute) take(L.pre, L.pre_bytes, (size_t)M * H * sizeof(float));
     take(L.gq, L.gq_bytes, (size_t)M * O);
     take(L.gt, L.gt_bytes, (size_t)O * Mp);
     take(L.pq, L.pq_bytes, (size_t)M * H);
@@ -478,7 +478,9 @@ mlp_status up_projection(const mlp_desc* d, const void* x, const void* wg, const
     a.s_post = f->s_post;
     a.amax = f->post_amax;
     const Plan p = plan_quantizing(DT_E4M3, M, H, D);
-    return gemm(DT_E4M3, DT_BF16, NT, EPI_F8ACT, p, a, M, H, D, nullptr, s, "e4m3 up projection");
+    // the fp8-gradient backward takes its rounding decisions on an fp32 pre-activation
+    return gemm(DT_E4M3, d->fp8_bwd ? DT_F32 : DT_BF16, NT, EPI_F8ACT, p, a, M, H, D, nullptr, s,
+                "e4m3 up projection");
   }
   a.A = x;
   a.B0 = wg;
@@ -536,7 +538,8 @@ mlp_status fwd_impl(const mlp_desc* d, const void* x, const void* wg, const void
   return gemm(fin, io, NT, EPI_STORE, p, b, M, O, H, w + L.partial, s, "down projection");
 }
 
-// Backward with fp8 gradients (ReLU^2, see mlp_fp8): dout -> e5m2 (row-major for the d-act
+// Backward with fp8 gradients (ReLU^2, see mlp_fp8; the pre-activation is fp32, so the e5m2 /
+// e4m3 rounding decisions on dpre and relu(pre)^2 are taken on an fp32 value): dout -> e5m2 (row-major for the d-act
 // product, transposed for dW2); dpre_q = e5m2(dm (dout_q W2) 2 relu(pre) / s_dpre) from the
 // e5m2 x e4m3 product against the transposed W2 cache; dx = dpre_q W1 against the transposed W1
 // cache; dW1 = dpre_q^T x_q and dW2 = dm dout_q^T post_q from transposed copies (token dimension
@@ -562,7 +565,7 @@ mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void*
     a.alpha_dev1 = f->s_w1;
     const Plan p = plan_quantizing(DT_E4M3, M, H, D);
     StageScope st(MLP_STAGE_RECOMPUTE, s);
-    MLP_TRY(gemm(DT_E4M3, DT_BF16, NT, EPI_STORE, p, a, M, H, D, nullptr, s, "recompute pre-activation"));
+    MLP_TRY(gemm(DT_E4M3, DT_F32, NT, EPI_STORE, p, a, M, H, D, nullptr, s, "recompute pre-activation"));
     pre = w + L.pre;
   }
   void* gq = w + L.gq;
@@ -587,7 +590,7 @@ mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void*
     a.s_post = f->s_dpre;
     a.amax = f->dpre_amax;
     const Plan p = plan_quantizing(DT_F8G, M, H, O);
-    MLP_TRY(gemm(DT_F8G, DT_BF16, NT, EPI_F8DACT, p, a, M, H, O, nullptr, s, "fp8 d-activation GEMM"));
+    MLP_TRY(gemm(DT_F8G, DT_F32, NT, EPI_F8DACT, p, a, M, H, O, nullptr, s, "fp8 d-activation GEMM"));
   } else if (dw2) {
     StageScope st(MLP_STAGE_DW_DOWN, s);
     MLP_TRY(hip_status(run_quantize_fp8_2d(DT_BF16, dout, M, O, O, 0, 1, f->s_grad, nullptr, gt, Mp, s),
@@ -595,7 +598,7 @@ mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void*
   }
   if (dw2) {   // dW2 (+)= dm dout_q^T post_q, post_q = e4m3(relu(pre)^2 / s_post)
     StageScope st(MLP_STAGE_DW_DOWN, s);
-    MLP_TRY(hip_status(run_quantize_fp8_2d(DT_BF16, pre, M, H, H, 1, 0, f->s_post, nullptr, w + L.postt, Mp, s),
+    MLP_TRY(hip_status(run_quantize_fp8_2d(DT_F32, pre, M, H, H, 1, 0, f->s_post, nullptr, w + L.postt, Mp, s),
                        "quantize relu(pre)^2"));
     GemmArgs a = base_args(d);
     a.A = gt;

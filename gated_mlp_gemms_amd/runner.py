@@ -42,7 +42,9 @@ class MlpRunner:
         P = 2 * hidden if self.gated else hidden
         self.out = torch.empty(M, d_out, dtype=tdt, device=dev)
         self.out_infer = torch.empty(M, d_out, dtype=tdt, device=dev)
-        self.saved = None if recompute else torch.empty(M, P, dtype=tdt, device=dev)
+        # the fp8-gradient backward keeps its pre-activation in fp32
+        sdt = torch.float32 if fp8_bwd else tdt
+        self.saved = None if recompute else torch.empty(M, P, dtype=sdt, device=dev)
         self.dpreact = self.saved if (dpreact_in_place and not recompute) else torch.empty(M, P, dtype=tdt, device=dev)
         self.dx = torch.empty(M, d_in, dtype=tdt, device=dev)
         gdt = torch.float32 if grad_accum else tdt

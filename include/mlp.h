@@ -90,7 +90,7 @@ typedef struct mlp_desc {
   int32_t recompute;  /* 1: nothing is saved; mlp_bwd recomputes the pre-activation from x */
   int32_t fp8_fwd;    /* 1: e4m3 forward GEMMs (ReLU^2, bf16 only); see mlp_fp8 */
   int32_t fp8_bwd;    /* 1: fp8 backward GEMMs with e5m2 gradients (needs fp8_fwd); see mlp_fp8.
-                       * The forward ignores it. */
+                       * The pre-activation saved by mlp_fwd is then fp32. */
 } mlp_desc;
 
 /*
@@ -140,9 +140,10 @@ size_t mlp_workspace_bytes(const mlp_desc* desc, int phase);
  * Training forward (quack mlp.py: mlp_func with grad enabled; flash-swiglu-mlp README,
  * "design points": fused gate/up forward, then the down projection).
  *   out          [M, d_out]                          written
- *   saved_preact gated: [M, 2H], row = [g | u]; non-gated: [M, H] pre. Written. Must be NULL
- *                iff desc->recompute (then nothing is kept for the backward: quack's
- *                MLPRecomputeFunc saves only x and the weights).
+ *   saved_preact gated: [M, 2H], row = [g | u]; non-gated: [M, H] pre. Written, in
+ *                desc->dtype (fp32 with desc->fp8_bwd: the fp8-gradient backward rounds dpre and
+ *                relu(pre)^2 to fp8 from it). Must be NULL iff desc->recompute (then nothing is
+ *                kept for the backward: quack's MLPRecomputeFunc saves only x and the weights).
  *   w_up         NULL for a non-gated activation (w_gate then holds W1, w_down holds W2).
  *   fp8          non-NULL iff desc->fp8_fwd; x / w_gate / w_down are then not read.
  */
