@@ -14,7 +14,8 @@ import torch
 from ._lib import (  # noqa: F401
     LIB_PATH, MLP_ACT_GEGLU, MLP_ACT_GELU_TANH, MLP_ACT_GLU, MLP_ACT_REGLU, MLP_ACT_RELU, MLP_ACT_RELU_SQ,
     MLP_ACT_SWIGLU, MLP_BF16, MLP_F16, MLP_F32, MLP_FP8_E4M3, MLP_FP8_E5M2, MLP_GATE_INSIDE, MLP_GATE_OUTSIDE,
-    MLP_PHASE_BWD, MLP_PHASE_FWD, MLP_PHASE_FWD_INFER, MlpDesc, MlpError, MlpFp8, check, lib,
+    MLP_NOALLOC_SCRATCH_BYTES, MLP_PHASE_BWD, MLP_PHASE_FWD, MLP_PHASE_FWD_INFER, MlpDesc, MlpError, MlpFp8, check,
+    lib,
 )
 
 _ACTS = {"swiglu": MLP_ACT_SWIGLU, "relu_sq": MLP_ACT_RELU_SQ, "geglu": MLP_ACT_GEGLU, "reglu": MLP_ACT_REGLU,
@@ -83,6 +84,15 @@ def mlp_fwd_infer(desc, x, w_gate, w_up, w_down, out, fp8=None, workspace=None, 
     st = lib().mlp_fwd_infer(C.byref(desc), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out),
                              C.byref(fp8) if fp8 is not None else None, _ptr(ws), nws, _stream(stream))
     check(st, "mlp_fwd_infer")
+    return out
+
+
+def mlp_fwd_infer_noalloc(desc, x, w_gate, w_up, w_down, out, fp8=None, stream=None):
+    """``mlp_fwd_infer`` on the library's static per-GPU scratch: no workspace argument and no
+    allocation (the problem's inference workspace must fit MLP_NOALLOC_SCRATCH_BYTES)."""
+    st = lib().mlp_fwd_infer_noalloc(C.byref(desc), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out),
+                                     C.byref(fp8) if fp8 is not None else None, _stream(stream))
+    check(st, "mlp_fwd_infer_noalloc")
     return out
 
 

@@ -14,6 +14,7 @@ MLP_F32, MLP_BF16, MLP_F16 = 0, 1, 2
 MLP_GATE_OUTSIDE, MLP_GATE_INSIDE = 0, 1
 MLP_PHASE_FWD, MLP_PHASE_FWD_INFER, MLP_PHASE_BWD = 0, 1, 2
 MLP_FP8_E4M3, MLP_FP8_E5M2 = 0, 1
+MLP_NOALLOC_SCRATCH_BYTES = 64 << 20
 STAGES = ("up", "down", "recompute", "dact", "dw_down", "dx", "dw_up", "act", "widen")
 
 
@@ -40,6 +41,7 @@ _SIGNATURES = {
     "mlp_workspace_bytes": (C.c_size_t, [C.POINTER(MlpDesc), C.c_int]),
     "mlp_fwd": (C.c_int, [C.POINTER(MlpDesc), _P, _P, _P, _P, _P, _P, C.POINTER(MlpFp8), _P, C.c_size_t, _P]),
     "mlp_fwd_infer": (C.c_int, [C.POINTER(MlpDesc), _P, _P, _P, _P, _P, C.POINTER(MlpFp8), _P, C.c_size_t, _P]),
+    "mlp_fwd_infer_noalloc": (C.c_int, [C.POINTER(MlpDesc), _P, _P, _P, _P, _P, C.POINTER(MlpFp8), _P]),
     "mlp_bwd": (C.c_int, [C.POINTER(MlpDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_int,
                           C.POINTER(MlpFp8), _P, C.c_size_t, _P]),
     "mlp_quantize_workspace_bytes": (C.c_size_t, []),

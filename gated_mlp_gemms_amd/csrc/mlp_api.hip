@@ -11,6 +11,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "launch.hpp"
@@ -488,9 +489,9 @@ mlp_status up_projection(const mlp_desc* d, const void* x, const void* wg, const
   return gemm(io, io, NT, EPI_ACT, p, a, M, H, D, nullptr, s, "up projection");
 }
 
-mlp_status fwd_impl(const mlp_desc* d, const void* x, const void* wg, const void* wu, const void* wd,
-                    void* out, void* saved, const mlp_fp8* f, void* ws, size_t ws_bytes, void* stream,
-                    bool infer) {
+// Host-side checks of a forward call's arguments (everything but the workspace).
+mlp_status fwd_check(const mlp_desc* d, const void* x, const void* wg, const void* wu, const void* wd,
+                     const void* out, const void* saved, const mlp_fp8* f, bool infer) {
   MLP_TRY(check_desc(d));
   const bool gated = is_gated(d->act);
   if (!d->fp8_fwd) {
@@ -505,10 +506,14 @@ mlp_status fwd_impl(const mlp_desc* d, const void* x, const void* wg, const void
     if (d->recompute) MLP_TRY(need_null(saved, "saved_preact", "with recompute"));
     else MLP_TRY(need_ptr(saved, "saved_preact"));
   }
-  MLP_TRY(check_fp8(d, f, true));
-  const int phase = infer ? MLP_PHASE_FWD_INFER : MLP_PHASE_FWD;
-  MLP_TRY(check_ws(d, phase, ws, ws_bytes));
+  return check_fp8(d, f, true);
+}
 
+// The forward's launches, on arguments that passed fwd_check and a workspace of at least
+// ws_layout(d, phase).total bytes.
+mlp_status fwd_run(const mlp_desc* d, const void* x, const void* wg, const void* wu, const void* wd,
+                   void* out, void* saved, const mlp_fp8* f, void* ws, void* stream, bool infer) {
+  const int phase = infer ? MLP_PHASE_FWD_INFER : MLP_PHASE_FWD;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const WsLayout L = ws_layout(d, phase);
   char* w = reinterpret_cast<char*>(ws);
@@ -536,6 +541,49 @@ mlp_status fwd_impl(const mlp_desc* d, const void* x, const void* wg, const void
   const Plan p = plan_all(d).down;
   StageScope st(MLP_STAGE_DOWN, s);
   return gemm(fin, io, NT, EPI_STORE, p, b, M, O, H, w + L.partial, s, "down projection");
+}
+
+mlp_status fwd_impl(const mlp_desc* d, const void* x, const void* wg, const void* wu, const void* wd,
+                    void* out, void* saved, const mlp_fp8* f, void* ws, size_t ws_bytes, void* stream,
+                    bool infer) {
+  MLP_TRY(fwd_check(d, x, wg, wu, wd, out, saved, f, infer));
+  MLP_TRY(check_ws(d, infer ? MLP_PHASE_FWD_INFER : MLP_PHASE_FWD, ws, ws_bytes));
+  return fwd_run(d, x, wg, wu, wd, out, saved, f, ws, stream, infer);
+}
+
+// ---- the library-held workspace of mlp_fwd_infer_noalloc ---------------------------------------
+// One copy per GPU, held from the library's load until the process ends. In host code `scratch`
+// names a host-side stand-in, not the device array: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that address is
+// ever handed to a kernel.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[MLP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The scratch array's device address on the device `stream` runs on, which must be the calling
+// thread's current device.
+mlp_status scratch_address(void* stream, void** out) {
+  int dev = -1;
+  MLP_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLP_ERR_UNSUPPORTED, "device %d is beyond the %d this library tracks", dev, kMaxDevices);
+  if (stream) {
+    int sdev = -1;
+    MLP_TRY(hip_status(hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &sdev), "hipStreamGetDevice"));
+    if (sdev != dev)
+      return fail(MLP_ERR_INVALID_ARG, "stream belongs to device %d but the current device is %d", sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    MLP_TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u))
+      return fail(MLP_ERR_HIP, "hipGetSymbolAddress(scratch) gave an unusable address %p", p);
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MLP_OK;
 }
 
 // Backward with fp8 gradients (ReLU^2, see mlp_fp8; the pre-activation is fp32, so the e5m2 /
@@ -651,7 +699,7 @@ mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void*
 
 extern "C" {
 
-int mlp_abi_version(void) { return 2; }
+int mlp_abi_version(void) { return 3; }
 
 const char* mlp_status_string(int st) {
   switch (st) {
@@ -685,6 +733,20 @@ mlp_status mlp_fwd_infer(const mlp_desc* d, const void* x, const void* wg, const
                          const void* wd, void* out, const mlp_fp8* f, void* ws, size_t ws_bytes,
                          void* stream) {
   return fwd_impl(d, x, wg, wu, wd, out, nullptr, f, ws, ws_bytes, stream, true);
+}
+
+mlp_status mlp_fwd_infer_noalloc(const mlp_desc* d, const void* x, const void* wg, const void* wu,
+                                 const void* wd, void* out, const mlp_fp8* f, void* stream) {
+  MLP_TRY(fwd_check(d, x, wg, wu, wd, out, nullptr, f, true));
+  const size_t need = ws_layout(d, MLP_PHASE_FWD_INFER).total;
+  if (need > (size_t)MLP_NOALLOC_SCRATCH_BYTES)
+    return fail(MLP_ERR_WORKSPACE,
+                "this inference forward needs %zu bytes of workspace; the library's static scratch holds %zu "
+                "(MLP_NOALLOC_SCRATCH_BYTES): call mlp_fwd_infer with a caller-owned workspace instead",
+                need, (size_t)MLP_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  MLP_TRY(scratch_address(stream, &ws));
+  return fwd_run(d, x, wg, wu, wd, out, nullptr, f, ws, stream, true);
 }
 
 mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const void* wg, const void* wu,

@@ -160,6 +160,28 @@ mlp_status mlp_fwd_infer(const mlp_desc* desc, const void* x, const void* w_gate
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): mlp_fwd_infer with the workspace taken from a
+ * static device array the library holds, MLP_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, from the
+ * library's load until the process ends. The call allocates and frees nothing (no hipMalloc,
+ * hipFree or allocating library routine); the caller still owns x, the weights, out and fp8.
+ *   - Everything else is as mlp_fwd_infer, and out is bit for bit what mlp_fwd_infer writes.
+ *   - MLP_ERR_WORKSPACE (before any HIP call) when mlp_workspace_bytes(desc,
+ *     MLP_PHASE_FWD_INFER) exceeds MLP_NOALLOC_SCRATCH_BYTES (e.g. beyond ~512 tokens at
+ *     d_in = 4096, hidden = 11008 in bf16).
+ *   - stream must belong to the calling thread's current device (else MLP_ERR_INVALID_ARG).
+ *     The first call on a device looks the array's address up on that device (make it before
+ *     a graph capture starts).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in time on the same
+ *     GPU (other streams, other threads) race on it and must be serialized by the caller.
+ *     Nothing in the array needs to start at zero; a call leaves its intermediates there.
+ */
+#define MLP_NOALLOC_SCRATCH_BYTES (64u << 20)
+mlp_status mlp_fwd_infer_noalloc(const mlp_desc* desc, const void* x, const void* w_gate,
+                                 const void* w_up, const void* w_down, void* out, const mlp_fp8* fp8,
+                                 void* stream);
+
+/*
  * Backward (quack mlp.py: MLPRecomputeFunc.backward, _compute_weight_grad; flash-swiglu-mlp
  * README, "design points": fused dA/dG/dU with dA never stored, dG/dU written over G/U,
  * merged dW_g/dW_u GEMM, single-accumulator dI).

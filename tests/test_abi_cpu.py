@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib._SIGNATURES), "binding and header disagree"
-    assert L.mlp_abi_version() == 2
+    assert L.mlp_abi_version() == 3
 
 
 def _desc(**kw):
@@ -277,3 +277,26 @@ def test_quantize_fp8_checks():
     assert q(ld_t=104) == gm._lib.MLP_ERR_INVALID_ARG         # not a multiple of 16
     assert q(scale=None) == gm._lib.MLP_ERR_INVALID_ARG
     assert q(dst_t=FAKE + 8) == gm._lib.MLP_ERR_ALIGNMENT
+
+
+def test_noalloc_entry_checks_run_before_any_hip_call():
+    """mlp_fwd_infer_noalloc: the argument checks and the static-scratch size check come before
+    any HIP call (so they run here, without a GPU); the size limit is the header's."""
+    text = open(os.path.join(ROOT, "include", "mlp.h")).read()
+    m = re.search(r"#define MLP_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == gm.MLP_NOALLOC_SCRATCH_BYTES
+    L = gm.lib()
+
+    def call(d, x=FAKE, wu=FAKE, fp8=None):
+        return L.mlp_fwd_infer_noalloc(C.byref(d), x, FAKE, wu, FAKE, FAKE, C.byref(fp8) if fp8 else None, None)
+
+    assert call(_desc(M=0)) == gm._lib.MLP_ERR_INVALID_ARG
+    assert call(_desc(), x=None) == gm._lib.MLP_ERR_INVALID_ARG and "x is NULL" in _err()
+    assert call(_desc(act="relu_sq")) == gm._lib.MLP_ERR_INVALID_ARG and "w_up" in _err()
+    big = _desc(M=2048, d_in=4096, hidden=11008, d_out=4096)
+    need = L.mlp_workspace_bytes(C.byref(big), gm.MLP_PHASE_FWD_INFER)
+    assert need > gm.MLP_NOALLOC_SCRATCH_BYTES
+    assert call(big) == gm._lib.MLP_ERR_WORKSPACE
+    assert "MLP_NOALLOC_SCRATCH_BYTES" in _err() and str(need) in _err()
+    fits = _desc(M=512, d_in=4096, hidden=11008, d_out=4096)
+    assert L.mlp_workspace_bytes(C.byref(fits), gm.MLP_PHASE_FWD_INFER) <= gm.MLP_NOALLOC_SCRATCH_BYTES
