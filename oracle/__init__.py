@@ -34,7 +34,7 @@ from .e5m2 import (  # noqa: F401
     E5M2_MAX, e5m2_decode, e5m2_encode, e5m2_grid,
 )
 from .fp8 import (  # noqa: F401
-    per_tensor_scale, quantize_per_tensor, dequantize, next_delayed_scale,
+    per_tensor_scale, quantize_per_tensor, dequantize, next_delayed_scale, weight_quantize_calls,
     relu_sq_fp8_forward, relu_sq_fp8_backward, quantize_e5m2, relu_sq_fp8_backward_e5m2,
     relu_sq_fp8_backward_e5m2_sampled,
 )

@@ -60,6 +60,27 @@ def next_delayed_scale(amax, prev_scale, gain, floor) -> np.float32:
     return _F32(new) if a > 0 else _F32(prev_scale)
 
 
+def weight_quantize_calls(weights, exact_calls=16):
+    """The weight-cache quantizer over a sequence of calls (``_quantize_mlp_weights_and_scales``
+    with FP8_EXACT_SCALE_CALLS): call t < exact_calls sets the scale exactly from that call's
+    weights, max(amax|W_t|, 1e-12) / 448; every later call uses the amax the previous call
+    recorded, max(amax|W_{t-1}|, 1e-12) / 448 (one call delayed), and e4m3's saturation takes
+    entries beyond it to +-448. Both are formed in float32. The page records the amax per tile;
+    the maximum over the tiles is the tensor's amax, which is what this function takes.
+
+    weights: a sequence of arrays (one per call). Returns a list of (codes, scale) per call."""
+    out = []
+    prev_amax = None
+    for t, w in enumerate(weights):
+        w32 = np.asarray(w, dtype=np.float32)
+        amax = _F32(np.max(np.abs(w32))) if w32.size else _F32(0.0)
+        basis = amax if (t < exact_calls or prev_amax is None) else prev_amax
+        scale = _F32(max(basis, _F32(1e-12)) / _F32(E4M3_MAX))
+        out.append((e4m3_encode(w32 / scale), scale))
+        prev_amax = amax
+    return out
+
+
 def relu_sq_fp8_forward(x_q, s_x, w1_q, s_w1, w2_q, s_w2, s_post=None, down_mult=1.0):
     """ReLU^2 MLP forward on e4m3 operands: pre = (s_x x_q)(s_w1 W1_q)^T, post = relu(pre)^2,
     out = down_mult * post_hat (s_w2 W2_q)^T, where post_hat = s_post * e4m3(fp32(post)/s_post)

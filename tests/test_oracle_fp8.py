@@ -150,3 +150,52 @@ def test_page_constants():
     assert np.sqrt(c["gpt_model_dim"]["value"]) < c["e4m3_max"]["value"] * c["fp8_mlp_x_scale"]["value"]
     assert round(float(np.sqrt(c["gpt_model_dim"]["value"])), 1) == c["sqrt_model_dim_printed"]["value"]
     assert c["fp8_post_headroom"]["value"] == 1.03 and c["multiplier_default"]["value"] == 1.0
+
+
+def test_weight_scale_bootstrap_then_delayed_by_hand():
+    """Exact weight scales for the first 16 calls, then the previous call's amax (gpt.py
+    FP8_EXACT_SCALE_CALLS = 16, _quantize_mlp_weights_and_scales). B has amax 1.75 = 448 * 2^-8, so
+    c * B has the exact scale c * 2^-8 and the codes below follow from the OCP E4M3 table by hand:
+    448 -> 0x7E, 128 -> 0x70, -64 -> 0xE8, 256 -> 0x78, -128 -> 0xF0, 0 -> 0x00."""
+    with open(os.path.join(GOLDEN, "page_constants.json")) as fh:
+        n_exact = int(json.load(fh)["fp8_exact_scale_calls"]["value"])
+    assert n_exact == 16
+    B = np.array([[1.75, 0.5], [-0.25, 0.0]])
+    c = [1.0] * 16 + [2.0, 2.0, 0.5]             # the weights double at call 16, halve at call 18
+    res = oracle.weight_quantize_calls([ci * B for ci in c], exact_calls=n_exact)
+    base = np.array([[0x7E, 0x70], [0xE8, 0x00]], dtype=np.uint8)
+    for t in range(16):                           # exact: scale 2^-8, B / 2^-8 = [[448, 128], [-64, 0]]
+        assert res[t][1] == np.float32(2.0 ** -8)
+        np.testing.assert_array_equal(res[t][0], base)
+    # call 16: delayed scale from call 15's amax (1.75 -> 2^-8); 2B / 2^-8 = [[896, 256], [-128, 0]]:
+    # 896 saturates to 448
+    assert res[16][1] == np.float32(2.0 ** -8)
+    np.testing.assert_array_equal(res[16][0], np.array([[0x7E, 0x78], [0xF0, 0x00]], dtype=np.uint8))
+    # call 17: call 16's amax was 3.5 -> scale 2^-7; 2B / 2^-7 = [[448, 128], [-64, 0]]
+    assert res[17][1] == np.float32(2.0 ** -7)
+    np.testing.assert_array_equal(res[17][0], base)
+    # call 18: B/2 quantized with call 17's scale 2^-7: [[112, 32], [-16, 0]]: 112 = 2^6 * 1.75 -> exponent
+    # field 6 + 7 = 13, mantissa 6 -> (13 << 3) | 6 = 0x6E,
+    # 32 = 2^5 -> 0x60, -16 = -2^4 -> 0xD8
+    assert res[18][1] == np.float32(2.0 ** -7)
+    np.testing.assert_array_equal(res[18][0], np.array([[0x6E, 0x60], [0xD8, 0x00]], dtype=np.uint8))
+    # the codes decode to what the hand arithmetic says
+    np.testing.assert_array_equal(oracle.e4m3_decode(res[18][0]) * 2.0 ** -7, np.array([[0.875, 0.25], [-0.125, 0.0]]))
+
+
+def test_weight_scale_exact_calls_equal_per_tensor_quantizer():
+    """Every exact call is the per-tensor quantizer, and a delayed call with unchanged weights is too."""
+    rng = np.random.default_rng(3)
+    ws = [rng.uniform(-0.05, 0.05, (24, 40)) * (1 + 0.1 * t) for t in range(4)]
+    res = oracle.weight_quantize_calls(ws, exact_calls=2)
+    for t in range(2):
+        q, sc = oracle.quantize_per_tensor(ws[t])
+        assert res[t][1] == sc
+        np.testing.assert_array_equal(res[t][0], q)
+    # call 2 uses call 1's amax: the scale is per_tensor_scale(ws[1]) and ws[2] (10 % larger) saturates
+    assert res[2][1] == oracle.per_tensor_scale(ws[1])
+    assert np.any(oracle.e4m3_decode(res[2][0]) == 448.0) or np.any(oracle.e4m3_decode(res[2][0]) == -448.0)
+    same = oracle.weight_quantize_calls([ws[0], ws[0], ws[0]], exact_calls=1)
+    for codes, sc in same:
+        np.testing.assert_array_equal(codes, same[0][0])
+        assert sc == same[0][1]
