@@ -134,5 +134,22 @@ def mlp_quantize_fp8(src, fmt, scale, dst=None, dst_t=None, ld_t=None, relu_sq=F
     check(st, "mlp_quantize_fp8")
 
 
+def mlp_weight_amax_slots(rows: int, cols: int) -> int:
+    return int(lib().mlp_weight_amax_slots(int(rows), int(cols)))
+
+
+def mlp_quantize_weight_e4m3(w, exact, scale, tile_amax, dst=None, dst_t=None, ld_t=None, stream=None):
+    """The fp8 weight-cache quantizer: e4m3 codes of the [rows, cols] weight ``w`` (bf16 / f32)
+    row-major into ``dst`` and / or transposed into ``dst_t`` [cols, ld_t]; the scale (a device fp32
+    scalar) is w's exact one when ``exact``, else the one the amax recorded by the previous call in
+    ``tile_amax`` gives; this call's per-tile amax is recorded there."""
+    rows, cols = w.shape
+    if ld_t is None:
+        ld_t = (rows + 15) // 16 * 16
+    st = lib().mlp_quantize_weight_e4m3(_ptr(w), _DTYPES[w.dtype], rows, cols, int(bool(exact)), _ptr(scale),
+                                        _ptr(tile_amax), _ptr(dst), _ptr(dst_t), int(ld_t), _stream(stream))
+    check(st, "mlp_quantize_weight_e4m3")
+
+
 def mlp_fp8_next_scale(amax: float, prev_scale: float, gain: float, floor: float) -> float:
     return float(lib().mlp_fp8_next_scale(amax, prev_scale, gain, floor))

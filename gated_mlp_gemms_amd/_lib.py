@@ -48,6 +48,8 @@ _SIGNATURES = {
     "mlp_quantize_e4m3": (C.c_int, [_P, C.c_int, C.c_int64, _P, _P, _P, C.c_size_t, _P]),
     "mlp_quantize_fp8": (C.c_int, [_P, C.c_int, C.c_int64, C.c_int64, C.c_int, C.c_int, _P, _P, _P, C.c_int64, _P]),
     "mlp_fp8_next_scale": (C.c_float, [C.c_float, C.c_float, C.c_float, C.c_float]),
+    "mlp_quantize_weight_e4m3": (C.c_int, [_P, C.c_int, C.c_int64, C.c_int64, C.c_int, _P, _P, _P, _P, C.c_int64, _P]),
+    "mlp_weight_amax_slots": (C.c_int64, [C.c_int64, C.c_int64]),
     "mlp_status_string": (C.c_char_p, [C.c_int]),
     "mlp_last_error": (C.c_char_p, []),
     "mlp_abi_version": (C.c_int, []),

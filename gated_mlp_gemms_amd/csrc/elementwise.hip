@@ -319,16 +319,21 @@ __device__ __forceinline__ uint32_t byte_col(uint32_t r0, uint32_t r1, uint32_t 
   return ((r0 >> sh) & 0xffu) | (((r1 >> sh) & 0xffu) << 8) | (((r2 >> sh) & 0xffu) << 16) | (((r3 >> sh) & 0xffu) << 24);
 }
 
-// SRC: 0 existing codes (copied), 1 bf16 values, 2 fp32 values.
+// SRC: 0 existing codes (copied), 1 bf16 values, 2 fp32 values. tile_amax (values only; may be
+// NULL): slot t = row tile * n_ct + column tile of each tile with rows inside the matrix gets the
+// tile's max |v| (of the source values, before relu_sq). amax_only: record tile_amax and write no
+// codes (the scale is not read).
 template <int SRC>
 __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t rows, int64_t cols, int64_t ld_src,
                                                       int relu_sq, int e5m2, const float* scale, uint8_t* dst,
-                                                      uint8_t* dst_t, int64_t ld_t, int64_t n_ct, int64_t n_tiles) {
+                                                      uint8_t* dst_t, int64_t ld_t, int64_t n_ct, int64_t n_tiles,
+                                                      float* tile_amax, int amax_only) {
   constexpr int TW = 33;   // words per LDS row: 128 codes + 1 word of padding
   __shared__ uint32_t tile[128 * TW];
+  __shared__ float wave_max[4];
   const int tid = threadIdx.x;
   constexpr bool CODES = SRC == 0;
-  const float sc = CODES ? 1.0f : *scale;
+  const float sc = (CODES || amax_only) ? 1.0f : *scale;
   for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
     const int64_t r0 = (t / n_ct) * 128, c0 = (t % n_ct) * 128;
     if constexpr (CODES) {   // 8 lanes x 16 codes per row, 32 rows per pass
@@ -342,6 +347,7 @@ __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t r
         for (int q = 0; q < 4; ++q) tile[lr * TW + lc / 4 + q] = x[q];
       }
     } else {                 // 16 lanes x 8 values per row, 16 rows per pass
+      float m = 0.0f;
 #pragma unroll
       for (int pass = 0; pass < 8; ++pass) {
         const int lr = (tid >> 4) + 16 * pass, lc = (tid & 15) * 8;
@@ -359,13 +365,16 @@ __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t r
 #pragma unroll
             for (int k = 0; k < 8; ++k) in[k] = bf16_bits_to_f32((k & 1) ? (x[k >> 1] >> 16) : (x[k >> 1] & 0xffffu));
           }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) m = fmaxf(m, __builtin_fabsf(in[k]));
+          if (amax_only) continue;
           float y[8];
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             float v = in[k];
             if (relu_sq) {
-              const float m = fmaxf(v, 0.0f);
-              v = m * m;
+              const float r = fmaxf(v, 0.0f);
+              v = r * r;
             }
             y[k] = __fdiv_rn(v, sc);
           }
@@ -380,6 +389,18 @@ __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t r
         }
         tile[lr * TW + lc / 4] = lo;
         tile[lr * TW + lc / 4 + 1] = hi;
+      }
+      if (tile_amax) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if ((tid & 63) == 0) wave_max[tid >> 6] = m;
+        __syncthreads();
+        if (tid == 0 && r0 < rows)
+          tile_amax[t] = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+      }
+      if (amax_only) {
+        __syncthreads();
+        continue;
       }
     }
     __syncthreads();
@@ -418,16 +439,61 @@ hipError_t run_quantize_fp8_2d(DType src_t, const void* src, int64_t rows, int64
   uint8_t* dt = reinterpret_cast<uint8_t*>(dst_t);
   if (src_t == DT_E4M3)
     hipLaunchKernelGGL(quant2d_kernel<0>, dim3(grid), dim3(256), 0, s, src, rows, cols, ld_src, 0, 0, scale,
-                       d, dt, ld_t, n_ct, n_tiles);
+                       d, dt, ld_t, n_ct, n_tiles, nullptr, 0);
   else if (src_t == DT_BF16)
     hipLaunchKernelGGL(quant2d_kernel<1>, dim3(grid), dim3(256), 0, s, src, rows, cols, ld_src, relu_sq, e5m2,
-                       scale, d, dt, ld_t, n_ct, n_tiles);
+                       scale, d, dt, ld_t, n_ct, n_tiles, nullptr, 0);
   else if (src_t == DT_F32)
     hipLaunchKernelGGL(quant2d_kernel<2>, dim3(grid), dim3(256), 0, s, src, rows, cols, ld_src, relu_sq, e5m2,
-                       scale, d, dt, ld_t, n_ct, n_tiles);
+                       scale, d, dt, ld_t, n_ct, n_tiles, nullptr, 0);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+namespace {
+// *scale = max(max_i tile_amax[i], 1e-12) / 448 in fp32 (the arithmetic of the per-tensor quantizer).
+__global__ __launch_bounds__(kEwThreads) void scale_from_tiles_kernel(const float* tile_amax, int64_t n, float* scale) {
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < n; i += kEwThreads) m = fmaxf(m, tile_amax[i]);
+  m = block_max(m);
+  if (threadIdx.x == 0) *scale = __fdiv_rn(fmaxf(m, 1e-12f), 448.0f);
+}
+}  // namespace
+
+int64_t weight_amax_slots(int64_t rows, int64_t cols) { return ((rows + 127) / 128) * ((cols + 127) / 128); }
+
+hipError_t run_quantize_weight_e4m3(DType src_t, const void* w, int64_t rows, int64_t cols, int exact, float* scale,
+                                    float* tile_amax, void* dst, void* dst_t, int64_t ld_t, hipStream_t s) {
+  if (rows < 1 || cols < 16 || cols % 16 || (src_t != DT_BF16 && src_t != DT_F32) || (dst_t && (ld_t < rows || ld_t % 16)))
+    return hipErrorInvalidValue;
+  const int64_t n_ct = (cols + 127) / 128;
+  const int64_t n_slots = weight_amax_slots(rows, cols);
+  auto q2d = [&](int amax_only, float* rec) {
+    const int64_t cover = (!amax_only && dst_t) ? ld_t : rows;
+    const int64_t n_tiles = n_ct * ((cover + 127) / 128);
+    const int grid = (int)std::min<int64_t>(n_tiles, 8192);
+    uint8_t* d = amax_only ? nullptr : reinterpret_cast<uint8_t*>(dst);
+    uint8_t* dt = amax_only ? nullptr : reinterpret_cast<uint8_t*>(dst_t);
+    if (src_t == DT_BF16)
+      hipLaunchKernelGGL(quant2d_kernel<1>, dim3(grid), dim3(256), 0, s, w, rows, cols, cols, 0, 0, scale, d, dt,
+                         ld_t, n_ct, n_tiles, rec, amax_only);
+    else
+      hipLaunchKernelGGL(quant2d_kernel<2>, dim3(grid), dim3(256), 0, s, w, rows, cols, cols, 0, 0, scale, d, dt,
+                         ld_t, n_ct, n_tiles, rec, amax_only);
+    return hipGetLastError();
+  };
+  hipError_t e;
+  if (exact) {   // this call's amax, then its scale, then the codes
+    if ((e = q2d(1, tile_amax)) != hipSuccess) return e;
+    hipLaunchKernelGGL(scale_from_tiles_kernel, dim3(1), dim3(kEwThreads), 0, s, tile_amax, n_slots, scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return q2d(0, nullptr);
+  }
+  // the previous call's recorded amax gives the scale; the codes pass records this call's amax
+  hipLaunchKernelGGL(scale_from_tiles_kernel, dim3(1), dim3(kEwThreads), 0, s, tile_amax, n_slots, scale);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return q2d(0, tile_amax);
 }
 
 hipError_t run_splitk_reduce(DType io, const float* partial, int splits, int M, int N, void* C0,

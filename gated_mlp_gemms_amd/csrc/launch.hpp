@@ -69,4 +69,12 @@ hipError_t run_quantize_fp8_2d(DType src_t, const void* src, int64_t rows, int64
                                int relu_sq, int e5m2, const float* scale, void* dst, void* dst_t,
                                int64_t ld_t, hipStream_t s);
 
+// The fp8 weight-cache quantizer (row-major codes into dst, transposed into dst_t; either may be
+// NULL): exact = 1 forms *scale from w's own amax (an amax pass first), exact = 0 from the per-tile
+// amax the previous call recorded in tile_amax (weight_amax_slots(rows, cols) floats); both record
+// w's per-tile amax there. src_t: DT_BF16 or DT_F32; cols a multiple of 16.
+int64_t weight_amax_slots(int64_t rows, int64_t cols);
+hipError_t run_quantize_weight_e4m3(DType src_t, const void* w, int64_t rows, int64_t cols, int exact, float* scale,
+                                    float* tile_amax, void* dst, void* dst_t, int64_t ld_t, hipStream_t s);
+
 }  // namespace gmlp

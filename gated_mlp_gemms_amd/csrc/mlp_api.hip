@@ -957,6 +957,31 @@ mlp_status mlp_quantize_fp8(const void* src, int dtype, int64_t rows, int64_t co
                     "quantize fp8");
 }
 
+int64_t mlp_weight_amax_slots(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 1) return 0;
+  return weight_amax_slots(rows, cols);
+}
+
+mlp_status mlp_quantize_weight_e4m3(const void* w, int dtype, int64_t rows, int64_t cols, int exact, float* scale,
+                                    float* tile_amax, void* dst, void* dst_t, int64_t ld_t, void* stream) {
+  if (dtype != MLP_BF16 && dtype != MLP_F32) return fail(MLP_ERR_UNSUPPORTED, "weights must be bf16 or f32");
+  if (exact != 0 && exact != 1) return fail(MLP_ERR_INVALID_ARG, "exact must be 0 or 1");
+  if (rows < 1 || cols < 1 || rows >= ((int64_t)1 << 31) || cols >= ((int64_t)1 << 31))
+    return fail(MLP_ERR_INVALID_ARG, "rows and cols must be in [1, 2^31)");
+  if (cols % 16) return fail(MLP_ERR_ALIGNMENT, "cols must be a multiple of 16");
+  if (!dst && !dst_t) return fail(MLP_ERR_INVALID_ARG, "dst and dst_t are both NULL");
+  if (dst_t && (ld_t < rows || ld_t % 16)) return fail(MLP_ERR_INVALID_ARG, "ld_t must be >= rows and a multiple of 16");
+  MLP_TRY(need_ptr(w, "w"));
+  MLP_TRY(need_ptr(scale, "scale", false));
+  MLP_TRY(need_ptr(tile_amax, "tile_amax", false));
+  if (dst) MLP_TRY(need_ptr(dst, "dst"));
+  if (dst_t) MLP_TRY(need_ptr(dst_t, "dst_t"));
+  return hip_status(run_quantize_weight_e4m3(dtype == MLP_BF16 ? DT_BF16 : DT_F32, w, rows, cols, exact, scale,
+                                             tile_amax, dst, dst_t, dst_t ? ld_t : 0,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                    "quantize weight");
+}
+
 float mlp_fp8_next_scale(float amax, float prev_scale, float gain, float floor_) {
   float a = (isnan(amax) || isinf(amax)) ? 0.0f : amax;
   if (a > 1e12f) a = 1e12f;

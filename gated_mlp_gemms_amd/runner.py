@@ -10,7 +10,8 @@ from __future__ import annotations
 import torch
 
 from . import (GATED_ACTS, make_desc, make_fp8, mlp_bwd, mlp_fp8_next_scale, mlp_fwd, mlp_fwd_infer,
-               mlp_quantize_e4m3, mlp_quantize_fp8, mlp_quantize_workspace_bytes, workspace_bytes)
+               mlp_quantize_e4m3, mlp_quantize_weight_e4m3, mlp_quantize_workspace_bytes, mlp_weight_amax_slots,
+               workspace_bytes)
 
 E4M3_MAX = 448.0
 E5M2_MAX = 57344.0
@@ -19,6 +20,7 @@ POST_FLOOR = 1e-6
 GRAD_SCALE = 2.0 ** -6  # static e5m2 scale of dout; also the bootstrap dpre scale
 DPRE_HEADROOM = 1.25    # delayed dpre scale = amax * 1.25 / 57344, floor 1e-12
 DPRE_FLOOR = 1e-12
+EXACT_SCALE_CALLS = 16  # weight scales are exact for this many quantize() calls, then one call delayed
 
 
 class MlpRunner:
@@ -72,6 +74,10 @@ class MlpRunner:
             self.scales[5] = GRAD_SCALE
             self.scales[6] = GRAD_SCALE       # bootstrap dpre scale
             self.ws_q = torch.empty(mlp_quantize_workspace_bytes(), dtype=torch.uint8, device=dev)
+            # per-tile amax each weight quantize records for the next call's delayed scale
+            self.w1_amax = torch.zeros(mlp_weight_amax_slots(hidden, d_in), dtype=torch.float32, device=dev)
+            self.w2_amax = torch.zeros(mlp_weight_amax_slots(d_out, hidden), dtype=torch.float32, device=dev)
+            self.quantize_calls = 0
             s = self.scales
             sp = [s[i:i + 1].data_ptr() for i in range(8)]
             extra = {}
@@ -83,14 +89,17 @@ class MlpRunner:
 
     # ---- steps
     def quantize(self):
-        """Per-tensor e4m3 of x, W1, W2 (exact scales)."""
+        """Per-tensor e4m3 of x (exact scale every call) and of the weight caches W1, W2 (row-major,
+        plus the transposed copies with fp8_bwd): exact scales for the first EXACT_SCALE_CALLS
+        calls, then the scale of the amax the previous call recorded."""
         s = self.scales
+        exact = self.quantize_calls < EXACT_SCALE_CALLS
+        self.quantize_calls += 1
         mlp_quantize_e4m3(self.x, self.x_q, s[0:1], self.ws_q)
-        mlp_quantize_e4m3(self.w_gate, self.w1_q, s[1:2], self.ws_q)
-        mlp_quantize_e4m3(self.w_down, self.w2_q, s[2:3], self.ws_q)
-        if self.fp8_bwd:
-            mlp_quantize_fp8(self.w_gate, "e4m3", s[1:2], dst_t=self.w1t_q, ld_t=self.w_gate.shape[0])
-            mlp_quantize_fp8(self.w_down, "e4m3", s[2:3], dst_t=self.w2t_q, ld_t=self.w_down.shape[0])
+        mlp_quantize_weight_e4m3(self.w_gate, exact, s[1:2], self.w1_amax, dst=self.w1_q,
+                                 dst_t=self.w1t_q if self.fp8_bwd else None, ld_t=self.w_gate.shape[0])
+        mlp_quantize_weight_e4m3(self.w_down, exact, s[2:3], self.w2_amax, dst=self.w2_q,
+                                 dst_t=self.w2t_q if self.fp8_bwd else None, ld_t=self.w_down.shape[0])
 
     def refresh_dpre_scale(self):
         """Host side of the delayed dpre scale: next = max(amax * 1.25/57344, 1e-12), kept when

@@ -233,6 +233,25 @@ mlp_status mlp_quantize_fp8(const void* src, int dtype, int64_t rows, int64_t co
                             const float* scale, void* dst, void* dst_t, int64_t ld_t, void* stream);
 
 /*
+ * The fp8 weight-cache quantizer (modded-nanogpt gpt.py: _quantize_mlp_weights_and_scales with
+ * FP8_EXACT_SCALE_CALLS, and the per-tile amax buffers of init_mlp_fp8). w is a [rows, cols]
+ * row-major weight (bf16 or f32, `dtype`); its e4m3 codes go row-major into dst and/or transposed
+ * into dst_t [cols, ld_t] (as mlp_quantize_fp8; either may be NULL, not both), with
+ *   exact = 1: *scale = max(amax|w|, 1e-12) / 448 in fp32 from w itself (an amax pass first);
+ *   exact = 0: *scale = max(max_i tile_amax[i], 1e-12) / 448 from the amax the previous call
+ *              recorded (one call delayed: entries of w beyond 448 * *scale saturate),
+ * and codes = e4m3(w / *scale) (IEEE fp32 division, nearest even, saturating). Either way the call
+ * records w's amax per 128 x 128 tile into tile_amax, mlp_weight_amax_slots(rows, cols) device
+ * floats, for the next call. The page sets the scales exactly for its first 16 calls (pass
+ * exact = 1 for them) and takes the delayed ones afterwards. cols must be a multiple of 16.
+ */
+mlp_status mlp_quantize_weight_e4m3(const void* w, int dtype, int64_t rows, int64_t cols, int exact, float* scale,
+                                    float* tile_amax, void* dst, void* dst_t, int64_t ld_t, void* stream);
+/* Number of per-tile amax slots mlp_quantize_weight_e4m3 keeps for a [rows, cols] weight
+ * (ceil(rows / 128) * ceil(cols / 128)); 0 for empty sizes. Host only. */
+int64_t mlp_weight_amax_slots(int64_t rows, int64_t cols);
+
+/*
  * The delayed-scale rule of modded-nanogpt gpt.py's _refresh_delayed_scale, for one slot, in
  * fp32: a = amax with NaN/inf mapped to 0, clamped above at 1e12; returns max(a * gain, floor)
  * if a > 0, else prev_scale. For relu(pre)^2 the page uses gain = 1.03/448, floor = 1e-6; for

@@ -300,3 +300,22 @@ def test_noalloc_entry_checks_run_before_any_hip_call():
     assert "MLP_NOALLOC_SCRATCH_BYTES" in _err() and str(need) in _err()
     fits = _desc(M=512, d_in=4096, hidden=11008, d_out=4096)
     assert L.mlp_workspace_bytes(C.byref(fits), gm.MLP_PHASE_FWD_INFER) <= gm.MLP_NOALLOC_SCRATCH_BYTES
+
+
+def test_weight_quantizer_checks():
+    """mlp_quantize_weight_e4m3 rejects bad arguments on the host; the slot count is per 128 x 128 tile."""
+    L = gm.lib()
+    assert L.mlp_weight_amax_slots(3072, 768) == 24 * 6
+    assert L.mlp_weight_amax_slots(300, 208) == 3 * 2
+    assert L.mlp_weight_amax_slots(0, 16) == 0
+
+    def q(dtype=gm.MLP_BF16, rows=64, cols=64, exact=1, scale=FAKE, tiles=FAKE, dst=FAKE, dst_t=None, ld_t=0):
+        return L.mlp_quantize_weight_e4m3(FAKE, dtype, rows, cols, exact, scale, tiles, dst, dst_t, ld_t, None)
+
+    assert q(dtype=gm.MLP_F16) == gm._lib.MLP_ERR_UNSUPPORTED
+    assert q(exact=2) == gm._lib.MLP_ERR_INVALID_ARG
+    assert q(cols=40) == gm._lib.MLP_ERR_ALIGNMENT
+    assert q(dst=None) == gm._lib.MLP_ERR_INVALID_ARG
+    assert q(dst_t=FAKE, ld_t=60) == gm._lib.MLP_ERR_INVALID_ARG
+    assert q(tiles=None) == gm._lib.MLP_ERR_INVALID_ARG and "tile_amax" in _err()
+    assert q(scale=None) == gm._lib.MLP_ERR_INVALID_ARG
