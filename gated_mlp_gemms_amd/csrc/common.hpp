@@ -138,6 +138,31 @@ __device__ __forceinline__ uint32_t f32x4_to_fp8(float v0, float v1, float v2, f
   return (uint32_t)w;
 }
 
+// The correctly rounded quotients v[i] / s (what IEEE division gives) from the correctly rounded
+// reciprocal r = RN(1 / s), computed once per scale: y0 = RN(v r) is within an ulp of v / s, the
+// residual e = v - y0 s is exact in one fma, and RN(y0 + e r) is then the correctly rounded
+// quotient (Markstein's theorem; Muller et al., Handbook of Floating-Point Arithmetic, the
+// division-by-fma chapter). Three instructions instead of a full division. The sign is y0's:
+// for v = -0 the correction step would turn the quotient's -0 into +0 (+0 + -0 = +0), which the
+// fp8 encoders keep as a different code. A quotient in the fp32 subnormal range may differ in its
+// last bit, which no fp8 code can see (such values encode to +-0 either way). If any first
+// product of the group is not finite (v infinite or NaN, or v r overflowing), the whole group
+// takes the IEEE division: one branch per group.
+template <int N>
+__device__ __forceinline__ void quot_rn_n(const float (&v)[N], float s, float r, float (&y)[N]) {
+  bool finite = true;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float y0 = v[i] * r;
+    finite &= __builtin_isfinite(y0);
+    y[i] = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-y0, s, v[i]), r, y0), y0);
+  }
+  if (!finite) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) y[i] = __fdiv_rn(v[i], s);
+  }
+}
+
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   const uint32_t s = c & 0x80u, e = (c >> 3) & 0xfu, m = c & 7u;
   float mag;

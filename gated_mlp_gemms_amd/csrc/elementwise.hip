@@ -271,14 +271,17 @@ template <typename T>
 __global__ __launch_bounds__(kEwThreads) void quantize8_kernel(const void* src, int64_t n, uint8_t* dst,
                                                                const float* amax, float* scale_out) {
   const float s = __fdiv_rn(fmaxf(*amax, 1e-12f), 448.0f);
+  const float rs = __fdiv_rn(1.0f, s);
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
   const char* base = reinterpret_cast<const char*>(src);
   const int64_t n8 = n / 8;
   for (int64_t j = blockIdx.x * (int64_t)kEwThreads + threadIdx.x; j < n8; j += (int64_t)gridDim.x * kEwThreads) {
     float v[8];
     load8<T>(base + j * 8 * esize<T>(), v);
+    float y[8];
+    quot_rn_n<8>(v, s, rs, y);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) v[r] = __fdiv_rn(v[r], s);
+    for (int r = 0; r < 8; ++r) v[r] = y[r];
     *reinterpret_cast<u32x2*>(dst + j * 8) =
         u32x2{f32x4_to_fp8<false>(v[0], v[1], v[2], v[3]), f32x4_to_fp8<false>(v[4], v[5], v[6], v[7])};
   }
@@ -334,6 +337,7 @@ __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t r
   const int tid = threadIdx.x;
   constexpr bool CODES = SRC == 0;
   const float sc = (CODES || amax_only) ? 1.0f : *scale;
+  const float rsc = __fdiv_rn(1.0f, sc);
   for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
     const int64_t r0 = (t / n_ct) * 128, c0 = (t % n_ct) * 128;
     if constexpr (CODES) {   // 8 lanes x 16 codes per row, 32 rows per pass
@@ -369,15 +373,14 @@ __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t r
           for (int k = 0; k < 8; ++k) m = fmaxf(m, __builtin_fabsf(in[k]));
           if (amax_only) continue;
           float y[8];
+          if (relu_sq) {
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            float v = in[k];
-            if (relu_sq) {
-              const float r = fmaxf(v, 0.0f);
-              v = r * r;
+            for (int k = 0; k < 8; ++k) {
+              const float r = fmaxf(in[k], 0.0f);
+              in[k] = r * r;
             }
-            y[k] = __fdiv_rn(v, sc);
           }
+          quot_rn_n<8>(in, sc, rsc, y);
           if (e5m2) {
             lo = f32x4_to_fp8<true>(y[0], y[1], y[2], y[3]);
             hi = f32x4_to_fp8<true>(y[4], y[5], y[6], y[7]);

@@ -137,14 +137,15 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
   } else if constexpr (EPI == EPI_F8ACT) {
     if (p.flags & 1) Vec8<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), v);
     const float sp = *p.s_post;
-    float y[8];
+    const float rp = __fdiv_rn(1.0f, sp);
+    float post[8], y[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const float t = fmaxf(v[r], 0.0f);
-      const float post = t * t;
-      local_amax = fmaxf(local_amax, post);
-      y[r] = __fdiv_rn(post, sp);
+      post[r] = t * t;
+      local_amax = fmaxf(local_amax, post[r]);
     }
+    quot_rn_n<8>(post, sp, rp, y);
     *reinterpret_cast<u32x2*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) =
         u32x2{f32x4_to_fp8<false>(y[0], y[1], y[2], y[3]), f32x4_to_fp8<false>(y[4], y[5], y[6], y[7])};
   } else if constexpr (EPI == EPI_F8DACT) {
@@ -156,13 +157,14 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
       unpack16x8<IoT>(x.a, pre);
     }
     const float sd = *p.s_post;
-    float y[8];
+    const float rd = __fdiv_rn(1.0f, sd);
+    float dpre[8], y[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const float dpre = v[r] * (2.0f * fmaxf(pre[r], 0.0f));
-      local_amax = fmaxf(local_amax, __builtin_fabsf(dpre));
-      y[r] = __fdiv_rn(dpre, sd);
+      dpre[r] = v[r] * (2.0f * fmaxf(pre[r], 0.0f));
+      local_amax = fmaxf(local_amax, __builtin_fabsf(dpre[r]));
     }
+    quot_rn_n<8>(dpre, sd, rd, y);
     *reinterpret_cast<u32x2*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) =
         u32x2{f32x4_to_fp8<true>(y[0], y[1], y[2], y[3]), f32x4_to_fp8<true>(y[4], y[5], y[6], y[7])};
   }

@@ -3,6 +3,7 @@
     python -m gated_mlp_gemms_amd.profile_summary trace  <kernel-trace dir> <out.txt>  --command "..."
     python -m gated_mlp_gemms_amd.profile_summary traffic <fetch dir> <write dir> <out.json> --command "..."
     python -m gated_mlp_gemms_amd.profile_summary mfma <pmc dir> <out.json> --command "..."
+    python -m gated_mlp_gemms_amd.profile_summary counters <pmc dir> <out.json> --command "..."
 
 The trace summary lists every kernel's dispatch count and average / total duration from the
 `*_kernel_stats.csv` rocprofv3 writes with `--kernel-trace --stats --output-format csv`, then the
@@ -97,7 +98,7 @@ def short_name(name: str) -> str:
         w = f",{waves}w" if waves else ""
         return f"gemm{'' if dma else '_regstaged'}<{t},{lay},{bm}x{bn}{w},{epin}{',' + out + ' out' if out else ''}>"
     for k in ("splitk_reduce", "gated_reduce", "gated_act", "plain_act", "absmax8_part", "absmax", "max_parts",
-              "quantize8", "quantize_kernel", "quant2d", "dequant8", "dequant", "zero_f32"):
+              "quantize8", "quantize_kernel", "quant2d", "dequant8", "dequant", "zero_f32", "scale_from_tiles"):
         if k in name:
             return k
     return name.split("(")[0][:60]
@@ -195,7 +196,7 @@ def _stage_bytes(disp, factor, stages, first_step=0, steps=0):
 
 
 def summarize_traffic(fetch_dir: str, write_dir: str, out_json: str, command: str, copy_mib: int,
-                      first_step: int = 0, steps: int = 0) -> None:
+                      first_step: int = 0, steps: int = 0, stages: list[str] = STAGE_ORDER_GATED) -> None:
     fetch, write = _dispatches(fetch_dir, "FETCH_SIZE"), _dispatches(write_dir, "WRITE_SIZE")
     copy_bytes = copy_mib * 1024 * 1024
     fc = [v for _, n, v in fetch if "copyBuffer" in n]
@@ -204,12 +205,13 @@ def summarize_traffic(fetch_dir: str, write_dir: str, out_json: str, command: st
         raise SystemExit("the profiled command ran no device copy (use bench.py --copy-probe-mib)")
     f_factor = copy_bytes / (fc[0] * 1024.0)
     w_factor = copy_bytes / (wc[0] * 1024.0)
-    fb = _stage_bytes(fetch, f_factor, STAGE_ORDER_GATED, first_step, steps)
-    wb = _stage_bytes(write, w_factor, STAGE_ORDER_GATED, first_step, steps)
+    fb = _stage_bytes(fetch, f_factor, stages, first_step, steps)
+    wb = _stage_bytes(write, w_factor, stages, first_step, steps)
     res = {"command": command, "kernel_sources_sha256": kernel_sources_sha256(),
            "copy_probe_bytes": copy_bytes, "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+           "note": "FETCH_SIZE counts L2 misses (last-level-cache hits included), so fetch_bytes is L2-miss traffic",
            "stages": {st: {"fetch_bytes": round(fb.get(st, 0.0)), "write_bytes": round(wb.get(st, 0.0)),
-                           "traffic_bytes": round(fb.get(st, 0.0) + wb.get(st, 0.0))} for st in STAGE_ORDER_GATED}}
+                           "traffic_bytes": round(fb.get(st, 0.0) + wb.get(st, 0.0))} for st in stages}}
     json.dump(res, open(out_json, "w"), indent=1)
     print(json.dumps(res, indent=1))
 
@@ -222,7 +224,8 @@ def _gpu_agent(pmc_dir: str) -> dict:
     raise SystemExit("no GPU agent in the agent info")
 
 
-def summarize_mfma(pmc_dir: str, out_json: str, command: str, first_step: int = 0, steps: int = 0) -> None:
+def summarize_mfma(pmc_dir: str, out_json: str, command: str, first_step: int = 0, steps: int = 0,
+                   stage_order: list[str] = STAGE_ORDER_GATED) -> None:
     """MFMA busy fraction and shader clock per stage from one `--pmc SQ_VALU_MFMA_BUSY_CYCLES
     GRBM_GUI_ACTIVE` pass. SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of every SIMD and
     GRBM_GUI_ACTIVE the active cycles of every XCD, so busy / (GUI / XCDs * SIMDs) is the
@@ -237,10 +240,10 @@ def summarize_mfma(pmc_dir: str, out_json: str, command: str, first_step: int = 
         d[r["Counter_Name"]] = float(r["Counter_Value"])
     disp = sorted((i, d["name"], (d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), d.get("GRBM_GUI_ACTIVE", 0.0), d["ns"]))
                   for i, d in per.items())
-    steps_all = _per_step(disp, STAGE_ORDER_GATED)
+    steps_all = _per_step(disp, stage_order)
     timed = steps_all[first_step:first_step + steps] if steps else steps_all[first_step:]
     stages = {}
-    for st in STAGE_ORDER_GATED:
+    for st in stage_order:
         busy = sum(v[0] for s in timed for _, v in s[st])
         gui = sum(v[1] for s in timed for _, v in s[st])
         ns = sum(v[2] for s in timed for _, v in s[st])
@@ -251,6 +254,37 @@ def summarize_mfma(pmc_dir: str, out_json: str, command: str, first_step: int = 
                       "mfma_busy": round(busy / (cyc * n_simd), 4)}
     res = {"command": command, "kernel_sources_sha256": kernel_sources_sha256(), "steps": len(timed),
            "xcc": n_xcc, "simds": n_simd, "stages": stages}
+    json.dump(res, open(out_json, "w"), indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def summarize_counters(pmc_dir: str, out_json: str, command: str, first_step: int = 0, steps: int = 0,
+                       stage_order: list[str] = STAGE_ORDER_GATED) -> None:
+    """Per-stage averages (per timed step) of every counter one `--pmc` pass collected, plus the
+    ratios a reader usually wants from them (L2 hit rate from TCC_HIT_sum / TCC_MISS_sum, LDS bank
+    conflict cycles per LDS-active cycle from SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE)."""
+    path = _one(os.path.join(pmc_dir, "**", "*counter_collection.csv"))
+    per, names = {}, []
+    for r in csv.DictReader(open(path)):
+        d = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        if r["Counter_Name"] not in names:
+            names.append(r["Counter_Name"])
+    disp = sorted((i, d["name"], d) for i, d in per.items())
+    steps_all = _per_step(disp, stage_order)
+    timed = steps_all[first_step:first_step + steps] if steps else steps_all[first_step:]
+    stages = {}
+    for st in stage_order:
+        if not timed:
+            break
+        tot = {c: sum(v.get(c, 0.0) for s in timed for _, v in s[st]) / len(timed) for c in names}
+        if "TCC_HIT_sum" in tot and "TCC_MISS_sum" in tot and tot["TCC_HIT_sum"] + tot["TCC_MISS_sum"] > 0:
+            tot["l2_hit_rate"] = round(tot["TCC_HIT_sum"] / (tot["TCC_HIT_sum"] + tot["TCC_MISS_sum"]), 4)
+        if tot.get("SQ_LDS_IDX_ACTIVE", 0) > 0 and "SQ_LDS_BANK_CONFLICT" in tot:
+            tot["lds_bank_conflict_per_active"] = round(tot["SQ_LDS_BANK_CONFLICT"] / tot["SQ_LDS_IDX_ACTIVE"], 5)
+        stages[st] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in tot.items()}
+    res = {"command": command, "kernel_sources_sha256": kernel_sources_sha256(), "steps": len(timed),
+           "counters": names, "stages": stages}
     json.dump(res, open(out_json, "w"), indent=1)
     print(json.dumps(res, indent=1))
 
@@ -273,20 +307,31 @@ def main(argv=None):
     f.add_argument("--copy-mib", type=int, default=256)
     f.add_argument("--first-step", type=int, default=0)
     f.add_argument("--steps", type=int, default=0)
+    f.add_argument("--recompute", action="store_true")
     m = sub.add_parser("mfma")
     m.add_argument("pmc_dir")
     m.add_argument("out_json")
     m.add_argument("--command", required=True)
     m.add_argument("--first-step", type=int, default=0)
     m.add_argument("--steps", type=int, default=0)
+    m.add_argument("--recompute", action="store_true")
+    c = sub.add_parser("counters")
+    c.add_argument("pmc_dir")
+    c.add_argument("out_json")
+    c.add_argument("--command", required=True)
+    c.add_argument("--first-step", type=int, default=0)
+    c.add_argument("--steps", type=int, default=0)
+    c.add_argument("--recompute", action="store_true")
     a = ap.parse_args(argv)
+    order = STAGE_ORDER_RECOMPUTE if a.recompute else STAGE_ORDER_GATED
     if a.what == "trace":
-        summarize_trace(a.trace_dir, a.out_txt, a.command, a.first_step, a.steps,
-                        STAGE_ORDER_RECOMPUTE if a.recompute else STAGE_ORDER_GATED)
+        summarize_trace(a.trace_dir, a.out_txt, a.command, a.first_step, a.steps, order)
     elif a.what == "mfma":
-        summarize_mfma(a.pmc_dir, a.out_json, a.command, a.first_step, a.steps)
+        summarize_mfma(a.pmc_dir, a.out_json, a.command, a.first_step, a.steps, order)
+    elif a.what == "counters":
+        summarize_counters(a.pmc_dir, a.out_json, a.command, a.first_step, a.steps, order)
     else:
-        summarize_traffic(a.fetch_dir, a.write_dir, a.out_json, a.command, a.copy_mib, a.first_step, a.steps)
+        summarize_traffic(a.fetch_dir, a.write_dir, a.out_json, a.command, a.copy_mib, a.first_step, a.steps, order)
 
 
 if __name__ == "__main__":

@@ -46,3 +46,67 @@ def test_weight_quantizer_calls_bit_exact(rows, cols):
         saturated += int(np.sum((codes & 0x7F) == 0x7E))
     # the sequence does exercise the delayed scale's saturation (call 16 and 17 at 2x)
     assert saturated > 0
+
+
+def _midpoints(grid):
+    g = np.unique(np.abs(grid[np.isfinite(grid)]))
+    return (g[:-1] + g[1:]) / 2.0
+
+
+@pytest.mark.parametrize("amax_frac", [0.731, 0.9999, 0.37, 1.0])
+def test_per_tensor_quantizer_at_rounding_midpoints(amax_frac):
+    """Quotients v / scale placed at and within a few fp32 ulps of every e4m3 rounding midpoint (and
+    at the saturation edge): the GPU codes equal the oracle's, whose quotient is one IEEE fp32
+    division."""
+    announce(f"e4m3 quantizer at rounding midpoints, amax {amax_frac} * 448")
+    amax = np.float32(448.0 * amax_frac)
+    s = np.float32(max(amax, np.float32(1e-12)) / np.float32(448.0))
+    mids = _midpoints(oracle.e4m3_grid())
+    base = (mids.astype(np.float64) * np.float64(s)).astype(np.float32)
+    vals = [base]
+    for k in range(1, 5):
+        up, dn = base.copy(), base.copy()
+        for _ in range(k):
+            up = np.nextafter(up, np.float32(np.inf))
+            dn = np.nextafter(dn, np.float32(0))
+        vals += [up, dn]
+    v = np.concatenate(vals)
+    v = np.concatenate([v, -v, [amax, -amax * np.float32(0.999)]]).astype(np.float32)
+    v = v[np.abs(v) <= amax]
+    pad = (-len(v)) % 8
+    v = np.concatenate([v, np.zeros(pad, np.float32)])
+    src = torch.from_numpy(v).cuda()
+    dst = torch.empty(len(v), dtype=torch.uint8, device="cuda")
+    sc = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(int(gm.mlp_quantize_workspace_bytes()), dtype=torch.uint8, device="cuda")
+    gm.mlp_quantize_e4m3(src, dst, sc, ws)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_per_tensor(v)
+    assert np.float32(sc.item()) == s_ref
+    np.testing.assert_array_equal(dst.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("relu_sq", [False, True])
+def test_2d_quantizer_every_bf16_value(fmt, relu_sq):
+    """Every finite bf16 value, quantized with three scales (one a power of two): the codes equal
+    the oracle's encoder of the fp32 quotient."""
+    announce(f"2-D quantizer over all finite bf16 values, {fmt}, relu_sq={relu_sq}")
+    bits = np.arange(65536, dtype=np.uint32)
+    f = (bits << 16).view(np.float32)
+    f = f[np.isfinite(f)]
+    f = f[: len(f) // 16 * 16].reshape(-1, 16)
+    src = torch.from_numpy(f).to(torch.bfloat16)
+    assert torch.equal(src.to(torch.float32), torch.from_numpy(f))
+    for scale in (np.float32(0.37), np.float32(2.0 ** -5), np.float32(3.3e-3)):
+        sc = torch.tensor([scale], dtype=torch.float32, device="cuda")
+        dst = torch.empty(f.shape, dtype=torch.uint8, device="cuda")
+        gm.mlp_quantize_fp8(src.cuda(), fmt, sc, dst=dst, relu_sq=relu_sq)
+        torch.cuda.synchronize()
+        x = f
+        if relu_sq:
+            m = np.maximum(x, np.float32(0.0))
+            x = m * m
+        y = x / scale
+        ref = oracle.e5m2_encode(y) if fmt == "e5m2" else oracle.e4m3_encode(y)
+        np.testing.assert_array_equal(dst.cpu().numpy(), ref, err_msg=f"scale {scale}")
