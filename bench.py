@@ -105,6 +105,8 @@ def stage_flops(w) -> dict:
         "up": 2.0 * M * D * P, "down": 2.0 * M * H * O, "dact": 2.0 * M * O * H,
         "dw_down": 2.0 * O * H * M, "dx": 2.0 * M * P * D, "dw_up": 2.0 * P * D * M,
         "recompute": 2.0 * M * D * P,
+        # dx, dW_gate/dW_up and dW_down as one launch
+        "bwd_gemms": 2.0 * M * P * D + 2.0 * P * D * M + 2.0 * O * H * M,
     }
 
 
@@ -289,7 +291,9 @@ def main():
     torch.cuda.synchronize()
 
     ev = HipEvents()
-    stages = ["up", "down", "dact", "dw_down", "dx", "dw_up"] + (["recompute"] if w.recompute else [])
+    # the library runs dx and the weight gradients as one launch when its planner prefers that
+    bwd = ["bwd_gemms"] if gm.mlp_bwd_grouped(r.desc) else ["dw_down", "dx", "dw_up"]
+    stages = ["up", "down", "dact"] + bwd + (["recompute"] if w.recompute else [])
     stage_id = {n: gm._lib.STAGES.index(n) for n in stages}
 
     def run_steps(hooked):

@@ -151,5 +151,12 @@ def mlp_quantize_weight_e4m3(w, exact, scale, tile_amax, dst=None, dst_t=None, l
     check(st, "mlp_quantize_weight_e4m3")
 
 
+def mlp_bwd_grouped(desc: MlpDesc) -> bool:
+    """Whether mlp_bwd runs dx, dW_gate/dW_up and dW_down as one launch for this problem."""
+    out = C.c_int(0)
+    check(lib().mlp_bwd_grouped(C.byref(desc), C.byref(out)), "mlp_bwd_grouped")
+    return bool(out.value)
+
+
 def mlp_fp8_next_scale(amax: float, prev_scale: float, gain: float, floor: float) -> float:
     return float(lib().mlp_fp8_next_scale(amax, prev_scale, gain, floor))

@@ -15,7 +15,7 @@ MLP_GATE_OUTSIDE, MLP_GATE_INSIDE = 0, 1
 MLP_PHASE_FWD, MLP_PHASE_FWD_INFER, MLP_PHASE_BWD = 0, 1, 2
 MLP_FP8_E4M3, MLP_FP8_E5M2 = 0, 1
 MLP_NOALLOC_SCRATCH_BYTES = 64 << 20
-STAGES = ("up", "down", "recompute", "dact", "dw_down", "dx", "dw_up", "act", "widen")
+STAGES = ("up", "down", "recompute", "dact", "dw_down", "dx", "dw_up", "act", "widen", "bwd_gemms")
 
 
 class MlpDesc(C.Structure):
@@ -54,6 +54,7 @@ _SIGNATURES = {
     "mlp_last_error": (C.c_char_p, []),
     "mlp_abi_version": (C.c_int, []),
     "mlp_time_stage_once": (C.c_int, [C.c_int, _P, _P]),
+    "mlp_bwd_grouped": (C.c_int, [C.POINTER(MlpDesc), C.POINTER(C.c_int)]),
 }
 
 _lib = None

@@ -44,4 +44,16 @@ struct GemmArgs {
   int tiles_m, tiles_n, group_m;
 };
 
+// Up to kGroupMax independent GEMMs run by one launch (gemm_dma_group_kernel): member j covers
+// workgroups [begin[j], begin[j+1]) (multiples of 8 apart), has items[j] tiles (one per
+// workgroup, no split) and takes tile body kind[j] (0 or 1) of the kernel's two.
+constexpr int kGroupMax = 3;
+struct GemmGroup {
+  GemmArgs g[kGroupMax];
+  int begin[kGroupMax + 1];
+  int items[kGroupMax];
+  int kind[kGroupMax];
+  int count;
+};
+
 }  // namespace gmlp

@@ -347,11 +347,20 @@ constexpr int ring_stages(int stage_bytes, int tile_elems) {
   return n > 4 ? 4 : n;
 }
 
+// LDS of one workgroup's ring (NS stages of a BM x BN tile's K-step).
+template <typename T, int BM, int BN>
+constexpr int dma_ring_bytes() {
+  constexpr int stage = (BM + BN) * StepGeo<T>::ROWB;
+  return ring_stages(stage, BM * BN) * stage;
+}
+
+// One output tile of a GEMM: tile `item` of p's grid (tiles_m x tiles_n x splits, the split
+// index major), with `smem` the workgroup's LDS ring of dma_ring_bytes<T, BM, BN>() bytes.
 // WAVES = 4: 2 x 2 waves, one per SIMD (wave tile up to 128 x 128, 256 accumulator registers).
 // WAVES = 8: 4 x 2 waves, two per SIMD, so one wave's MFMAs fill the other's stalls (wave tile
 // 64 x 128, 128 accumulator registers, half the register file each).
 template <typename T, typename IoT, int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs p) {
+__device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* smem) {
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must split into 2x2 waves of 32x32 blocks");
   static_assert((A_KMAJ && B_KMAJ) || ElemTraits<T>::bytes == 2, "MN-major operands are 16-bit only");
   constexpr int ES = ElemTraits<T>::bytes;
@@ -375,12 +384,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
   static_assert(NSUB % 2 == 0, "fragment double buffer alternates per substep");
   static_assert(A_KMAJ || BK == MNTileDma<BM, WAVES>::KROWS, "MN-major stage depth");
 
-  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+  static_assert(NS * STAGE == dma_ring_bytes<T, BM, BN>(), "ring size");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  int lid = xcd_remap(blockIdx.x, gridDim.x);
+  int lid = item;
   const int tiles = p.tiles_m * p.tiles_n;
   const int split = lid / tiles;
   lid -= split * tiles;
@@ -670,6 +679,39 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
   wait_lgkmcnt0();
   __builtin_amdgcn_s_barrier();
   epilogue_rows<EPI, IoT, BM, BN, MI, NI, WAVES>(p, acc, m0, n0, split, wm, wn, lane, wave, smem);
+}
+
+// One GEMM: a workgroup per tile, placed XCD-aware (xcd_remap).
+template <typename T, typename IoT, int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem[dma_ring_bytes<T, BM, BN>()];
+  gemm_dma_tile<T, IoT, BM, BN, A_KMAJ, B_KMAJ, EPI, WAVES>(p, xcd_remap(blockIdx.x, gridDim.x), smem);
+}
+
+// Several independent GEMMs in one launch (GemmGroup): member j has the workgroups
+// [begin[j], begin[j+1]) and runs the store epilogue with the first tile body (kind 0: layout
+// AK0/BK0, output Io0) or the second (kind 1). Each member's range is a multiple of 8 long, so
+// xcd_remap keeps its tiles XCD-contiguous; workgroups past a member's tile count do nothing.
+// Workgroups are dispatched in index order, so the members listed first start first: listing
+// the members with the longest K first lets the short tiles of the others fill the CUs around
+// them (list scheduling) instead of each GEMM idling part of the chip in its last round.
+template <typename T, int BM, int BN, int WAVES, typename Io0, bool AK0, bool BK0, typename Io1, bool AK1, bool BK1>
+__global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_group_kernel(const GemmGroup g) {
+  __shared__ __attribute__((aligned(1024))) char smem[dma_ring_bytes<T, BM, BN>()];
+  const int b = blockIdx.x;
+  int j = 0;
+  while (j + 1 < g.count && b >= g.begin[j + 1]) ++j;
+  const int item = xcd_remap(b - g.begin[j], g.begin[j + 1] - g.begin[j]);
+  if (item >= g.items[j]) return;
+  if (g.kind[j] == 0) gemm_dma_tile<T, Io0, BM, BN, AK0, BK0, EPI_STORE, WAVES>(g.g[j], item, smem);
+  else gemm_dma_tile<T, Io1, BM, BN, AK1, BK1, EPI_STORE, WAVES>(g.g[j], item, smem);
+}
+
+template <typename T, int BM, int BN, int WAVES, typename Io0, bool AK0, bool BK0, typename Io1, bool AK1, bool BK1>
+hipError_t launch_gemm_dma_group(const GemmGroup& g, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_dma_group_kernel<T, BM, BN, WAVES, Io0, AK0, BK0, Io1, AK1, BK1>), dim3(g.begin[g.count]),
+                     dim3(64 * WAVES), 0, stream, g);
+  return hipGetLastError();
 }
 
 template <typename T, typename IoT, int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int WAVES = 4>

@@ -11,6 +11,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <vector>
 #include <mutex>
 #include <string>
 
@@ -86,6 +87,7 @@ DType io_of(const mlp_desc* d) { return dtype_of(d->dtype); }
 struct Plan {
   TileShape tile;
   int splits, k_per_split, tiles_m, tiles_n, group_m, grid;
+  double est;   // the planner's time model of this plan, seconds
 };
 
 struct TileInfo { TileShape t; int bm, bn, slots; double eff; };
@@ -140,6 +142,7 @@ Plan plan_gemm(DType in, int64_t M, int64_t N, int64_t K, bool allow_split, bool
         best.tiles_n = (int)tn;
         best.group_m = (int)std::min<int64_t>(tm, 8);
         best.grid = (int)ntile;
+        best.est = t;
       }
     }
   }
@@ -232,6 +235,91 @@ Gemms plan_all(const mlp_desc* d) {
   g.dx = plan_gemm(io, M, D, P, true, false);
   g.dw_up = plan_gemm(io, P, D, M, true, false);
   return g;
+}
+
+// ---- the backward's dx and weight gradients in one launch -----------------------------------
+//
+// After the d-activation GEMM, dW_down = dout^T a, dx = dpreact [W_gate; W_up] and
+// [dW_gate; dW_up] = dpreact^T x are independent. Run one after another, each idles part of the
+// chip in its last round (the LLaMA step's dW_gate/dW_up has 1376 tiles = 5.4 rounds of 256) or
+// pays split-K for too few tiles (dx: 128 tiles of 344 K-steps, split 2 plus a reduce). One
+// launch of all three lets the short weight-gradient tiles fill the CUs around the long dx
+// tiles, unsplit: quack's backward runs these GEMMs on a dynamic tile scheduler for the same
+// reason (mlp.py, dynamic_scheduler=True), done here with a static order instead of atomics.
+
+enum BwdGemm : int { BG_DW_DOWN = 0, BG_DX = 1, BG_DW_UP = 2 };
+
+struct BwdGroup {
+  int count = 0;              // 0: separate launches
+  int member[kGroupMax] = {}; // BwdGemm ids, longest K first
+  Plan plan[kGroupMax] = {};  // unsplit 8-wave 256 x 256 plans
+};
+
+struct GemmDims { int64_t M, N, K; };
+
+// M, N, K of BwdGemm `which`.
+GemmDims bwd_dims(const mlp_desc* d, int which) {
+  const int64_t M = d->M, D = d->d_in, H = d->hidden, O = d->d_out, P = is_gated(d->act) ? 2 * H : H;
+  switch (which) {
+    case BG_DW_DOWN: return {O, H, M};
+    case BG_DX: return {M, D, P};
+    default: return {P, D, M};
+  }
+}
+
+// Makespan, in K-steps, of list-scheduling the members' tiles on one XCD (it takes every 8th
+// workgroup of each member, in launch order): each tile goes to the first of the 32 CUs to free
+// up and holds it for its K-steps plus `overhead` (prologue and epilogue).
+double list_makespan(const int64_t* tiles, const int64_t* steps, int count, double overhead) {
+  std::vector<double> cu(32, 0.0);
+  for (int j = 0; j < count; ++j)
+    for (int64_t t = 0, n = (tiles[j] + 7) / 8; t < n; ++t)
+      *std::min_element(cu.begin(), cu.end()) += (double)steps[j] + overhead;
+  return *std::max_element(cu.begin(), cu.end());
+}
+
+// The grouped launch of the products in `mask` (bit BwdGemm), when the time model prefers it to
+// separate launches planned by plan_gemm (split-K allowed); count = 0 otherwise.
+BwdGroup plan_bwd_group(const mlp_desc* d, unsigned mask) {
+  BwdGroup g;
+  const DType io = io_of(d);
+  if (d->fp8_bwd || (io != DT_BF16 && io != DT_F16)) return g;
+  int ids[kGroupMax], n = 0;
+  for (int m : {BG_DX, BG_DW_UP, BG_DW_DOWN})
+    if (mask & (1u << m)) ids[n++] = m;
+  if (n < 2) return g;
+  int64_t tiles[kGroupMax], steps[kGroupMax];
+  Plan plans[kGroupMax];
+  double t_sep = 0.0;
+  for (int j = 0; j < n; ++j) {
+    const GemmDims dm = bwd_dims(d, ids[j]);
+    plans[j] = plan_gemm(io, dm.M, dm.N, dm.K, false, false, TILE_256x256_W8);
+    tiles[j] = plans[j].grid;
+    steps[j] = (dm.K + 63) / 64;
+    t_sep += plan_gemm(io, dm.M, dm.N, dm.K, true, false).est;
+  }
+  // longest K first (stable: dx, then dW_gate/dW_up, then dW_down on ties)
+  int order[kGroupMax] = {0, 1, 2};
+  std::stable_sort(order, order + n, [&](int a, int b) { return steps[a] > steps[b]; });
+  int64_t ot[kGroupMax], os[kGroupMax];
+  for (int j = 0; j < n; ++j) {
+    ot[j] = tiles[order[j]];
+    os[j] = steps[order[j]];
+  }
+  const TileInfo& w8 = kTiles[0];
+  const double t_step = 2.0 * w8.bm * w8.bn * 64 / (w8.eff * 9.83e12);
+  const double t_group = list_makespan(ot, os, n, 1.0) * t_step;
+  if (!(t_group < 0.97 * t_sep)) return g;
+  g.count = n;
+  for (int j = 0; j < n; ++j) {
+    g.member[j] = ids[order[j]];
+    g.plan[j] = plans[order[j]];
+  }
+  return g;
+}
+
+unsigned bwd_mask(const void* dx, const void* dwg, const void* dwd) {
+  return (dwd ? 1u << BG_DW_DOWN : 0u) | (dx ? 1u << BG_DX : 0u) | (dwg ? 1u << BG_DW_UP : 0u);
 }
 
 WsLayout ws_layout(const mlp_desc* d, int phase) {
@@ -369,10 +457,8 @@ mlp_status hip_status(hipError_t e, const char* what) {
   return fail(MLP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// One GEMM, split along K when the plan says so (fp32 partials, then a fixed-order reduce
-// that applies the store epilogue).
-mlp_status gemm(DType in, DType io, Layout lay, int epi, const Plan& p, GemmArgs a, int64_t M,
-                int64_t N, int64_t K, void* partial, hipStream_t s, const char* what) {
+// a with the problem sizes and the tile grid of plan p
+GemmArgs planned(GemmArgs a, const Plan& p, int64_t M, int64_t N, int64_t K) {
   a.M = (int)M;
   a.N = (int)N;
   a.K = (int)K;
@@ -380,6 +466,14 @@ mlp_status gemm(DType in, DType io, Layout lay, int epi, const Plan& p, GemmArgs
   a.tiles_n = p.tiles_n;
   a.group_m = p.group_m;
   a.k_per_split = p.k_per_split;
+  return a;
+}
+
+// One GEMM, split along K when the plan says so (fp32 partials, then a fixed-order reduce
+// that applies the store epilogue).
+mlp_status gemm(DType in, DType io, Layout lay, int epi, const Plan& p, GemmArgs a, int64_t M,
+                int64_t N, int64_t K, void* partial, hipStream_t s, const char* what) {
+  a = planned(a, p, M, N, K);
   if (p.splits > 1) {
     GemmArgs b = a;
     b.partial = reinterpret_cast<float*>(partial);
@@ -699,7 +793,14 @@ mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void*
 
 extern "C" {
 
-int mlp_abi_version(void) { return 3; }
+int mlp_abi_version(void) { return 4; }
+
+mlp_status mlp_bwd_grouped(const mlp_desc* d, int* grouped) {
+  MLP_TRY(check_desc(d));
+  if (!grouped) return fail(MLP_ERR_INVALID_ARG, "grouped must not be NULL");
+  *grouped = plan_bwd_group(d, bwd_mask(d, d, d)).count > 0;
+  return MLP_OK;
+}
 
 const char* mlp_status_string(int st) {
   switch (st) {
@@ -867,47 +968,70 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
                             "activation"));
   }
 
-  if (dwd) {   // dW_down (+)= dm * dout^T a
-    GemmArgs a = base_args(d);
-    a.A = dout;
-    a.lda = O;
-    a.B0 = act;
-    a.ldb = H;
-    a.C0 = dwd;
-    a.ldc0 = H;
-    a.alpha = d->down_mult;
-    a.accumulate = grad_accum;
+  // dW_down (+)= dm * dout^T a
+  GemmArgs a_dwd = base_args(d);
+  a_dwd.A = dout;
+  a_dwd.lda = O;
+  a_dwd.B0 = act;
+  a_dwd.ldb = H;
+  a_dwd.C0 = dwd;
+  a_dwd.ldc0 = H;
+  a_dwd.alpha = d->down_mult;
+  a_dwd.accumulate = grad_accum;
+  // dx = [dg | du] [W_gate; W_up]  (non-gated: dpre W1)
+  GemmArgs a_dx = base_args(d);
+  a_dx.A = dpre;
+  a_dx.lda = P;
+  a_dx.B0 = wg;
+  a_dx.B1 = gated ? wu : nullptr;
+  a_dx.b_split = (int)H;
+  a_dx.ldb = D;
+  a_dx.C0 = dx;
+  a_dx.ldc0 = D;
+  a_dx.alpha_dev0 = sw1;
+  // [dW_gate; dW_up] (+)= [dg | du]^T x  (non-gated: dW1 = dpre^T x)
+  GemmArgs a_dwg = base_args(d);
+  a_dwg.A = dpre;
+  a_dwg.lda = P;
+  a_dwg.B0 = x;
+  a_dwg.ldb = D;
+  a_dwg.C0 = dwg;
+  a_dwg.C1 = gated ? dwu : nullptr;
+  a_dwg.c_split = gated ? (int)H : (int)P;
+  a_dwg.ldc0 = D;
+  a_dwg.accumulate = grad_accum;
+  a_dwg.alpha_dev0 = sx;
+
+  const BwdGroup grp = plan_bwd_group(d, bwd_mask(dx, dwg, dwd));
+  if (grp.count > 0) {
+    const GemmArgs* args[3] = {&a_dwd, &a_dx, &a_dwg};
+    GemmGroup gg{};
+    int at = 0;
+    for (int j = 0; j < grp.count; ++j) {
+      const int m = grp.member[j];
+      const GemmDims dm = bwd_dims(d, m);
+      gg.g[j] = planned(*args[m], grp.plan[j], dm.M, dm.N, dm.K);
+      gg.kind[j] = m == BG_DX ? 0 : 1;
+      gg.items[j] = grp.plan[j].grid;
+      gg.begin[j] = at;
+      at += (grp.plan[j].grid + 7) / 8 * 8;
+    }
+    gg.begin[grp.count] = at;
+    gg.count = grp.count;
+    StageScope st(MLP_STAGE_BWD_GEMMS, s);
+    return hip_status(run_gemm_group16(io, gio, gg, s), "dx and weight gradients (one launch)");
+  }
+  if (dwd) {
     StageScope st(MLP_STAGE_DW_DOWN, s);
-    MLP_TRY(gemm(io, gio, TN, EPI_STORE, G.dw_down, a, O, H, M, partial, s, "dW_down"));
+    MLP_TRY(gemm(io, gio, TN, EPI_STORE, G.dw_down, a_dwd, O, H, M, partial, s, "dW_down"));
   }
-  if (dx) {    // dx = [dg | du] [W_gate; W_up]  (non-gated: dpre W1)
-    GemmArgs a = base_args(d);
-    a.A = dpre;
-    a.lda = P;
-    a.B0 = wg;
-    a.B1 = gated ? wu : nullptr;
-    a.b_split = (int)H;
-    a.ldb = D;
-    a.C0 = dx;
-    a.ldc0 = D;
-    a.alpha_dev0 = sw1;
+  if (dx) {
     StageScope st(MLP_STAGE_DX, s);
-    MLP_TRY(gemm(io, io, NN, EPI_STORE, G.dx, a, M, D, P, partial, s, "dx"));
+    MLP_TRY(gemm(io, io, NN, EPI_STORE, G.dx, a_dx, M, D, P, partial, s, "dx"));
   }
-  if (dwg) {   // [dW_gate; dW_up] (+)= [dg | du]^T x  (non-gated: dW1 = dpre^T x)
-    GemmArgs a = base_args(d);
-    a.A = dpre;
-    a.lda = P;
-    a.B0 = x;
-    a.ldb = D;
-    a.C0 = dwg;
-    a.C1 = gated ? dwu : nullptr;
-    a.c_split = gated ? (int)H : (int)P;
-    a.ldc0 = D;
-    a.accumulate = grad_accum;
-    a.alpha_dev0 = sx;
+  if (dwg) {
     StageScope st(MLP_STAGE_DW_UP, s);
-    MLP_TRY(gemm(io, gio, TN, EPI_STORE, G.dw_up, a, P, D, M, partial, s, "dW_gate/dW_up"));
+    MLP_TRY(gemm(io, gio, TN, EPI_STORE, G.dw_up, a_dwg, P, D, M, partial, s, "dW_gate/dW_up"));
   }
   return MLP_OK;
 }
@@ -983,11 +1107,9 @@ mlp_status mlp_quantize_weight_e4m3(const void* w, int dtype, int64_t rows, int6
 }
 
 float mlp_fp8_next_scale(float amax, float prev_scale, float gain, float floor_) {
-  float a = (isnan(amax) || isinf(amax)) ? 0.0f : amax;
-  if (a > 1e12f) a = 1e12f;
-  float fresh = a * gain;
-  if (fresh < floor_) fresh = floor_;
-  return a > 0.0f ? fresh : prev_scale;
+  // only a finite amax above zero moves the scale, and it counts at most 1e12
+  const float fresh = fminf(amax, 1e12f) * gain;
+  return (isfinite(amax) && amax > 0.0f) ? (fresh < floor_ ? floor_ : fresh) : prev_scale;
 }
 
 }  // extern "C"

@@ -35,6 +35,29 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 STAGE_ORDER_GATED = ["up", "down", "dact", "dw_down", "dx", "dw_up"]
 # the backward with activation recompute re-runs the up projection before the d-activation
 STAGE_ORDER_RECOMPUTE = ["up", "down", "recompute", "dact", "dw_down", "dx", "dw_up"]
+# the backward's dx and weight-gradient products run as one launch (gemm_dma_group_kernel) when
+# the library's planner groups them: one "bwd_gemms" stage in place of the three
+_GROUPED = ("dw_down", "dx", "dw_up")
+GROUP_EPI = 100   # gemm_epilogue's value for the grouped launch (a GEMM that opens a stage)
+
+
+def is_group(name: str) -> bool:
+    return "gemm_dma_group_kernel" in name
+
+
+def grouped_order(stages: list[str], names) -> list[str]:
+    """`stages` with dw_down, dx and dw_up replaced by one bwd_gemms stage when the dispatch
+    names include the grouped launch."""
+    if not any(is_group(n) for n in names):
+        return list(stages)
+    out = []
+    for st in stages:
+        if st in _GROUPED:
+            if "bwd_gemms" not in out:
+                out.append("bwd_gemms")
+        else:
+            out.append(st)
+    return out
 
 
 def kernel_sources_sha256() -> str:
@@ -80,13 +103,22 @@ def is_library_kernel(name: str) -> bool:
 
 
 def gemm_epilogue(name: str):
-    """The epilogue index of one of this library's GEMM kernels (None for other kernels)."""
+    """The epilogue index of one of this library's GEMM kernels (None for other kernels;
+    GROUP_EPI for the grouped backward launch)."""
+    if is_group(name):
+        return GROUP_EPI
     f = _gemm_fields(name)
     return int(f[6]) if f else None
 
 
 def short_name(name: str) -> str:
     """A readable name for the engine's kernels (template arguments spelled out)."""
+    if is_group(name):
+        m = re.search(r"Li(\d+)ELi(\d+)ELi(\d+)E", name) or re.search(r"<[^,]+, (\d+), (\d+), (\d+),", name)
+        bm, bn, w = m.groups() if m else ("?", "?", "?")
+        t = "f16" if ("DF16_" in name or "_Float16" in name or "half" in name) else "bf16"
+        f32 = "EfLb0ELb0E" in name or ", float, false, false>" in name
+        return f"gemm_group<{t},NN+TN,{bm}x{bn},{w}w,STORE{',f32 dW out' if f32 else ''}>"
     f = _gemm_fields(name)
     if f:
         dma, types, bm, bn, ak, bk, epi, waves = f
@@ -120,6 +152,7 @@ def summarize_trace(trace_dir: str, out_txt: str, command: str, first_step: int 
     trace = _one(os.path.join(trace_dir, "**", "*kernel_trace.csv"))
     disp = sorted((int(r["Dispatch_Id"]), r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
                   for r in csv.DictReader(open(trace)))
+    stages = grouped_order(stages, (n for _, n, _ in disp))
     per_step = _per_step(disp, stages)
     timed = per_step[first_step:first_step + steps] if steps else per_step[first_step:]
     lines += ["", f"# per-stage kernel time, average over {len(timed)} timed steps (dispatch order; a split-K "
@@ -203,6 +236,7 @@ def summarize_traffic(fetch_dir: str, write_dir: str, out_json: str, command: st
     wc = [v for _, n, v in write if "copyBuffer" in n]
     if not fc or not wc:
         raise SystemExit("the profiled command ran no device copy (use bench.py --copy-probe-mib)")
+    stages = grouped_order(stages, (n for _, n, _ in fetch))
     f_factor = copy_bytes / (fc[0] * 1024.0)
     w_factor = copy_bytes / (wc[0] * 1024.0)
     fb = _stage_bytes(fetch, f_factor, stages, first_step, steps)
@@ -240,6 +274,7 @@ def summarize_mfma(pmc_dir: str, out_json: str, command: str, first_step: int = 
         d[r["Counter_Name"]] = float(r["Counter_Value"])
     disp = sorted((i, d["name"], (d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), d.get("GRBM_GUI_ACTIVE", 0.0), d["ns"]))
                   for i, d in per.items())
+    stage_order = grouped_order(stage_order, (n for _, n, _ in disp))
     steps_all = _per_step(disp, stage_order)
     timed = steps_all[first_step:first_step + steps] if steps else steps_all[first_step:]
     stages = {}
@@ -271,6 +306,7 @@ def summarize_counters(pmc_dir: str, out_json: str, command: str, first_step: in
         if r["Counter_Name"] not in names:
             names.append(r["Counter_Name"])
     disp = sorted((i, d["name"], d) for i, d in per.items())
+    stage_order = grouped_order(stage_order, (n for _, n, _ in disp))
     steps_all = _per_step(disp, stage_order)
     timed = steps_all[first_step:first_step + steps] if steps else steps_all[first_step:]
     stages = {}

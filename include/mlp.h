@@ -252,11 +252,11 @@ mlp_status mlp_quantize_weight_e4m3(const void* w, int dtype, int64_t rows, int6
 int64_t mlp_weight_amax_slots(int64_t rows, int64_t cols);
 
 /*
- * The delayed-scale rule of modded-nanogpt gpt.py's _refresh_delayed_scale, for one slot, in
- * fp32: a = amax with NaN/inf mapped to 0, clamped above at 1e12; returns max(a * gain, floor)
- * if a > 0, else prev_scale. For relu(pre)^2 the page uses gain = 1.03/448, floor = 1e-6; for
- * dpre (fp8_bwd) gain = 1.25/57344, floor = 1e-12.
- * Host only.
+ * The next delayed scale of one fp8 tensor from the amax its last call recorded, in fp32
+ * (modded-nanogpt gpt.py, the FP8 MLP's delayed scaling): a finite amax above zero gives
+ * max(min(amax, 1e12) * gain, floor); any other amax (zero, negative, NaN, infinite) keeps
+ * prev_scale. For relu(pre)^2 the page uses gain = 1.03/448, floor = 1e-6; for dpre (fp8_bwd)
+ * gain = 1.25/57344, floor = 1e-12. Host only.
  */
 float mlp_fp8_next_scale(float amax, float prev_scale, float gain, float floor_);
 
@@ -269,12 +269,26 @@ float mlp_fp8_next_scale(float amax, float prev_scale, float gain, float floor_)
  *   DW_DOWN   dW2 = dout^T a;   DX  dx = dpreact W1;   DW_UP  dW1 = dpreact^T x
  *   ACT       the activation-only pass of the "only dW2" branch
  *   WIDEN     the e4m3 -> bf16 widening of the e4m3 backward
+ *   BWD_GEMMS DX, DW_UP and DW_DOWN (those asked for) as one launch, in place of their own
+ *             stages, when mlp_bwd_grouped says so
  */
 typedef enum mlp_stage {
   MLP_STAGE_UP = 0, MLP_STAGE_DOWN = 1, MLP_STAGE_RECOMPUTE = 2, MLP_STAGE_DACT = 3,
   MLP_STAGE_DW_DOWN = 4, MLP_STAGE_DX = 5, MLP_STAGE_DW_UP = 6, MLP_STAGE_ACT = 7,
-  MLP_STAGE_WIDEN = 8, MLP_STAGE_COUNT = 9
+  MLP_STAGE_WIDEN = 8, MLP_STAGE_BWD_GEMMS = 9, MLP_STAGE_COUNT = 10
 } mlp_stage;
+
+/*
+ * Schedule of mlp_bwd's products after the d-activation GEMM (quack mlp.py, MLPRecomputeFunc
+ * backward: dx and the two weight gradients, which its backward runs on a dynamic tile
+ * scheduler). *grouped = 1 when a call of mlp_bwd for `desc` that asks for dx, dw_gate (/dw_up)
+ * and dw_down runs them as one launch (stage BWD_GEMMS: the long-K tiles of one product and the
+ * short ones of the others share the CUs, no split-K); 0 when it runs them one after another
+ * (stages DX, DW_UP, DW_DOWN). A call that asks for two of them decides the same way for those
+ * two; a call that asks for one runs it alone. Results do not depend on it beyond the rounding
+ * of split-K sums. Host only. Errors: MLP_ERR_INVALID_ARG for a bad desc or a NULL grouped.
+ */
+mlp_status mlp_bwd_grouped(const mlp_desc* desc, int* grouped);
 
 /*
  * Timing hook (profiling only): the next time the calling thread's mlp_* call runs `stage`,

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib._SIGNATURES), "binding and header disagree"
-    assert L.mlp_abi_version() == 3
+    assert L.mlp_abi_version() == 4
 
 
 def _desc(**kw):
@@ -319,3 +319,25 @@ def test_weight_quantizer_checks():
     assert q(dst_t=FAKE, ld_t=60) == gm._lib.MLP_ERR_INVALID_ARG
     assert q(tiles=None) == gm._lib.MLP_ERR_INVALID_ARG and "tile_amax" in _err()
     assert q(scale=None) == gm._lib.MLP_ERR_INVALID_ARG
+
+
+def test_backward_schedule_query():
+    """mlp_bwd_grouped is host-only planning: one launch for the LLaMA and Falcon-H1 backward
+    products (many short weight-gradient tiles around long dx tiles), separate launches where the
+    weight gradients have few tiles with a very long K (the GPT ReLU^2 shape, whose split-K
+    launches beat any single-pass tile order) or the problem is small, and never for fp32 or the
+    fp8-gradient backward; a NULL out pointer or a bad descriptor is an argument error."""
+    L = gm.lib()
+    assert gm.mlp_bwd_grouped(_desc(M=2048, d_in=4096, hidden=11008, d_out=4096))
+    assert gm.mlp_bwd_grouped(_desc(M=8192, d_in=2048, hidden=4864, d_out=2048, recompute=True))
+    assert gm.mlp_bwd_grouped(_desc(M=2048, d_in=4096, hidden=11008, d_out=4096, dtype="f16"))
+    assert not gm.mlp_bwd_grouped(_desc(M=49152, d_in=768, hidden=3072, d_out=768, act="relu_sq"))
+    assert not gm.mlp_bwd_grouped(_desc(M=16, d_in=4096, hidden=11008, d_out=4096))
+    assert not gm.mlp_bwd_grouped(_desc(M=2048, d_in=4096, hidden=11008, d_out=4096, dtype="f32"))
+    assert not gm.mlp_bwd_grouped(_desc(M=49152, d_in=768, hidden=3072, d_out=768, act="relu_sq",
+                                        fp8_fwd=True, fp8_bwd=True))
+    d = _desc()
+    assert L.mlp_bwd_grouped(C.byref(d), None) == _lib.MLP_ERR_INVALID_ARG
+    bad = _desc(M=0)
+    out = C.c_int(7)
+    assert L.mlp_bwd_grouped(C.byref(bad), C.byref(out)) == _lib.MLP_ERR_INVALID_ARG

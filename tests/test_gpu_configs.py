@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import gated_mlp_gemms_amd as gm
 import oracle
 from gpu_helpers import TOL, announce, assert_close, f64, run
 from workloads import WORKLOADS, Workload, make_inputs
@@ -124,6 +125,38 @@ def test_llama_shard_shapes(name):
     r.backward()
     torch.cuda.synchronize()
     _check_gated(w, t, r, "outside")
+
+
+def test_grouped_backward_equals_separate_launches():
+    """At the LLaMA size mlp_bwd runs dx, dW_gate/dW_up and dW_down as one launch (asserted: the
+    planner's choice for this shape). A tile of that launch runs the same tile body, tile shape
+    and K order as the unsplit 8-wave 256x256 launch its product gets when asked for alone, so
+    dW_gate/dW_up alone and dW_down alone equal the grouped results bit for bit. dx, split along
+    K when alone, is checked against the oracle on sampled rows (test_llama_swiglu_full_size);
+    here a second grouped backward repeats the first bit for bit."""
+    w = WORKLOADS["llama_swiglu_bf16_m2048_d4096_h11008"]
+    announce(f"{w.name} grouped vs separate")
+    t = make_inputs(w)
+    r = run(w, t)
+    assert gm.mlp_bwd_grouped(r.desc)
+    r.forward()
+    r.backward(dpreact=False)
+    torch.cuda.synchronize()
+    first = {k: v.clone() for k, v in r.grads().items()}
+    r.dw_gate.zero_()
+    r.dw_up.zero_()
+    r.backward(dx=False, dw_down=False, dpreact=False)
+    torch.cuda.synchronize()
+    assert torch.equal(r.dw_gate, first["dw_gate"]) and torch.equal(r.dw_up, first["dw_up"])
+    r.dw_down.zero_()
+    r.backward(dx=False, dw_gate=False, dpreact=False)
+    torch.cuda.synchronize()
+    assert torch.equal(r.dw_down, first["dw_down"])
+    r.dx.zero_()
+    r.backward(dpreact=False)
+    torch.cuda.synchronize()
+    for k, v in r.grads().items():
+        assert torch.equal(v, first[k]), k
 
 
 @pytest.mark.parametrize("mode", ["outside", "inside"])

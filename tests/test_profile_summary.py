@@ -68,3 +68,24 @@ def test_recompute_gemm_is_a_stage_not_a_new_step():
     # without the recompute stage the same launches read as one up projection per forward and
     # per backward, and no step is whole
     assert ps._per_step(disp, ps.STAGE_ORDER_GATED) == []
+
+
+GROUP = "_ZN4gmlp21gemm_dma_group_kernelIDF16bLi256ELi256ELi8EDF16bLb1ELb0EfLb0ELb0EEEvNS_9GemmGroupE"
+GROUP_DEM = "void gmlp::gemm_dma_group_kernel<__bf16, 256, 256, 8, __bf16, true, false, __bf16, false, false>(gmlp::GemmGroup)"
+
+
+def test_grouped_backward_launch_is_one_stage():
+    # dx and the weight gradients as one launch: the stage order loses dw_down/dx/dw_up for one
+    # bwd_gemms stage, with and without the recompute stage
+    step = [UP, DOWN, RED, DACT_A, DACT_B, GROUP]
+    names = [FILL] + step + step + step[:3]
+    disp = [(i, n, 1.0) for i, n in enumerate(names)]
+    order = ps.grouped_order(ps.STAGE_ORDER_GATED, names)
+    assert order == ["up", "down", "dact", "bwd_gemms"]
+    steps = ps._per_step(disp, order)
+    assert len(steps) == 2
+    assert [len(steps[0][st]) for st in order] == [1, 2, 2, 1]
+    assert ps.grouped_order(ps.STAGE_ORDER_RECOMPUTE, names) == ["up", "down", "recompute", "dact", "bwd_gemms"]
+    assert ps.grouped_order(ps.STAGE_ORDER_GATED, [UP, DOWN]) == ps.STAGE_ORDER_GATED
+    assert ps.short_name(GROUP) == "gemm_group<bf16,NN+TN,256x256,8w,STORE,f32 dW out>"
+    assert ps.short_name(GROUP_DEM) == "gemm_group<bf16,NN+TN,256x256,8w,STORE>"
