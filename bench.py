@@ -98,16 +98,29 @@ def device_info() -> dict:
     return info
 
 
-def stage_flops(w) -> dict:
+def stage_flops(w, sched: int = 0) -> dict:
+    """FLOP of each stage's products; `sched` is the library's backward schedule (mlp_bwd_grouped
+    flags: 1 = dx and the weight gradients left as one launch, 2 = dW_down with the d-activation
+    GEMM)."""
     M, D, H, O = w.M, w.d_in, w.hidden, w.d_out
     P = 2 * H if w.gated else H
-    return {
+    f = {
         "up": 2.0 * M * D * P, "down": 2.0 * M * H * O, "dact": 2.0 * M * O * H,
         "dw_down": 2.0 * O * H * M, "dx": 2.0 * M * P * D, "dw_up": 2.0 * P * D * M,
         "recompute": 2.0 * M * D * P,
-        # dx, dW_gate/dW_up and dW_down as one launch
-        "bwd_gemms": 2.0 * M * P * D + 2.0 * P * D * M + 2.0 * O * H * M,
     }
+    with_dact = bool(sched & 2)
+    if with_dact:
+        f["dact"] += f["dw_down"]
+    f["bwd_gemms"] = f["dx"] + f["dw_up"] + (0.0 if with_dact else f["dw_down"])
+    return f
+
+
+def bwd_stages(sched: int) -> list:
+    """The backward's stages after the d-activation GEMM for a schedule (see stage_flops)."""
+    if sched & 1:
+        return ["bwd_gemms"]
+    return ([] if sched & 2 else ["dw_down"]) + ["dx", "dw_up"]
 
 
 def measured_traffic(workload: str, stage: str):
@@ -247,6 +260,9 @@ def main():
                     help="also time the inference forward at this many tokens, eager and from a graph (0: skip)")
     ap.add_argument("--vendor-gemm-reference", action="store_true",
                     help="also time the six plain GEMMs through torch.matmul (hipBLASLt), for context")
+    ap.add_argument("--save-act", choices=("workload", "on", "off"), default="workload",
+                    help="keep the activation from the forward for the backward (mlp_desc.save_act): as the "
+                         "workload says, or forced on / off")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warmup (a known-size "
                          "reference for profiler byte counters)")
@@ -272,6 +288,8 @@ def main():
         del src, dst
 
     w = WORKLOADS[args.workload or HEADLINE]
+    if args.save_act != "workload":
+        w = w.replace(save_act=args.save_act == "on")
     log(f"[bench] workload {w.name}: building inputs")
     tensors = make_inputs(w)
     r = runner_for(w, tensors)
@@ -291,9 +309,9 @@ def main():
     torch.cuda.synchronize()
 
     ev = HipEvents()
-    # the library runs dx and the weight gradients as one launch when its planner prefers that
-    bwd = ["bwd_gemms"] if gm.mlp_bwd_grouped(r.desc) else ["dw_down", "dx", "dw_up"]
-    stages = ["up", "down", "dact"] + bwd + (["recompute"] if w.recompute else [])
+    # the library groups backward GEMMs into one launch when its planner prefers that
+    sched = gm.mlp_bwd_grouped(r.desc)
+    stages = ["up", "down", "dact"] + bwd_stages(sched) + (["recompute"] if w.recompute else [])
     stage_id = {n: gm._lib.STAGES.index(n) for n in stages}
 
     def run_steps(hooked):
@@ -328,7 +346,7 @@ def main():
     # the one the headline is timed on)
     log(f"[bench] stage pass: {args.steps} steps with events around every stage")
     pairs, _, _, _ = run_steps(stages)
-    sf = stage_flops(w)
+    sf = stage_flops(w, sched)
     stage_us, stage_tf = {}, {}
     for j, n in enumerate(stages):
         us = avg_us(pairs, j)
@@ -421,7 +439,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "d_in": w.d_in, "hidden": w.hidden, "d_out": w.d_out,
                    "act": w.act, "gate_mult": w.gate_mult, "down_mult": w.down_mult,
-                   "recompute": w.recompute, "grad_accum": w.grad_accum,
+                   "recompute": w.recompute, "grad_accum": w.grad_accum, "save_act": w.save_act,
+                   "bwd_schedule": {"grouped": bool(sched & 1), "dw_down_with_dact": bool(sched & 2)},
                    "step": "mlp_fwd (training) + mlp_bwd (dx, all weight grads)",
                    "model_flop_per_step": flops, "pct_of_bf16_peak": round(100 * tflops / peak, 2),
                    "wall_s_timed": round(wall, 3)},

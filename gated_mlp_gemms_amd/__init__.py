@@ -13,7 +13,8 @@ import torch
 
 from ._lib import (  # noqa: F401
     LIB_PATH, MLP_ACT_GEGLU, MLP_ACT_GELU_TANH, MLP_ACT_GLU, MLP_ACT_REGLU, MLP_ACT_RELU, MLP_ACT_RELU_SQ,
-    MLP_ACT_SWIGLU, MLP_BF16, MLP_F16, MLP_F32, MLP_FP8_E4M3, MLP_FP8_E5M2, MLP_GATE_INSIDE, MLP_GATE_OUTSIDE,
+    MLP_ACT_SWIGLU, MLP_BF16, MLP_BWD_DW_DOWN_WITH_DACT, MLP_BWD_GROUPED, MLP_F16, MLP_F32, MLP_FP8_E4M3,
+    MLP_FP8_E5M2, MLP_GATE_INSIDE, MLP_GATE_OUTSIDE,
     MLP_NOALLOC_SCRATCH_BYTES, MLP_PHASE_BWD, MLP_PHASE_FWD, MLP_PHASE_FWD_INFER, MlpDesc, MlpError, MlpFp8, check,
     lib,
 )
@@ -28,10 +29,11 @@ _PHASES = {"fwd": MLP_PHASE_FWD, "fwd_infer": MLP_PHASE_FWD_INFER, "bwd": MLP_PH
 
 
 def make_desc(M, d_in, hidden, d_out=None, act="swiglu", dtype=torch.bfloat16, gate_mult=1.0,
-              down_mult=1.0, gate_mode="outside", recompute=False, fp8_fwd=False, fp8_bwd=False) -> MlpDesc:
+              down_mult=1.0, gate_mode="outside", recompute=False, fp8_fwd=False, fp8_bwd=False,
+              save_act=False) -> MlpDesc:
     return MlpDesc(int(M), int(d_in), int(hidden), int(d_in if d_out is None else d_out), _ACTS[act],
                    _DTYPES[dtype], float(gate_mult), float(down_mult), _MODES[gate_mode], int(bool(recompute)),
-                   int(bool(fp8_fwd)), int(bool(fp8_bwd)))
+                   int(bool(fp8_fwd)), int(bool(fp8_bwd)), int(bool(save_act)))
 
 
 def _ptr(t):
@@ -151,11 +153,13 @@ def mlp_quantize_weight_e4m3(w, exact, scale, tile_amax, dst=None, dst_t=None, l
     check(st, "mlp_quantize_weight_e4m3")
 
 
-def mlp_bwd_grouped(desc: MlpDesc) -> bool:
-    """Whether mlp_bwd runs dx, dW_gate/dW_up and dW_down as one launch for this problem."""
+def mlp_bwd_grouped(desc: MlpDesc) -> int:
+    """mlp_bwd's schedule flags for this problem: MLP_BWD_GROUPED (dx and the weight gradients
+    left after the d-activation GEMM run as one launch) | MLP_BWD_DW_DOWN_WITH_DACT (dW_down runs
+    in the d-activation GEMM's launch; save_act only). 0: every product alone."""
     out = C.c_int(0)
     check(lib().mlp_bwd_grouped(C.byref(desc), C.byref(out)), "mlp_bwd_grouped")
-    return bool(out.value)
+    return int(out.value)
 
 
 def mlp_fp8_next_scale(amax: float, prev_scale: float, gain: float, floor: float) -> float:

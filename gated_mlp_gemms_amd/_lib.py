@@ -15,6 +15,7 @@ MLP_GATE_OUTSIDE, MLP_GATE_INSIDE = 0, 1
 MLP_PHASE_FWD, MLP_PHASE_FWD_INFER, MLP_PHASE_BWD = 0, 1, 2
 MLP_FP8_E4M3, MLP_FP8_E5M2 = 0, 1
 MLP_NOALLOC_SCRATCH_BYTES = 64 << 20
+MLP_BWD_GROUPED, MLP_BWD_DW_DOWN_WITH_DACT = 1, 2
 STAGES = ("up", "down", "recompute", "dact", "dw_down", "dx", "dw_up", "act", "widen", "bwd_gemms")
 
 
@@ -23,6 +24,7 @@ class MlpDesc(C.Structure):
         ("M", C.c_int64), ("d_in", C.c_int64), ("hidden", C.c_int64), ("d_out", C.c_int64),
         ("act", C.c_int32), ("dtype", C.c_int32), ("gate_mult", C.c_float), ("down_mult", C.c_float),
         ("gate_mode", C.c_int32), ("recompute", C.c_int32), ("fp8_fwd", C.c_int32), ("fp8_bwd", C.c_int32),
+        ("save_act", C.c_int32),
     ]
 
 

@@ -689,13 +689,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_kernel(const GemmArgs 
 }
 
 // Several independent GEMMs in one launch (GemmGroup): member j has the workgroups
-// [begin[j], begin[j+1]) and runs the store epilogue with the first tile body (kind 0: layout
-// AK0/BK0, output Io0) or the second (kind 1). Each member's range is a multiple of 8 long, so
+// [begin[j], begin[j+1]) and runs the first tile body (kind 0: layout AK0/BK0, epilogue EPI0,
+// epilogue type Io0) or the second (kind 1). Each member's range is a multiple of 8 long, so
 // xcd_remap keeps its tiles XCD-contiguous; workgroups past a member's tile count do nothing.
 // Workgroups are dispatched in index order, so the members listed first start first: listing
 // the members with the longest K first lets the short tiles of the others fill the CUs around
 // them (list scheduling) instead of each GEMM idling part of the chip in its last round.
-template <typename T, int BM, int BN, int WAVES, typename Io0, bool AK0, bool BK0, typename Io1, bool AK1, bool BK1>
+template <typename T, int BM, int BN, int WAVES, typename Io0, bool AK0, bool BK0, int EPI0, typename Io1, bool AK1,
+          bool BK1, int EPI1>
 __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_group_kernel(const GemmGroup g) {
   __shared__ __attribute__((aligned(1024))) char smem[dma_ring_bytes<T, BM, BN>()];
   const int b = blockIdx.x;
@@ -703,14 +704,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_dma_group_kernel(const Gem
   while (j + 1 < g.count && b >= g.begin[j + 1]) ++j;
   const int item = xcd_remap(b - g.begin[j], g.begin[j + 1] - g.begin[j]);
   if (item >= g.items[j]) return;
-  if (g.kind[j] == 0) gemm_dma_tile<T, Io0, BM, BN, AK0, BK0, EPI_STORE, WAVES>(g.g[j], item, smem);
-  else gemm_dma_tile<T, Io1, BM, BN, AK1, BK1, EPI_STORE, WAVES>(g.g[j], item, smem);
+  if (g.kind[j] == 0) gemm_dma_tile<T, Io0, BM, BN, AK0, BK0, EPI0, WAVES>(g.g[j], item, smem);
+  else gemm_dma_tile<T, Io1, BM, BN, AK1, BK1, EPI1, WAVES>(g.g[j], item, smem);
 }
 
-template <typename T, int BM, int BN, int WAVES, typename Io0, bool AK0, bool BK0, typename Io1, bool AK1, bool BK1>
+template <typename T, int BM, int BN, int WAVES, typename Io0, bool AK0, bool BK0, int EPI0, typename Io1, bool AK1,
+          bool BK1, int EPI1>
 hipError_t launch_gemm_dma_group(const GemmGroup& g, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_dma_group_kernel<T, BM, BN, WAVES, Io0, AK0, BK0, Io1, AK1, BK1>), dim3(g.begin[g.count]),
-                     dim3(64 * WAVES), 0, stream, g);
+  hipLaunchKernelGGL((gemm_dma_group_kernel<T, BM, BN, WAVES, Io0, AK0, BK0, EPI0, Io1, AK1, BK1, EPI1>),
+                     dim3(g.begin[g.count]), dim3(64 * WAVES), 0, stream, g);
   return hipGetLastError();
 }
 

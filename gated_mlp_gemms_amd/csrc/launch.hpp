@@ -33,9 +33,11 @@ hipError_t run_gemm_f32(Layout layout, int epi, TileShape tile, const GemmArgs& 
 hipError_t run_gemm_e4m3_nt(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
 hipError_t run_gemm_f8g_nt(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
 
-// The 16-bit backward's dx (kind 0: NN, output `in`) and weight gradients (kind 1: TN, output
-// gio: `in`, or DT_F32 to accumulate) in one launch of 8-wave 256 x 256 tiles (GemmGroup).
-hipError_t run_gemm_group16(DType in, DType gio, const GemmGroup& g, hipStream_t s);
+// Independent GEMMs of the 16-bit backward in one launch of 8-wave 256 x 256 tiles (GemmGroup):
+// kind 0 an NN product with epilogue epi0 (EPI_STORE: dx; EPI_DGATED / EPI_DACT: the
+// d-activation GEMM), output `in`; kind 1 a TN weight gradient with the store epilogue, output
+// gio (`in`, or DT_F32 to accumulate).
+hipError_t run_gemm_group16(DType in, DType gio, int epi0, const GemmGroup& g, hipStream_t s);
 
 // out = alpha * sum_s partial[s] (fixed order), stored as `io` or added into fp32 (accumulate).
 // Rows >= c_split go to C1 (row - c_split).

@@ -247,7 +247,7 @@ Gemms plan_all(const mlp_desc* d) {
 // tiles, unsplit: quack's backward runs these GEMMs on a dynamic tile scheduler for the same
 // reason (mlp.py, dynamic_scheduler=True), done here with a static order instead of atomics.
 
-enum BwdGemm : int { BG_DW_DOWN = 0, BG_DX = 1, BG_DW_UP = 2 };
+enum BwdGemm : int { BG_DW_DOWN = 0, BG_DX = 1, BG_DW_UP = 2, BG_DACT = 3 };
 
 struct BwdGroup {
   int count = 0;              // 0: separate launches
@@ -263,6 +263,7 @@ GemmDims bwd_dims(const mlp_desc* d, int which) {
   switch (which) {
     case BG_DW_DOWN: return {O, H, M};
     case BG_DX: return {M, D, P};
+    case BG_DACT: return {M, H, O};
     default: return {P, D, M};
   }
 }
@@ -278,16 +279,13 @@ double list_makespan(const int64_t* tiles, const int64_t* steps, int count, doub
   return *std::max_element(cu.begin(), cu.end());
 }
 
-// The grouped launch of the products in `mask` (bit BwdGemm), when the time model prefers it to
-// separate launches planned by plan_gemm (split-K allowed); count = 0 otherwise.
-BwdGroup plan_bwd_group(const mlp_desc* d, unsigned mask) {
+// One launch of the products `ids` (at least two), when the time model prefers it to launching
+// them one after another (each planned by plan_gemm: split-K allowed for the weight gradients and
+// dx, the d-activation GEMM unsplit); count = 0 otherwise.
+BwdGroup plan_group(const mlp_desc* d, const int* ids, int n) {
   BwdGroup g;
   const DType io = io_of(d);
-  if (d->fp8_bwd || (io != DT_BF16 && io != DT_F16)) return g;
-  int ids[kGroupMax], n = 0;
-  for (int m : {BG_DX, BG_DW_UP, BG_DW_DOWN})
-    if (mask & (1u << m)) ids[n++] = m;
-  if (n < 2) return g;
+  if (n < 2 || d->fp8_bwd || (io != DT_BF16 && io != DT_F16)) return g;
   int64_t tiles[kGroupMax], steps[kGroupMax];
   Plan plans[kGroupMax];
   double t_sep = 0.0;
@@ -296,9 +294,9 @@ BwdGroup plan_bwd_group(const mlp_desc* d, unsigned mask) {
     plans[j] = plan_gemm(io, dm.M, dm.N, dm.K, false, false, TILE_256x256_W8);
     tiles[j] = plans[j].grid;
     steps[j] = (dm.K + 63) / 64;
-    t_sep += plan_gemm(io, dm.M, dm.N, dm.K, true, false).est;
+    t_sep += plan_gemm(io, dm.M, dm.N, dm.K, ids[j] != BG_DACT, false).est;
   }
-  // longest K first (stable: dx, then dW_gate/dW_up, then dW_down on ties)
+  // longest K first (stable on ties: the order of ids)
   int order[kGroupMax] = {0, 1, 2};
   std::stable_sort(order, order + n, [&](int a, int b) { return steps[a] > steps[b]; });
   int64_t ot[kGroupMax], os[kGroupMax];
@@ -320,6 +318,26 @@ BwdGroup plan_bwd_group(const mlp_desc* d, unsigned mask) {
 
 unsigned bwd_mask(const void* dx, const void* dwg, const void* dwd) {
   return (dwd ? 1u << BG_DW_DOWN : 0u) | (dx ? 1u << BG_DX : 0u) | (dwg ? 1u << BG_DW_UP : 0u);
+}
+
+// The backward's launches after the (optional) recompute: `dact` groups the d-activation GEMM
+// with dW_down (only with save_act: dW_down then reads the forward's activation, not one the
+// d-activation GEMM writes); `rest` groups what remains of dx, dW_gate/dW_up and dW_down.
+struct BwdSchedule { BwdGroup dact, rest; };
+
+BwdSchedule plan_bwd_schedule(const mlp_desc* d, unsigned mask) {
+  BwdSchedule sc;
+  const bool need_dpre = mask & ((1u << BG_DX) | (1u << BG_DW_UP));
+  if (d->save_act && need_dpre && (mask & (1u << BG_DW_DOWN))) {
+    const int ids[2] = {BG_DACT, BG_DW_DOWN};
+    sc.dact = plan_group(d, ids, 2);
+    if (sc.dact.count > 0) mask &= ~(1u << BG_DW_DOWN);
+  }
+  int ids[kGroupMax], n = 0;
+  for (int m : {BG_DX, BG_DW_UP, BG_DW_DOWN})
+    if (mask & (1u << m)) ids[n++] = m;
+  sc.rest = plan_group(d, ids, n);
+  return sc;
 }
 
 WsLayout ws_layout(const mlp_desc* d, int phase) {
@@ -390,6 +408,10 @@ mlp_status check_desc(const mlp_desc* d) {
       (d->fp8_bwd != 0 && d->fp8_bwd != 1))
     return fail(MLP_ERR_INVALID_ARG, "recompute, fp8_fwd and fp8_bwd must be 0 or 1");
   if (d->fp8_bwd && !d->fp8_fwd) return fail(MLP_ERR_INVALID_ARG, "fp8_bwd needs fp8_fwd");
+  if (d->save_act != 0 && d->save_act != 1) return fail(MLP_ERR_INVALID_ARG, "save_act must be 0 or 1");
+  if (d->save_act && (d->recompute || d->fp8_fwd))
+    return fail(MLP_ERR_INVALID_ARG, "save_act keeps the activation next to the saved pre-activation: it "
+                "needs recompute = 0 and fp8_fwd = 0");
   if (!isfinite(d->gate_mult) || !isfinite(d->down_mult))
     return fail(MLP_ERR_INVALID_ARG, "gate_mult and down_mult must be finite");
   if (d->fp8_fwd && (d->act != MLP_ACT_RELU_SQ || d->dtype != MLP_BF16))
@@ -584,6 +606,12 @@ mlp_status up_projection(const mlp_desc* d, const void* x, const void* wg, const
 }
 
 // Host-side checks of a forward call's arguments (everything but the workspace).
+// With save_act: the [M, H] activation after the [M, P] pre-activation in saved_preact.
+void* saved_act(const mlp_desc* d, const void* saved) {
+  const int64_t P = is_gated(d->act) ? 2 * d->hidden : d->hidden;
+  return const_cast<char*>(static_cast<const char*>(saved)) + d->M * P * esize(d->dtype);
+}
+
 mlp_status fwd_check(const mlp_desc* d, const void* x, const void* wg, const void* wu, const void* wd,
                      const void* out, const void* saved, const mlp_fp8* f, bool infer) {
   MLP_TRY(check_desc(d));
@@ -611,8 +639,9 @@ mlp_status fwd_run(const mlp_desc* d, const void* x, const void* wg, const void*
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const WsLayout L = ws_layout(d, phase);
   char* w = reinterpret_cast<char*>(ws);
-  void* act = w + L.act;
   const int64_t M = d->M, H = d->hidden, O = d->d_out;
+  // the activation the down projection reads: kept after the pre-activation with save_act
+  void* act = (d->save_act && !infer) ? saved_act(d, saved) : w + L.act;
   {
     StageScope st(MLP_STAGE_UP, s);
     MLP_TRY(up_projection(d, x, wg, wu, f, infer ? nullptr : saved, act, w + L.partial, s));
@@ -793,12 +822,13 @@ mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void*
 
 extern "C" {
 
-int mlp_abi_version(void) { return 4; }
+int mlp_abi_version(void) { return 5; }
 
 mlp_status mlp_bwd_grouped(const mlp_desc* d, int* grouped) {
   MLP_TRY(check_desc(d));
   if (!grouped) return fail(MLP_ERR_INVALID_ARG, "grouped must not be NULL");
-  *grouped = plan_bwd_group(d, bwd_mask(d, d, d)).count > 0;
+  const BwdSchedule sch = plan_bwd_schedule(d, bwd_mask(d, d, d));
+  *grouped = (sch.rest.count > 0 ? MLP_BWD_GROUPED : 0) | (sch.dact.count > 0 ? MLP_BWD_DW_DOWN_WITH_DACT : 0);
   return MLP_OK;
 }
 
@@ -935,39 +965,27 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
 
   const bool need_dpre = dx != nullptr || dwg != nullptr;
   void* dpre = dpreact ? dpreact : (d->recompute ? w + L.pre : w + L.dpre);
-  void* act = w + L.act;
+  // the activation dW_down reads: the forward's (save_act), else re-emitted by the d-activation
+  // GEMM or the activation-only pass into the workspace
+  void* act = d->save_act ? saved_act(d, saved) : w + L.act;
 
-  if (need_dpre) {
-    // da = dm * dout W_down, fused with d(act) against the pre-activation; re-emits a / post
-    GemmArgs a = base_args(d);
-    a.A = dout;
-    a.lda = O;
-    a.B0 = wd;
-    a.ldb = H;
-    a.aux = const_cast<void*>(pre);
-    a.ld_aux = P;
-    a.half = (int)H;
-    a.C0 = dpre;
-    a.ldc0 = P;
-    a.C1 = act;
-    a.ldc1 = H;
-    a.flags = dwd ? 2 : 0;
-    a.alpha = d->down_mult;
-    a.alpha_dev0 = sw2;
-    const Plan p = plan_gemm(io, M, H, O, false, false);
-    StageScope st(MLP_STAGE_DACT, s);
-    MLP_TRY(gemm_cols_split(io, io, NN, gated ? EPI_DGATED : EPI_DACT, p, a, M, H, O, esize(d->dtype), s,
-                            "d-activation GEMM"));
-  } else if (dwd) {
-    // only the down-projection gradient: the post-activation from the pre-activation alone
-    StageScope st(MLP_STAGE_ACT, s);
-    if (gated) MLP_TRY(hip_status(run_gated_act(io, pre, act, (int)M, (int)H, d->gate_mult,
-                                                d->gate_mode == MLP_GATE_INSIDE, act_fn_of(d->act), s),
-                                  "activation"));
-    else MLP_TRY(hip_status(run_plain_act(io, pre, act, M * H, 1.0f, nullptr, nullptr, act_fn_of(d->act), s),
-                            "activation"));
-  }
-
+  // da = dm * dout W_down, fused with d(act) against the pre-activation; re-emits a / post
+  // when dW_down needs it and the forward did not keep it
+  GemmArgs a_dact = base_args(d);
+  a_dact.A = dout;
+  a_dact.lda = O;
+  a_dact.B0 = wd;
+  a_dact.ldb = H;
+  a_dact.aux = const_cast<void*>(pre);
+  a_dact.ld_aux = P;
+  a_dact.half = (int)H;
+  a_dact.C0 = dpre;
+  a_dact.ldc0 = P;
+  a_dact.C1 = act;
+  a_dact.ldc1 = H;
+  a_dact.flags = (dwd && !d->save_act) ? 2 : 0;
+  a_dact.alpha = d->down_mult;
+  a_dact.alpha_dev0 = sw2;
   // dW_down (+)= dm * dout^T a
   GemmArgs a_dwd = base_args(d);
   a_dwd.A = dout;
@@ -1002,26 +1020,49 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
   a_dwg.accumulate = grad_accum;
   a_dwg.alpha_dev0 = sx;
 
-  const BwdGroup grp = plan_bwd_group(d, bwd_mask(dx, dwg, dwd));
-  if (grp.count > 0) {
-    const GemmArgs* args[3] = {&a_dwd, &a_dx, &a_dwg};
+  const GemmArgs* args[4] = {&a_dwd, &a_dx, &a_dwg, &a_dact};   // by BwdGemm id
+  // one launch of a planned group: member j's workgroups start at a multiple of 8
+  auto run_group = [&](const BwdGroup& grp, int epi0, const char* what) {
     GemmGroup gg{};
     int at = 0;
     for (int j = 0; j < grp.count; ++j) {
       const int m = grp.member[j];
       const GemmDims dm = bwd_dims(d, m);
       gg.g[j] = planned(*args[m], grp.plan[j], dm.M, dm.N, dm.K);
-      gg.kind[j] = m == BG_DX ? 0 : 1;
+      gg.kind[j] = (m == BG_DX || m == BG_DACT) ? 0 : 1;
       gg.items[j] = grp.plan[j].grid;
       gg.begin[j] = at;
       at += (grp.plan[j].grid + 7) / 8 * 8;
     }
     gg.begin[grp.count] = at;
     gg.count = grp.count;
-    StageScope st(MLP_STAGE_BWD_GEMMS, s);
-    return hip_status(run_gemm_group16(io, gio, gg, s), "dx and weight gradients (one launch)");
+    return hip_status(run_gemm_group16(io, gio, epi0, gg, s), what);
+  };
+
+  const BwdSchedule sch = plan_bwd_schedule(d, bwd_mask(dx, dwg, dwd));
+  const int dact_epi = gated ? EPI_DGATED : EPI_DACT;
+  if (need_dpre) {
+    StageScope st(MLP_STAGE_DACT, s);
+    if (sch.dact.count > 0)
+      MLP_TRY(run_group(sch.dact, dact_epi, "d-activation GEMM and dW_down (one launch)"));
+    else
+      MLP_TRY(gemm_cols_split(io, io, NN, dact_epi, plan_gemm(io, M, H, O, false, false), a_dact, M, H, O,
+                              esize(d->dtype), s, "d-activation GEMM"));
+  } else if (dwd && !d->save_act) {
+    // only the down-projection gradient: the post-activation from the pre-activation alone
+    StageScope st(MLP_STAGE_ACT, s);
+    if (gated) MLP_TRY(hip_status(run_gated_act(io, pre, act, (int)M, (int)H, d->gate_mult,
+                                                d->gate_mode == MLP_GATE_INSIDE, act_fn_of(d->act), s),
+                                  "activation"));
+    else MLP_TRY(hip_status(run_plain_act(io, pre, act, M * H, 1.0f, nullptr, nullptr, act_fn_of(d->act), s),
+                            "activation"));
   }
-  if (dwd) {
+
+  if (sch.rest.count > 0) {
+    StageScope st(MLP_STAGE_BWD_GEMMS, s);
+    return run_group(sch.rest, EPI_STORE, "dx and weight gradients (one launch)");
+  }
+  if (dwd && sch.dact.count == 0) {
     StageScope st(MLP_STAGE_DW_DOWN, s);
     MLP_TRY(gemm(io, gio, TN, EPI_STORE, G.dw_down, a_dwd, O, H, M, partial, s, "dW_down"));
   }

@@ -35,29 +35,42 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 STAGE_ORDER_GATED = ["up", "down", "dact", "dw_down", "dx", "dw_up"]
 # the backward with activation recompute re-runs the up projection before the d-activation
 STAGE_ORDER_RECOMPUTE = ["up", "down", "recompute", "dact", "dw_down", "dx", "dw_up"]
-# the backward's dx and weight-gradient products run as one launch (gemm_dma_group_kernel) when
-# the library's planner groups them: one "bwd_gemms" stage in place of the three
+# Grouped launches (gemm_dma_group_kernel) of the backward: the d-activation GEMM with dW_down
+# (first tile body with a d-activation epilogue; the "dact" stage then holds dW_down too), and
+# dx with the weight gradients (first tile body with the store epilogue): one "bwd_gemms" stage
+# in place of the dw_down / dx / dw_up left.
 _GROUPED = ("dw_down", "dx", "dw_up")
-GROUP_EPI = 100   # gemm_epilogue's value for the grouped launch (a GEMM that opens a stage)
+GROUP_EPI = 100   # gemm_epilogue of a grouped launch: GROUP_EPI + its first body's epilogue
+_GROUP_MANGLED = re.compile(r"gemm_dma_group_kernelI.*?Lb[01]ELb[01]ELi(\d)E")
+_GROUP_DEMANGLED = re.compile(r"gemm_dma_group_kernel<[^,]+, \d+, \d+, \d+, [^,]+, (?:true|false), (?:true|false), (\d)")
 
 
 def is_group(name: str) -> bool:
     return "gemm_dma_group_kernel" in name
 
 
+def group_epilogue(name: str) -> int:
+    """The epilogue of a grouped launch's first tile body (0 when the name does not say)."""
+    m = _GROUP_MANGLED.search(name) or _GROUP_DEMANGLED.search(name)
+    return int(m.group(1)) if m else 0
+
+
 def grouped_order(stages: list[str], names) -> list[str]:
-    """`stages` with dw_down, dx and dw_up replaced by one bwd_gemms stage when the dispatch
-    names include the grouped launch."""
-    if not any(is_group(n) for n in names):
-        return list(stages)
-    out = []
-    for st in stages:
+    """`stages` adjusted to the grouped launches among the dispatch names: dw_down dropped when
+    it runs with the d-activation GEMM, and what is left of dw_down, dx and dw_up as one
+    bwd_gemms stage when those run as one launch."""
+    epis = {group_epilogue(n) for n in names if is_group(n)}
+    out = [st for st in stages if not (st == "dw_down" and epis - {0})]
+    if 0 not in epis:
+        return out
+    res = []
+    for st in out:
         if st in _GROUPED:
-            if "bwd_gemms" not in out:
-                out.append("bwd_gemms")
+            if "bwd_gemms" not in res:
+                res.append("bwd_gemms")
         else:
-            out.append(st)
-    return out
+            res.append(st)
+    return res
 
 
 def kernel_sources_sha256() -> str:
@@ -106,7 +119,7 @@ def gemm_epilogue(name: str):
     """The epilogue index of one of this library's GEMM kernels (None for other kernels;
     GROUP_EPI for the grouped backward launch)."""
     if is_group(name):
-        return GROUP_EPI
+        return GROUP_EPI + group_epilogue(name)
     f = _gemm_fields(name)
     return int(f[6]) if f else None
 
@@ -117,8 +130,8 @@ def short_name(name: str) -> str:
         m = re.search(r"Li(\d+)ELi(\d+)ELi(\d+)E", name) or re.search(r"<[^,]+, (\d+), (\d+), (\d+),", name)
         bm, bn, w = m.groups() if m else ("?", "?", "?")
         t = "f16" if ("DF16_" in name or "_Float16" in name or "half" in name) else "bf16"
-        f32 = "EfLb0ELb0E" in name or ", float, false, false>" in name
-        return f"gemm_group<{t},NN+TN,{bm}x{bn},{w}w,STORE{',f32 dW out' if f32 else ''}>"
+        f32 = re.search(r"EfLb0ELb0ELi\dE", name) is not None or ", float, false, false" in name
+        return f"gemm_group<{t},NN:{_EPI[group_epilogue(name)]}+TN:STORE,{bm}x{bn},{w}w{',f32 dW out' if f32 else ''}>"
     f = _gemm_fields(name)
     if f:
         dma, types, bm, bn, ak, bk, epi, waves = f

@@ -26,14 +26,14 @@ EXACT_SCALE_CALLS = 16  # weight scales are exact for this many quantize() calls
 class MlpRunner:
     def __init__(self, *, act, dtype, M, d_in, hidden, d_out, gate_mult=1.0, down_mult=1.0,
                  gate_mode="outside", recompute=False, grad_accum=False, fp8_fwd=False, fp8_bwd=False,
-                 tensors: dict, device="cuda", dpreact_in_place=False):
+                 save_act=False, tensors: dict, device="cuda", dpreact_in_place=False):
         self.gated = act in GATED_ACTS
         self.grad_accum = grad_accum
         self.fp8 = fp8_fwd
         self.fp8_bwd = fp8_bwd
         tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}.get(dtype, dtype)
         self.desc = make_desc(M, d_in, hidden, d_out, act, tdt, gate_mult, down_mult, gate_mode,
-                              recompute, fp8_fwd, fp8_bwd)
+                              recompute, fp8_fwd, fp8_bwd, save_act)
         dev = torch.device(device)
         up = {k: v.to(dev) for k, v in tensors.items()}
         self.t = up
@@ -44,9 +44,15 @@ class MlpRunner:
         P = 2 * hidden if self.gated else hidden
         self.out = torch.empty(M, d_out, dtype=tdt, device=dev)
         self.out_infer = torch.empty(M, d_out, dtype=tdt, device=dev)
-        # the fp8-gradient backward keeps its pre-activation in fp32
+        # the fp8-gradient backward keeps its pre-activation in fp32; with save_act the [M, P]
+        # pre-activation is followed by the [M, H] activation in one buffer
         sdt = torch.float32 if fp8_bwd else tdt
-        self.saved = None if recompute else torch.empty(M, P, dtype=sdt, device=dev)
+        self.saved, self.saved_act = None, None
+        if not recompute:
+            buf = torch.empty(M * (P + (hidden if save_act else 0)), dtype=sdt, device=dev)
+            self.saved = buf[: M * P].view(M, P)
+            if save_act:
+                self.saved_act = buf[M * P:].view(M, hidden)
         self.dpreact = self.saved if (dpreact_in_place and not recompute) else torch.empty(M, P, dtype=tdt, device=dev)
         self.dx = torch.empty(M, d_in, dtype=tdt, device=dev)
         gdt = torch.float32 if grad_accum else tdt
@@ -154,8 +160,8 @@ class MlpRunner:
 
 def runner_for(w, tensors, device="cuda", **kw) -> MlpRunner:
     """A runner for a workload description with fields act, dtype, M, d_in, hidden, d_out,
-    gate_mult, down_mult, recompute, grad_accum, fp8_fwd (and optionally fp8_bwd)."""
+    gate_mult, down_mult, recompute, grad_accum, fp8_fwd (and optionally fp8_bwd, save_act)."""
     return MlpRunner(act=w.act, dtype=w.dtype, M=w.M, d_in=w.d_in, hidden=w.hidden, d_out=w.d_out,
                      gate_mult=w.gate_mult, down_mult=w.down_mult, recompute=w.recompute,
                      grad_accum=w.grad_accum, fp8_fwd=w.fp8_fwd, fp8_bwd=getattr(w, "fp8_bwd", False),
-                     tensors=tensors, device=device, **kw)
+                     save_act=getattr(w, "save_act", False), tensors=tensors, device=device, **kw)

@@ -91,6 +91,11 @@ typedef struct mlp_desc {
   int32_t fp8_fwd;    /* 1: e4m3 forward GEMMs (ReLU^2, bf16 only); see mlp_fp8 */
   int32_t fp8_bwd;    /* 1: fp8 backward GEMMs with e5m2 gradients (needs fp8_fwd); see mlp_fp8.
                        * The pre-activation saved by mlp_fwd is then fp32. */
+  int32_t save_act;   /* 1: mlp_fwd also keeps the activation a = act(g) * u (non-gated: post =
+                       * f(pre)) after the pre-activation in saved_preact, and mlp_bwd reads it
+                       * there instead of re-forming it in the d-activation GEMM, so dW_down no
+                       * longer waits for that GEMM (flash-swiglu-mlp README, "design points":
+                       * the forward keeps A, G and U). Needs recompute = 0 and fp8_fwd = 0. */
 } mlp_desc;
 
 /*
@@ -144,6 +149,9 @@ size_t mlp_workspace_bytes(const mlp_desc* desc, int phase);
  *                desc->dtype (fp32 with desc->fp8_bwd: the fp8-gradient backward rounds dpre and
  *                relu(pre)^2 to fp8 from it). Must be NULL iff desc->recompute (then nothing is
  *                kept for the backward: quack's MLPRecomputeFunc saves only x and the weights).
+ *                With desc->save_act the [M, P] pre-activation (P = 2H gated, H otherwise) is
+ *                followed by the [M, H] activation the down projection read (a, or post), in
+ *                desc->dtype: M * (P + H) elements in all.
  *   w_up         NULL for a non-gated activation (w_gate then holds W1, w_down holds W2).
  *   fp8          non-NULL iff desc->fp8_fwd; x / w_gate / w_down are then not read.
  */
@@ -185,9 +193,12 @@ mlp_status mlp_fwd_infer_noalloc(const mlp_desc* desc, const void* x, const void
  * Backward (quack mlp.py: MLPRecomputeFunc.backward, _compute_weight_grad; flash-swiglu-mlp
  * README, "design points": fused dA/dG/dU with dA never stored, dG/dU written over G/U,
  * merged dW_g/dW_u GEMM, single-accumulator dI).
- *   saved_preact  as written by mlp_fwd; NULL iff desc->recompute.
+ *   saved_preact  as written by mlp_fwd; NULL iff desc->recompute. With desc->save_act its
+ *                 activation part is read, not written, and dW_down may run in one launch with
+ *                 the d-activation GEMM (see mlp_bwd_grouped).
  *   dpreact       gated [M, 2H] = [dg | du], non-gated [M, H]; written. NULL: kept in the
- *                 workspace. May equal saved_preact (overwritten in place; no other overlap).
+ *                 workspace. May equal saved_preact (its pre-activation part is overwritten in
+ *                 place; no other overlap).
  *   dx            [M, d_in], NULL to skip.
  *   dw_gate/dw_up [H, d_in] (non-gated: dw_gate = dW1, dw_up NULL); both or neither (gated).
  *   dw_down       [d_out, H], NULL to skip.
@@ -265,7 +276,8 @@ float mlp_fp8_next_scale(float amax, float prev_scale, float gain, float floor_)
  *   UP        x W1^T with the activation epilogue (gated: gate and up together)
  *   DOWN      a W2^T (the down projection, split-K reduce included)
  *   RECOMPUTE the backward's x W1^T when desc->recompute
- *   DACT      dout W2 with the d-activation epilogue
+ *   DACT      dout W2 with the d-activation epilogue (and dW2 with it when mlp_bwd_grouped
+ *             says MLP_BWD_DW_DOWN_WITH_DACT)
  *   DW_DOWN   dW2 = dout^T a;   DX  dx = dpreact W1;   DW_UP  dW1 = dpreact^T x
  *   ACT       the activation-only pass of the "only dW2" branch
  *   WIDEN     the e4m3 -> bf16 widening of the e4m3 backward
@@ -279,15 +291,21 @@ typedef enum mlp_stage {
 } mlp_stage;
 
 /*
- * Schedule of mlp_bwd's products after the d-activation GEMM (quack mlp.py, MLPRecomputeFunc
- * backward: dx and the two weight gradients, which its backward runs on a dynamic tile
- * scheduler). *grouped = 1 when a call of mlp_bwd for `desc` that asks for dx, dw_gate (/dw_up)
- * and dw_down runs them as one launch (stage BWD_GEMMS: the long-K tiles of one product and the
- * short ones of the others share the CUs, no split-K); 0 when it runs them one after another
- * (stages DX, DW_UP, DW_DOWN). A call that asks for two of them decides the same way for those
- * two; a call that asks for one runs it alone. Results do not depend on it beyond the rounding
- * of split-K sums. Host only. Errors: MLP_ERR_INVALID_ARG for a bad desc or a NULL grouped.
+ * Schedule of mlp_bwd's GEMMs (quack mlp.py, MLPRecomputeFunc backward: dx and the two weight
+ * gradients, which its backward runs on a dynamic tile scheduler), for a call that asks for dx,
+ * dw_gate (/dw_up) and dw_down. *grouped is a set of flags:
+ *   MLP_BWD_DW_DOWN_WITH_DACT  dW_down runs in one launch with the d-activation GEMM (stage
+ *                              DACT; only with desc->save_act, which makes them independent);
+ *   MLP_BWD_GROUPED            the remaining ones of dx, dW_gate/dW_up and dW_down run as one
+ *                              launch (stage BWD_GEMMS) instead of their own (DX, DW_UP, DW_DOWN).
+ * A grouped launch lets the long-K tiles of one product and the short ones of another share the
+ * CUs, with no split-K. 0: every product alone. A call that asks for fewer products decides the
+ * same way for those it asks for (a product alone runs alone). Results do not depend on it
+ * beyond the rounding of split-K sums. Host only. Errors: MLP_ERR_INVALID_ARG for a bad desc or
+ * a NULL grouped.
  */
+#define MLP_BWD_GROUPED 1
+#define MLP_BWD_DW_DOWN_WITH_DACT 2
 mlp_status mlp_bwd_grouped(const mlp_desc* desc, int* grouped);
 
 /*

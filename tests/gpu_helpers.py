@@ -70,6 +70,8 @@ def check_full(w, t, r, gate_mode="outside", tol=None):
         if r.saved is not None:
             pairs.append(("g", r.saved[:, : w.hidden], f["g"]))
             pairs.append(("u", r.saved[:, w.hidden:], f["u"]))
+        if getattr(r, "saved_act", None) is not None:
+            pairs.append(("a (kept)", r.saved_act, f["a"]))
     else:
         f = oracle.act_forward(a["x"], a["w1"], a["w2"], w.down_mult, w.act)
         b = oracle.act_backward(a["dout"], a["x"], a["w1"], a["w2"], w.down_mult, w.act)
@@ -77,6 +79,8 @@ def check_full(w, t, r, gate_mode="outside", tol=None):
         grads = [("dw1", r.dw_gate, b["dw1"]), ("dw2", r.dw_down, b["dw2"])]
         if r.saved is not None:
             pairs.append(("pre", r.saved, f["pre"]))
+        if getattr(r, "saved_act", None) is not None:
+            pairs.append(("post (kept)", r.saved_act, f["post"]))
     for name, g, ref in pairs:
         assert_close(name, f64(g), ref, tol)
     for name, g, ref in grads:

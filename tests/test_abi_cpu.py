@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib._SIGNATURES), "binding and header disagree"
-    assert L.mlp_abi_version() == 4
+    assert L.mlp_abi_version() == 5
 
 
 def _desc(**kw):
@@ -328,9 +328,12 @@ def test_backward_schedule_query():
     launches beat any single-pass tile order) or the problem is small, and never for fp32 or the
     fp8-gradient backward; a NULL out pointer or a bad descriptor is an argument error."""
     L = gm.lib()
-    assert gm.mlp_bwd_grouped(_desc(M=2048, d_in=4096, hidden=11008, d_out=4096))
-    assert gm.mlp_bwd_grouped(_desc(M=8192, d_in=2048, hidden=4864, d_out=2048, recompute=True))
-    assert gm.mlp_bwd_grouped(_desc(M=2048, d_in=4096, hidden=11008, d_out=4096, dtype="f16"))
+    G, W = gm.MLP_BWD_GROUPED, gm.MLP_BWD_DW_DOWN_WITH_DACT
+    assert gm.mlp_bwd_grouped(_desc(M=2048, d_in=4096, hidden=11008, d_out=4096)) == G
+    assert gm.mlp_bwd_grouped(_desc(M=8192, d_in=2048, hidden=4864, d_out=2048, recompute=True)) == G
+    assert gm.mlp_bwd_grouped(_desc(M=2048, d_in=4096, hidden=11008, d_out=4096, dtype="f16")) == G
+    # the kept activation frees dW_down from the d-activation GEMM: both launches group
+    assert gm.mlp_bwd_grouped(_desc(M=2048, d_in=4096, hidden=11008, d_out=4096, save_act=True)) == G | W
     assert not gm.mlp_bwd_grouped(_desc(M=49152, d_in=768, hidden=3072, d_out=768, act="relu_sq"))
     assert not gm.mlp_bwd_grouped(_desc(M=16, d_in=4096, hidden=11008, d_out=4096))
     assert not gm.mlp_bwd_grouped(_desc(M=2048, d_in=4096, hidden=11008, d_out=4096, dtype="f32"))
@@ -341,3 +344,19 @@ def test_backward_schedule_query():
     bad = _desc(M=0)
     out = C.c_int(7)
     assert L.mlp_bwd_grouped(C.byref(bad), C.byref(out)) == _lib.MLP_ERR_INVALID_ARG
+
+
+def test_save_act_checks():
+    """save_act is 0 or 1 and keeps the activation next to a saved pre-activation: it cannot be
+    combined with recompute (nothing is saved) or the e4m3 forward (its activation is e4m3)."""
+    L = gm.lib()
+    ok = _desc(save_act=True)
+    assert L.mlp_workspace_bytes(C.byref(ok), _lib.MLP_PHASE_BWD) > 0
+    for bad in (_desc(save_act=True, recompute=True),
+                _desc(act="relu_sq", save_act=True, fp8_fwd=True, d_in=256, hidden=704, d_out=256)):
+        assert L.mlp_workspace_bytes(C.byref(bad), _lib.MLP_PHASE_BWD) == 0
+        assert b"save_act" in L.mlp_last_error()
+    d = _desc()
+    d.save_act = 2
+    assert L.mlp_workspace_bytes(C.byref(d), _lib.MLP_PHASE_FWD) == 0
+    assert b"save_act" in L.mlp_last_error()

@@ -21,3 +21,21 @@ def test_bench_help_lists_contract_flags():
     assert r.returncode == 0
     for flag in ("--gpus", "--steps", "--warmup"):
         assert flag in r.stdout
+
+
+def test_stage_flops_cover_the_step_under_every_schedule():
+    """Whatever the backward schedule, the timed stages' FLOP add up to the model's count, each
+    product counted once (dW_down inside the d-activation stage or the grouped stage)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from workloads import WORKLOADS
+
+    for name in ("llama_swiglu_bf16_m2048_d4096_h11008", "gpt_relu2_bf16_m49152_d768_h3072"):
+        w = WORKLOADS[name]
+        for sched in (0, 1, 2, 3):
+            f = bench.stage_flops(w, sched)
+            stages = ["up", "down", "dact"] + bench.bwd_stages(sched)
+            assert abs(sum(f[s] for s in stages) - w.model_flops()) <= 1e-9 * w.model_flops(), (name, sched)
+    assert bench.bwd_stages(0) == ["dw_down", "dx", "dw_up"]
+    assert bench.bwd_stages(2) == ["dx", "dw_up"]
+    assert bench.bwd_stages(1) == bench.bwd_stages(3) == ["bwd_gemms"]

@@ -159,6 +159,52 @@ def test_grouped_backward_equals_separate_launches():
         assert torch.equal(v, first[k]), k
 
 
+def test_save_act_llama_full_size():
+    """The LLaMA step with the activation kept by the forward (save_act): the backward runs the
+    d-activation GEMM with dW_down in one launch, then dx with dW_gate/dW_up in another (both
+    asserted). Against the same step without save_act, out, dx, dW_gate and dW_up agree bit for
+    bit (the same tiles in the same K order; only dW_down's operand a comes from elsewhere: the
+    forward's fp32 epilogue instead of the d-activation GEMM's re-emission from the bf16 g and u);
+    dW_down and the kept a are checked against the oracle on sampled rows and units."""
+    w = WORKLOADS["llama_swiglu_bf16_m2048_d4096_h11008"].replace(save_act=True)
+    announce(f"{w.name} save_act")
+    t = make_inputs(w)
+    r = run(w, t)
+    assert gm.mlp_bwd_grouped(r.desc) == gm.MLP_BWD_GROUPED | gm.MLP_BWD_DW_DOWN_WITH_DACT
+    r.forward()
+    r.backward(dpreact=False)
+    torch.cuda.synchronize()
+    _check_gated(w, t, r, "outside")
+    a = {k: f64(v) for k, v in t.items()}
+    rows = _sample(w.M, seed=4)
+    f = oracle.gated_forward(a["x"][rows], a["w_gate"], a["w_up"], a["w_down"])
+    assert_close("a[rows] (kept)", f64(r.saved_act[rows]), f["a"], TOL["bf16"])
+    r0 = run(w.replace(save_act=False), t)
+    r0.forward()
+    r0.backward(dpreact=False)
+    torch.cuda.synchronize()
+    assert torch.equal(r.out, r0.out)
+    assert torch.equal(r.saved, r0.saved)
+    for k in ("dx", "dw_gate", "dw_up"):
+        assert torch.equal(getattr(r, k), getattr(r0, k)), k
+
+
+def test_save_act_ragged_in_every_dimension():
+    """The ragged LLaMA-sized problem (M = 2000, d = 4104, H = 11000) with the activation kept by
+    the forward: both grouped launches (asserted) with partial tiles and partial last K-steps,
+    sampled against the oracle."""
+    w = Workload("llama_ragged_swiglu_bf16_m2000_d4104_h11000_save_act", "swiglu", "bf16", (2000,), 4104, 11000,
+                 4104, gate_mult=1.125, down_mult=2.0, seed=11, save_act=True)
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    assert gm.mlp_bwd_grouped(r.desc) == gm.MLP_BWD_GROUPED | gm.MLP_BWD_DW_DOWN_WITH_DACT
+    r.forward()
+    r.backward(dpreact=False)
+    torch.cuda.synchronize()
+    _check_gated(w, t, r, "outside")
+
+
 @pytest.mark.parametrize("mode", ["outside", "inside"])
 def test_falcon_h1_recompute_accumulate_full_size(mode):
     w = WORKLOADS["falcon_h1_swiglu_bf16_m8192_d2048_h4864"]

@@ -55,6 +55,34 @@ def test_swiglu_f32_reference_config():
     assert torch.equal(r.out, r.out_infer)
 
 
+SAVE_ACT = [
+    _w("swiglu", "bf16", 300, 264, 712, 200, gate_mult=1.125, down_mult=2.0, save_act=True),
+    _w("relu_sq", "bf16", 300, 264, 712, 200, save_act=True),
+    _w("geglu", "f16", 129, 136, 400, 72, down_mult=1.5, save_act=True),
+    _w("swiglu", "f32", 77, 132, 200, 68, save_act=True),
+]
+
+
+@pytest.mark.parametrize("w", SAVE_ACT, ids=lambda w: w.name)
+def test_save_act_small(w):
+    """The forward keeps the activation (a, or post) after the pre-activation: it and every
+    output and gradient compared in full with the oracle. The "only dW_down" backward then reads
+    the kept activation (no activation pass) and gives the full backward's dW_down bit for bit."""
+    announce(f"save_act {w.name}")
+    t = make_inputs(w)
+    r = run(w, t)
+    assert r.saved_act is not None
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    check_full(w, t, r)
+    full = r.dw_down.clone()
+    r.dw_down.zero_()
+    r.backward(dx=False, dw_gate=False)
+    torch.cuda.synchronize()
+    assert torch.equal(r.dw_down, full)
+
+
 @pytest.mark.parametrize("mode", ["outside", "inside"])
 def test_gated_recompute_accumulate_small(mode):
     w = _w("swiglu", "bf16", 390, 256, 704, 264, gate_mult=1.125, down_mult=2.0, recompute=True, grad_accum=True)

@@ -70,8 +70,10 @@ def test_recompute_gemm_is_a_stage_not_a_new_step():
     assert ps._per_step(disp, ps.STAGE_ORDER_GATED) == []
 
 
-GROUP = "_ZN4gmlp21gemm_dma_group_kernelIDF16bLi256ELi256ELi8EDF16bLb1ELb0EfLb0ELb0EEEvNS_9GemmGroupE"
-GROUP_DEM = "void gmlp::gemm_dma_group_kernel<__bf16, 256, 256, 8, __bf16, true, false, __bf16, false, false>(gmlp::GemmGroup)"
+GROUP = "_ZN4gmlp21gemm_dma_group_kernelIDF16bLi256ELi256ELi8EDF16bLb1ELb0ELi0EfLb0ELb0ELi0EEEvNS_9GemmGroupE"
+GROUP_DEM = ("void gmlp::gemm_dma_group_kernel<__bf16, 256, 256, 8, __bf16, true, false, 0, __bf16, false, false, 0>"
+             "(gmlp::GemmGroup)")
+GROUP_DACT = "_ZN4gmlp21gemm_dma_group_kernelIDF16bLi256ELi256ELi8EDF16bLb1ELb0ELi4EDF16bLb0ELb0ELi0EEEvNS_9GemmGroupE"
 
 
 def test_grouped_backward_launch_is_one_stage():
@@ -87,5 +89,23 @@ def test_grouped_backward_launch_is_one_stage():
     assert [len(steps[0][st]) for st in order] == [1, 2, 2, 1]
     assert ps.grouped_order(ps.STAGE_ORDER_RECOMPUTE, names) == ["up", "down", "recompute", "dact", "bwd_gemms"]
     assert ps.grouped_order(ps.STAGE_ORDER_GATED, [UP, DOWN]) == ps.STAGE_ORDER_GATED
-    assert ps.short_name(GROUP) == "gemm_group<bf16,NN+TN,256x256,8w,STORE,f32 dW out>"
-    assert ps.short_name(GROUP_DEM) == "gemm_group<bf16,NN+TN,256x256,8w,STORE>"
+    assert ps.short_name(GROUP) == "gemm_group<bf16,NN:STORE+TN:STORE,256x256,8w,f32 dW out>"
+    assert ps.short_name(GROUP_DEM) == "gemm_group<bf16,NN:STORE+TN:STORE,256x256,8w>"
+    assert ps.short_name(GROUP_DACT) == "gemm_group<bf16,NN:DGATED+TN:STORE,256x256,8w>"
+
+
+def test_dact_group_holds_dw_down():
+    # with the activation kept by the forward: the d-activation GEMM with dW_down, then dx with
+    # dW_gate/dW_up; and the d-activation group alone (dx and dW_gate/dW_up separate)
+    step = [UP, DOWN, RED, GROUP_DACT, GROUP]
+    names = step + step
+    order = ps.grouped_order(ps.STAGE_ORDER_GATED, names)
+    assert order == ["up", "down", "dact", "bwd_gemms"]
+    steps = ps._per_step([(i, n, 1.0) for i, n in enumerate(names)], order)
+    assert len(steps) == 2 and [len(steps[0][st]) for st in order] == [1, 2, 1, 1]
+    step = [UP, DOWN, RED, GROUP_DACT, DX, RED, DW]
+    names = step + step
+    order = ps.grouped_order(ps.STAGE_ORDER_GATED, names)
+    assert order == ["up", "down", "dact", "dx", "dw_up"]
+    steps = ps._per_step([(i, n, 1.0) for i, n in enumerate(names)], order)
+    assert len(steps) == 2 and [len(steps[0][st]) for st in order] == [1, 2, 1, 2, 1]

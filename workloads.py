@@ -46,6 +46,7 @@ class Workload:
     fp8_fwd: bool = False
     seed: int = 0
     fp8_bwd: bool = False   # backward products in fp8 too (e5m2 gradients); needs fp8_fwd
+    save_act: bool = False  # the forward keeps the activation next to the pre-activation
 
     @property
     def M(self) -> int:
