@@ -293,6 +293,7 @@ BwdGroup plan_group(const mlp_desc* d, const int* ids, int n) {
     const GemmDims dm = bwd_dims(d, ids[j]);
     plans[j] = plan_gemm(io, dm.M, dm.N, dm.K, false, false, TILE_256x256_W8);
     tiles[j] = plans[j].grid;
+    if (tiles[j] > 32 * 256) return g;   // many rounds: a last round's idle CUs cost under 3 %
     steps[j] = (dm.K + 63) / 64;
     t_sep += plan_gemm(io, dm.M, dm.N, dm.K, ids[j] != BG_DACT, false).est;
   }
@@ -400,6 +401,15 @@ mlp_status check_desc(const mlp_desc* d) {
       (d->fp8_bwd && d->M >= ld_lim))
     return fail(MLP_ERR_UNSUPPORTED, "a leading dimension is 2^25 elements or more (d_in, d_out, the gate/up "
                 "width, or M with fp8_bwd): the DMA offsets are 32-bit");
+  // no matrix of the problem may exceed 2^37 elements (256 GiB in bf16, beyond one GPU's HBM): tile
+  // and workgroup counts then fit an int and size arithmetic has ample headroom
+  {
+    const int64_t P = (is_gated(d->act) ? 2 : 1) * d->hidden, mat_lim = (int64_t)1 << 37;
+    const int64_t rows[] = {d->M, d->M, d->M, P, d->d_out}, cols[] = {d->d_in, P, d->d_out, d->d_in, d->hidden};
+    for (int i = 0; i < 5; ++i)
+      if (rows[i] > mat_lim / cols[i])
+        return fail(MLP_ERR_UNSUPPORTED, "a matrix of the problem has more than 2^37 elements");
+  }
   if (d->dtype != MLP_F32 && d->dtype != MLP_BF16 && d->dtype != MLP_F16)
     return fail(MLP_ERR_INVALID_ARG, "dtype %d is not an mlp_dtype", d->dtype);
   if (d->gate_mode != MLP_GATE_OUTSIDE && d->gate_mode != MLP_GATE_INSIDE)
@@ -1123,7 +1133,9 @@ mlp_status mlp_quantize_fp8(const void* src, int dtype, int64_t rows, int64_t co
 }
 
 int64_t mlp_weight_amax_slots(int64_t rows, int64_t cols) {
-  if (rows < 1 || cols < 1) return 0;
+  // sizes mlp_quantize_weight_e4m3 refuses have no slots (and the count cannot overflow)
+  const int64_t lim = (int64_t)1 << 31;
+  if (rows < 1 || cols < 1 || rows >= lim || cols >= lim) return 0;
   return weight_amax_slots(rows, cols);
 }
 

@@ -31,7 +31,8 @@
  *  - Size limits (MLP_ERR_UNSUPPORTED, before any HIP call): M, d_in, d_out < 2^30 and
  *    hidden < 2^29; every leading dimension below 2^25 elements (d_in, d_out, 2 * hidden for a
  *    gated activation or hidden otherwise, and M with fp8_bwd), since a GEMM operand is addressed
- *    as a base plus a 32-bit offset spanning up to 64 rows.
+ *    as a base plus a 32-bit offset spanning up to 64 rows; and no matrix of the problem (x, the
+ *    pre-activation, out, the weights) above 2^37 elements, more than one GPU's memory holds.
  */
 #ifndef GATED_MLP_H
 #define GATED_MLP_H
@@ -259,7 +260,8 @@ mlp_status mlp_quantize_fp8(const void* src, int dtype, int64_t rows, int64_t co
 mlp_status mlp_quantize_weight_e4m3(const void* w, int dtype, int64_t rows, int64_t cols, int exact, float* scale,
                                     float* tile_amax, void* dst, void* dst_t, int64_t ld_t, void* stream);
 /* Number of per-tile amax slots mlp_quantize_weight_e4m3 keeps for a [rows, cols] weight
- * (ceil(rows / 128) * ceil(cols / 128)); 0 for empty sizes. Host only. */
+ * (ceil(rows / 128) * ceil(cols / 128)); 0 for sizes it refuses (either below 1 or from 2^31 on).
+ * Host only. */
 int64_t mlp_weight_amax_slots(int64_t rows, int64_t cols);
 
 /*

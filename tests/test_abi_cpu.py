@@ -231,8 +231,19 @@ def test_leading_dimension_limits():
     assert _fwd(_desc(M=big, **fp8), nws=0) == gm._lib.MLP_ERR_UNSUPPORTED and "2^25" in _err()
     # just below each limit the size checks pass and the next check (a NULL workspace) fails
     for kw in (dict(d_in=big - 8), dict(d_out=big - 8), dict(hidden=big // 2 - 8), dict(act="relu_sq", hidden=big - 8),
-               dict(M=(1 << 30) - 1)):
+               dict(M=(1 << 30) - 1, d_in=16, hidden=16, d_out=16)):
         assert _fwd(_desc(**kw), ws=None) == gm._lib.MLP_ERR_INVALID_ARG, kw
+
+
+def test_matrix_size_limit():
+    """No matrix of the problem (x, the pre-activation, out, the weights) may exceed 2^37
+    elements (more than one GPU holds), which keeps every tile and workgroup count within an int;
+    exactly 2^37 passes the size checks."""
+    for kw in (dict(M=1 << 20, d_in=(1 << 17) + 8), dict(M=1 << 20, hidden=(1 << 16) + 8),
+               dict(M=1 << 20, d_out=(1 << 17) + 8), dict(d_in=1 << 24, hidden=(1 << 13) + 8)):
+        assert _fwd(_desc(**kw), nws=0) == gm._lib.MLP_ERR_UNSUPPORTED, kw
+        assert "2^37" in _err()
+    assert _fwd(_desc(M=1 << 20, d_in=1 << 17, hidden=1 << 10, d_out=1 << 10), ws=None) == gm._lib.MLP_ERR_INVALID_ARG
 
 
 def test_fp8_backward_checks():
