@@ -163,6 +163,41 @@ size_t partial_bytes(const Plan& p, int64_t M, int64_t N) {
   return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
 }
 
+// A store-epilogue GEMM whose unsplit 8-wave 256 x 256 tiles leave its last round mostly idle
+// (the GPT-shape down projection and dx: 576 tiles = 2.25 rounds of 256), cut along M: rows
+// [0, m1) in whole rounds of those tiles, rows [m1, M) planned on their own, where split-K fills
+// the chip (GPT shape: 510 tiles of 48 K-steps, then 66 tiles split 3 ways, one round of 16).
+// A static form of what a stream-K schedule does for the last round. m1 = 0: `main` covers all.
+struct RowsPlan {
+  Plan main{};
+  int64_t m1 = 0;
+  Plan tail{};
+};
+
+RowsPlan plan_rows(DType in, int64_t M, int64_t N, int64_t K) {
+  RowsPlan r;
+  r.main = plan_gemm(in, M, N, K, true, false);
+  if ((in != DT_BF16 && in != DT_F16) || r.main.splits != 1 || r.main.tile != TILE_256x256_W8) return r;
+  const int64_t tn = r.main.tiles_n, tiles = (int64_t)r.main.tiles_m * tn;
+  const int64_t rounds = tiles / 256, rem = tiles % 256;
+  if (rounds < 1 || rem == 0 || rem > 128) return r;
+  const int64_t m1 = rounds * 256 / tn * 256;   // whole row tiles that fill `rounds` rounds
+  if (m1 < 256 || m1 >= M) return r;
+  const Plan main = plan_gemm(in, m1, N, K, false, false, TILE_256x256_W8);
+  const Plan tail = plan_gemm(in, M - m1, N, K, true, false);
+  if (main.est + tail.est + 4e-6 < 0.97 * r.main.est) {
+    r.main = main;
+    r.m1 = m1;
+    r.tail = tail;
+  }
+  return r;
+}
+
+size_t partial_bytes(const RowsPlan& r, int64_t M, int64_t N) {
+  return r.m1 ? std::max(partial_bytes(r.main, r.m1, N), partial_bytes(r.tail, M - r.m1, N))
+              : partial_bytes(r.main, M, N);
+}
+
 // ---- workspace layout ----------------------------------------------------------------------
 
 struct WsLayout {
@@ -212,8 +247,10 @@ Plan plan_gated_split(DType in, int64_t M, int64_t H, int64_t D) {
 
 struct Gemms {   // the GEMMs a phase may run, in planning form
   Plan up_split;      // forward gated up projection split along K (splits = 1: fused instead)
-  Plan down;          // forward down projection
-  Plan dw_down, dx, dw_up;
+  RowsPlan down;      // forward down projection
+  Plan dw_down;
+  RowsPlan dx;
+  Plan dw_up;
 };
 
 Gemms plan_all(const mlp_desc* d) {
@@ -223,16 +260,16 @@ Gemms plan_all(const mlp_desc* d) {
   const int64_t M = d->M, D = d->d_in, H = d->hidden, O = d->d_out, P = gated ? 2 * H : H;
   Gemms g;
   g.up_split = (gated && !d->fp8_fwd) ? plan_gated_split(io, M, H, D) : Plan{TILE_128x128, 1, 0, 0, 0, 0, 0};
-  g.down = plan_gemm(fin, M, O, H, true, false);
+  g.down = plan_rows(fin, M, O, H);
   if (d->fp8_bwd) {   // every backward product on fp8 operands; the token dimension padded
     const int64_t Mp = pad16(M);
     g.dw_down = plan_gemm(DT_F8G, O, H, Mp, true, false);
-    g.dx = plan_gemm(DT_F8G, M, D, H, true, false);
+    g.dx.main = plan_gemm(DT_F8G, M, D, H, true, false);
     g.dw_up = plan_gemm(DT_F8G, H, D, Mp, true, false);
     return g;
   }
   g.dw_down = plan_gemm(io, O, H, M, true, false);
-  g.dx = plan_gemm(io, M, D, P, true, false);
+  g.dx = plan_rows(io, M, D, P);
   g.dw_up = plan_gemm(io, P, D, M, true, false);
   return g;
 }
@@ -545,6 +582,19 @@ mlp_status gemm_cols_split(DType in, DType io, Layout lay, int epi, const Plan& 
   return gemm(in, io, lay, epi, p2, b, M, N - n1, K, nullptr, s, what);
 }
 
+// A store-epilogue GEMM planned by plan_rows: rows [0, m1) with `main`, then rows [m1, M) with
+// `tail` (A and the output moved down by m1 rows; A is K-major for NT / NN, MN-major for TN).
+mlp_status gemm_rows(DType in, DType io, Layout lay, const RowsPlan& r, GemmArgs a, int64_t M, int64_t N,
+                     int64_t K, void* partial, hipStream_t s, const char* what) {
+  if (r.m1 == 0 || a.C1 != nullptr) return gemm(in, io, lay, EPI_STORE, r.main, a, M, N, K, partial, s, what);
+  MLP_TRY(gemm(in, io, lay, EPI_STORE, r.main, a, r.m1, N, K, partial, s, what));
+  const int64_t ei = in == DT_F32 ? 4 : (is_fp8(in) ? 1 : 2), eo = io == DT_F32 ? 4 : 2;
+  GemmArgs b = a;
+  b.A = static_cast<const char*>(a.A) + (lay == TN ? r.m1 : r.m1 * a.lda) * ei;
+  b.C0 = static_cast<char*>(a.C0) + r.m1 * a.ldc0 * eo;
+  return gemm(in, io, lay, EPI_STORE, r.tail, b, M - r.m1, N, K, partial, s, what);
+}
+
 GemmArgs base_args(const mlp_desc* d) {
   GemmArgs a{};
   a.alpha = 1.0f;
@@ -615,13 +665,13 @@ mlp_status up_projection(const mlp_desc* d, const void* x, const void* wg, const
   return gemm(io, io, NT, EPI_ACT, p, a, M, H, D, nullptr, s, "up projection");
 }
 
-// Host-side checks of a forward call's arguments (everything but the workspace).
 // With save_act: the [M, H] activation after the [M, P] pre-activation in saved_preact.
 void* saved_act(const mlp_desc* d, const void* saved) {
   const int64_t P = is_gated(d->act) ? 2 * d->hidden : d->hidden;
   return const_cast<char*>(static_cast<const char*>(saved)) + d->M * P * esize(d->dtype);
 }
 
+// Host-side checks of a forward call's arguments (everything but the workspace).
 mlp_status fwd_check(const mlp_desc* d, const void* x, const void* wg, const void* wu, const void* wd,
                      const void* out, const void* saved, const mlp_fp8* f, bool infer) {
   MLP_TRY(check_desc(d));
@@ -671,9 +721,9 @@ mlp_status fwd_run(const mlp_desc* d, const void* x, const void* wg, const void*
     b.alpha_dev0 = f->s_post;
     b.alpha_dev1 = f->s_w2;
   }
-  const Plan p = plan_all(d).down;
+  const RowsPlan p = plan_all(d).down;
   StageScope st(MLP_STAGE_DOWN, s);
-  return gemm(fin, io, NT, EPI_STORE, p, b, M, O, H, w + L.partial, s, "down projection");
+  return gemm_rows(fin, io, NT, p, b, M, O, H, w + L.partial, s, "down projection");
 }
 
 mlp_status fwd_impl(const mlp_desc* d, const void* x, const void* wg, const void* wu, const void* wd,
@@ -805,7 +855,7 @@ mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void*
     a.alpha_dev0 = f->s_dpre;
     a.alpha_dev1 = f->s_w1;
     StageScope st(MLP_STAGE_DX, s);
-    MLP_TRY(gemm(DT_F8G, DT_BF16, NT, EPI_STORE, G.dx, a, M, D, H, w + L.partial, s, "fp8 dx"));
+    MLP_TRY(gemm(DT_F8G, DT_BF16, NT, EPI_STORE, G.dx.main, a, M, D, H, w + L.partial, s, "fp8 dx"));
   }
   if (dw1) {   // dW1 (+)= dpre_q^T x_q
     StageScope st(MLP_STAGE_DW_UP, s);
@@ -1078,7 +1128,7 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
   }
   if (dx) {
     StageScope st(MLP_STAGE_DX, s);
-    MLP_TRY(gemm(io, io, NN, EPI_STORE, G.dx, a_dx, M, D, P, partial, s, "dx"));
+    MLP_TRY(gemm_rows(io, io, NN, G.dx, a_dx, M, D, P, partial, s, "dx"));
   }
   if (dwg) {
     StageScope st(MLP_STAGE_DW_UP, s);

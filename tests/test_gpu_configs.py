@@ -233,12 +233,13 @@ def test_recompute_accumulate_ragged_in_every_dimension():
     _check_gated(w, t, r, "outside")
 
 
-def _check_relu(w, t, r, x64=None, w1=None, w2=None, tol=None):
+def _check_relu(w, t, r, x64=None, w1=None, w2=None, tol=None, extra_rows=()):
     a = {k: f64(v) for k, v in t.items()}
     x64 = a["x"] if x64 is None else x64
     w1 = a["w1"] if w1 is None else w1
     w2 = a["w2"] if w2 is None else w2
-    rows, units = _sample(w.M, seed=4), _sample(w.hidden, seed=5)
+    rows = np.unique(np.concatenate([_sample(w.M, seed=4), np.asarray(extra_rows, np.int64)]))
+    units = _sample(w.hidden, seed=5)
     s = oracle.relu_sq_sampled(a["dout"], x64, w1, w2, rows, units, w.down_mult)
     tol = tol or TOL[w.dtype]
     assert_close("dx[rows]", f64(r.dx[rows]), s["dx_rows"], tol)
@@ -248,6 +249,9 @@ def _check_relu(w, t, r, x64=None, w1=None, w2=None, tol=None):
 
 
 def test_gpt_relu_sq_full_size():
+    """The GPT-shape ReLU^2 step. Its down projection and dx (576 tiles of 256 x 256) run cut
+    along M: rows below 43520 in two whole rounds, the rest split along K; the rows on both sides
+    of the cut are among the samples."""
     w = WORKLOADS["gpt_relu2_bf16_m49152_d768_h3072"]
     announce(w.name)
     t = make_inputs(w)
@@ -255,7 +259,24 @@ def test_gpt_relu_sq_full_size():
     r.forward()
     r.backward()
     torch.cuda.synchronize()
-    rows, s = _check_relu(w, t, r)
+    rows, s = _check_relu(w, t, r, extra_rows=(43519, 43520, 43521))
+    assert_close("out[rows]", f64(r.out[rows]), s["out_rows"], TOL["bf16"])
+
+
+def test_rows_split_ragged():
+    """A ReLU^2 problem with ragged d and H whose down projection and dx run cut along M
+    (M = 30000, d = 1032, H = 3080: 118 x 5 = 590 tiles, rows below 26112 in two whole rounds,
+    the last 3888 rows split along K, the last row and column tiles partial); sampled rows
+    include both sides of the cut and the last row."""
+    w = Workload("relu2_rows_split_bf16_m30000_d1032_h3080", "relu_sq", "bf16", (30000,), 1032, 3080, 1032,
+                 down_mult=1.5, seed=15)
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    rows, s = _check_relu(w, t, r, extra_rows=(26111, 26112, 26113, 29999))
     assert_close("out[rows]", f64(r.out[rows]), s["out_rows"], TOL["bf16"])
 
 
