@@ -39,6 +39,13 @@ hipError_t run_gemm_f8g_nt(DType io, int epi, TileShape tile, const GemmArgs& a,
 // gio (`in`, or DT_F32 to accumulate).
 hipError_t run_gemm_group16(DType in, DType gio, int epi0, const GemmGroup& g, hipStream_t s);
 
+// Products with at most kSkinnyMaxRows rows (decode-size token counts), K-major A [M, K] and
+// B [N, K] (gated: B0 gate rows, B1 up rows), in `in` = DT_BF16 / DT_F16; K a multiple of 8.
+// Epilogues EPI_STORE (C0 = alpha * A B^T), EPI_ACT and EPI_GATED with GemmArgs::flags as in the
+// GEMM kernels (bit 0: the pre-activation into aux, bit 1: the activation into C0).
+constexpr int kSkinnyMaxRows = 16;
+hipError_t run_skinny(DType in, int epi, const GemmArgs& a, hipStream_t s);
+
 // out = alpha * sum_s partial[s] (fixed order), stored as `io` or added into fp32 (accumulate).
 // Rows >= c_split go to C1 (row - c_split).
 hipError_t run_splitk_reduce(DType io, const float* partial, int splits, int M, int N, void* C0,

@@ -608,6 +608,15 @@ GemmArgs base_args(const mlp_desc* d) {
 
 // Forward GEMM 1: the gated / non-gated / e4m3 ReLU^2 up projection with its activation epilogue.
 // preact_out: where g|u or pre goes (NULL: not kept); act_out: where a / post / post_q goes.
+// Decode-size problems (at most kSkinnyMaxRows tokens, 16-bit, not e4m3): every product of the
+// forward, and the backward's recompute, runs on the small-M kernel (run_skinny), which streams
+// the weights once instead of padding the tokens to a 128- or 256-row tile. The training and the
+// inference forward and the recompute then share one kernel, so they agree bit for bit.
+bool skinny_ok(const mlp_desc* d) {
+  const DType io = io_of(d);
+  return (io == DT_BF16 || io == DT_F16) && !d->fp8_fwd && d->M <= kSkinnyMaxRows;
+}
+
 mlp_status up_projection(const mlp_desc* d, const void* x, const void* wg, const void* wu,
                          const mlp_fp8* f, void* preact_out, void* act_out, void* partial, hipStream_t s) {
   const DType io = io_of(d);
@@ -625,6 +634,8 @@ mlp_status up_projection(const mlp_desc* d, const void* x, const void* wg, const
     a.B1 = wu;
     a.ld_aux = 2 * H;
     a.half = (int)H;
+    if (skinny_ok(d))
+      return hip_status(run_skinny(io, EPI_GATED, planned(a, Plan{}, M, H, D), s), "gate/up projection (small M)");
     const Plan ps = plan_all(d).up_split;
     if (ps.splits > 1) {   // decode-size: split-K partials of [g | u], activation in the reduce
       GemmArgs b = a;
@@ -661,6 +672,7 @@ mlp_status up_projection(const mlp_desc* d, const void* x, const void* wg, const
   }
   a.A = x;
   a.B0 = wg;
+  if (skinny_ok(d)) return hip_status(run_skinny(io, EPI_ACT, planned(a, Plan{}, M, H, D), s), "up projection (small M)");
   const Plan p = plan_gemm(io, M, H, D, false, false);
   return gemm(io, io, NT, EPI_ACT, p, a, M, H, D, nullptr, s, "up projection");
 }
@@ -721,8 +733,9 @@ mlp_status fwd_run(const mlp_desc* d, const void* x, const void* wg, const void*
     b.alpha_dev0 = f->s_post;
     b.alpha_dev1 = f->s_w2;
   }
-  const RowsPlan p = plan_all(d).down;
   StageScope st(MLP_STAGE_DOWN, s);
+  if (skinny_ok(d)) return hip_status(run_skinny(io, EPI_STORE, planned(b, Plan{}, M, O, H), s), "down projection (small M)");
+  const RowsPlan p = plan_all(d).down;
   return gemm_rows(fin, io, NT, p, b, M, O, H, w + L.partial, s, "down projection");
 }
 
@@ -1017,9 +1030,13 @@ mlp_status mlp_bwd(const mlp_desc* d, const void* dout, const void* x, const voi
     a.alpha_dev0 = sx;
     a.alpha_dev1 = sw1;
     const int epi = gated ? EPI_GATED : EPI_ACT;
-    const Plan p = plan_gemm(io, M, H, D, false, gated);
     StageScope st(MLP_STAGE_RECOMPUTE, s);
-    MLP_TRY(gemm(io, io, NT, epi, p, a, M, H, D, nullptr, s, "recompute pre-activation"));
+    if (skinny_ok(d)) {
+      MLP_TRY(hip_status(run_skinny(io, epi, planned(a, Plan{}, M, H, D), s), "recompute pre-activation (small M)"));
+    } else {
+      const Plan p = plan_gemm(io, M, H, D, false, gated);
+      MLP_TRY(gemm(io, io, NT, epi, p, a, M, H, D, nullptr, s, "recompute pre-activation"));
+    }
     pre = w + L.pre;
   }
 

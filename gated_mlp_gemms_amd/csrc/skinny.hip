@@ -1,0 +1,188 @@
+// Products with at most 16 rows (decode-size inference: a few tokens against the full weights).
+// They are bound by reading the weights once from HBM, so the kernel streams weight rows straight
+// into registers, with no LDS staging and no tile of zero-padded token rows:
+//  * a workgroup owns 16 or 32 output units (their weight rows; gated: the gate rows and the up
+//    rows of the same units) and splits K over its waves;
+//  * lane l works on weight row l % 16 and token row l % 16; MFMA c of a 128-wide K block takes
+//    the 8 elements k = 32 c + 8 q .. + 7 from lane group q = l / 16 (the instruction's own
+//    operand layout), so one 16-byte load per lane reads 64 contiguous bytes of each of 16 weight
+//    rows, and a block is four such loads per matrix;
+//  * loads run two or three blocks ahead of the MFMAs that use them;
+//  * the waves' partial sums meet in LDS and are added in wave order (deterministic), then the
+//    first wave runs the epilogue: store, activation, or gated activation (and the pre-activation
+//    when training), with the same activation functions as the GEMM epilogues.
+#include "common.hpp"
+#include "gemm_kernel.hpp"
+#include "launch.hpp"
+
+namespace gmlp {
+
+namespace {
+
+constexpr int kKBlock = 128;       // K per block: four lane groups x 32
+constexpr int kTwoBlocksFrom = 1024;   // output column blocks of 16 from which a workgroup takes two
+
+// NCB column blocks of 16 units per workgroup (more units share each load of the token rows);
+// NBUF blocks of loads in flight per wave.
+template <typename T, int EPI, int WAVES, int NCB, int NBUF>
+__global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const GemmArgs p) {
+  constexpr bool GATED = EPI == EPI_GATED;
+  constexpr int NB = GATED ? 2 : 1;   // weight matrices read: gate and up, or one
+  constexpr int NACC = NB * NCB;
+  __shared__ f32x4 red[WAVES][NACC][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int nbase = blockIdx.x * 16 * NCB + r;   // this lane's weight row in column block 0
+  const bool tok_ok = r < p.M;
+  const char* xrow = reinterpret_cast<const char*>(elem_ptr<T>(p.A, tok_ok ? r : 0, p.lda, 0));
+  const char* wrow[NB][NCB];
+  bool row_ok[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int n = nbase + 16 * cb;
+    row_ok[cb] = n < p.N;
+    wrow[0][cb] = reinterpret_cast<const char*>(elem_ptr<T>(p.B0, row_ok[cb] ? n : 0, p.ldb, 0));
+    if constexpr (GATED) wrow[1][cb] = reinterpret_cast<const char*>(elem_ptr<T>(p.B1, row_ok[cb] ? n : 0, p.ldb, 0));
+  }
+  const int nblk = (p.K + kKBlock - 1) / kKBlock;
+  const int b0 = wave * nblk / WAVES, nb = (wave + 1) * nblk / WAVES - b0;
+  // each workgroup walks its waves' K ranges from a different block: every workgroup reads the
+  // same token rows, and a common order would send all of them to the same lines at once
+  const int rot = nb > 0 ? (int)(blockIdx.x % (unsigned)nb) : 0;
+  auto blk = [&](int i) { const int j = i + rot; return b0 + (j >= nb ? j - nb : j); };
+
+  u32x4 xa[NBUF][4], wa[NBUF][NB][NCB][4];
+  // block b into buffer s; a chunk past K (K is a multiple of 8: a chunk is wholly in or out),
+  // a token row past M or a weight row past N loads zeros
+  auto load = [&](int b, int s) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int k = b * kKBlock + c * 32 + q * 8;
+      const bool k_ok = k < p.K;
+      const int64_t off = (int64_t)k * (int64_t)sizeof(T);
+      xa[s][c] = (tok_ok && k_ok) ? *reinterpret_cast<const u32x4*>(xrow + off) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          wa[s][m][cb][c] = (row_ok[cb] && k_ok) ? *reinterpret_cast<const u32x4*>(wrow[m][cb] + off)
+                                                 : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  f32x4 acc[NACC];
+#pragma unroll
+  for (int j = 0; j < NACC; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](int s) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) Mma16<T>::mma(xa[s][c], wa[s][m][cb][c], acc[m * NCB + cb]);
+  };
+  // NBUF buffers in rotation, indexed by constants only (a register array indexed at run time
+  // would go to scratch memory): the i-th block of the walk lives in buffer i % NBUF
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j)
+    if (j < nb) load(blk(j), j);
+  int i = 0;
+  for (; i + NBUF <= nb; i += NBUF) {
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      if (i + j + NBUF - 1 < nb) load(blk(i + j + NBUF - 1), (j + NBUF - 1) % NBUF);
+      compute(j);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NBUF; ++j)
+    if (i + j < nb) compute(j);
+
+#pragma unroll
+  for (int j = 0; j < NACC; ++j) red[wave][j][lane] = acc[j];
+  __syncthreads();
+  if (wave != 0) return;
+  float alpha = p.alpha;
+  if (p.alpha_dev0) alpha *= *p.alpha_dev0;
+  if (p.alpha_dev1) alpha *= *p.alpha_dev1;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    if (!row_ok[cb]) continue;
+    const int n = nbase + 16 * cb;
+    f32x4 s0 = red[0][cb][lane], s1 = red[0][NACC - NCB + cb][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) {
+      s0 += red[w][cb][lane];
+      if constexpr (GATED) s1 += red[w][NCB + cb][lane];
+    }
+    // lane l holds tokens 4 q + i (i = 0..3) of unit n
+    float v[4], u[4], o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = alpha * s0[i];
+      u[i] = alpha * s1[i];
+    }
+    auto put = [&](void* base, int64_t ld, int col, const float (&val)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * q + i;
+        if (t < p.M) *reinterpret_cast<uint16_t*>(elem_ptr<T>(base, t, ld, col)) = (uint16_t)Bits16<T>::from_f32(val[i]);
+      }
+    };
+    if constexpr (GATED) {
+      if (p.flags & 1) {
+        put(p.aux, p.ld_aux, n, v);
+        put(p.aux, p.ld_aux, p.half + n, u);
+      }
+      if (p.flags & 2) {
+        gated_act<4>(p.act, p.gate_mult, p.gate_inside, v, u, o);
+        put(p.C0, p.ldc0, n, o);
+      }
+    } else if constexpr (EPI == EPI_ACT) {
+      if (p.flags & 1) put(p.aux, p.ld_aux, n, v);
+      if (p.flags & 2) {
+        act_fn<4>(p.act, v, o);
+        put(p.C0, p.ldc0, n, o);
+      }
+    } else {
+      put(p.C0, p.ldc0, n, v);
+    }
+  }
+}
+
+template <typename T, int EPI>
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
+  const int groups = (a.N + 15) / 16;   // column blocks of 16 units
+  if (groups >= kTwoBlocksFrom) {
+    // wide outputs: two column blocks per workgroup halve the re-reads of the token rows
+    hipLaunchKernelGGL((skinny_kernel<T, EPI, 4, 2, 2>), dim3((groups + 1) / 2), dim3(256), 0, s, a);
+  } else if (groups >= 512) {
+    hipLaunchKernelGGL((skinny_kernel<T, EPI, 4, 1, 3>), dim3(groups), dim3(256), 0, s, a);
+  } else {
+    // few workgroups: K split over more waves, so enough loads are in flight (the gated body
+    // keeps two weight matrices in flight and stops at 8 waves, within its register budget)
+    constexpr int W = EPI == EPI_GATED ? 8 : 16;
+    hipLaunchKernelGGL((skinny_kernel<T, EPI, W, 1, 3>), dim3(groups), dim3(64 * W), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t skinny_epi(int epi, const GemmArgs& a, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: return launch_skinny<T, EPI_STORE>(a, s);
+    case EPI_ACT: return launch_skinny<T, EPI_ACT>(a, s);
+    case EPI_GATED: return launch_skinny<T, EPI_GATED>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t run_skinny(DType in, int epi, const GemmArgs& a, hipStream_t s) {
+  if (a.M < 1 || a.M > kSkinnyMaxRows || a.N < 1 || a.K < 1 || a.K % 8) return hipErrorInvalidValue;
+  if (in == DT_BF16) return skinny_epi<bf16>(epi, a, s);
+  if (in == DT_F16) return skinny_epi<f16>(epi, a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gmlp

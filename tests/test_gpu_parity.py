@@ -209,9 +209,10 @@ def test_smallest_problem(act, dtype):
 ], ids=lambda w: w.name)
 @pytest.mark.parametrize("mode", ["outside", "inside"])
 def test_decode_size_split_up_projection(w, mode):
-    """At decode sizes (M <= 128, few hidden tiles) the gated up projection runs split along K over
-    the stacked [W_gate; W_up] with the activation applied in the reduce; the training forward
-    (saved g|u), the inference forward and the backward against the oracle."""
+    """At decode sizes the forward takes its small-M paths: up to 16 tokens the small-M kernel for
+    every product, up to 128 the gated up projection split along K over the stacked
+    [W_gate; W_up] with the activation applied in the reduce. The training forward (saved g|u),
+    the inference forward and the backward against the oracle."""
     announce(f"decode split {w.name} {mode}")
     t = make_inputs(w)
     r = run(w, t, gate_mode=mode)
@@ -221,6 +222,51 @@ def test_decode_size_split_up_projection(w, mode):
     torch.cuda.synchronize()
     assert torch.equal(r.out, r.out_infer)
     check_full(w, t, r, mode)
+
+
+SKINNY = [
+    # K = 4104 is 32 blocks of 128 and one chunk of 8; 712 hidden units and 520 / 136 outputs end
+    # in a partial group of 16
+    _w("swiglu", "bf16", 16, 4104, 712, 520, gate_mult=1.125, down_mult=2.0, seed=21),
+    _w("relu_sq", "bf16", 5, 776, 3080, 264, down_mult=1.5, seed=22),
+    _w("geglu", "f16", 13, 520, 712, 136, seed=23),
+    _w("swiglu", "bf16", 1, 264, 1400, 8, seed=24),
+]
+
+
+@pytest.mark.parametrize("w", SKINNY, ids=lambda w: w.name)
+def test_small_m_kernel(w):
+    """Up to 16 tokens every product of the forward runs on the small-M kernel (weights streamed
+    once, K split over the waves): compared in full with the oracle, with the training forward
+    (saved pre-activation), the inference forward and a recompute backward agreeing bit for bit."""
+    announce(f"small-M {w.name}")
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward()
+    r.forward_infer()
+    r.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(r.out, r.out_infer)
+    check_full(w, t, r)
+    rc = run(w.replace(recompute=True), t)
+    rc.backward()
+    torch.cuda.synchronize()
+    for k, v in r.grads().items():
+        assert torch.equal(v, rc.grads()[k]), f"recompute {k}"
+
+
+def test_small_m_llama_decode():
+    """The decode step the bench times: 16 tokens through the LLaMA MLP (4096 x 11008), inference
+    forward on the small-M kernel, sampled rows and every output column against the oracle."""
+    w = _w("swiglu", "bf16", 16, 4096, 11008, 4096, seed=25)
+    announce(w.name)
+    t = make_inputs(w)
+    r = run(w, t)
+    r.forward_infer()
+    torch.cuda.synchronize()
+    a = {k: f64(v) for k, v in t.items()}
+    f = oracle.gated_forward(a["x"], a["w_gate"], a["w_up"], a["w_down"])
+    assert_close("out (decode)", f64(r.out_infer), f["out"], TOL["bf16"])
 
 
 def test_tall_thin_problem():
