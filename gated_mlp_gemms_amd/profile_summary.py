@@ -184,15 +184,33 @@ def is_reduce(name: str) -> bool:
     return "splitk_reduce" in name or "gated_reduce" in name
 
 
+def _gemm_key(name: str):
+    """(layout, epilogue, 16-bit) of a GEMM launch; the grouped launch is its own layout."""
+    if is_group(name):
+        return ("group", GROUP_EPI + group_epilogue(name), True)
+    f = _gemm_fields(name)
+    return ((f[4], f[5]), int(f[6]), not ("e4m3" in f[1] or "f8g" in f[1]))
+
+
+def _continues(prev, cur) -> bool:
+    """Whether GEMM launch `cur` belongs to the stage of the launch `prev` before it: the same
+    layout with the same epilogue (a stage run as two launches over its output columns), or a
+    16-bit split-K launch right after a store launch (a store GEMM cut along M: the rows below
+    the cut with the store epilogue, the rest split along K)."""
+    if prev is None or prev[0] != cur[0]:
+        return False
+    return prev[1] == cur[1] or (cur[2] and prev[1] == 0 and cur[1] == 1)
+
+
 def _per_step(disp, stages):
     """Split this library's dispatches into steps (a step starts at each up-projection) and each
-    step into stages. Each GEMM opens the next stage, except one with the same epilogue as the GEMM
-    before it (a stage run as two launches over its output columns). A split-K reduce joins the
-    GEMM before it; other kernels of the library (quantize, transpose, widen) prepare an operand
-    and join the GEMM after them. With a "recompute" stage, an up-projection GEMM right after the
-    down projection is the backward's recompute, not a new step. Only whole steps are returned;
-    launches of other libraries (a fill, a copy) are skipped."""
-    steps, cur, idx, last_epi, pending = [], None, -1, None, []
+    step into stages. Each GEMM opens the next stage unless it continues the one before it
+    (`_continues`). A split-K reduce joins the GEMM before it; other kernels of the library
+    (quantize, transpose, widen) prepare an operand and join the GEMM after them. With a
+    "recompute" stage, an up-projection GEMM right after the down projection is the backward's
+    recompute, not a new step. Only whole steps are returned; launches of other libraries (a fill,
+    a copy) are skipped."""
+    steps, cur, idx, last_key, pending = [], None, -1, None, []
     rec = stages.index("recompute") if "recompute" in stages else -1
     for _, name, val in disp:
         if not is_library_kernel(name):
@@ -211,9 +229,9 @@ def _per_step(disp, stages):
         elif cur is None:
             pending = []
             continue
-        elif epi != last_epi:
+        elif not _continues(last_key, _gemm_key(name)):
             idx += 1
-        last_epi = epi
+        last_key = _gemm_key(name)
         if idx < len(stages):
             cur[stages[idx]].extend(pending + [(name, val)])
         else:

@@ -109,3 +109,19 @@ def test_dact_group_holds_dw_down():
     assert order == ["up", "down", "dact", "dx", "dw_up"]
     steps = ps._per_step([(i, n, 1.0) for i, n in enumerate(names)], order)
     assert len(steps) == 2 and [len(steps[0][st]) for st in order] == [1, 2, 1, 2, 1]
+
+
+STORE_NT, PART_NT = _g(256, 256, 1, 1, 0), _g(256, 256, 1, 1, 1).replace("DF16bDF16b", "DF16bf")
+STORE_NN, PART_NN = _g(256, 256, 1, 0, 0), _g(256, 256, 1, 0, 1).replace("DF16bDF16b", "DF16bf")
+ACT16, DACT16 = _g(256, 256, 1, 1, 3), _g(256, 256, 1, 0, 5)
+DW_TN = _g(256, 256, 0, 0, 1).replace("DF16bDF16b", "DF16bf")
+
+
+def test_rows_split_store_gemm_is_one_stage():
+    # the GPT-shape ReLU^2 step: the down projection and dx each cut along M (a store launch,
+    # then a split-K launch and its reduce); the weight gradients split-K in another layout
+    step = [ACT16, STORE_NT, PART_NT, RED, DACT16, DW_TN, RED, STORE_NN, PART_NN, RED, DW_TN, RED]
+    names = step + step
+    steps = ps._per_step([(i, n, 1.0) for i, n in enumerate(names)], ps.STAGE_ORDER_GATED)
+    assert len(steps) == 2
+    assert [len(steps[0][st]) for st in ps.STAGE_ORDER_GATED] == [1, 3, 1, 2, 3, 2]
