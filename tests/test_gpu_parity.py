@@ -588,11 +588,17 @@ def test_graph_replay_of_inference_forward(M):
             assert torch.equal(r.out_infer, ref)
 
 
-def test_graph_replay_of_training_step():
-    """A whole training step (forward + backward with split-K GEMMs) replayed from a graph gives
-    the eager step's outputs and gradients bit for bit, replay after replay."""
-    w = _w("swiglu", "bf16", 300, 264, 712, 200, gate_mult=1.125, down_mult=2.0)
-    announce("graph replay, training step")
+@pytest.mark.parametrize("w", [
+    _w("swiglu", "bf16", 300, 264, 712, 200, gate_mult=1.125, down_mult=2.0),
+    # the LLaMA shape: the backward's grouped launch, the d-activation's column split, split-K
+    _w("swiglu", "bf16", 2048, 4096, 11008, 4096, seed=26),
+    # store GEMMs cut along M (rows split), split-K weight gradients
+    _w("relu_sq", "bf16", 30000, 1032, 3080, 1032, down_mult=1.5, seed=27),
+], ids=lambda w: w.name)
+def test_graph_replay_of_training_step(w):
+    """A whole training step (forward + backward, with each shape's launch schedule) replayed
+    from a graph gives the eager step's outputs and gradients bit for bit, replay after replay."""
+    announce(f"graph replay, training step {w.name}")
     t = make_inputs(w)
     r = run(w, t)
 
