@@ -98,12 +98,15 @@ struct TileInfo { TileShape t; int bm, bn, slots; double eff; };
 // the 8-wave 256x256 tile takes ~1.95 us per 64-deep K-step, the 4-wave one ~2.1 us, a pair of
 // 128x128 workgroups ~1.2 us, and the 256x128 tile ~1.3 us. These were fitted before the 8-wave
 // tiles with a K-major A moved their DMAs to one wave per SIMD, which made those K-steps ~3-8 %
-// faster; that only widens the 8-wave tiles' lead, which the planner already gives them.
+// faster; that only widens the 8-wave tiles' lead, which the planner already gives them. The
+// 8-wave 256x128 figure was refitted later from forced-plan runs: the LLaMA down projection
+// unsplit in 256 such tiles (one round, no reduce) runs 156 us against 164 for split-K 2 over
+// 256x256 tiles plus the reduce, i.e. 0.40 of the per-CU peak.
 const TileInfo kTiles[] = {
     {TILE_256x256_W8, 256, 256, 1, 0.44},   // 8 waves: two per SIMD hide each other's stalls
     {TILE_256x256, 256, 256, 1, 0.40},
     {TILE_256x128, 256, 128, 1, 0.33},
-    {TILE_256x128_W8, 256, 128, 1, 0.36},
+    {TILE_256x128_W8, 256, 128, 1, 0.40},
     {TILE_128x128, 128, 128, 2, 0.36},
 };
 
@@ -177,8 +180,10 @@ struct RowsPlan {
 RowsPlan plan_rows(DType in, int64_t M, int64_t N, int64_t K) {
   RowsPlan r;
   r.main = plan_gemm(in, M, N, K, true, false);
-  if ((in != DT_BF16 && in != DT_F16) || r.main.splits != 1 || r.main.tile != TILE_256x256_W8) return r;
-  const int64_t tn = r.main.tiles_n, tiles = (int64_t)r.main.tiles_m * tn;
+  if (in != DT_BF16 && in != DT_F16) return r;
+  // the cut is taken from the 8-wave 256x256 tiling, and kept if it beats the best plain plan
+  const Plan w8 = plan_gemm(in, M, N, K, false, false, TILE_256x256_W8);
+  const int64_t tn = w8.tiles_n, tiles = (int64_t)w8.tiles_m * tn;
   const int64_t rounds = tiles / 256, rem = tiles % 256;
   if (rounds < 1 || rem == 0 || rem > 128) return r;
   const int64_t m1 = rounds * 256 / tn * 256;   // whole row tiles that fill `rounds` rounds
@@ -378,6 +383,13 @@ BwdSchedule plan_bwd_schedule(const mlp_desc* d, unsigned mask) {
   return sc;
 }
 
+// Decode-size problems whose forward products all run on the small-M kernel (no split-K
+// partials): at most kSkinnyMaxRows tokens, 16-bit, not e4m3.
+bool skinny_ok(const mlp_desc* d) {
+  const DType io = io_of(d);
+  return (io == DT_BF16 || io == DT_F16) && !d->fp8_fwd && d->M <= kSkinnyMaxRows;
+}
+
 WsLayout ws_layout(const mlp_desc* d, int phase) {
   WsLayout L;
   const bool gated = is_gated(d->act);
@@ -388,7 +400,8 @@ WsLayout ws_layout(const mlp_desc* d, int phase) {
   auto take = [&](size_t& at, size_t& sz, size_t bytes) { at = off; sz = bytes; off += round_up(bytes); };
   if (phase == MLP_PHASE_FWD || phase == MLP_PHASE_FWD_INFER) {
     take(L.act, L.act_bytes, (size_t)M * H * (d->fp8_fwd ? 1 : es));
-    take(L.partial, L.partial_bytes, std::max(partial_bytes(g.down, M, O), partial_bytes(g.up_split, M, 2 * H)));
+    take(L.partial, L.partial_bytes,
+         skinny_ok(d) ? 0 : std::max(partial_bytes(g.down, M, O), partial_bytes(g.up_split, M, 2 * H)));
   } else if (d->fp8_bwd) {
     const int64_t Mp = pad16(M);
     if (d->recompute) take(L.pre, L.pre_bytes, (size_t)M * H * sizeof(float));
@@ -612,10 +625,6 @@ GemmArgs base_args(const mlp_desc* d) {
 // forward, and the backward's recompute, runs on the small-M kernel (run_skinny), which streams
 // the weights once instead of padding the tokens to a 128- or 256-row tile. The training and the
 // inference forward and the recompute then share one kernel, so they agree bit for bit.
-bool skinny_ok(const mlp_desc* d) {
-  const DType io = io_of(d);
-  return (io == DT_BF16 || io == DT_F16) && !d->fp8_fwd && d->M <= kSkinnyMaxRows;
-}
 
 mlp_status up_projection(const mlp_desc* d, const void* x, const void* wg, const void* wu,
                          const mlp_fp8* f, void* preact_out, void* act_out, void* partial, hipStream_t s) {

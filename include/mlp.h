@@ -176,8 +176,9 @@ mlp_status mlp_fwd_infer(const mlp_desc* desc, const void* x, const void* w_gate
  * hipFree or allocating library routine); the caller still owns x, the weights, out and fp8.
  *   - Everything else is as mlp_fwd_infer, and out is bit for bit what mlp_fwd_infer writes.
  *   - MLP_ERR_WORKSPACE (before any HIP call) when mlp_workspace_bytes(desc,
- *     MLP_PHASE_FWD_INFER) exceeds MLP_NOALLOC_SCRATCH_BYTES (e.g. beyond ~512 tokens at
- *     d_in = 4096, hidden = 11008 in bf16).
+ *     MLP_PHASE_FWD_INFER) exceeds MLP_NOALLOC_SCRATCH_BYTES. That size follows the planned
+ *     split-K partials, so it is not monotone in M: at d_in = 4096, hidden = 11008 in bf16 every
+ *     M up to 645 fits, 2048 fits (45 MB) and 3000 does not.
  *   - stream must belong to the calling thread's current device (else MLP_ERR_INVALID_ARG).
  *     The first call on a device looks the array's address up on that device (make it before
  *     a graph capture starts).

@@ -111,7 +111,7 @@ static void rejected_calls(void) {
   EXPECT(mlp_fwd(&f8, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, NULL, FAKE, 1 << 30, NULL) == MLP_ERR_INVALID_ARG);
   EXPECT(mlp_fwd(&f8, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, &f, FAKE, 1 << 30, NULL) == MLP_ERR_INVALID_ARG);
   /* the no-allocation forward: checks and the static-scratch limit come before any HIP call */
-  const mlp_desc big = desc(2048, 4096, 11008, 4096, MLP_ACT_SWIGLU, MLP_BF16);
+  const mlp_desc big = desc(3000, 4096, 11008, 4096, MLP_ACT_SWIGLU, MLP_BF16);
   EXPECT(mlp_fwd_infer_noalloc(&big, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == MLP_ERR_WORKSPACE);
   EXPECT(mlp_fwd_infer_noalloc(&ok, NULL, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == MLP_ERR_INVALID_ARG);
   EXPECT(mlp_fwd_infer_noalloc(NULL, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == MLP_ERR_INVALID_ARG);

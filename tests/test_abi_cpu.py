@@ -304,7 +304,7 @@ def test_noalloc_entry_checks_run_before_any_hip_call():
     assert call(_desc(M=0)) == gm._lib.MLP_ERR_INVALID_ARG
     assert call(_desc(), x=None) == gm._lib.MLP_ERR_INVALID_ARG and "x is NULL" in _err()
     assert call(_desc(act="relu_sq")) == gm._lib.MLP_ERR_INVALID_ARG and "w_up" in _err()
-    big = _desc(M=2048, d_in=4096, hidden=11008, d_out=4096)
+    big = _desc(M=3000, d_in=4096, hidden=11008, d_out=4096)
     need = L.mlp_workspace_bytes(C.byref(big), gm.MLP_PHASE_FWD_INFER)
     assert need > gm.MLP_NOALLOC_SCRATCH_BYTES
     assert call(big) == gm._lib.MLP_ERR_WORKSPACE
@@ -343,8 +343,11 @@ def test_backward_schedule_query():
     assert gm.mlp_bwd_grouped(_desc(M=2048, d_in=4096, hidden=11008, d_out=4096)) == G
     assert gm.mlp_bwd_grouped(_desc(M=8192, d_in=2048, hidden=4864, d_out=2048, recompute=True)) == G
     assert gm.mlp_bwd_grouped(_desc(M=2048, d_in=4096, hidden=11008, d_out=4096, dtype="f16")) == G
-    # the kept activation frees dW_down from the d-activation GEMM: both launches group
-    assert gm.mlp_bwd_grouped(_desc(M=2048, d_in=4096, hidden=11008, d_out=4096, save_act=True)) == G | W
+    # the kept activation frees dW_down from the d-activation GEMM, and the two share a launch
+    # where the d-activation GEMM's own tiles leave a last round to fill (3072 tokens: 516 tiles
+    # of 256 x 256); at 2048 tokens it runs alone on 256 x 128 tiles
+    assert gm.mlp_bwd_grouped(_desc(M=3072, d_in=4096, hidden=11008, d_out=4096, save_act=True)) == G | W
+    assert gm.mlp_bwd_grouped(_desc(M=2048, d_in=4096, hidden=11008, d_out=4096, save_act=True)) == G
     assert not gm.mlp_bwd_grouped(_desc(M=49152, d_in=768, hidden=3072, d_out=768, act="relu_sq"))
     assert not gm.mlp_bwd_grouped(_desc(M=16, d_in=4096, hidden=11008, d_out=4096))
     assert not gm.mlp_bwd_grouped(_desc(M=2048, d_in=4096, hidden=11008, d_out=4096, dtype="f32"))

@@ -161,8 +161,8 @@ def test_grouped_backward_equals_separate_launches():
 
 def test_save_act_llama_full_size():
     """The LLaMA step with the activation kept by the forward (save_act): the backward runs the
-    d-activation GEMM with dW_down in one launch, then dx with dW_gate/dW_up in another (both
-    asserted). Against the same step without save_act, out, dx, dW_gate and dW_up agree bit for
+    d-activation GEMM alone, then dx with dW_gate/dW_up and dW_down in one launch (asserted).
+    Against the same step without save_act, out, dx, dW_gate and dW_up agree bit for
     bit (the same tiles in the same K order; only dW_down's operand a comes from elsewhere: the
     forward's fp32 epilogue instead of the d-activation GEMM's re-emission from the bf16 g and u);
     dW_down and the kept a are checked against the oracle on sampled rows and units."""
@@ -170,7 +170,7 @@ def test_save_act_llama_full_size():
     announce(f"{w.name} save_act")
     t = make_inputs(w)
     r = run(w, t)
-    assert gm.mlp_bwd_grouped(r.desc) == gm.MLP_BWD_GROUPED | gm.MLP_BWD_DW_DOWN_WITH_DACT
+    assert gm.mlp_bwd_grouped(r.desc) == gm.MLP_BWD_GROUPED
     r.forward()
     r.backward(dpreact=False)
     torch.cuda.synchronize()
@@ -190,10 +190,11 @@ def test_save_act_llama_full_size():
 
 
 def test_save_act_ragged_in_every_dimension():
-    """The ragged LLaMA-sized problem (M = 2000, d = 4104, H = 11000) with the activation kept by
-    the forward: both grouped launches (asserted) with partial tiles and partial last K-steps,
-    sampled against the oracle."""
-    w = Workload("llama_ragged_swiglu_bf16_m2000_d4104_h11000_save_act", "swiglu", "bf16", (2000,), 4104, 11000,
+    """A ragged LLaMA-sized problem (M = 2900, d = 4104, H = 11000) with the activation kept by
+    the forward: the d-activation GEMM with dW_down in one launch, dx with dW_gate/dW_up in
+    another (both asserted), with partial tiles and partial last K-steps, sampled against the
+    oracle."""
+    w = Workload("llama_ragged_swiglu_bf16_m2900_d4104_h11000_save_act", "swiglu", "bf16", (2900,), 4104, 11000,
                  4104, gate_mult=1.125, down_mult=2.0, seed=11, save_act=True)
     announce(w.name)
     t = make_inputs(w)

@@ -1,8 +1,8 @@
 """GPU test of mlp_fwd_infer_noalloc (the inference forward on the library's static per-GPU
 scratch) through the C ABI: its output equals mlp_fwd_infer's (caller workspace) bit for bit, on
-two calls in a row, the second with a smaller problem, for the decode-size LLaMA MLP (whose up
-projection runs split along K into fp32 partials held in the scratch), a ragged SwiGLU problem,
-a ReLU^2 problem and the e4m3 forward."""
+two calls in a row, the second with a smaller problem, for the LLaMA MLP at 64 tokens (whose up
+projection runs split along K into fp32 partials held in the scratch) then 16 (the small-M
+kernel), a ragged SwiGLU problem, a ReLU^2 problem and the e4m3 forward."""
 import pytest
 import torch
 
@@ -30,7 +30,7 @@ def _pair(w, t, fp8=False):
 
 CASES = [
     # (act, M_first, M_second, d, H, d_out, extra)
-    ("swiglu", 16, 5, 4096, 11008, 4096, {}),
+    ("swiglu", 64, 16, 4096, 11008, 4096, {}),
     ("swiglu", 300, 100, 264, 712, 200, {"gate_mult": 1.125, "down_mult": 2.0}),
     ("relu_sq", 200, 64, 256, 704, 208, {}),
     ("relu_sq", 129, 16, 768, 3072, 768, {"fp8_fwd": True}),
@@ -52,7 +52,7 @@ def test_noalloc_matches_workspace_entry(act, m1, m2, d, H, do, extra):
 def test_noalloc_rejects_beyond_scratch():
     """A problem whose inference workspace exceeds the scratch is refused before any launch and
     leaves out untouched."""
-    M, d, H = 2048, 4096, 11008
+    M, d, H = 3000, 4096, 11008
     desc = gm.make_desc(M, d, H, d, "swiglu", torch.bfloat16)
     assert gm.workspace_bytes(desc, "fwd_infer") > gm.MLP_NOALLOC_SCRATCH_BYTES
     x = torch.zeros(M, d, dtype=torch.bfloat16, device="cuda")
