@@ -143,7 +143,12 @@ Plan plan_gemm(DType in, int64_t M, int64_t N, int64_t K, bool allow_split, bool
         best.k_per_split = (int)kps;
         best.tiles_m = (int)tm;
         best.tiles_n = (int)tn;
-        best.group_m = (int)std::min<int64_t>(tm, 8);
+        // row bands of 8 tiles, column-major inside (32 tiles on an XCD at once share 8 A and
+        // 4 B panels); with three tile columns a band of 24 tiles would straddle the XCD's
+        // rounds and its A panels be fetched again, so those walk row by row (the GPT-shape
+        // down projection and dx: 599 MB fetched for a 302 MB A; same box 247 -> 243 us,
+        // 230 -> 228 us)
+        best.group_m = tn == 3 ? 1 : (int)std::min<int64_t>(tm, 8);
         best.grid = (int)ntile;
         best.est = t;
       }
@@ -169,7 +174,8 @@ size_t partial_bytes(const Plan& p, int64_t M, int64_t N) {
 // A store-epilogue GEMM whose unsplit 8-wave 256 x 256 tiles leave its last round mostly idle
 // (the GPT-shape down projection and dx: 576 tiles = 2.25 rounds of 256), cut along M: rows
 // [0, m1) in whole rounds of those tiles, rows [m1, M) planned on their own, where split-K fills
-// the chip (GPT shape: 510 tiles of 48 K-steps, then 66 tiles split 3 ways, one round of 16).
+// the chip or smaller tiles do (GPT shape: 510 tiles of 48 K-steps, then the other 5632 rows as
+// 132 tiles of 8-wave 256 x 128, one round).
 // A static form of what a stream-K schedule does for the last round. m1 = 0: `main` covers all.
 struct RowsPlan {
   Plan main{};
