@@ -347,11 +347,21 @@ constexpr int ring_stages(int stage_bytes, int tile_elems) {
   return n > 4 ? 4 : n;
 }
 
-// LDS of one workgroup's ring (NS stages of a BM x BN tile's K-step).
+// A stages beyond the ring's NS: tiles of 128 x 128 and below (two workgroups per CU) have a
+// K loop of few MFMAs per step, so each step waits on its A operand (streamed from HBM; B, the
+// weights, stays in L2); the 16 KB their two-stage ring leaves of half the LDS hold one more.
+template <typename T, int BM, int BN>
+constexpr int extra_a_stages() {
+  constexpr int stage = (BM + BN) * StepGeo<T>::ROWB, a = BM * StepGeo<T>::ROWB;
+  constexpr int ns = ring_stages(stage, BM * BN);
+  return (BM * BN <= 128 * 128 && ns < 4 && ns * stage + a <= 80 * 1024) ? 1 : 0;
+}
+
+// LDS of one workgroup's ring (NS stages of a BM x BN tile's K-step, plus the extra A stages).
 template <typename T, int BM, int BN>
 constexpr int dma_ring_bytes() {
   constexpr int stage = (BM + BN) * StepGeo<T>::ROWB;
-  return ring_stages(stage, BM * BN) * stage;
+  return ring_stages(stage, BM * BN) * stage + extra_a_stages<T, BM, BN>() * BM * StepGeo<T>::ROWB;
 }
 
 // One output tile of a GEMM: tile `item` of p's grid (tiles_m x tiles_n x splits, the split
@@ -384,7 +394,16 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
   static_assert(NSUB % 2 == 0, "fragment double buffer alternates per substep");
   static_assert(A_KMAJ || BK == MNTileDma<BM, WAVES>::KROWS, "MN-major stage depth");
 
-  static_assert(NS * STAGE == dma_ring_bytes<T, BM, BN>(), "ring size");
+  // XA = 1: A has a ring of its own, NSA = NS + 1 stages, and B one of NS (A stages first,
+  // then B's); the DMAs of K-step kt+NSA (A) and kt+NS (B) go out in step kt, B's first, so the
+  // wait for step kt+1's B leaves the A of step kt+2 in flight
+  constexpr int XA = extra_a_stages<T, BM, BN>();
+  static_assert(XA == 0 || WAVES == 4, "the extra A stage serves the one-wave-per-SIMD tiles");
+  constexpr int NSA = NS + XA;
+  constexpr int B_BYTES = BN * ROWB;
+  static_assert(NS * STAGE + XA * A_BYTES == dma_ring_bytes<T, BM, BN>(), "ring size");
+  auto a_stage = [&](int st) -> char* { return XA ? smem + st * A_BYTES : smem + st * STAGE; };
+  auto b_stage = [&](int st) -> char* { return XA ? smem + NSA * A_BYTES + st * B_BYTES : smem + st * STAGE + A_BYTES; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -453,52 +472,60 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
   const int b_split = (!B_KMAJ && p.B1 != nullptr) ? p.b_split : INT_MAX;
   constexpr int N_DMA = (A_KMAJ ? KTileDma<T, BM, DW>::kInst : MNTileDma<BM, DW>::kInst) +
                         (B_KMAJ ? KTileDma<T, BN, DW>::kInst : MNTileDma<BN, DW>::kInst);
-  static_assert((NS - 1) * N_DMA < 64, "vmcnt range");
+  constexpr int KIA = A_KMAJ ? KTileDma<T, BM, DW>::kInst : MNTileDma<BM, DW>::kInst;
+  static_assert((NS - 1) * N_DMA + XA * KIA < 64, "vmcnt range");
 
-  // K-step kt into ring stage `stage`; steps past the end load zeros.
+  // A / B of K-step kt into A / B ring stage `st`; steps past the end load zeros.
+  auto issue_a = [&](int kt, int st) {
+    if (!dma_wave) return;
+    if constexpr (A_KMAJ) {
+      ka.issue(a_stage(st), wave, lane, kt * BK, kend - kbeg, locA);
+    } else {
+      na.issue(a_stage(st), wave, lane, kbeg + kt * BK, kend, (int64_t)kt * BK * p.lda * ES, INT_MAX, 0);
+    }
+  };
+  auto issue_b = [&](int kt, int st) {
+    if (!dma_wave) return;
+    if constexpr (B_KMAJ) {
+      kb.issue(b_stage(st), wave, lane, kt * BK, kend - kbeg, locB);
+    } else {
+      nb.issue(b_stage(st), wave, lane, kbeg + kt * BK, kend, (int64_t)kt * BK * p.ldb * ES, b_split, b_second);
+    }
+  };
+  // K-step kt into ring stage `stage` (XA = 0)
   auto issue = [&](int kt, int stage) {
     if (!dma_wave) return;
-    char* sa = smem + stage * STAGE;
-    char* sb = sa + A_BYTES;
-    if constexpr (A_KMAJ) {
-      ka.issue(sa, wave, lane, kt * BK, kend - kbeg, locA);
-    } else {
-      na.issue(sa, wave, lane, kbeg + kt * BK, kend, (int64_t)kt * BK * p.lda * ES, INT_MAX, 0);
-    }
-    if constexpr (B_KMAJ) {
-      kb.issue(sb, wave, lane, kt * BK, kend - kbeg, locB);
-    } else {
-      nb.issue(sb, wave, lane, kbeg + kt * BK, kend, (int64_t)kt * BK * p.ldb * ES, b_split, b_second);
-    }
+    issue_a(kt, stage);
+    issue_b(kt, stage);
     // the issuing wave is now behind its partner on the SIMD: it wins issue ties until the barrier
     if constexpr (DW < WAVES) __builtin_amdgcn_s_setprio(1);
   };
 
-  // DMA d (0 .. N_DMA-1: A's, then B's) of issue(kt, stage) alone
-  constexpr int KIA = A_KMAJ ? KTileDma<T, BM, DW>::kInst : MNTileDma<BM, DW>::kInst;
-  // FAST: the K-step is wholly in range and on one side of b_split, and K-major tiles are
-  // interior (the main part of the K loop): scalar bases, no per-lane work
-  auto issue_one = [&](int kt, int stage, int d, auto fast) {
+  // DMA d (0 .. N_DMA-1: A's, then B's) alone: A's of K-step kta into A stage sta, B's of
+  // K-step ktb into B stage stb. FAST: the K-step is wholly in range and on one side of
+  // b_split, and K-major tiles are interior (the main part of the K loop): scalar bases, no
+  // per-lane work
+  auto issue_one = [&](int kta, int sta, int ktb, int stb, int d, auto fast) {
     if (!dma_wave) return;
-    char* sa = smem + stage * STAGE;
-    char* sb = sa + A_BYTES;
+    char* sa = a_stage(sta);
+    char* sb = b_stage(stb);
     if constexpr (decltype(fast)::value) {
       if (d < KIA) {
-        if constexpr (A_KMAJ) ka.issue_fast_i(sa, wave, d, kt * BK);
-        else na.issue_fast_i(sa, wave, d, na.base + (int64_t)kt * BK * p.lda * ES);
+        if constexpr (A_KMAJ) ka.issue_fast_i(sa, wave, d, kta * BK);
+        else na.issue_fast_i(sa, wave, d, na.base + (int64_t)kta * BK * p.lda * ES);
       } else {
-        if constexpr (B_KMAJ) kb.issue_fast_i(sb, wave, d - KIA, kt * BK);
+        if constexpr (B_KMAJ) kb.issue_fast_i(sb, wave, d - KIA, ktb * BK);
         else nb.issue_fast_i(sb, wave, d - KIA,
-                             nb.base + (int64_t)kt * BK * p.ldb * ES + (kbeg + kt * BK >= b_split ? b_second : 0));
+                             nb.base + (int64_t)ktb * BK * p.ldb * ES + (kbeg + ktb * BK >= b_split ? b_second : 0));
       }
       return;
     }
     if (d < KIA) {
-      if constexpr (A_KMAJ) ka.issue_i(sa, wave, lane, d, kt * BK, kend - kbeg, locA);
-      else na.issue_i(sa, wave, lane, d, kbeg + kt * BK, kend, (int64_t)kt * BK * p.lda * ES, INT_MAX, 0);
+      if constexpr (A_KMAJ) ka.issue_i(sa, wave, lane, d, kta * BK, kend - kbeg, locA);
+      else na.issue_i(sa, wave, lane, d, kbeg + kta * BK, kend, (int64_t)kta * BK * p.lda * ES, INT_MAX, 0);
     } else {
-      if constexpr (B_KMAJ) kb.issue_i(sb, wave, lane, d - KIA, kt * BK, kend - kbeg, locB);
-      else nb.issue_i(sb, wave, lane, d - KIA, kbeg + kt * BK, kend, (int64_t)kt * BK * p.ldb * ES, b_split, b_second);
+      if constexpr (B_KMAJ) kb.issue_i(sb, wave, lane, d - KIA, ktb * BK, kend - kbeg, locB);
+      else nb.issue_i(sb, wave, lane, d - KIA, kbeg + ktb * BK, kend, (int64_t)ktb * BK * p.ldb * ES, b_split, b_second);
     }
   };
 
@@ -522,7 +549,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
   constexpr bool ROLL = M16 && NI >= 8;
   u32x4 fa[2][MI][KC], fb[ROLL ? 1 : 2][NI][KC];
   auto read_a = [&](int stage, int s, int slot) {
-    const char* sa = smem + stage * STAGE;
+    const char* sa = a_stage(stage);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -535,7 +562,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
     }
   };
   auto read_b = [&](int stage, int s, int slot, int j) {
-    const char* sb = smem + stage * STAGE + A_BYTES;
+    const char* sb = b_stage(stage);
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       if constexpr (B_KMAJ && M16) fb[slot][j][c] = KTileDma<T, BN, WAVES>::read_block(sb, b_base[j], frow, 4 * s + fq);
@@ -544,10 +571,10 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
       else fb[slot][j][c] = MNTileDma<BN, WAVES>::read(sb, b_base[j], s, lane);
     }
   };
-  auto read_frags = [&](int stage, int s, int slot) {
-    read_a(stage, s, slot);
+  auto read_frags = [&](int stage_a, int stage_b, int s, int slot) {
+    read_a(stage_a, s, slot);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) read_b(stage, s, ROLL ? 0 : slot, j);
+    for (int j = 0; j < NI; ++j) read_b(stage_b, s, ROLL ? 0 : slot, j);
   };
 
   using AccV = typename std::conditional<M16, f32x4, f32x16>::type;
@@ -591,7 +618,8 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
         if constexpr (DMA_COLS > 0) {
           if (kt_dma >= 0 && j < DMA_COLS) {
 #pragma unroll
-            for (int d = j * N_DMA / DMA_COLS; d < (j + 1) * N_DMA / DMA_COLS; ++d) issue_one(kt_dma, stage_dma, d, fast);
+            for (int d = j * N_DMA / DMA_COLS; d < (j + 1) * N_DMA / DMA_COLS; ++d)
+              issue_one(kt_dma, stage_dma, kt_dma, stage_dma, d, fast);
           }
         }
       }
@@ -601,12 +629,25 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
   constexpr int NRA = (A_KMAJ ? KC : 2) * MI;     // LDS reads of the A fragments of a substep
 
   if (nk > 0) {
+    if constexpr (XA) {
+      // A of step 0, then (B of step s, A of step s + 1) for s < NS: the order of the loop's
+      // issue groups; all but the first group's B and what precedes it may stay in flight.
+      // (Written out: as a loop, the compiler took the DMA bases for per-lane values.)
+      static_assert(NS == 2, "the extra A stage comes with a two-stage ring");
+      issue_a(0, 0);
+      issue_b(0, 0);
+      issue_a(1, 1);
+      issue_b(1, 1);
+      issue_a(2, 2);
+      wait_vmcnt<KIA + (NS - 1) * N_DMA>();   // step 0 landed
+    } else {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) issue(s, s);
-    wait_vmcnt<(NS - 1) * N_DMA>();   // step 0 landed
+      for (int s = 0; s < NS; ++s) issue(s, s);
+      wait_vmcnt<(NS - 1) * N_DMA>();   // step 0 landed
+    }
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
-    read_frags(0, 0, 0);
+    read_frags(0, 0, 0, 0);
     // drained here so that the loop header's LDS waits are counted from the loop body alone:
     // the prologue issues these reads in another order, and a wait merged over both paths
     // would be lgkmcnt(0) before the first MFMA of every K-step (waiting for the last B
@@ -621,19 +662,20 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
   const int nk_full = (kend - kbeg) / BK;
   const bool fast_ok = (!A_KMAJ || ka.interior) && (!B_KMAJ || kb.interior) &&
                        (b_split == INT_MAX || b_split <= kbeg || b_split >= kend || (b_split - kbeg) % BK == 0);
-  const int nk_main = fast_ok ? max(0, min(nk, nk_full - NS)) : 0;
-  int cur = 0;
+  const int nk_main = fast_ok ? max(0, min(nk, nk_full - NSA)) : 0;
+  int cur = 0, cur_a = 0;   // B's (and with XA = 0 A's) ring stage of step kt; A's with XA = 1
   auto k_step = [&](int kt, auto fast) {
     const int nxt = cur + 1 == NS ? 0 : cur + 1;
+    const int nxt_a = XA ? (cur_a + 1 == NSA ? 0 : cur_a + 1) : nxt;
     // substeps 0 .. NSUB-2: read substep s+1's fragments while multiplying substep s
 #pragma unroll
     for (int s = 0; s + 1 < NSUB; ++s) {
       if constexpr (ROLL) {
-        read_a(cur, s + 1, (s + 1) & 1);
+        read_a(cur_a, s + 1, (s + 1) & 1);
         mma_roll(s & 1, cur, s + 1, -1, 0, fast);
         interleave_roll<MI, NI, RB, NRA>();
       } else {
-        read_frags(cur, s + 1, (s + 1) & 1);
+        read_frags(cur_a, cur, s + 1, (s + 1) & 1);
         mma_all(s & 1);
         interleave<N_MMA, N_RD, 0>();
       }
@@ -642,28 +684,38 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
     // the barrier every wave is done reading this stage, which takes step kt+NS
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (DW < WAVES) __builtin_amdgcn_s_setprio(0);
-    wait_vmcnt<(NS - 2) * N_DMA>();
+    // XA = 1: step kt+1's B went out in the group of step kt+1-NS, before that group's A (of
+    // step kt+2) and the NS-2 groups after it; its A went out a group earlier
+    wait_vmcnt<(NS - 2) * N_DMA + XA * KIA>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
     if constexpr (ROLL) {
       if constexpr (DMA_COLS == 0) issue(kt + NS, cur);
-      read_a(nxt, 0, 0);
+      read_a(nxt_a, 0, 0);
       mma_roll((NSUB - 1) & 1, nxt, 0, kt + NS, cur, fast);
       interleave_roll<MI, NI, RB, NRA>();
     } else {
       if constexpr (WAVES == 4) {
         // one wave per SIMD: a burst would idle the matrix pipe, so the DMAs go one at a time
         // and the interleave pattern places them between the MFMAs
+        if constexpr (XA) {
 #pragma unroll
-        for (int d = 0; d < N_DMA; ++d) issue_one(kt + NS, cur, d, fast);
+          for (int d = KIA; d < N_DMA; ++d) issue_one(0, 0, kt + NS, cur, d, fast);
+#pragma unroll
+          for (int d = 0; d < KIA; ++d) issue_one(kt + NSA, cur_a, 0, 0, d, fast);
+        } else {
+#pragma unroll
+          for (int d = 0; d < N_DMA; ++d) issue_one(kt + NS, cur, kt + NS, cur, d, fast);
+        }
       } else {
         issue(kt + NS, cur);
       }
-      read_frags(nxt, 0, 0);
+      read_frags(nxt_a, nxt, 0, 0);
       mma_all((NSUB - 1) & 1);
       interleave<N_MMA, N_RD, N_DMA>();
     }
     cur = nxt;
+    cur_a = nxt_a;
   };
   int kt = 0;
   // (not for the 4-wave 256x256 tiles: a second copy of their loop costs them registers)
