@@ -347,9 +347,10 @@ constexpr int ring_stages(int stage_bytes, int tile_elems) {
   return n > 4 ? 4 : n;
 }
 
-// A stages beyond the ring's NS: tiles of 128 x 128 and below (two workgroups per CU) have a
-// K loop of few MFMAs per step, so each step waits on its A operand (streamed from HBM; B, the
-// weights, stays in L2); the 16 KB their two-stage ring leaves of half the LDS hold one more.
+// A stages beyond the ring's NS: tiles of 128 x 128 and below (two workgroups per CU) run few
+// MFMAs per K-step, so in their large-M products (the fp8 GEMMs of the GPT-shape MLP, where A is
+// streamed from HBM and B, the weights, stays in L2) each step waited on its A operand; the
+// 16 KB their two-stage ring leaves of half the LDS hold one more A stage.
 template <typename T, int BM, int BN>
 constexpr int extra_a_stages() {
   constexpr int stage = (BM + BN) * StepGeo<T>::ROWB, a = BM * StepGeo<T>::ROWB;

@@ -73,12 +73,23 @@ def grouped_order(stages: list[str], names) -> list[str]:
     return res
 
 
+_BLOCK_COMMENT = re.compile(r"/\*.*?\*/", re.S)
+_LINE_COMMENT = re.compile(r"//[^\n]*")
+
+
+def code_text(src: str) -> str:
+    """A C++ source with its comments and blank or trailing space removed: what the hash of the
+    kernel sources covers, so that a profile stays current across edits of comments only."""
+    src = _LINE_COMMENT.sub("", _BLOCK_COMMENT.sub("", src))
+    return "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+
+
 def kernel_sources_sha256() -> str:
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(_HERE, "csrc", "*"))):
         if f.endswith((".hip", ".hpp")):
             h.update(os.path.basename(f).encode())
-            h.update(open(f, "rb").read())
+            h.update(code_text(open(f, encoding="utf-8").read()).encode())
     return h.hexdigest()
 
 

@@ -125,3 +125,19 @@ def test_rows_split_store_gemm_is_one_stage():
     steps = ps._per_step([(i, n, 1.0) for i, n in enumerate(names)], ps.STAGE_ORDER_GATED)
     assert len(steps) == 2
     assert [len(steps[0][st]) for st in ps.STAGE_ORDER_GATED] == [1, 3, 1, 2, 3, 2]
+
+
+def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    """The kernel-source hash that marks a profile current covers the code, not its comments or
+    blank lines: a comment edit keeps it, a code edit changes it."""
+    d = tmp_path / "csrc"
+    d.mkdir()
+    src = "// header\nint f(int x) {  /* note */\n  return x + 1;  // inc\n}\n"
+    (d / "k.hip").write_text(src)
+    monkeypatch.setattr(ps, "_HERE", str(tmp_path))
+    h0 = ps.kernel_sources_sha256()
+    (d / "k.hip").write_text("// header, reworded\n\nint f(int x) {  /* another\n note */\n  return x + 1;\n}\n")
+    assert ps.kernel_sources_sha256() == h0
+    (d / "k.hip").write_text(src.replace("x + 1", "x + 2"))
+    assert ps.kernel_sources_sha256() != h0
+    assert ps.code_text("a; // c\n/* b\n c */ d;\n\n") == "a;\n d;"
