@@ -167,6 +167,19 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
     quot_rn_n<8>(dpre, sd, rd, y);
     *reinterpret_cast<u32x2*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) =
         u32x2{f32x4_to_fp8<true>(y[0], y[1], y[2], y[3]), f32x4_to_fp8<true>(y[4], y[5], y[6], y[7])};
+    if (p.C1) {   // relu(pre)^2 codes for dW2, the arithmetic of the 2-D quantizer's relu^2 mode
+      const float sp = *p.s_c1;
+      const float rp = __fdiv_rn(1.0f, sp);
+      float post[8], z[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float t = fmaxf(pre[r], 0.0f);
+        post[r] = t * t;
+      }
+      quot_rn_n<8>(post, sp, rp, z);
+      *reinterpret_cast<u32x2*>(elem_ptr<e4m3>(p.C1, m, p.ldc1, n)) =
+          u32x2{f32x4_to_fp8<false>(z[0], z[1], z[2], z[3]), f32x4_to_fp8<false>(z[4], z[5], z[6], z[7])};
+    }
   }
 }
 

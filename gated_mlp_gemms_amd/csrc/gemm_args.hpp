@@ -23,7 +23,7 @@ enum Epi : int {
                     // C0 = e4m3(post / *s_post); *amax = max(*amax, max post)
   EPI_F8DACT = 7,   // dpre = alpha * acc * 2 max(pre, 0), pre <- aux (bf16 or fp32);
                     // C0 = e5m2(dpre / *s_post) (s_post holds the dpre scale here);
-                    // *amax = max(*amax, max |dpre|)
+                    // *amax = max(*amax, max |dpre|); C1 set: C1 = e4m3(relu(pre)^2 / *s_c1)
 };
 
 struct GemmArgs {
@@ -42,6 +42,7 @@ struct GemmArgs {
   const float* s_post; float* amax;
   int k_per_split; float* partial;
   int tiles_m, tiles_n, group_m;
+  const float* s_c1;   // F8DACT: scale of the e4m3 relu(pre)^2 codes written to C1
 };
 
 // Up to kGroupMax independent GEMMs run by one launch (gemm_dma_group_kernel): member j covers

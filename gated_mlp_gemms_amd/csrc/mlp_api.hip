@@ -848,6 +848,11 @@ mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void*
     a.alpha_dev1 = f->s_w2;
     a.s_post = f->s_dpre;
     a.amax = f->dpre_amax;
+    if (dw2) {   // relu(pre)^2's e4m3 codes, row-major, from the pre-activation this GEMM reads
+      a.C1 = w + L.pt;   // free until dW1 transposes dpre_q into it
+      a.ldc1 = H;
+      a.s_c1 = f->s_post;
+    }
     const Plan p = plan_quantizing(DT_F8G, M, H, O);
     MLP_TRY(gemm(DT_F8G, DT_F32, NT, EPI_F8DACT, p, a, M, H, O, nullptr, s, "fp8 d-activation GEMM"));
   } else if (dw2) {
@@ -857,8 +862,14 @@ mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void*
   }
   if (dw2) {   // dW2 (+)= dm dout_q^T post_q, post_q = e4m3(relu(pre)^2 / s_post)
     StageScope st(MLP_STAGE_DW_DOWN, s);
-    MLP_TRY(hip_status(run_quantize_fp8_2d(DT_F32, pre, M, H, H, 1, 0, f->s_post, nullptr, w + L.postt, Mp, s),
-                       "quantize relu(pre)^2"));
+    // transposed codes: from the d-activation GEMM's row-major ones (a 1-byte transpose), or
+    // formed here from the fp32 pre-activation when that GEMM did not run
+    if (need_dpre)
+      MLP_TRY(hip_status(run_quantize_fp8_2d(DT_E4M3, w + L.pt, M, H, H, 0, 0, nullptr, nullptr, w + L.postt, Mp, s),
+                         "transpose relu(pre)^2 codes"));
+    else
+      MLP_TRY(hip_status(run_quantize_fp8_2d(DT_F32, pre, M, H, H, 1, 0, f->s_post, nullptr, w + L.postt, Mp, s),
+                         "quantize relu(pre)^2"));
     GemmArgs a = base_args(d);
     a.A = gt;
     a.lda = Mp;
