@@ -149,8 +149,146 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const GemmArgs p) {
   }
 }
 
+// The gated product with the token rows staged in LDS and shared. A workgroup of CB x KQ waves
+// owns CB column blocks of 16 units; wave (cb, kq) streams the gate and up rows of block cb over
+// the kq-th part of K, NBUF 128-wide blocks ahead, as the kernel above does, but takes its token
+// fragments from LDS: the whole of x (16 rows, zeros past M and K) is staged there once, in
+// fragment order (one 16-byte slot per K block, MFMA and lane: 4 KB per block), so the rows
+// cross from L2 once per CB column blocks instead of once per block. The KQ partial sums of a
+// column block meet in LDS (over the staged x, no longer read) and are added in kq order.
+constexpr int kLdsBlocks = 32;   // K up to 4096: 128 KB of LDS
+
+template <typename T, int CB, int KQ, int NBUF>
+__global__ __launch_bounds__(64 * CB * KQ, 1) void skinny_gated_lds_kernel(const GemmArgs p) {
+  constexpr int WAVES = CB * KQ;
+  __shared__ u32x4 xs[kLdsBlocks * 4 * 64];
+  static_assert(WAVES * 2 * 64 <= kLdsBlocks * 4 * 64, "partial sums fit the staged x's LDS");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int cb = wave % CB, kq = wave / CB;
+  const int nblk = (p.K + kKBlock - 1) / kKBlock;
+
+  // x -> LDS: chunk idx of 8 elements runs along each row (coalesced reads); row `row`, chunk kc
+  // of its nblk * 16 goes to slot ((kc / 16) * 4 + (kc % 16) / 4) * 64 + (kc % 4) * 16 + row
+  {
+    const int per_row = nblk * 16, total = 16 * per_row;
+    constexpr int BATCH = 2;   // loads in flight per thread before their LDS stores
+    for (int base = threadIdx.x; base < total; base += BATCH * 64 * WAVES) {
+      u32x4 v[BATCH];
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const int idx = base + j * 64 * WAVES;
+        const int row = idx / per_row, kc = idx - row * per_row, k = kc * 8;
+        const bool ok = idx < total && row < p.M && k < p.K;
+        v[j] = ok ? *reinterpret_cast<const u32x4*>(elem_ptr<T>(p.A, row, p.lda, k)) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const int idx = base + j * 64 * WAVES;
+        if (idx < total) {
+          const int row = idx / per_row, kc = idx - row * per_row;
+          xs[((kc >> 4) * 4 + ((kc & 15) >> 2)) * 64 + (kc & 3) * 16 + row] = v[j];
+        }
+      }
+    }
+  }
+
+  const int n = (blockIdx.x * CB + cb) * 16 + r;   // this lane's gate / up row (unit)
+  const bool row_ok = n < p.N;
+  const char* wrow[2] = {reinterpret_cast<const char*>(elem_ptr<T>(p.B0, row_ok ? n : 0, p.ldb, 0)),
+                         reinterpret_cast<const char*>(elem_ptr<T>(p.B1, row_ok ? n : 0, p.ldb, 0))};
+  const int b0 = kq * nblk / KQ, nb = (kq + 1) * nblk / KQ - b0;
+  u32x4 wa[NBUF][2][4];
+  auto load = [&](int b, int s) {   // block b into buffer s; past K or N: zeros
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int k = b * kKBlock + c * 32 + q * 8;
+      const bool ok = row_ok && k < p.K;
+      const int64_t off = (int64_t)k * (int64_t)sizeof(T);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        wa[s][m][c] = ok ? *reinterpret_cast<const u32x4*>(wrow[m] + off) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  f32x4 acc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+  auto compute = [&](int b, int s) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 xa = xs[(b * 4 + c) * 64 + lane];
+      Mma16<T>::mma(xa, wa[s][0][c], acc[0]);
+      Mma16<T>::mma(xa, wa[s][1][c], acc[1]);
+    }
+  };
+  // the first weight blocks go out before the wait for the staged x
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j)
+    if (j < nb) load(b0 + j, j);
+  __syncthreads();
+  // NBUF buffers in rotation, indexed by constants only: the i-th block of the part lives in
+  // buffer i % NBUF
+  int i = 0;
+  for (; i + NBUF <= nb; i += NBUF) {
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      if (i + j + NBUF - 1 < nb) load(b0 + i + j + NBUF - 1, (j + NBUF - 1) % NBUF);
+      compute(b0 + i + j, j);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NBUF; ++j)
+    if (i + j < nb) compute(b0 + i + j, j);
+
+  // partial sums over the staged x (every wave is done reading it)
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(xs);   // [KQ][CB][2][64]
+  red[((kq * CB + cb) * 2 + 0) * 64 + lane] = acc[0];
+  red[((kq * CB + cb) * 2 + 1) * 64 + lane] = acc[1];
+  __syncthreads();
+  if (kq != 0 || !row_ok) return;
+  f32x4 s0 = red[(cb * 2 + 0) * 64 + lane], s1 = red[(cb * 2 + 1) * 64 + lane];
+#pragma unroll
+  for (int w = 1; w < KQ; ++w) {
+    s0 += red[((w * CB + cb) * 2 + 0) * 64 + lane];
+    s1 += red[((w * CB + cb) * 2 + 1) * 64 + lane];
+  }
+  float alpha = p.alpha;
+  if (p.alpha_dev0) alpha *= *p.alpha_dev0;
+  if (p.alpha_dev1) alpha *= *p.alpha_dev1;
+  // lane l holds tokens 4 q + t (t = 0..3) of unit n
+  float v[4], u[4], o[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    v[t] = alpha * s0[t];
+    u[t] = alpha * s1[t];
+  }
+  auto put = [&](void* base, int64_t ld, int col, const float (&val)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tok = 4 * q + t;
+      if (tok < p.M) *reinterpret_cast<uint16_t*>(elem_ptr<T>(base, tok, ld, col)) = (uint16_t)Bits16<T>::from_f32(val[t]);
+    }
+  };
+  if (p.flags & 1) {
+    put(p.aux, p.ld_aux, n, v);
+    put(p.aux, p.ld_aux, p.half + n, u);
+  }
+  if (p.flags & 2) {
+    gated_act<4>(p.act, p.gate_mult, p.gate_inside, v, u, o);
+    put(p.C0, p.ldc0, n, o);
+  }
+}
+
 template <typename T, int EPI>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
+  if (EPI == EPI_GATED && a.M > 8 && a.K <= kLdsBlocks * kKBlock) {
+    // 3 column blocks x 4 parts of K: 48 units per workgroup of 12 waves, one per CU (128 KB of
+    // LDS; 230 workgroups at H = 11008). Measured against the kernel above at the LLaMA widths:
+    // 16 tokens 63.9 -> 60.5 us per inference forward, 8 tokens even, 1-4 tokens 1.4 us slower
+    // (the x rows it saves are few there), hence the 8-token threshold. 4 x 4 blocks (172
+    // workgroups) streamed slower than 230 on more CUs.
+    hipLaunchKernelGGL((skinny_gated_lds_kernel<T, 3, 4, 3>), dim3((a.N + 47) / 48), dim3(768), 0, s, a);
+    return hipGetLastError();
+  }
   const int groups = (a.N + 15) / 16;   // column blocks of 16 units
   if (groups >= kTwoBlocksFrom) {
     // wide outputs: two column blocks per workgroup halve the re-reads of the token rows
