@@ -231,6 +231,9 @@ SKINNY = [
     _w("relu_sq", "bf16", 5, 776, 3080, 264, down_mult=1.5, seed=22),
     _w("geglu", "f16", 13, 520, 712, 136, seed=23),
     _w("swiglu", "bf16", 1, 264, 1400, 8, seed=24),
+    # 9 to 16 tokens with K <= 4096: the gated product stages x in LDS, shared by 3 column blocks
+    # x 4 parts of K; K = 1000 ends in a partial block, 1000 units in a partial workgroup of 48
+    _w("swiglu", "bf16", 11, 1000, 1000, 72, gate_mult=1.125, down_mult=2.0, seed=25),
 ]
 
 
