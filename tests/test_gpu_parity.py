@@ -234,6 +234,9 @@ SKINNY = [
     # 9 to 16 tokens with K <= 4096: the gated product stages x in LDS, shared by 3 column blocks
     # x 4 parts of K; K = 1000 ends in a partial block, 1000 units in a partial workgroup of 48
     _w("swiglu", "bf16", 11, 1000, 1000, 72, gate_mult=1.125, down_mult=2.0, seed=25),
+    # 10 tokens, K = 2056 for the gated product (LDS-staged, 5000 units), K = 5000 for the down
+    # projection (the x-streaming kernel: partial last blocks, 2056 outputs)
+    _w("swiglu", "bf16", 10, 2056, 5000, 2056, down_mult=1.5, seed=26),
 ]
 
 
