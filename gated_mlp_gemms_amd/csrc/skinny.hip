@@ -11,6 +11,8 @@
 //  * the waves' partial sums meet in LDS and are added in wave order (deterministic), then the
 //    first wave runs the epilogue: store, activation, or gated activation (and the pre-activation
 //    when training), with the same activation functions as the GEMM epilogues.
+// Above 8 tokens the gated product takes a second form (skinny_gated_lds_kernel below) that
+// stages the token rows in LDS once per workgroup and shares them between column blocks.
 #include "common.hpp"
 #include "gemm_kernel.hpp"
 #include "launch.hpp"
