@@ -311,9 +311,8 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 
 // fp8 codes of a [rows, cols] matrix, row-major and / or transposed, one 128 x 128 tile of codes
 // at a time through LDS (as 32-bit words, rows padded by one word). Every global access of a wave
-// covers whole 128-byte lines: a bf16 source row of the tile is 16 lanes x 16 bytes, a code row
-// 8 lanes x 16 bytes, and each transposed output column's 128 rows are written by 8 lanes of one
-// wave. For the transposed stores a lane reads a 16-row x 4-column block of codes (16 words),
+// covers whole 128-byte lines: a source row of the tile is 16 lanes x 16 (bf16) or 32 (fp32)
+// bytes, and each transposed output column's 128 rows are written by 8 lanes of one wave. For the transposed stores a lane reads a 16-row x 4-column block of codes (16 words),
 // regroups its bytes into the 4 columns in registers, and writes 16 bytes to each column. Source
 // rows past `rows` (up to the transposed leading dimension) give code 0, which pads the
 // transposed output.
@@ -322,9 +321,9 @@ __device__ __forceinline__ uint32_t byte_col(uint32_t r0, uint32_t r1, uint32_t 
   return ((r0 >> sh) & 0xffu) | (((r1 >> sh) & 0xffu) << 8) | (((r2 >> sh) & 0xffu) << 16) | (((r3 >> sh) & 0xffu) << 24);
 }
 
-// SRC: 0 existing codes (copied), 1 bf16 values, 2 fp32 values. tile_amax (values only; may be
-// NULL): slot t = row tile * n_ct + column tile of each tile with rows inside the matrix gets the
-// tile's max |v| (of the source values, before relu_sq). amax_only: record tile_amax and write no
+// SRC: 1 bf16 values, 2 fp32 values. tile_amax (may be NULL): slot t = row tile * n_ct + column
+// tile of each tile with rows inside the matrix gets the tile's max |v| (of the source values,
+// before relu_sq). amax_only: record tile_amax and write no
 // codes (the scale is not read).
 template <int SRC>
 __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t rows, int64_t cols, int64_t ld_src,
@@ -335,76 +334,64 @@ __global__ __launch_bounds__(256) void quant2d_kernel(const void* src, int64_t r
   __shared__ uint32_t tile[128 * TW];
   __shared__ float wave_max[4];
   const int tid = threadIdx.x;
-  constexpr bool CODES = SRC == 0;
-  const float sc = (CODES || amax_only) ? 1.0f : *scale;
+  const float sc = amax_only ? 1.0f : *scale;
   const float rsc = __fdiv_rn(1.0f, sc);
   for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
     const int64_t r0 = (t / n_ct) * 128, c0 = (t % n_ct) * 128;
-    if constexpr (CODES) {   // 8 lanes x 16 codes per row, 32 rows per pass
+    // 16 lanes x 8 values per row, 16 rows per pass
+    float m = 0.0f;
 #pragma unroll
-      for (int pass = 0; pass < 4; ++pass) {
-        const int lr = (tid >> 3) + 32 * pass, lc = (tid & 7) * 16;
-        const int64_t r = r0 + lr, c = c0 + lc;
-        u32x4 x = {0, 0, 0, 0};
-        if (r < rows && c < cols) x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(src) + r * ld_src + c);
+    for (int pass = 0; pass < 8; ++pass) {
+      const int lr = (tid >> 4) + 16 * pass, lc = (tid & 15) * 8;
+      const int64_t r = r0 + lr, c = c0 + lc;
+      uint32_t lo = 0, hi = 0;
+      if (r < rows && c < cols) {
+        float in[8];
+        if constexpr (SRC == 2) {
+          const u32x4* q = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(src) + r * ld_src + c);
+          const u32x4 x0 = q[0], x1 = q[1];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) tile[lr * TW + lc / 4 + q] = x[q];
-      }
-    } else {                 // 16 lanes x 8 values per row, 16 rows per pass
-      float m = 0.0f;
+          for (int k = 0; k < 4; ++k) { in[k] = __uint_as_float(x0[k]); in[4 + k] = __uint_as_float(x1[k]); }
+        } else {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(src) + r * ld_src + c);
 #pragma unroll
-      for (int pass = 0; pass < 8; ++pass) {
-        const int lr = (tid >> 4) + 16 * pass, lc = (tid & 15) * 8;
-        const int64_t r = r0 + lr, c = c0 + lc;
-        uint32_t lo = 0, hi = 0;
-        if (r < rows && c < cols) {
-          float in[8];
-          if constexpr (SRC == 2) {
-            const u32x4* q = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(src) + r * ld_src + c);
-            const u32x4 x0 = q[0], x1 = q[1];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) { in[k] = __uint_as_float(x0[k]); in[4 + k] = __uint_as_float(x1[k]); }
-          } else {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(src) + r * ld_src + c);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) in[k] = bf16_bits_to_f32((k & 1) ? (x[k >> 1] >> 16) : (x[k >> 1] & 0xffffu));
-          }
-#pragma unroll
-          for (int k = 0; k < 8; ++k) m = fmaxf(m, __builtin_fabsf(in[k]));
-          if (amax_only) continue;
-          float y[8];
-          if (relu_sq) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              const float r = fmaxf(in[k], 0.0f);
-              in[k] = r * r;
-            }
-          }
-          quot_rn_n<8>(in, sc, rsc, y);
-          if (e5m2) {
-            lo = f32x4_to_fp8<true>(y[0], y[1], y[2], y[3]);
-            hi = f32x4_to_fp8<true>(y[4], y[5], y[6], y[7]);
-          } else {
-            lo = f32x4_to_fp8<false>(y[0], y[1], y[2], y[3]);
-            hi = f32x4_to_fp8<false>(y[4], y[5], y[6], y[7]);
-          }
-          if (dst) *reinterpret_cast<u32x2*>(dst + r * cols + c) = u32x2{lo, hi};
+          for (int k = 0; k < 8; ++k) in[k] = bf16_bits_to_f32((k & 1) ? (x[k >> 1] >> 16) : (x[k >> 1] & 0xffffu));
         }
-        tile[lr * TW + lc / 4] = lo;
-        tile[lr * TW + lc / 4 + 1] = hi;
-      }
-      if (tile_amax) {
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-        if ((tid & 63) == 0) wave_max[tid >> 6] = m;
-        __syncthreads();
-        if (tid == 0 && r0 < rows)
-          tile_amax[t] = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, __builtin_fabsf(in[k]));
+        if (amax_only) continue;
+        float y[8];
+        if (relu_sq) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float r = fmaxf(in[k], 0.0f);
+            in[k] = r * r;
+          }
+        }
+        quot_rn_n<8>(in, sc, rsc, y);
+        if (e5m2) {
+          lo = f32x4_to_fp8<true>(y[0], y[1], y[2], y[3]);
+          hi = f32x4_to_fp8<true>(y[4], y[5], y[6], y[7]);
+        } else {
+          lo = f32x4_to_fp8<false>(y[0], y[1], y[2], y[3]);
+          hi = f32x4_to_fp8<false>(y[4], y[5], y[6], y[7]);
+        }
+        if (dst) *reinterpret_cast<u32x2*>(dst + r * cols + c) = u32x2{lo, hi};
       }
-      if (amax_only) {
-        __syncthreads();
-        continue;
-      }
+      tile[lr * TW + lc / 4] = lo;
+      tile[lr * TW + lc / 4 + 1] = hi;
+    }
+    if (tile_amax) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      if ((tid & 63) == 0) wave_max[tid >> 6] = m;
+      __syncthreads();
+      if (tid == 0 && r0 < rows)
+        tile_amax[t] = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+    }
+    if (amax_only) {
+      __syncthreads();
+      continue;
     }
     __syncthreads();
     if (dst_t) {   // lane: rows 16 rb .. 16 rb + 15, columns 4 cw .. 4 cw + 3 of the tile
@@ -440,10 +427,7 @@ hipError_t run_quantize_fp8_2d(DType src_t, const void* src, int64_t rows, int64
   const int grid = (int)std::min<int64_t>(n_tiles, 8192);
   uint8_t* d = reinterpret_cast<uint8_t*>(dst);
   uint8_t* dt = reinterpret_cast<uint8_t*>(dst_t);
-  if (src_t == DT_E4M3)
-    hipLaunchKernelGGL(quant2d_kernel<0>, dim3(grid), dim3(256), 0, s, src, rows, cols, ld_src, 0, 0, scale,
-                       d, dt, ld_t, n_ct, n_tiles, nullptr, 0);
-  else if (src_t == DT_BF16)
+  if (src_t == DT_BF16)
     hipLaunchKernelGGL(quant2d_kernel<1>, dim3(grid), dim3(256), 0, s, src, rows, cols, ld_src, relu_sq, e5m2,
                        scale, d, dt, ld_t, n_ct, n_tiles, nullptr, 0);
   else if (src_t == DT_F32)

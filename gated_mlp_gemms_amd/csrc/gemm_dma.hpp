@@ -337,6 +337,103 @@ struct MNTileDma {
   }
 };
 
+// ---- MN-major 8-bit operand: 128 k-rows x ROWS columns per stage -------------------------------
+// The fp8 weight-gradient products read their row-major operands ([tokens][columns] codes) along
+// the tokens, i.e. MN-major. DMA instruction j fills KPI = 1024 / ROWS k-rows (lane l: k-row
+// KPI j + l / CPR, CPR = ROWS / 16 chunks of 16 columns per k-row, physical chunk l % CPR holding
+// logical chunk (l % CPR) ^ (k-row & 7)). Fragments come out through the 8-bit transposing LDS
+// read, which hands each lane of a 16-lane group eight consecutive k of one column; the XOR puts
+// the eight k-rows one such read gathers from a logical chunk into eight different chunk
+// positions, which cover every LDS bank. In a 128-column tile an instruction's k-rows start at a
+// multiple of 8, so a lane's swizzle, and its 32-bit offset, is the same for every instruction;
+// in a 256-column tile (four k-rows per instruction) it alternates with the instruction's parity.
+// Tile columns past the matrix read its last chunk (their products reach only outputs that are
+// never stored), so the matrix width must be a multiple of 16 columns.
+template <int ROWS, int WAVES>
+struct MNTileDma8 {
+  static constexpr int KROWS = 128;
+  static constexpr int ROWB = ROWS;                      // bytes per k-row
+  static constexpr int CPR = ROWB / 16;                  // 16-byte chunks per k-row
+  static constexpr int KPI = 1024 / ROWB;                // k-rows per DMA instruction
+  static constexpr int kInst = KROWS * ROWB / 1024 / WAVES;   // per wave per stage
+  static_assert(ROWS == 128 || ROWS == 256, "128- or 256-column tiles");
+  static_assert(kInst >= 1, "tile too narrow");
+  static constexpr int NOFF = KPI == 8 ? 1 : 2;
+  uint32_t voff[NOFF];    // per lane: k-row pitch + column bytes, per instruction parity
+  const char* base;       // uniform: the matrix at the split's first k, tile column 0
+  int64_t ld_bytes;       // uniform pitch
+
+  static __device__ __forceinline__ int phys_chunk(int c, int kr) { return c ^ (kr & 7); }
+
+  // b: element (0, tile column 0); ld: row pitch in bytes; ncols: columns of the matrix from tile
+  // column 0 on (a multiple of 16)
+  __device__ __forceinline__ void init(int, int lane, const char* b, int64_t ld, int kbeg, int ncols) {
+    base = b + (int64_t)kbeg * ld;
+    ld_bytes = ld;
+    const int q = lane / CPR, p = lane % CPR;
+#pragma unroll
+    for (int o = 0; o < NOFF; ++o) {
+      const int col = min(phys_chunk(p, KPI * o + q) * 16, ncols - 16);   // the XOR is an involution
+      voff[o] = (uint32_t)(q * ld) + (uint32_t)col;
+    }
+  }
+  __device__ __forceinline__ int64_t kbase(int j) const { return (int64_t)(KPI * j) * ld_bytes; }
+  __device__ __forceinline__ uint32_t voff_of(int, int j) const {
+    if constexpr (NOFF == 1) return voff[0];
+    else return (j & 1) ? voff[1] : voff[0];
+  }
+  // K-step starting at k0 (absolute) of a range ending at kend; step_off: byte offset of this
+  // K-step from the first. (No operand here is stacked along K: the last two arguments of the
+  // 16-bit loader's interface are unused.)
+  __device__ __forceinline__ void issue(char* tile, int wave, int lane, int k0, int kend, int64_t step_off, int,
+                                        int64_t) const {
+    if (k0 + KROWS <= kend) {
+      const char* b = base + step_off;
+#pragma unroll
+      for (int i = 0; i < kInst; ++i) {
+        const int j = wave * kInst + i;
+        dma16s(b + kbase(j), voff_of(i, j), tile + j * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kInst; ++i) issue_i(tile, wave, lane, i, k0, kend, step_off, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void issue_fast_i(char* tile, int wave, int i, const char* b) const {
+    const int j = wave * kInst + i;
+    dma16s(b + kbase(j), voff_of(i, j), tile + j * 1024);
+  }
+  // DMA i of issue() alone, each k-row range-checked per lane (rows past kend load zeros)
+  __device__ __forceinline__ void issue_i(char* tile, int wave, int lane, int i, int k0, int kend, int64_t step_off,
+                                          int, int64_t) const {
+    const int j = wave * kInst + i;
+    const int k = k0 + KPI * j + lane / CPR;
+    const char* src = opaque_sgpr(base + step_off + kbase(j)) + voff_of(i, j);
+    dma16(k < kend ? (const void*)src : (const void*)g_zero_chunk, tile + j * 1024);
+  }
+  // The two 16-byte chunks of the 32-column block at tile column cb for the 32x32x64 MFMA,
+  // substep s (64 k): lane l gets k 64 s + 32 (l / 32) .. +31 of column cb + l % 32, in k order,
+  // from four transposing reads of eight k-rows. In each 16-lane group lane i points at k-row i / 2
+  // of the read's eight and at bytes 8 (i % 2) .. +7 of the group's 16 columns; the read returns
+  // to lane i column i of those eight k-rows.
+  static __device__ __forceinline__ void read8(const char* tile, int cb, int s, int lane, u32x4& lo, u32x4& hi) {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    const int i = lane & 15, g = lane >> 4;
+    const int c16 = (cb >> 4) + (g & 1);   // the group's logical chunk
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kr = 64 * s + 32 * (g >> 1) + 8 * j + (i >> 1);
+      const int off = kr * ROWB + (phys_chunk(c16, kr) << 4) + 8 * (i & 1);
+      const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(tile + off));
+      w[2 * j] = (uint32_t)v[0];
+      w[2 * j + 1] = (uint32_t)v[1];
+    }
+    lo = u32x4{w[0], w[1], w[2], w[3]};
+    hi = u32x4{w[4], w[5], w[6], w[7]};
+  }
+};
+
 // Stages in the ring: as many as fit the 160 KiB of LDS, at most 4; tiles of 128 x 128 and
 // below keep room for two workgroups per CU (a second workgroup hides latency better than a
 // deeper ring).
@@ -373,7 +470,8 @@ constexpr int dma_ring_bytes() {
 template <typename T, typename IoT, int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int WAVES>
 __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* smem) {
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must split into 2x2 waves of 32x32 blocks");
-  static_assert((A_KMAJ && B_KMAJ) || ElemTraits<T>::bytes == 2, "MN-major operands are 16-bit only");
+  static_assert((A_KMAJ && B_KMAJ) || ElemTraits<T>::bytes == 2 || (WAVES == 4 && !A_KMAJ && !B_KMAJ),
+                "8-bit operands are MN-major only in 4-wave TN tiles");
   constexpr int ES = ElemTraits<T>::bytes;
   constexpr int ROWB = StepGeo<T>::ROWB;
   constexpr int BK = ROWB / ES;
@@ -393,7 +491,9 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
   constexpr int NSUB = BK / KMMA;
   constexpr int KC = Mma<T>::kChunks;
   static_assert(NSUB % 2 == 0, "fragment double buffer alternates per substep");
-  static_assert(A_KMAJ || BK == MNTileDma<BM, WAVES>::KROWS, "MN-major stage depth");
+  // the MN-major loaders (16-bit, or 8-bit codes)
+  using MNA = typename std::conditional<ES == 1, MNTileDma8<BM, WAVES>, MNTileDma<BM, WAVES>>::type;
+  static_assert(A_KMAJ || BK == MNA::KROWS, "MN-major stage depth");
 
   // XA = 1: A has a ring of its own, NSA = NS + 1 stages, and B one of NS (A stages first,
   // then B's); the DMAs of K-step kt+NSA (A) and kt+NS (B) go out in step kt, B's first, so the
@@ -428,8 +528,11 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
   const bool dma_wave = DW == WAVES || wave < DW;
   KTileDma<T, BM, DW> ka;
   KTileDma<T, BN, DW> kb;
-  MNTileDma<BM, DW, A_KMAJ> na;   // offsets per pattern with the burst issue, per instruction when spread
-  MNTileDma<BN, DW, A_KMAJ> nb;
+  // offsets per pattern with the burst issue, per instruction when spread (16-bit)
+  using NLA = typename std::conditional<ES == 1, MNTileDma8<BM, DW>, MNTileDma<BM, DW, A_KMAJ>>::type;
+  using NLB = typename std::conditional<ES == 1, MNTileDma8<BN, DW>, MNTileDma<BN, DW, A_KMAJ>>::type;
+  NLA na;
+  NLB nb;
   // K-major tile rows: locA / locB(r) -> {base, rows past it} (rows past the matrix clamped)
   const int b_half = BN / 2;
   const int64_t ldb_bytes = (int64_t)p.ldb * ES;
@@ -471,9 +574,9 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
       ? (reinterpret_cast<const char*>(p.B1) - reinterpret_cast<const char*>(p.B0)) - (int64_t)p.b_split * p.ldb * ES
       : 0;
   const int b_split = (!B_KMAJ && p.B1 != nullptr) ? p.b_split : INT_MAX;
-  constexpr int N_DMA = (A_KMAJ ? KTileDma<T, BM, DW>::kInst : MNTileDma<BM, DW>::kInst) +
-                        (B_KMAJ ? KTileDma<T, BN, DW>::kInst : MNTileDma<BN, DW>::kInst);
-  constexpr int KIA = A_KMAJ ? KTileDma<T, BM, DW>::kInst : MNTileDma<BM, DW>::kInst;
+  constexpr int N_DMA = (A_KMAJ ? KTileDma<T, BM, DW>::kInst : NLA::kInst) +
+                        (B_KMAJ ? KTileDma<T, BN, DW>::kInst : NLB::kInst);
+  constexpr int KIA = A_KMAJ ? KTileDma<T, BM, DW>::kInst : NLA::kInst;
   static_assert((NS - 1) * N_DMA + XA * KIA < 64, "vmcnt range");
 
   // A / B of K-step kt into A / B ring stage `st`; steps past the end load zeros.
@@ -558,7 +661,9 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
         if constexpr (A_KMAJ && M16) fa[slot][i][c] = KTileDma<T, BM, WAVES>::read_block(sa, a_base[i], frow, 4 * s + fq);
         else if constexpr (A_KMAJ) fa[slot][i][c] = KTileDma<T, BM, WAVES>::read_block(sa, a_base[i], frow, Mma<T>::chunk(s, fhalf, c));
         else if constexpr (M16) fa[slot][i][c] = MNTileDma<BM, WAVES>::read16(sa, a_base[i], s, lane);
-        else fa[slot][i][c] = MNTileDma<BM, WAVES>::read(sa, a_base[i], s, lane);
+        else if constexpr (ES == 1) {
+          if (c == 0) MNTileDma8<BM, WAVES>::read8(sa, a_base[i], s, lane, fa[slot][i][0], fa[slot][i][1]);
+        } else fa[slot][i][c] = MNTileDma<BM, WAVES>::read(sa, a_base[i], s, lane);
       }
     }
   };
@@ -569,7 +674,9 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
       if constexpr (B_KMAJ && M16) fb[slot][j][c] = KTileDma<T, BN, WAVES>::read_block(sb, b_base[j], frow, 4 * s + fq);
       else if constexpr (B_KMAJ) fb[slot][j][c] = KTileDma<T, BN, WAVES>::read_block(sb, b_base[j], frow, Mma<T>::chunk(s, fhalf, c));
       else if constexpr (M16) fb[slot][j][c] = MNTileDma<BN, WAVES>::read16(sb, b_base[j], s, lane);
-      else fb[slot][j][c] = MNTileDma<BN, WAVES>::read(sb, b_base[j], s, lane);
+      else if constexpr (ES == 1) {
+        if (c == 0) MNTileDma8<BN, WAVES>::read8(sb, b_base[j], s, lane, fb[slot][j][0], fb[slot][j][1]);
+      } else fb[slot][j][c] = MNTileDma<BN, WAVES>::read(sb, b_base[j], s, lane);
     }
   };
   auto read_frags = [&](int stage_a, int stage_b, int s, int slot) {
@@ -588,7 +695,8 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
 #pragma unroll
       for (int r = 0; r < ACC_N; ++r) acc[i][j][r] = 0.0f;
 
-  constexpr int N_RD = (A_KMAJ ? MI * KC : 2 * MI) + (B_KMAJ ? NI * KC : 2 * NI);
+  constexpr int MN_RD = ES == 1 ? 4 : 2;   // transposing LDS reads per MN-major fragment
+  constexpr int N_RD = (A_KMAJ ? MI * KC : MN_RD * MI) + (B_KMAJ ? NI * KC : MN_RD * NI);
   constexpr int N_MMA = MI * NI;
 
   auto mma_all = [&](int slot) {
@@ -626,8 +734,8 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs p, int item, char* 
       }
     }
   };
-  constexpr int RB = B_KMAJ ? KC : 2;             // LDS reads per B fragment
-  constexpr int NRA = (A_KMAJ ? KC : 2) * MI;     // LDS reads of the A fragments of a substep
+  constexpr int RB = B_KMAJ ? KC : MN_RD;         // LDS reads per B fragment
+  constexpr int NRA = (A_KMAJ ? KC : MN_RD) * MI;  // LDS reads of the A fragments of a substep
 
   if (nk > 0) {
     if constexpr (XA) {

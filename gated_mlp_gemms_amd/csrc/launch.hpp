@@ -32,6 +32,7 @@ hipError_t run_gemm_f16_tn(DType io, int epi, TileShape tile, const GemmArgs& a,
 hipError_t run_gemm_f32(Layout layout, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
 hipError_t run_gemm_e4m3_nt(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
 hipError_t run_gemm_f8g_nt(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
+hipError_t run_gemm_f8g_tn(DType io, int epi, TileShape tile, const GemmArgs& a, int grid, hipStream_t s);
 
 // Independent GEMMs of the 16-bit backward in one launch of 8-wave 256 x 256 tiles (GemmGroup):
 // kind 0 an NN product with epilogue epi0 (EPI_STORE: dx; EPI_DGATED / EPI_DACT: the
@@ -75,8 +76,8 @@ hipError_t run_dequant_e4m3_bf16(const void* src, void* dst, int64_t n, hipStrea
 
 // fp8 codes of a [rows, cols] row-major matrix (leading dimension ld_src elements), in row-major
 // form (dst, leading dimension cols; may be NULL) and transposed (dst_t [cols, ld_t], ld_t >= rows
-// a multiple of 16, columns rows .. ld_t-1 zero; may be NULL). src_t: DT_BF16 (value v), or
-// DT_E4M3 for existing codes (copied, no scale). relu_sq: quantize max(v, 0)^2 instead of v.
+// a multiple of 16, columns rows .. ld_t-1 zero; may be NULL). src_t: DT_BF16 or DT_F32 (value
+// v). relu_sq: quantize max(v, 0)^2 instead of v.
 // e5m2: OCP E5M2 codes, else E4M3; code = fmt(v / *scale). cols must be a multiple of 16.
 hipError_t run_quantize_fp8_2d(DType src_t, const void* src, int64_t rows, int64_t cols, int64_t ld_src,
                                int relu_sq, int e5m2, const float* scale, void* dst, void* dst_t,

@@ -218,15 +218,11 @@ struct WsLayout {
   size_t xq = 0, xq_bytes = 0;          // widened e4m3 operands of the fp8 backward
   size_t w1q = 0, w1q_bytes = 0;
   size_t w2q = 0, w2q_bytes = 0;
-  // fp8-gradient backward: e5m2 dout (row-major, transposed), e5m2 dpre (row-major,
-  // transposed), e4m3 relu(pre)^2 and x transposed; transposes have M padded to Mp
-  size_t gq = 0, gq_bytes = 0, gt = 0, gt_bytes = 0, pq = 0, pq_bytes = 0, pt = 0, pt_bytes = 0;
-  size_t postt = 0, postt_bytes = 0, xt = 0, xt_bytes = 0;
+  // fp8-gradient backward, all row-major [M, width]: e5m2 dout, e5m2 dpre, e4m3 relu(pre)^2
+  size_t gq = 0, gq_bytes = 0, pq = 0, pq_bytes = 0, post = 0, post_bytes = 0;
   size_t partial = 0, partial_bytes = 0;
   size_t total = 0;
 };
-
-int64_t pad16(int64_t v) { return (v + 15) / 16 * 16; }
 
 // Small-M (decode) gated up projection: when the fused gate/up GEMM has fewer tiles than the
 // CUs, run it split along K over the stacked [W_gate; W_up] (N = 2H, 128 x 128 tiles, enough
@@ -272,11 +268,10 @@ Gemms plan_all(const mlp_desc* d) {
   Gemms g;
   g.up_split = (gated && !d->fp8_fwd) ? plan_gated_split(io, M, H, D) : Plan{TILE_128x128, 1, 0, 0, 0, 0, 0};
   g.down = plan_rows(fin, M, O, H);
-  if (d->fp8_bwd) {   // every backward product on fp8 operands; the token dimension padded
-    const int64_t Mp = pad16(M);
-    g.dw_down = plan_gemm(DT_F8G, O, H, Mp, true, false);
+  if (d->fp8_bwd) {   // every backward product on fp8 operands
+    g.dw_down = plan_gemm(DT_F8G, O, H, M, true, false);
     g.dx.main = plan_gemm(DT_F8G, M, D, H, true, false);
-    g.dw_up = plan_gemm(DT_F8G, H, D, Mp, true, false);
+    g.dw_up = plan_gemm(DT_F8G, H, D, M, true, false);
     return g;
   }
   g.dw_down = plan_gemm(io, O, H, M, true, false);
@@ -409,14 +404,10 @@ WsLayout ws_layout(const mlp_desc* d, int phase) {
     take(L.partial, L.partial_bytes,
          skinny_ok(d) ? 0 : std::max(partial_bytes(g.down, M, O), partial_bytes(g.up_split, M, 2 * H)));
   } else if (d->fp8_bwd) {
-    const int64_t Mp = pad16(M);
     if (d->recompute) take(L.pre, L.pre_bytes, (size_t)M * H * sizeof(float));
     take(L.gq, L.gq_bytes, (size_t)M * O);
-    take(L.gt, L.gt_bytes, (size_t)O * Mp);
     take(L.pq, L.pq_bytes, (size_t)M * H);
-    take(L.pt, L.pt_bytes, (size_t)H * Mp);
-    take(L.postt, L.postt_bytes, (size_t)H * Mp);
-    take(L.xt, L.xt_bytes, (size_t)D * Mp);
+    take(L.post, L.post_bytes, (size_t)M * H);
     const size_t pb = std::max({partial_bytes(g.dw_down, O, H), partial_bytes(g.dx, M, D),
                                 partial_bytes(g.dw_up, H, D)});
     take(L.partial, L.partial_bytes, pb);
@@ -450,13 +441,12 @@ mlp_status check_desc(const mlp_desc* d) {
   if (d->act < MLP_ACT_SWIGLU || d->act > MLP_ACT_RELU)
     return fail(MLP_ERR_INVALID_ARG, "act %d is not an mlp_act", d->act);
   // the GEMMs' DMA addresses are a scalar base plus a 32-bit per-lane offset of up to 64 rows of
-  // the operand: every leading dimension (d_in, d_out, the gate/up width, and the padded token
-  // count of the fp8 backward's transposed copies) must keep 64 row pitches under 4 GiB
+  // the operand: every leading dimension (d_in, d_out, the gate/up width) must keep 64 row
+  // pitches under 4 GiB
   const int64_t ld_lim = (int64_t)1 << 25;
-  if (d->d_in >= ld_lim || d->d_out >= ld_lim || (is_gated(d->act) ? 2 : 1) * d->hidden >= ld_lim ||
-      (d->fp8_bwd && d->M >= ld_lim))
-    return fail(MLP_ERR_UNSUPPORTED, "a leading dimension is 2^25 elements or more (d_in, d_out, the gate/up "
-                "width, or M with fp8_bwd): the DMA offsets are 32-bit");
+  if (d->d_in >= ld_lim || d->d_out >= ld_lim || (is_gated(d->act) ? 2 : 1) * d->hidden >= ld_lim)
+    return fail(MLP_ERR_UNSUPPORTED, "a leading dimension is 2^25 elements or more (d_in, d_out or the gate/up "
+                "width): the DMA offsets are 32-bit");
   // no matrix of the problem may exceed 2^37 elements (256 GiB in bf16, beyond one GPU's HBM): tile
   // and workgroup counts then fit an int and size arithmetic has ample headroom
   {
@@ -798,14 +788,15 @@ mlp_status scratch_address(void* stream, void** out) {
 }
 
 // Backward with fp8 gradients (ReLU^2, see mlp_fp8; the pre-activation is fp32, so the e5m2 /
-// e4m3 rounding decisions on dpre and relu(pre)^2 are taken on an fp32 value): dout -> e5m2 (row-major for the d-act
-// product, transposed for dW2); dpre_q = e5m2(dm (dout_q W2) 2 relu(pre) / s_dpre) from the
-// e5m2 x e4m3 product against the transposed W2 cache; dx = dpre_q W1 against the transposed W1
-// cache; dW1 = dpre_q^T x_q and dW2 = dm dout_q^T post_q from transposed copies (token dimension
-// zero-padded to a multiple of 16), so every product reads both operands along K.
+// e4m3 rounding decisions on dpre and relu(pre)^2 are taken on an fp32 value): dout -> e5m2
+// codes, row-major; dpre_q = e5m2(dm (dout_q W2) 2 relu(pre) / s_dpre) from the e5m2 x e4m3
+// product against the transposed W2 cache, which also writes relu(pre)^2's e4m3 codes; dx =
+// dpre_q W1 against the transposed W1 cache. The weight gradients dW1 = dpre_q^T x_q and dW2 =
+// dm dout_q^T post_q reduce over the tokens: they read the same row-major codes MN-major (the
+// 8-bit transposing LDS read), so no code is ever copied transposed.
 mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void* dx, void* dw1, void* dw2,
                    int grad_accum, const mlp_fp8* f, char* w, const WsLayout& L, const Gemms& G, hipStream_t s) {
-  const int64_t M = d->M, D = d->d_in, H = d->hidden, O = d->d_out, Mp = pad16(M);
+  const int64_t M = d->M, D = d->d_in, H = d->hidden, O = d->d_out;
   const DType gio = grad_accum ? DT_F32 : DT_BF16;
   const bool need_dpre = dx != nullptr || dw1 != nullptr;
 
@@ -828,11 +819,11 @@ mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void*
     pre = w + L.pre;
   }
   void* gq = w + L.gq;
-  void* gt = w + L.gt;
   void* pq = w + L.pq;
+  void* post_codes = w + L.post;
   if (need_dpre) {   // dpre_q = e5m2(dm (dout_q W2) 2 relu(pre) / s_dpre), max|dpre| -> dpre_amax
     StageScope st(MLP_STAGE_DACT, s);
-    MLP_TRY(hip_status(run_quantize_fp8_2d(DT_BF16, dout, M, O, O, 0, 1, f->s_grad, gq, dw2 ? gt : nullptr, Mp, s),
+    MLP_TRY(hip_status(run_quantize_fp8_2d(DT_BF16, dout, M, O, O, 0, 1, f->s_grad, gq, nullptr, 0, s),
                        "quantize dout"));
     GemmArgs a = base_args(d);
     a.A = gq;
@@ -849,7 +840,7 @@ mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void*
     a.s_post = f->s_dpre;
     a.amax = f->dpre_amax;
     if (dw2) {   // relu(pre)^2's e4m3 codes, row-major, from the pre-activation this GEMM reads
-      a.C1 = w + L.pt;   // free until dW1 transposes dpre_q into it
+      a.C1 = post_codes;
       a.ldc1 = H;
       a.s_c1 = f->s_post;
     }
@@ -857,31 +848,28 @@ mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void*
     MLP_TRY(gemm(DT_F8G, DT_F32, NT, EPI_F8DACT, p, a, M, H, O, nullptr, s, "fp8 d-activation GEMM"));
   } else if (dw2) {
     StageScope st(MLP_STAGE_DW_DOWN, s);
-    MLP_TRY(hip_status(run_quantize_fp8_2d(DT_BF16, dout, M, O, O, 0, 1, f->s_grad, nullptr, gt, Mp, s),
+    MLP_TRY(hip_status(run_quantize_fp8_2d(DT_BF16, dout, M, O, O, 0, 1, f->s_grad, gq, nullptr, 0, s),
                        "quantize dout"));
   }
   if (dw2) {   // dW2 (+)= dm dout_q^T post_q, post_q = e4m3(relu(pre)^2 / s_post)
     StageScope st(MLP_STAGE_DW_DOWN, s);
-    // transposed codes: from the d-activation GEMM's row-major ones (a 1-byte transpose), or
-    // formed here from the fp32 pre-activation when that GEMM did not run
-    if (need_dpre)
-      MLP_TRY(hip_status(run_quantize_fp8_2d(DT_E4M3, w + L.pt, M, H, H, 0, 0, nullptr, nullptr, w + L.postt, Mp, s),
-                         "transpose relu(pre)^2 codes"));
-    else
-      MLP_TRY(hip_status(run_quantize_fp8_2d(DT_F32, pre, M, H, H, 1, 0, f->s_post, nullptr, w + L.postt, Mp, s),
+    // relu(pre)^2's codes: the d-activation GEMM wrote them; without that GEMM they are formed
+    // here from the fp32 pre-activation
+    if (!need_dpre)
+      MLP_TRY(hip_status(run_quantize_fp8_2d(DT_F32, pre, M, H, H, 1, 0, f->s_post, post_codes, nullptr, 0, s),
                          "quantize relu(pre)^2"));
     GemmArgs a = base_args(d);
-    a.A = gt;
-    a.lda = Mp;
-    a.B0 = w + L.postt;
-    a.ldb = Mp;
+    a.A = gq;
+    a.lda = O;
+    a.B0 = post_codes;
+    a.ldb = H;
     a.C0 = dw2;
     a.ldc0 = H;
     a.alpha = d->down_mult;
     a.alpha_dev0 = f->s_grad;
     a.alpha_dev1 = f->s_post;
     a.accumulate = grad_accum;
-    MLP_TRY(gemm(DT_F8G, gio, NT, EPI_STORE, G.dw_down, a, O, H, Mp, w + L.partial, s, "fp8 dW_down"));
+    MLP_TRY(gemm(DT_F8G, gio, TN, EPI_STORE, G.dw_down, a, O, H, M, w + L.partial, s, "fp8 dW_down"));
   }
   if (dx) {   // dx = dpre_q W1
     GemmArgs a = base_args(d);
@@ -898,21 +886,17 @@ mlp_status bwd_fp8(const mlp_desc* d, const void* dout, const void* saved, void*
   }
   if (dw1) {   // dW1 (+)= dpre_q^T x_q
     StageScope st(MLP_STAGE_DW_UP, s);
-    MLP_TRY(hip_status(run_quantize_fp8_2d(DT_E4M3, pq, M, H, H, 0, 0, nullptr, nullptr, w + L.pt, Mp, s),
-                       "transpose dpre_q"));
-    MLP_TRY(hip_status(run_quantize_fp8_2d(DT_E4M3, f->x_q, M, D, D, 0, 0, nullptr, nullptr, w + L.xt, Mp, s),
-                       "transpose x_q"));
     GemmArgs a = base_args(d);
-    a.A = w + L.pt;
-    a.lda = Mp;
-    a.B0 = w + L.xt;
-    a.ldb = Mp;
+    a.A = pq;
+    a.lda = H;
+    a.B0 = f->x_q;
+    a.ldb = D;
     a.C0 = dw1;
     a.ldc0 = D;
     a.alpha_dev0 = f->s_dpre;
     a.alpha_dev1 = f->s_x;
     a.accumulate = grad_accum;
-    MLP_TRY(gemm(DT_F8G, gio, NT, EPI_STORE, G.dw_up, a, H, D, Mp, w + L.partial, s, "fp8 dW1"));
+    MLP_TRY(gemm(DT_F8G, gio, TN, EPI_STORE, G.dw_up, a, H, D, M, w + L.partial, s, "fp8 dW1"));
   }
   return MLP_OK;
 }
@@ -1280,6 +1264,7 @@ hipError_t run_gemm(DType in, DType io, Layout layout, int epi, TileShape tile, 
       return hipErrorInvalidValue;
     case DT_F8G:
       if (layout == NT) return run_gemm_f8g_nt(io, epi, tile, a, grid, s);
+      if (layout == TN) return run_gemm_f8g_tn(io, epi, tile, a, grid, s);
       return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;

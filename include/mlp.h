@@ -30,7 +30,7 @@
  *    multiples of 16. M >= 1 is arbitrary.
  *  - Size limits (MLP_ERR_UNSUPPORTED, before any HIP call): M, d_in, d_out < 2^30 and
  *    hidden < 2^29; every leading dimension below 2^25 elements (d_in, d_out, 2 * hidden for a
- *    gated activation or hidden otherwise, and M with fp8_bwd), since a GEMM operand is addressed
+ *    gated activation or hidden otherwise), since a GEMM operand is addressed
  *    as a base plus a 32-bit offset spanning up to 64 rows; and no matrix of the problem (x, the
  *    pre-activation, out, the weights) above 2^37 elements, more than one GPU's memory holds.
  */
@@ -209,8 +209,8 @@ mlp_status mlp_fwd_infer_noalloc(const mlp_desc* desc, const void* x, const void
  *   fp8           non-NULL iff desc->fp8_fwd: the backward GEMMs then read the dequantized
  *                 x, W1, W2 of the forward (x / w_gate / w_down are not read). With
  *                 desc->fp8_bwd they run in fp8 instead (see mlp_fp8); dpreact must then be
- *                 NULL (dpre exists only as e5m2 codes in the workspace) and M may be any
- *                 value >= 1 (the token dimension is zero-padded to a multiple of 16 inside).
+ *                 NULL (dpre exists only as e5m2 codes in the workspace); M may be any
+ *                 value >= 1.
  * Skips: with dx and dw_gate/dw_up all NULL only the down-projection gradient is formed
  * (quack's "only dW2 needed" branch); with dw_down NULL it is not.
  */

@@ -221,14 +221,15 @@ def test_size_limits():
 def test_leading_dimension_limits():
     """The GEMMs address an operand as a scalar base plus a 32-bit per-lane offset of up to 64
     row pitches, so every leading dimension stays under 2^25 elements: d_in, d_out, the stacked
-    gate/up width 2 * hidden (hidden for a non-gated activation), and M when the fp8 backward
-    keeps transposed [*, M] copies. Refused before any HIP call; one below each limit passes."""
+    gate/up width 2 * hidden (hidden for a non-gated activation). Refused before any HIP call;
+    one below each limit passes. The token count is no leading dimension (the fp8 backward's
+    weight gradients read its row-major codes along the tokens), so M = 2^25 passes."""
     big = 1 << 25
     for kw in (dict(d_in=big), dict(d_out=big), dict(hidden=big // 2), dict(act="relu_sq", hidden=big)):
         assert _fwd(_desc(**kw), nws=0) == gm._lib.MLP_ERR_UNSUPPORTED, kw
         assert "2^25" in _err()
     fp8 = dict(act="relu_sq", fp8_fwd=True, fp8_bwd=True, d_in=256, hidden=704, d_out=256)
-    assert _fwd(_desc(M=big, **fp8), nws=0) == gm._lib.MLP_ERR_UNSUPPORTED and "2^25" in _err()
+    assert _fwd(_desc(M=big, **fp8), ws=None) == gm._lib.MLP_ERR_INVALID_ARG
     # just below each limit the size checks pass and the next check (a NULL workspace) fails
     for kw in (dict(d_in=big - 8), dict(d_out=big - 8), dict(hidden=big // 2 - 8), dict(act="relu_sq", hidden=big - 8),
                dict(M=(1 << 30) - 1, d_in=16, hidden=16, d_out=16)):
@@ -253,7 +254,7 @@ def test_fp8_backward_checks():
     L = gm.lib()
     d = _desc(act="relu_sq", fp8_fwd=True, fp8_bwd=True, M=300, d_in=256, hidden=704, d_out=208)
     nws = L.mlp_workspace_bytes(C.byref(d), gm.MLP_PHASE_BWD)
-    assert nws > 300 * 704 + 704 * 304       # dpre codes, row-major and transposed (M padded to 304)
+    assert nws >= 2 * 300 * 704 + 300 * 208   # dpre and relu(pre)^2 codes, dout codes (row-major)
     full = dict(w1t_q=FAKE, w2t_q=FAKE, s_grad=FAKE, s_dpre=FAKE, dpre_amax=FAKE)
 
     def bwd(dd=d, dpre=None, ws=nws, **over):

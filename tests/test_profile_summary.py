@@ -40,22 +40,23 @@ QUANT = "_ZN4gmlp12_GLOBAL__N_116quantize8_kernelEPKvlPhPKfi"
 ABSMAX = "_ZN4gmlp12_GLOBAL__N_119absmax8_part_kernelEPKvlPf"
 DACT8 = _g(128, 128, 1, 1, 7, 4).replace("DF16bDF16b", "N4gmlp3f8gEDF16b")
 T2D = "_ZN4gmlp12_GLOBAL__N_114quant2d_kernelEPKvlllPhlPKfiiPhl"
-DW8 = _g(256, 256, 1, 1, 0, 4).replace("DF16bDF16b", "N4gmlp3f8gEDF16b")
+DW8 = _g(256, 256, 0, 0, 0, 4).replace("DF16bDF16b", "N4gmlp3f8gEDF16b")   # MN-major operands
 DX8 = _g(256, 256, 1, 1, 1, 4).replace("DF16bDF16b", "N4gmlp3f8gEf")
 
 
 def test_operand_preparation_joins_the_next_gemm():
-    # fp8 step: per-tensor quantize before the up projection, dout quantize before the
-    # d-activation, transposes before the weight-gradient products
-    step = [ABSMAX, QUANT, ACT, DOWN8, QUANT, DACT8, T2D, DW8, DX8, RED, T2D, T2D, DW8]
+    # fp8 step: per-tensor quantize before the up projection, the 2-D dout quantize before the
+    # d-activation; the weight-gradient products read the row-major codes directly
+    step = [ABSMAX, QUANT, ACT, DOWN8, T2D, DACT8, DW8, DX8, RED, DW8]
     names = step + step + [ABSMAX]
     steps = ps._per_step([(i, n, 1.0) for i, n in enumerate(names)], ps.STAGE_ORDER_GATED)
     assert len(steps) == 2
     for s in steps:
-        assert [len(s[st]) for st in ps.STAGE_ORDER_GATED] == [3, 1, 2, 2, 2, 3]
+        assert [len(s[st]) for st in ps.STAGE_ORDER_GATED] == [3, 1, 2, 1, 2, 1]
         assert [ps.short_name(n) for n, _ in s["up"]] == ["absmax8_part", "quantize8", "gemm<e4m3,NT,128x128,4w,F8ACT>"]
         assert ps.short_name(s["dx"][-1][0]) == "splitk_reduce"
     assert ps.short_name(DACT8) == "gemm<e5m2xe4m3,NT,128x128,4w,F8DACT>"
+    assert ps.short_name(DW8) == "gemm<e5m2xe4m3,TN,256x256,4w,STORE>"
 
 
 def test_recompute_gemm_is_a_stage_not_a_new_step():
