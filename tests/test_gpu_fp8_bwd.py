@@ -78,8 +78,10 @@ def _prepare(w, t):
     return r, b
 
 
+# 2900 x 3008: more than two rounds of 128 x 128 tiles, with ragged last tiles in both dimensions
 @pytest.mark.parametrize("M,d,H,do,dm", [(300, 256, 704, 208, 1.0), (129, 768, 3072, 768, 2.0),
-                                         (1, 256, 512, 256, 1.0), (1000, 128, 384, 128, 1.0)])
+                                         (1, 256, 512, 256, 1.0), (1000, 128, 384, 128, 1.0),
+                                         (2900, 256, 3008, 256, 1.0)])
 def test_fp8_backward_matches_oracle(M, d, H, do, dm):
     w = _w(M, d, H, do, down_mult=dm)
     announce(w.name)

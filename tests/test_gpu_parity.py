@@ -389,7 +389,10 @@ def _fp8_oracle_inputs(r):
     return (r.x_q.cpu().numpy(), s[0], r.w1_q.cpu().numpy(), s[1], r.w2_q.cpu().numpy(), s[2], s[3])
 
 
-@pytest.mark.parametrize("M,d,H,do,dm", [(300, 256, 704, 208, 1.0), (129, 768, 3072, 768, 2.0)])
+# 2900 x 3008: 23 x 24 tiles of 128 x 128 (more than two rounds of two per CU) with ragged last
+# tiles in both dimensions
+@pytest.mark.parametrize("M,d,H,do,dm", [(300, 256, 704, 208, 1.0), (129, 768, 3072, 768, 2.0),
+                                         (2900, 256, 3008, 256, 1.0)])
 def test_fp8_forward_small(M, d, H, do, dm):
     w = _w("relu_sq", "bf16", M, d, H, do, down_mult=dm, fp8_fwd=True)
     t = make_inputs(w)
