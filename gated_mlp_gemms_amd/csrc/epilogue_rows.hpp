@@ -183,6 +183,72 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
   }
 }
 
+// The quantizing epilogues on 16 consecutive columns n .. n+15 of row m (widths a multiple of
+// 16): the same arithmetic as epi_row8 on each half, with each tensor of 1-byte codes written
+// as one 16-byte store per lane instead of two 8-byte ones (a store instruction costs about the
+// same whatever its width). x: the pre-activation's 16 values, 4 (fp32) or 2 (16-bit) pieces.
+template <int EPI, typename IoT>
+__device__ __forceinline__ void epi_row16(const GemmArgs& p, int m, int n, const float (&v)[16],
+                                          const u32x4 (&x)[4], float& local_amax) {
+  static_assert(EPI == EPI_F8ACT || EPI == EPI_F8DACT, "the quantizing epilogues");
+  if constexpr (EPI == EPI_F8ACT) {
+    if (p.flags & 1) {
+      Vec8<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), reinterpret_cast<const float(&)[8]>(v[0]));
+      Vec8<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n + 8), reinterpret_cast<const float(&)[8]>(v[8]));
+    }
+    const float sp = *p.s_post;
+    const float rp = __fdiv_rn(1.0f, sp);
+    float post[16], y[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float t = fmaxf(v[r], 0.0f);
+      post[r] = t * t;
+      local_amax = fmaxf(local_amax, post[r]);
+    }
+    quot_rn_n<16>(post, sp, rp, y);
+    *reinterpret_cast<u32x4*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) =
+        u32x4{f32x4_to_fp8<false>(y[0], y[1], y[2], y[3]), f32x4_to_fp8<false>(y[4], y[5], y[6], y[7]),
+              f32x4_to_fp8<false>(y[8], y[9], y[10], y[11]), f32x4_to_fp8<false>(y[12], y[13], y[14], y[15])};
+  } else {
+    float pre[16];
+    if constexpr (ElemTraits<IoT>::bytes == 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pre[4 * k + r] = __uint_as_float(x[k][r]);
+    } else {
+      unpack16x8<IoT>(x[0], reinterpret_cast<float(&)[8]>(pre[0]));
+      unpack16x8<IoT>(x[1], reinterpret_cast<float(&)[8]>(pre[8]));
+    }
+    const float sd = *p.s_post;
+    const float rd = __fdiv_rn(1.0f, sd);
+    float dpre[16], y[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dpre[r] = v[r] * (2.0f * fmaxf(pre[r], 0.0f));
+      local_amax = fmaxf(local_amax, __builtin_fabsf(dpre[r]));
+    }
+    quot_rn_n<16>(dpre, sd, rd, y);
+    *reinterpret_cast<u32x4*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) =
+        u32x4{f32x4_to_fp8<true>(y[0], y[1], y[2], y[3]), f32x4_to_fp8<true>(y[4], y[5], y[6], y[7]),
+              f32x4_to_fp8<true>(y[8], y[9], y[10], y[11]), f32x4_to_fp8<true>(y[12], y[13], y[14], y[15])};
+    if (p.C1) {   // relu(pre)^2 codes for dW2, the arithmetic of the 2-D quantizer's relu^2 mode
+      const float sp = *p.s_c1;
+      const float rp = __fdiv_rn(1.0f, sp);
+      float post[16], z[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float t = fmaxf(pre[r], 0.0f);
+        post[r] = t * t;
+      }
+      quot_rn_n<16>(post, sp, rp, z);
+      *reinterpret_cast<u32x4*>(elem_ptr<e4m3>(p.C1, m, p.ldc1, n)) =
+          u32x4{f32x4_to_fp8<false>(z[0], z[1], z[2], z[3]), f32x4_to_fp8<false>(z[4], z[5], z[6], z[7]),
+                f32x4_to_fp8<false>(z[8], z[9], z[10], z[11]), f32x4_to_fp8<false>(z[12], z[13], z[14], z[15])};
+    }
+  }
+}
+
 // Rows of a block-row staged per round: 32 with 4 waves, 16 with 8 (the staging of all waves
 // must fit the ring's LDS).
 template <int WAVES> constexpr int epilogue_rows_per_round() { return WAVES == 8 ? 16 : 32; }
@@ -205,7 +271,11 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& p, AccV (&acc)[MI]
   constexpr int RR = epilogue_rows_per_round<WAVES>();   // rows staged per round
   constexpr int STRIDE = WN * 4 + 16;                 // padded: rows 16 bytes apart in bank space
   constexpr int UNITS = GATED ? WN / 2 : WN;          // output columns of the wave
-  constexpr int LPR = UNITS / 8;                      // lanes per row
+  // columns per lane: 16 for the quantizing epilogues (16-byte code stores), except where the
+  // pre-activation it stores is fp32 (16 fp32 columns per lane spread each store instruction over
+  // twice the rows; measured slower), else 8
+  constexpr int PW = (EPI == EPI_F8DACT || (EPI == EPI_F8ACT && ElemTraits<IoT>::bytes == 2)) ? 16 : 8;
+  constexpr int LPR = UNITS / PW;                     // lanes per row
   constexpr int RPI = 64 / LPR;                       // rows per pass
   static_assert(RR % RPI == 0, "passes must cover a round's rows");
   static_assert(RR <= BLK, "a round stays within one block row");
@@ -219,17 +289,27 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& p, AccV (&acc)[MI]
   float local_amax = 0.0f;
 
   const int nbase = GATED ? n0 + wn * (WN / 2) : n0 + wn * WN;
-  const int rl = lane / LPR, cl = (lane % LPR) * 8;       // this lane's row-in-pass / column
+  const int rl = lane / LPR, cl = (lane % LPR) * PW;      // this lane's row-in-pass / column
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int h = 0; h < BLK / RR; ++h) {
       const int mrow0 = m0 + wm * WM + i * BLK + h * RR;
-      AuxPiece x[RR / RPI];
+      AuxPiece x[PW == 8 ? RR / RPI : 1];
+      u32x4 x16[PW == 16 ? RR / RPI : 1][4];   // 16-wide: the pre-activation's pieces
 #pragma unroll
       for (int pass = 0; pass < RR / RPI; ++pass) {
         const int m = mrow0 + pass * RPI + rl, n = nbase + cl;
-        if (m < p.M && n < p.N) epi_prefetch<EPI, IoT>(p, m, n, x[pass]);
+        if constexpr (PW == 16) {
+          if (EPI == EPI_F8DACT && m < p.M && n < p.N) {
+            constexpr int NP = ElemTraits<IoT>::bytes == 4 ? 4 : 2;   // 16-byte pieces of 16 values
+#pragma unroll
+            for (int k = 0; k < NP; ++k)
+              x16[pass][k] = *reinterpret_cast<const u32x4*>(elem_ptr<IoT>(p.aux, m, p.ld_aux, n + k * 16 / ElemTraits<IoT>::bytes));
+          }
+        } else {
+          if (m < p.M && n < p.N) epi_prefetch<EPI, IoT>(p, m, n, x[pass]);
+        }
       }
       // MFMA layout -> LDS rows: lanes whose row falls in this round write columns
       // j*32 + 8g + 4*fhalf .. +3 of row (frow - h*RR)
@@ -256,19 +336,31 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& p, AccV (&acc)[MI]
         const int r = pass * RPI + rl;
         const int m = mrow0 + r;
         const int n = nbase + cl;
-        float v[8], u[8];
-        const f32x4* src = reinterpret_cast<const f32x4*>(wbuf + r * STRIDE + cl * 4);
-        f32x4 a0 = src[0], a1 = src[1];
+        if constexpr (PW == 16) {
+          float v16[16];
+          const f32x4* src = reinterpret_cast<const f32x4*>(wbuf + r * STRIDE + cl * 4);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) { v[q] = a0[q]; v[4 + q] = a1[q]; }
-        if constexpr (GATED) {
-          const f32x4* su = reinterpret_cast<const f32x4*>(wbuf + r * STRIDE + (UNITS + cl) * 4);
-          a0 = su[0];
-          a1 = su[1];
+          for (int k = 0; k < 4; ++k) {
+            const f32x4 a = src[k];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) { u[q] = a0[q]; u[4 + q] = a1[q]; }
+            for (int q = 0; q < 4; ++q) v16[4 * k + q] = a[q];
+          }
+          if (m < p.M && n < p.N) epi_row16<EPI, IoT>(p, m, n, v16, x16[pass], local_amax);
+        } else {
+          float v[8], u[8];
+          const f32x4* src = reinterpret_cast<const f32x4*>(wbuf + r * STRIDE + cl * 4);
+          f32x4 a0 = src[0], a1 = src[1];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { v[q] = a0[q]; v[4 + q] = a1[q]; }
+          if constexpr (GATED) {
+            const f32x4* su = reinterpret_cast<const f32x4*>(wbuf + r * STRIDE + (UNITS + cl) * 4);
+            a0 = su[0];
+            a1 = su[1];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { u[q] = a0[q]; u[4 + q] = a1[q]; }
+          }
+          if (m < p.M && n < p.N) epi_row8<EPI, IoT>(p, m, n, split, v, u, x[pass], local_amax);
         }
-        if (m < p.M && n < p.N) epi_row8<EPI, IoT>(p, m, n, split, v, u, x[pass], local_amax);
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);       // reads done before the next round's writes
       __builtin_amdgcn_wave_barrier();
