@@ -46,6 +46,14 @@ hipError_t run_gemm_group16(DType in, DType gio, int epi0, const GemmGroup& g, h
 // GEMM kernels (bit 0: the pre-activation into aux, bit 1: the activation into C0).
 constexpr int kSkinnyMaxRows = 16;
 hipError_t run_skinny(DType in, int epi, const GemmArgs& a, hipStream_t s);
+// EPI_PARTIAL: the store product with K split over kSkinnyParts workgroups per column block,
+// unscaled fp32 partial sums into a.partial [kSkinnyParts][M][N] (then the split-K reduce).
+// Taken above 8 tokens for narrow outputs with a long K (skinny_parts_for), where the whole-K
+// form has few column blocks and each of them re-reads all of the token rows. LLaMA widths, same
+// box: 16 tokens 60.8 -> 57.5 us per inference forward; 8 and 1 tokens 54.3 -> 56.4 and 48.6 ->
+// 53.1 us (few token rows to save, one more launch), hence the threshold.
+constexpr int kSkinnyParts = 4;
+inline bool skinny_parts_for(int64_t M, int64_t N, int64_t K) { return M > 8 && N <= 8192 && K >= 2048; }
 
 // out = alpha * sum_s partial[s] (fixed order), stored as `io` or added into fp32 (accumulate).
 // Rows >= c_split go to C1 (row - c_split).

@@ -402,7 +402,8 @@ WsLayout ws_layout(const mlp_desc* d, int phase) {
   if (phase == MLP_PHASE_FWD || phase == MLP_PHASE_FWD_INFER) {
     take(L.act, L.act_bytes, (size_t)M * H * (d->fp8_fwd ? 1 : es));
     take(L.partial, L.partial_bytes,
-         skinny_ok(d) ? 0 : std::max(partial_bytes(g.down, M, O), partial_bytes(g.up_split, M, 2 * H)));
+         skinny_ok(d) ? (skinny_parts_for(M, O, H) ? (size_t)kSkinnyParts * M * O * sizeof(float) : 0)
+                      : std::max(partial_bytes(g.down, M, O), partial_bytes(g.up_split, M, 2 * H)));
   } else if (d->fp8_bwd) {
     if (d->recompute) take(L.pre, L.pre_bytes, (size_t)M * H * sizeof(float));
     take(L.gq, L.gq_bytes, (size_t)M * O);
@@ -739,7 +740,17 @@ mlp_status fwd_run(const mlp_desc* d, const void* x, const void* wg, const void*
     b.alpha_dev1 = f->s_w2;
   }
   StageScope st(MLP_STAGE_DOWN, s);
-  if (skinny_ok(d)) return hip_status(run_skinny(io, EPI_STORE, planned(b, Plan{}, M, O, H), s), "down projection (small M)");
+  if (skinny_ok(d)) {
+    if (skinny_parts_for(M, O, H)) {   // K split over workgroups, then the fixed-order reduce
+      GemmArgs c = planned(b, Plan{}, M, O, H);
+      c.partial = reinterpret_cast<float*>(w + L.partial);
+      MLP_TRY(hip_status(run_skinny(io, EPI_PARTIAL, c, s), "down projection (small M, K parts)"));
+      return hip_status(run_splitk_reduce(io, c.partial, kSkinnyParts, (int)M, (int)O, out, nullptr, O, c.c_split,
+                                          c.alpha, c.alpha_dev0, c.alpha_dev1, 0, s),
+                        "down projection (small M, reduce)");
+    }
+    return hip_status(run_skinny(io, EPI_STORE, planned(b, Plan{}, M, O, H), s), "down projection (small M)");
+  }
   const RowsPlan p = plan_all(d).down;
   return gemm_rows(fin, io, NT, p, b, M, O, H, w + L.partial, s, "down projection");
 }

@@ -12,7 +12,9 @@
 //    first wave runs the epilogue: store, activation, or gated activation (and the pre-activation
 //    when training), with the same activation functions as the GEMM epilogues.
 // Above 8 tokens the gated product takes a second form (skinny_gated_lds_kernel below) that
-// stages the token rows in LDS once per workgroup and shares them between column blocks.
+// stages the token rows in LDS once per workgroup and shares them between column blocks, and a
+// narrow store product with a long K (the down projection) splits K over workgroups into fp32
+// partials for the split-K reduce, so that each workgroup reads a quarter of the token rows.
 #include "common.hpp"
 #include "gemm_kernel.hpp"
 #include "launch.hpp"
@@ -25,16 +27,21 @@ constexpr int kKBlock = 128;       // K per block: four lane groups x 32
 constexpr int kTwoBlocksFrom = 1024;   // output column blocks of 16 from which a workgroup takes two
 
 // NCB column blocks of 16 units per workgroup (more units share each load of the token rows);
-// NBUF blocks of loads in flight per wave.
-template <typename T, int EPI, int WAVES, int NCB, int NBUF>
+// NBUF blocks of loads in flight per wave. KQ > 1 (EPI_PARTIAL): workgroup b takes part b % KQ
+// of K (in 128-wide blocks) for the column blocks of b / KQ and writes unscaled fp32 partial
+// sums, partial[part][token][unit], for the fixed-order split-K reduce; a workgroup then reads
+// the token rows of its part only, so per unit of weights streamed it reads KQ x fewer of them.
+template <typename T, int EPI, int WAVES, int NCB, int NBUF, int KQ = 1>
 __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const GemmArgs p) {
+  static_assert((KQ > 1) == (EPI == EPI_PARTIAL), "K parts across workgroups write partial sums");
   constexpr bool GATED = EPI == EPI_GATED;
   constexpr int NB = GATED ? 2 : 1;   // weight matrices read: gate and up, or one
   constexpr int NACC = NB * NCB;
   __shared__ f32x4 red[WAVES][NACC][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
-  const int nbase = blockIdx.x * 16 * NCB + r;   // this lane's weight row in column block 0
+  const int part = KQ > 1 ? (int)(blockIdx.x % KQ) : 0;
+  const int nbase = (KQ > 1 ? (int)(blockIdx.x / KQ) : (int)blockIdx.x) * 16 * NCB + r;   // weight row, block 0
   const bool tok_ok = r < p.M;
   const char* xrow = reinterpret_cast<const char*>(elem_ptr<T>(p.A, tok_ok ? r : 0, p.lda, 0));
   const char* wrow[NB][NCB];
@@ -46,11 +53,12 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const GemmArgs p) {
     wrow[0][cb] = reinterpret_cast<const char*>(elem_ptr<T>(p.B0, row_ok[cb] ? n : 0, p.ldb, 0));
     if constexpr (GATED) wrow[1][cb] = reinterpret_cast<const char*>(elem_ptr<T>(p.B1, row_ok[cb] ? n : 0, p.ldb, 0));
   }
-  const int nblk = (p.K + kKBlock - 1) / kKBlock;
-  const int b0 = wave * nblk / WAVES, nb = (wave + 1) * nblk / WAVES - b0;
+  const int nblk_all = (p.K + kKBlock - 1) / kKBlock;
+  const int kb0 = part * nblk_all / KQ, nblk = (part + 1) * nblk_all / KQ - kb0;   // this part's blocks
+  const int b0 = kb0 + wave * nblk / WAVES, nb = kb0 + (wave + 1) * nblk / WAVES - b0;
   // each workgroup walks its waves' K ranges from a different block: every workgroup reads the
   // same token rows, and a common order would send all of them to the same lines at once
-  const int rot = nb > 0 ? (int)(blockIdx.x % (unsigned)nb) : 0;
+  const int rot = nb > 0 ? (int)((blockIdx.x / KQ) % (unsigned)nb) : 0;
   auto blk = [&](int i) { const int j = i + rot; return b0 + (j >= nb ? j - nb : j); };
 
   u32x4 xa[NBUF][4], wa[NBUF][NB][NCB][4];
@@ -103,6 +111,22 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const GemmArgs p) {
   for (int j = 0; j < NACC; ++j) red[wave][j][lane] = acc[j];
   __syncthreads();
   if (wave != 0) return;
+  if constexpr (EPI == EPI_PARTIAL) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      if (!row_ok[cb]) continue;
+      const int n = nbase + 16 * cb;
+      f32x4 s0 = red[0][cb][lane];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) s0 += red[w][cb][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {   // lane l holds tokens 4 q + i of unit n
+        const int t = 4 * q + i;
+        if (t < p.M) p.partial[((int64_t)part * p.M + t) * p.N + n] = s0[i];
+      }
+    }
+    return;
+  }
   float alpha = p.alpha;
   if (p.alpha_dev0) alpha *= *p.alpha_dev0;
   if (p.alpha_dev1) alpha *= *p.alpha_dev1;
@@ -306,12 +330,24 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The store product split along K over workgroups into fp32 partials (a.partial, [parts][M][N]),
+// parts = kSkinnyParts; the caller runs the split-K reduce.
+template <typename T>
+hipError_t launch_skinny_parts(const GemmArgs& a, hipStream_t s) {
+  constexpr int NCB = 4, W = 4;
+  const int groups = (a.N + 16 * NCB - 1) / (16 * NCB);
+  hipLaunchKernelGGL((skinny_kernel<T, EPI_PARTIAL, W, NCB, 3, kSkinnyParts>), dim3(groups * kSkinnyParts),
+                     dim3(64 * W), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t skinny_epi(int epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
     case EPI_STORE: return launch_skinny<T, EPI_STORE>(a, s);
     case EPI_ACT: return launch_skinny<T, EPI_ACT>(a, s);
     case EPI_GATED: return launch_skinny<T, EPI_GATED>(a, s);
+    case EPI_PARTIAL: return launch_skinny_parts<T>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -235,8 +235,12 @@ SKINNY = [
     # x 4 parts of K; K = 1000 ends in a partial block, 1000 units in a partial workgroup of 48
     _w("swiglu", "bf16", 11, 1000, 1000, 72, gate_mult=1.125, down_mult=2.0, seed=25),
     # 10 tokens, K = 2056 for the gated product (LDS-staged, 5000 units), K = 5000 for the down
-    # projection (the x-streaming kernel: partial last blocks, 2056 outputs)
+    # projection (above 8 tokens split in 4 parts of K over workgroups, then the split-K reduce:
+    # partial last blocks, 2056 outputs)
     _w("swiglu", "bf16", 10, 2056, 5000, 2056, down_mult=1.5, seed=26),
+    # 12 tokens of ReLU^2: the down projection's 4 parts of K = 3080 (25 blocks, the last partial)
+    # over 264 outputs (a partial group of 64)
+    _w("relu_sq", "bf16", 12, 776, 3080, 264, down_mult=1.5, seed=27),
 ]
 
 
