@@ -133,6 +133,23 @@ def test_workspace_sizes():
         assert b1 == b0 >= 300 * 704 * es + 300 * 2 * 704 * es
 
 
+def test_small_m_workspace_holds_the_down_projection_parts():
+    """Up to 16 tokens every forward product runs on the small-M kernel, which needs no split-K
+    partials, except that above 8 tokens a narrow down projection with a long K (LLaMA: 4096
+    outputs, K = 11008) is split over 4 parts of K into fp32 partials [4][M][d_out]."""
+    L = gm.lib()
+    llama = dict(d_in=4096, hidden=11008, d_out=4096)
+    for phase in (gm.MLP_PHASE_FWD, gm.MLP_PHASE_FWD_INFER):
+        for M in (1, 8, 9, 16):
+            ws = L.mlp_workspace_bytes(C.byref(_desc(M=M, **llama)), phase)
+            act = M * 11008 * 2   # the [M, H] bf16 activation
+            parts = 4 * M * 4096 * 4 if M > 8 else 0
+            assert act + parts <= ws < act + parts + 4096, (phase, M, ws)
+    # a short K keeps the whole-K form
+    ws = L.mlp_workspace_bytes(C.byref(_desc(M=16, d_in=256, hidden=1000, d_out=256)), gm.MLP_PHASE_FWD_INFER)
+    assert ws < 16 * 1000 * 2 + 4096
+
+
 def test_quantize_checks():
     L = gm.lib()
     assert L.mlp_quantize_e4m3(FAKE, 1, 0, FAKE, FAKE, FAKE, 256, None) == gm._lib.MLP_ERR_INVALID_ARG
