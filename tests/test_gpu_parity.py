@@ -241,6 +241,9 @@ SKINNY = [
     # 12 tokens of ReLU^2: the down projection's 4 parts of K = 3080 (25 blocks, the last partial)
     # over 264 outputs (a partial group of 64)
     _w("relu_sq", "bf16", 12, 776, 3080, 264, down_mult=1.5, seed=27),
+    # 9 tokens in fp16: the K-part down projection (K = 2056: 17 blocks, 4 uneven parts) and its
+    # reduce in fp16
+    _w("swiglu", "f16", 9, 264, 2056, 136, gate_mult=0.75, seed=28),
 ]
 
 
