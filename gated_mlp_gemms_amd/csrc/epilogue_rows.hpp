@@ -51,10 +51,8 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& p, int m, int n, Au
   if constexpr (EPI == EPI_DGATED) {
     x.a = *reinterpret_cast<const u32x4*>(elem_ptr<IoT>(p.aux, m, p.ld_aux, n));
     x.b = *reinterpret_cast<const u32x4*>(elem_ptr<IoT>(p.aux, m, p.ld_aux, p.half + n));
-  } else if constexpr (EPI == EPI_DACT || EPI == EPI_F8DACT) {
+  } else if constexpr (EPI == EPI_DACT) {
     x.a = *reinterpret_cast<const u32x4*>(elem_ptr<IoT>(p.aux, m, p.ld_aux, n));
-    if constexpr (ElemTraits<IoT>::bytes == 4)   // fp32 pre-activation: 8 values in two pieces
-      x.c = *reinterpret_cast<const u32x4*>(elem_ptr<IoT>(p.aux, m, p.ld_aux, n + 4));
   } else if constexpr (EPI == EPI_STORE) {
     if (p.accumulate) {
       const bool lo = m < p.c_split;
@@ -76,10 +74,12 @@ __device__ __forceinline__ void unpack16x8(const u32x4 x, float (&v)[8]) {
 
 // The epilogue function on 8 consecutive columns n .. n+7 of row m. v = alpha * acc (or the
 // raw accumulator for split-K partials); u = the up-projection values for the gated epilogue;
-// x = what epi_prefetch fetched for this piece.
+// x = what epi_prefetch fetched for this piece. (The quantizing epilogues take 16 columns:
+// epi_row16.)
 template <int EPI, typename IoT>
 __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int split, const float (&v)[8],
                                          const float (&u)[8], const AuxPiece& x, float& local_amax) {
+  static_assert(EPI != EPI_F8ACT && EPI != EPI_F8DACT, "the quantizing epilogues are 16 columns wide");
   if constexpr (EPI == EPI_STORE) {
     const bool lo = m < p.c_split;
     void* base = lo ? p.C0 : p.C1;
@@ -134,60 +134,14 @@ __device__ __forceinline__ void epi_row8(const GemmArgs& p, int m, int n, int sp
     for (int r = 0; r < 8; ++r) dpre[r] *= v[r];
     Vec8<IoT>::store(elem_ptr<IoT>(p.C0, m, p.ldc0, n), dpre);
     if (p.flags & 2) Vec8<IoT>::store(elem_ptr<IoT>(p.C1, m, p.ldc1, n), post);
-  } else if constexpr (EPI == EPI_F8ACT) {
-    if (p.flags & 1) Vec8<IoT>::store(elem_ptr<IoT>(p.aux, m, p.ld_aux, n), v);
-    const float sp = *p.s_post;
-    const float rp = __fdiv_rn(1.0f, sp);
-    float post[8], y[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float t = fmaxf(v[r], 0.0f);
-      post[r] = t * t;
-      local_amax = fmaxf(local_amax, post[r]);
-    }
-    quot_rn_n<8>(post, sp, rp, y);
-    *reinterpret_cast<u32x2*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) =
-        u32x2{f32x4_to_fp8<false>(y[0], y[1], y[2], y[3]), f32x4_to_fp8<false>(y[4], y[5], y[6], y[7])};
-  } else if constexpr (EPI == EPI_F8DACT) {
-    float pre[8];
-    if constexpr (ElemTraits<IoT>::bytes == 4) {   // fp32 pre-activation (the fp8-gradient backward)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) { pre[r] = __uint_as_float(x.a[r]); pre[4 + r] = __uint_as_float(x.c[r]); }
-    } else {
-      unpack16x8<IoT>(x.a, pre);
-    }
-    const float sd = *p.s_post;
-    const float rd = __fdiv_rn(1.0f, sd);
-    float dpre[8], y[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      dpre[r] = v[r] * (2.0f * fmaxf(pre[r], 0.0f));
-      local_amax = fmaxf(local_amax, __builtin_fabsf(dpre[r]));
-    }
-    quot_rn_n<8>(dpre, sd, rd, y);
-    *reinterpret_cast<u32x2*>(elem_ptr<e4m3>(p.C0, m, p.ldc0, n)) =
-        u32x2{f32x4_to_fp8<true>(y[0], y[1], y[2], y[3]), f32x4_to_fp8<true>(y[4], y[5], y[6], y[7])};
-    if (p.C1) {   // relu(pre)^2 codes for dW2, the arithmetic of the 2-D quantizer's relu^2 mode
-      const float sp = *p.s_c1;
-      const float rp = __fdiv_rn(1.0f, sp);
-      float post[8], z[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float t = fmaxf(pre[r], 0.0f);
-        post[r] = t * t;
-      }
-      quot_rn_n<8>(post, sp, rp, z);
-      *reinterpret_cast<u32x2*>(elem_ptr<e4m3>(p.C1, m, p.ldc1, n)) =
-          u32x2{f32x4_to_fp8<false>(z[0], z[1], z[2], z[3]), f32x4_to_fp8<false>(z[4], z[5], z[6], z[7])};
-    }
   }
 }
 
 // The quantizing epilogues on 16 consecutive columns n .. n+15 of row m (widths a multiple of
-// 16): the same arithmetic as epi_row8 on each half, with each tensor of 1-byte codes written
-// as one 16-byte store per lane instead of two 8-byte ones (a store instruction costs about the
-// same whatever its width). x: the pre-activation's 16 values, 4 (fp32) or 2 (16-bit) pieces.
-// The e4m3 forward's fp32 pre-activation is stored by the caller, in a layout of its own.
+// 16), so that each tensor of 1-byte codes is written as one 16-byte store per lane (two 8-byte
+// stores cost about twice one: a store instruction costs about the same whatever its width).
+// x: the pre-activation's 16 values (F8DACT), 4 (fp32) or 2 (16-bit) 16-byte pieces. The e4m3
+// forward's fp32 pre-activation is stored by the caller, in a layout of its own.
 template <int EPI, typename IoT>
 __device__ __forceinline__ void epi_row16(const GemmArgs& p, int m, int n, const float (&v)[16],
                                           const u32x4 (&x)[4], float& local_amax) {
