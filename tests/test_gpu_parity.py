@@ -580,12 +580,13 @@ def _capture(fn):
     return g
 
 
-@pytest.mark.parametrize("M", [1, 16, 300])
-def test_graph_replay_of_inference_forward(M):
+# (12, 2056): the small-M down projection split over parts of K, then the split-K reduce
+@pytest.mark.parametrize("M,H", [(1, 712), (16, 712), (300, 712), (12, 2056)])
+def test_graph_replay_of_inference_forward(M, H):
     """mlp_fwd_infer captured in a graph (no allocation, no memset node, no host sync inside):
     every replay equals the eager call, with new inputs copied in eagerly between replays."""
-    w = _w("swiglu", "bf16", M, 264, 712, 200, gate_mult=1.125, down_mult=2.0)
-    announce(f"graph replay, inference forward, M={M}")
+    w = _w("swiglu", "bf16", M, 264, H, 200, gate_mult=1.125, down_mult=2.0)
+    announce(f"graph replay, inference forward, M={M}, H={H}")
     t = make_inputs(w)
     r = run(w, t)
     xs = [r.x.clone(), (r.x * 0.5).contiguous(), torch.flip(r.x, [0]).contiguous()]
