@@ -45,10 +45,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
-
 // The 16-bit storage types as bits: to fp32 exactly, from fp32 rounded to nearest even (fp16:
 // the hardware conversion in the default rounding mode; beyond +-65504 it gives +-inf).
 template <typename T> struct Bits16;

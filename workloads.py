@@ -102,10 +102,6 @@ HEADLINE = "llama_swiglu_bf16_m2048_d4096_h11008"
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
-def torch_dtype(name: str) -> torch.dtype:
-    return _TORCH_DTYPE[name]
-
-
 def _to_storage(a: np.ndarray, dtype: str, shape) -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(a.astype(np.float32))).reshape(shape)
     return t.to(_TORCH_DTYPE[dtype]).contiguous()
